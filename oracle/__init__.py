@@ -1,0 +1,159 @@
+"""Independent CPU reference ("oracle") for paged decode attention and its companions.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package. The product library
+never loads it, and the two share no code: the only thing both sides use is the
+seeded input generator in :mod:`workloads`.
+
+Two implementations live here:
+  * ``oracle.c`` (loaded through ctypes): the fp64 token-by-token walk of the
+    block table, two-pass softmax, OpenMP over (sequence, query head); plus the
+    slot-mapped append and the whole-block copy. This is the reference the GPU
+    results are compared with.
+  * :mod:`oracle.dense` (NumPy, fp64): gather each sequence's blocks into a
+    contiguous K/V, then softmax(q K^T * scale) V. A brute-force cross-check of
+    the C walk on small inputs.
+Both are pinned by the CPU test-suite to things other than themselves: the
+worked example of the pages, closed forms, invariants, a library attention
+routine, and planted mistakes that must fail.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from .dense import dense_attention  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+
+
+def _load(path: Optional[str] = None):
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from .build import build
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _bind(lib):
+    lib.oracle_paged_attention.restype = _I
+    lib.oracle_paged_attention.argtypes = [_P, _P, _P, _P, _I, _P, _P, ctypes.c_double, _I, _I,
+                                           _I, _I, _I, _I, _I, _P, _I, _I]
+    lib.oracle_reshape_and_cache.restype = _I
+    lib.oracle_reshape_and_cache.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I]
+    lib.oracle_copy_blocks.restype = _I
+    lib.oracle_copy_blocks.argtypes = [_P, _P, _I, _I, ctypes.c_long]
+    lib.oracle_decode.restype = _I
+    lib.oracle_decode.argtypes = [_P, _P, ctypes.c_long, _I]
+    lib.oracle_max_threads.restype = _I
+    return lib
+
+
+def _raw(t: torch.Tensor) -> np.ndarray:
+    """Host bytes of a tensor as a contiguous NumPy array (bf16/f16 as raw int16)."""
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16).numpy()
+    return t.numpy()
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def decode(t: torch.Tensor, lib=None) -> np.ndarray:
+    """Element values of a float32/bfloat16/float16 tensor as float64 (C decoder)."""
+    lib = lib or _load()
+    raw = _raw(t)
+    out = np.empty(raw.size, dtype=np.float64)
+    rc = lib.oracle_decode(_ptr(out), _ptr(raw), raw.size, DTYPE_CODE[t.dtype])
+    if rc != 0:
+        raise ValueError(f"oracle_decode failed ({rc})")
+    return out.reshape(tuple(t.shape))
+
+
+def paged_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                    rows: Optional[Sequence[Tuple[int, int]]] = None, threads: int = 0,
+                    lib=None) -> np.ndarray:
+    """fp64 paged decode attention. Returns [B, Hq, D], or [len(rows), D] for the
+    (sequence, head) pairs in ``rows``."""
+    lib = lib or _load()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,Hq,D] and caches [num_blocks,Hkv,bs,D]")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q and caches must share a dtype")
+    B, Hq, D = q.shape
+    NB, Hkv, bs, D2 = k_cache.shape
+    if D2 != D:
+        raise ValueError("head_dim mismatch")
+    qa, ka, va = _raw(q), _raw(k_cache), _raw(v_cache)
+    tables = np.ascontiguousarray(block_tables.to("cpu", torch.int32).numpy())
+    ctx = np.ascontiguousarray(context_lens.to("cpu", torch.int32).numpy())
+    mb = tables.shape[1] if tables.ndim == 2 else 0
+    if rows is not None:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
+        out = np.zeros((r.shape[0], D), dtype=np.float64)
+        rp, nr = _ptr(r), r.shape[0]
+    else:
+        out = np.zeros((B, Hq, D), dtype=np.float64)
+        rp, nr = None, 0
+    rc = lib.oracle_paged_attention(_ptr(out), _ptr(qa), _ptr(ka), _ptr(va),
+                                    DTYPE_CODE[q.dtype], _ptr(tables), _ptr(ctx),
+                                    float(scale), B, Hq, Hkv, D, bs, mb, NB, rp, nr,
+                                    int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_paged_attention rejected its inputs ({rc})")
+    return out
+
+
+def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, slot_mapping: torch.Tensor, lib=None):
+    """Expected pools after the slot-mapped append (new CPU tensors)."""
+    lib = lib or _load()
+    T, Hkv, D = k.shape
+    NB, Hkv2, bs, D2 = k_cache.shape
+    if (Hkv2, D2) != (Hkv, D) or v.shape != k.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    kc = k_cache.detach().to("cpu").clone().contiguous()
+    vc = v_cache.detach().to("cpu").clone().contiguous()
+    ka, va = _raw(k), _raw(v)
+    kca, vca = _raw(kc), _raw(vc)   # views of kc/vc's storage
+    slots = np.ascontiguousarray(slot_mapping.to("cpu", torch.int64).numpy())
+    rc = lib.oracle_reshape_and_cache(_ptr(ka), _ptr(va), _ptr(kca), _ptr(vca), _ptr(slots), T,
+                                      Hkv, D, bs, NB, k.element_size())
+    if rc != 0:
+        raise ValueError(f"oracle_reshape_and_cache rejected its inputs ({rc})")
+    return kc, vc
+
+
+def copy_blocks(cache: torch.Tensor, pairs: torch.Tensor, lib=None) -> torch.Tensor:
+    """Expected pool after copying each (src, dst) block pair (a new CPU tensor)."""
+    lib = lib or _load()
+    c = cache.detach().to("cpu").clone().contiguous()
+    ca = _raw(c)
+    p = np.ascontiguousarray(pairs.to("cpu", torch.int32).numpy().reshape(-1, 2))
+    block_bytes = c[0].numel() * c.element_size() if c.shape[0] else 0
+    rc = lib.oracle_copy_blocks(_ptr(ca), _ptr(p), p.shape[0], c.shape[0], block_bytes)
+    if rc != 0:
+        raise ValueError(f"oracle_copy_blocks rejected its inputs ({rc})")
+    return c

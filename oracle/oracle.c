@@ -1,0 +1,206 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for paged decode attention and the
+ * two KV-cache companions (slot-mapped append, whole-block copy).
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or call
+ * this code; it exists so that tests, the smoke check and the benchmark's CPU
+ * baseline can compare the GPU library with an independent implementation. It
+ * shares no source, header, table or helper with the GPU library.
+ *
+ * Pages followed (titles as published):
+ *   [P1] "vLLM 源码解析：PagedAttention 如何让大模型推理提速 10 倍"
+ *   [P2] "vLLM 核心源码深度解析：PagedAttention 的 KV Cache 管理、Scheduler 调度引擎与
+ *         Continuous Batching 实现全解"
+ *   [P3] "论文专题讲解：vLLM / PagedAttention：为什么 KV cache 需要分页管理"
+ *
+ * What is computed is the plain definition, not an algorithm replica: paged
+ * attention gives exactly the attention of the query over its whole context; only
+ * where the keys and values sit in memory differs ([P3] "PagedAttention：逻辑连续，
+ * 物理不必连续": the query at position i attends tokens 1..i, read block by block;
+ * [P1] section 四: per query, walk its physical blocks through the page table).
+ * So for each sequence b and query head h:
+ *   token t (0-based) of b lives in physical block tables[b][t / bs] at offset
+ *   t % bs ([P2] "Block Table 数据结构": block number = position // block_size,
+ *   offset = position % block_size, physical = block_table[block number]);
+ *   s[t]  = scale * sum_d q[b,h,d] * K[t,d]
+ *   out   = sum_t exp(s[t] - max s) V[t,:] / sum_t exp(s[t] - max s)
+ * evaluated in double precision in two passes. Readings where the pages are
+ * silent: KV pools are laid out [num_blocks, num_kv_heads, block_size, head_dim];
+ * query head h reads KV head h / (num_heads / num_kv_heads); a zero-length
+ * context yields a zero output; the scale is an input.
+ *
+ * reshape_and_cache: a token with slot s >= 0 is written at block s / bs, offset
+ * s % bs, for every KV head ([P3] "Block table：为什么它能减少碎片": the new token
+ * goes into the free slot of the last block, or into a newly taken block; the
+ * flat slot encoding block * bs + offset is the reading taken for the mapping).
+ * copy_blocks: each (src, dst) pair copies a whole block ([P1] section 五,
+ * copy-on-write copies the shared block to the new one before the write).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F16 = 2 };
+
+/* IEEE 754 binary16 -> double, from the format's definition. */
+static double half_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double v;
+    if (expo == 0) {
+        v = ldexp((double)frac, -24);
+    } else if (expo == 31) {
+        v = frac ? NAN : INFINITY;
+    } else {
+        v = ldexp(1024.0 + (double)frac, expo - 25);
+    }
+    return sign ? -v : v;
+}
+
+/* bfloat16 is the upper half of a binary32: widen the bits and reinterpret. */
+static double bf16_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double elem(const void* base, size_t i, int dtype) {
+    if (dtype == ORACLE_F32) return (double)((const float*)base)[i];
+    uint16_t bits = ((const uint16_t*)base)[i];
+    return dtype == ORACLE_BF16 ? bf16_to_double(bits) : half_to_double(bits);
+}
+
+/* Exposed for the tests: decode n raw elements to double. */
+int oracle_decode(double* out, const void* src, long n, int dtype) {
+    if (dtype < 0 || dtype > 2) return -1;
+    for (long i = 0; i < n; ++i) out[i] = elem(src, (size_t)i, dtype);
+    return 0;
+}
+
+/*
+ * out:          double [B, Hq, D]
+ * q:            [B, Hq, D]            (dtype)
+ * k_cache:      [num_blocks, Hkv, bs, D]
+ * v_cache:      [num_blocks, Hkv, bs, D]
+ * block_tables: int32 [B, max_blocks]
+ * context_lens: int32 [B]
+ * rows:         optional int32 [num_rows, 2] of (b, h) to evaluate; NULL = all.
+ *               With rows given, out is [num_rows, D].
+ * Returns 0, or -1 for inconsistent sizes, -2 for a table entry outside the pool
+ * inside the used part of a table, -3 for a context longer than its table.
+ */
+int oracle_paged_attention(double* out, const void* q, const void* k_cache,
+                           const void* v_cache, int dtype, const int32_t* block_tables,
+                           const int32_t* context_lens, double scale, int B, int Hq,
+                           int Hkv, int D, int bs, int max_blocks, int num_blocks,
+                           const int32_t* rows, int num_rows, int nthreads) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || Hq % Hkv != 0) return -1;
+    if (dtype < 0 || dtype > 2) return -1;
+    const int G = Hq / Hkv;
+    for (int b = 0; b < B; ++b) {
+        int n = context_lens[b];
+        if (n < 0 || (long)n > (long)max_blocks * bs) return -3;
+        for (int j = 0; j < (n + bs - 1) / bs; ++j) {
+            int p = block_tables[(long)b * max_blocks + j];
+            if (p < 0 || p >= num_blocks) return -2;
+        }
+    }
+    const long work = rows ? num_rows : (long)B * Hq;
+    int status = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (long w = 0; w < work; ++w) {
+        int b = rows ? rows[2 * w] : (int)(w / Hq);
+        int h = rows ? rows[2 * w + 1] : (int)(w % Hq);
+        double* o = out + w * D;
+        if (b < 0 || b >= B || h < 0 || h >= Hq) { status = -1; continue; }
+        int g = h / G;
+        int n = context_lens[b];
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        if (n == 0) continue;
+        double* s = (double*)malloc(sizeof(double) * (size_t)n);
+        size_t* at = (size_t*)malloc(sizeof(size_t) * (size_t)n);
+        if (!s || !at) { free(s); free(at); status = -1; continue; }
+        const size_t qoff = ((size_t)b * Hq + h) * D;
+        /* pass 1: scores, token by token through the block table */
+        double mx = -INFINITY;
+        for (int t = 0; t < n; ++t) {
+            int phys = block_tables[(long)b * max_blocks + t / bs];
+            at[t] = (((size_t)phys * Hkv + g) * bs + (size_t)(t % bs)) * D;
+            double acc = 0.0;
+            for (int d = 0; d < D; ++d)
+                acc += elem(q, qoff + d, dtype) * elem(k_cache, at[t] + d, dtype);
+            s[t] = scale * acc;
+            if (s[t] > mx) mx = s[t];
+        }
+        /* pass 2: normalised weights applied to the values */
+        double denom = 0.0;
+        for (int t = 0; t < n; ++t) {
+            s[t] = exp(s[t] - mx);
+            denom += s[t];
+        }
+        for (int t = 0; t < n; ++t)
+            for (int d = 0; d < D; ++d) o[d] += s[t] * elem(v_cache, at[t] + d, dtype);
+        for (int d = 0; d < D; ++d) o[d] /= denom;
+        free(s);
+        free(at);
+    }
+    return status;
+}
+
+/*
+ * k, v:          [T, Hkv, D] raw elements of elt_bytes each
+ * k_cache, v_cache: [num_blocks, Hkv, bs, D], updated in place
+ * slot_mapping:  int64 [T]; a negative slot skips the token
+ * Returns 0, or -2 if a slot points outside the pool.
+ */
+int oracle_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                             const int64_t* slot_mapping, int T, int Hkv, int D, int bs,
+                             int num_blocks, int elt_bytes) {
+    const size_t row = (size_t)D * elt_bytes;
+    for (int t = 0; t < T; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0) continue;
+        int64_t blk = slot / bs, off = slot % bs;
+        if (blk >= num_blocks) return -2;
+        for (int h = 0; h < Hkv; ++h) {
+            size_t dst = (((size_t)blk * Hkv + h) * bs + (size_t)off) * row;
+            size_t src = ((size_t)t * Hkv + h) * row;
+            memcpy((char*)k_cache + dst, (const char*)k + src, row);
+            memcpy((char*)v_cache + dst, (const char*)v + src, row);
+        }
+    }
+    return 0;
+}
+
+/*
+ * cache: one pool of num_blocks blocks of block_bytes each, updated in place.
+ * pairs: int32 [n, 2] of (src, dst), applied in order.
+ * Returns 0, or -2 for an ID outside the pool.
+ */
+int oracle_copy_blocks(void* cache, const int32_t* pairs, int n, int num_blocks,
+                       long block_bytes) {
+    for (int i = 0; i < n; ++i) {
+        int src = pairs[2 * i], dst = pairs[2 * i + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return -2;
+        memmove((char*)cache + (size_t)dst * block_bytes,
+                (const char*)cache + (size_t)src * block_bytes, (size_t)block_bytes);
+    }
+    return 0;
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,385 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Every ``pin_*`` function takes a loaded oracle library (``lib``) and raises
+AssertionError when the oracle disagrees with:
+  * the pages' worked example (tests/golden/*.json, each with its citation),
+  * a closed form derived by hand or from the definition (ctx = 1, uniform
+    scores, a two-token case),
+  * a library routine on the un-paged data (torch's scaled_dot_product_attention
+    in float64 on the contiguous sequence, torch's dtype conversions),
+  * an invariant of the method (placement permutation, grouped-query = repeated
+    multi-head, stale slots never read, linearity in V, write-then-read identity
+    of the append, copy-on-write isolation),
+  * the NumPy dense brute force, a second, independently written definition.
+The same functions run against deliberately broken builds of the oracle in
+tests/test_oracle_mutants.py: each planted mistake must trip at least one pin.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+from workloads import BlockPool, append_token, blocks_needed, pack_tables, prefill, slot_of
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------- helpers
+def paged_from_contiguous(keys, values, bs, num_blocks, order, dtype, fill=0.0, seed=0):
+    """Scatter per-sequence contiguous K/V ([n_b, Hkv, D] each) into a paged pool.
+
+    Placement uses the block manager (free-list order ``order``); every slot not
+    holding a token gets ``fill`` (NaN poisons stale slots, padding and free blocks)
+    or, with fill=None, random values. Returns (k_cache, v_cache, tables, ctx).
+    """
+    hkv, d = keys[0].shape[1], keys[0].shape[2]
+    pool = BlockPool(num_blocks, order)
+    seqs = [prefill(pool, k.shape[0], bs) for k in keys]
+    if fill is None:
+        g = torch.Generator().manual_seed(seed)
+        kc = torch.randn(num_blocks, hkv, bs, d, generator=g, dtype=torch.float64)
+        vc = torch.randn(num_blocks, hkv, bs, d, generator=g, dtype=torch.float64)
+    else:
+        kc = torch.full((num_blocks, hkv, bs, d), float(fill), dtype=torch.float64)
+        vc = torch.full((num_blocks, hkv, bs, d), float(fill), dtype=torch.float64)
+    for s, k, v in zip(seqs, keys, values):
+        for t in range(k.shape[0]):
+            slot = slot_of(s, t, bs)
+            kc[slot // bs, :, slot % bs, :] = k[t].to(torch.float64)
+            vc[slot // bs, :, slot % bs, :] = v[t].to(torch.float64)
+    width = max(1, max(len(s.table) for s in seqs))
+    tables = torch.tensor(pack_tables(seqs, width), dtype=torch.int32)
+    ctx = torch.tensor([k.shape[0] for k in keys], dtype=torch.int32)
+    return kc.to(dtype), vc.to(dtype), tables, ctx
+
+
+def sdpa_reference(q, keys, values, scale):
+    """Library attention on the contiguous (un-paged) sequences, float64.
+
+    q [B, Hq, D]; keys[b], values[b] [n_b, Hkv, D]. Grouped heads are expanded by
+    repeat_interleave (query head h reads KV head h // group)."""
+    B, Hq, D = q.shape
+    out = torch.zeros(B, Hq, D, dtype=torch.float64)
+    for b in range(B):
+        n = keys[b].shape[0]
+        if n == 0:
+            continue
+        hkv = keys[b].shape[1]
+        K = keys[b].to(torch.float64).permute(1, 0, 2).repeat_interleave(Hq // hkv, dim=0)
+        V = values[b].to(torch.float64).permute(1, 0, 2).repeat_interleave(Hq // hkv, dim=0)
+        qq = q[b].to(torch.float64).unsqueeze(1)           # [Hq, 1, D]
+        out[b] = F.scaled_dot_product_attention(qq, K, V, scale=float(scale)).squeeze(1)
+    return out.numpy()
+
+
+def _random_seqs(seed, lens, hkv, d, dtype):
+    g = torch.Generator().manual_seed(seed)
+    keys = [torch.randn(n, hkv, d, generator=g).to(dtype) for n in lens]
+    values = [torch.randn(n, hkv, d, generator=g).to(dtype) for n in lens]
+    return keys, values
+
+
+def _order(seed, n):
+    return torch.randperm(n, generator=torch.Generator().manual_seed(seed)).tolist()
+
+
+def _close(a, b, tol, what):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.1e}"
+
+
+DTYPES = (torch.float32, torch.bfloat16, torch.float16)
+
+
+# ----------------------------------------------------------------------------- pins
+def pin_decoders(lib):
+    """Every bf16 and f16 bit pattern decodes to what torch's conversion gives."""
+    bits = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16)
+    for dt in (torch.bfloat16, torch.float16):
+        t = bits.view(dt)
+        got = oracle.decode(t, lib=lib)
+        want = t.to(torch.float64).numpy()
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan), f"{dt}: NaN set differs"
+        assert np.array_equal(got[~nan], want[~nan]), f"{dt}: decoded values differ"
+    x = torch.randn(1000, generator=torch.Generator().manual_seed(5))
+    assert np.array_equal(oracle.decode(x, lib=lib), x.double().numpy())
+
+
+def pin_sdpa_library(lib):
+    """Paged walk == library attention on the contiguous sequences (all dtypes,
+    several block sizes, grouped heads, ragged lengths incl. 1 and block multiples)."""
+    cases = [(1, 4, 4, 8, [5, 1, 12, 9]), (4, 8, 2, 64, [7, 16, 33, 40]),
+             (16, 4, 1, 16, [31, 16, 17]), (2, 8, 8, 32, [3, 4, 1, 6])]
+    for i, (bs, hq, hkv, d, lens) in enumerate(cases):
+        for dt in DTYPES:
+            keys, values = _random_seqs(100 + i, lens, hkv, d, dt)
+            need = sum(blocks_needed(n, bs) for n in lens) + 5
+            kc, vc, tables, ctx = paged_from_contiguous(keys, values, bs, need, _order(i, need),
+                                                        dt, fill=None, seed=i)
+            q = torch.randn(len(lens), hq, d, generator=torch.Generator().manual_seed(i)).to(dt)
+            scale = 1.0 / math.sqrt(d)
+            got = oracle.paged_attention(q, kc, vc, tables, ctx, scale, lib=lib)
+            _close(got, sdpa_reference(q, keys, values, scale), 1e-12, f"sdpa case {i} {dt}")
+
+
+def pin_dense_bruteforce(lib):
+    """C walk == NumPy dense gather-then-softmax on random tiny batches."""
+    from workloads import random_small
+    shapes = [(3, 2, 2, 8, 1, 9), (4, 8, 2, 64, 4, 40), (2, 8, 1, 8, 16, 40), (4, 4, 4, 16, 2, 23)]
+    for i, (B, hq, hkv, d, bs, mx) in enumerate(shapes):
+        for dt in DTYPES:
+            s = random_small(200 + i, batch=B, num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                             block_size=bs, max_ctx=mx, dtype=dt)
+            got = oracle.paged_attention(s.q, s.k_cache, s.v_cache, s.block_tables,
+                                         s.context_lens, s.scale, lib=lib)
+            want = oracle.dense_attention(s.q, s.k_cache, s.v_cache, s.block_tables,
+                                          s.context_lens, s.scale)
+            scale = max(1.0, float(np.max(np.abs(want))))
+            _close(got / scale, want / scale, 1e-12, f"dense case {i} {dt}")
+
+
+def pin_dense_vs_library():
+    """The NumPy brute force itself matches the library attention (pins dense.py)."""
+    lens = [9, 1, 20]
+    keys, values = _random_seqs(7, lens, 2, 16, torch.float32)
+    kc, vc, tables, ctx = paged_from_contiguous(keys, values, 4, 20, _order(3, 20),
+                                                torch.float32, fill=None, seed=1)
+    q = torch.randn(3, 4, 16, generator=torch.Generator().manual_seed(2))
+    got = oracle.dense_attention(q, kc, vc, tables, ctx, 0.25)
+    _close(got, sdpa_reference(q, keys, values, 0.25), 1e-12, "dense vs sdpa")
+
+
+def pin_worked_example(lib):
+    """The pages' block-size-4 walk-through: a 7-token prompt placed on physical
+    blocks 5 and 3, the 8th token fills the free slot, the 9th opens block 8; after
+    each append the decode equals attention over the contiguous 8 and 9 tokens."""
+    g = _golden("worked_example_fig6.json")
+    bs, n0 = g["block_size"], g["prompt_tokens"]
+    order = list(g["physical_order"]) + [x for x in range(10) if x not in g["physical_order"]]
+    hkv, hq, d = 2, 4, 8
+    gen = torch.Generator().manual_seed(11)
+    K = torch.randn(n0 + 2, hkv, d, generator=gen, dtype=torch.float64)
+    V = torch.randn(n0 + 2, hkv, d, generator=gen, dtype=torch.float64)
+    q = torch.randn(1, hq, d, generator=gen, dtype=torch.float64).to(torch.float32)
+    K, V = K.to(torch.float32), V.to(torch.float32)
+    kc, vc, tables, ctx = paged_from_contiguous([K[:n0]], [V[:n0]], bs, 10, order,
+                                                torch.float32, fill=float("nan"))
+    assert tables[0, :2].tolist() == g["expect"]["table_after_prompt"]
+    pool = BlockPool(10, order)
+    seq = prefill(pool, n0, bs)
+    for step in g["expect"]["decodes"]:
+        slot = append_token(pool, seq, bs)
+        assert slot == step["slot"], f"slot {slot} != {step['slot']}"
+        assert seq.table == step["table_after"]
+        pos = step["position"]
+        kc, vc = oracle.reshape_and_cache(K[pos:pos + 1], V[pos:pos + 1], kc, vc,
+                                          torch.tensor([slot]), lib=lib)
+        tb = torch.tensor([seq.table + [-1] * (3 - len(seq.table))], dtype=torch.int32)
+        got = oracle.paged_attention(q, kc, vc, tb, torch.tensor([pos + 1], dtype=torch.int32),
+                                     0.3, lib=lib)
+        want = sdpa_reference(q, [K[:pos + 1]], [V[:pos + 1]], 0.3)
+        _close(got, want, 1e-12, f"worked example after token {step['token_number']}")
+
+
+def pin_two_token_closed_form(lib):
+    g = _golden("two_token_closed_form.json")
+    keys = torch.tensor(g["keys"], dtype=torch.float32).unsqueeze(1)     # [2, 1, 2]
+    values = torch.tensor(g["values"], dtype=torch.float32).unsqueeze(1)
+    kc, vc, tables, ctx = paged_from_contiguous([keys], [values], g["block_size"], 2,
+                                                g["physical_order"], torch.float32,
+                                                fill=float("nan"))
+    q = torch.tensor([[g["q"]]], dtype=torch.float32)
+    got = oracle.paged_attention(q, kc, vc, tables, ctx, g["scale"], lib=lib)
+    _close(got.reshape(-1), g["expect"], g["tolerance"], "two-token closed form")
+
+
+def pin_context_one(lib):
+    """A single token gets weight exactly one: the output is v0, bit for bit."""
+    for dt in DTYPES:
+        keys, values = _random_seqs(31, [1, 1], 2, 16, dt)
+        kc, vc, tables, ctx = paged_from_contiguous(keys, values, 4, 6, _order(1, 6), dt,
+                                                    fill=None, seed=4)
+        q = torch.randn(2, 4, 16, generator=torch.Generator().manual_seed(3)).to(dt)
+        got = oracle.paged_attention(q, kc, vc, tables, ctx, 0.25, lib=lib)
+        want = torch.stack([v[0].repeat_interleave(2, dim=0) for v in values]).double().numpy()
+        assert np.array_equal(got, want), f"ctx=1 {dt}"
+
+
+def pin_uniform_scores(lib):
+    """q = 0 (or scale = 0) makes every score equal: the output is the mean of V."""
+    lens = [13, 4, 32]
+    keys, values = _random_seqs(41, lens, 2, 8, torch.float32)
+    kc, vc, tables, ctx = paged_from_contiguous(keys, values, 4, 20, _order(2, 20),
+                                                torch.float32, fill=None, seed=6)
+    want = np.stack([v.double().mean(0).repeat_interleave(2, dim=0).numpy() for v in values])
+    q0 = torch.zeros(3, 4, 8)
+    _close(oracle.paged_attention(q0, kc, vc, tables, ctx, 0.5, lib=lib), want, 1e-12, "q=0")
+    q1 = torch.randn(3, 4, 8, generator=torch.Generator().manual_seed(8))
+    _close(oracle.paged_attention(q1, kc, vc, tables, ctx, 0.0, lib=lib), want, 1e-12,
+           "scale=0")
+
+
+def pin_zero_context(lib):
+    """Reading taken: an empty context gives a zero output (and other rows unaffected)."""
+    keys, values = _random_seqs(51, [0, 5], 1, 8, torch.float32)
+    kc, vc, tables, ctx = paged_from_contiguous(keys, values, 4, 4, _order(5, 4),
+                                                torch.float32, fill=None, seed=2)
+    q = torch.randn(2, 1, 8, generator=torch.Generator().manual_seed(9))
+    got = oracle.paged_attention(q, kc, vc, tables, ctx, 0.3, lib=lib)
+    assert np.array_equal(got[0], np.zeros((1, 8)))
+    _close(got[1:], sdpa_reference(q[1:], keys[1:], values[1:], 0.3), 1e-12, "row after empty")
+
+
+def pin_placement_permutation(lib):
+    """The same tokens on a different physical placement give the identical output."""
+    lens = [7, 16, 33, 21]
+    for dt in (torch.float32, torch.bfloat16):
+        keys, values = _random_seqs(61, lens, 2, 16, dt)
+        q = torch.randn(4, 8, 16, generator=torch.Generator().manual_seed(12)).to(dt)
+        outs = []
+        for perm_seed in (1, 2, 3):
+            kc, vc, tables, ctx = paged_from_contiguous(keys, values, 4, 30,
+                                                        _order(perm_seed, 30), dt, fill=None,
+                                                        seed=perm_seed)
+            outs.append(oracle.paged_attention(q, kc, vc, tables, ctx, 0.25, lib=lib))
+        assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2]), dt
+
+
+def pin_gqa_equals_repeated_mha(lib):
+    """Grouped-query attention equals multi-head attention with each KV head repeated
+    for its group (query head h reads KV head h // group)."""
+    lens = [9, 20, 4]
+    hkv, group, d = 2, 4, 16
+    keys, values = _random_seqs(71, lens, hkv, d, torch.float32)
+    q = torch.randn(3, hkv * group, d, generator=torch.Generator().manual_seed(13))
+    kc, vc, tables, ctx = paged_from_contiguous(keys, values, 4, 12, _order(4, 12),
+                                                torch.float32, fill=None, seed=3)
+    got = oracle.paged_attention(q, kc, vc, tables, ctx, 0.25, lib=lib)
+    rk = [k.repeat_interleave(group, dim=1) for k in keys]
+    rv = [v.repeat_interleave(group, dim=1) for v in values]
+    kc2, vc2, tables2, ctx2 = paged_from_contiguous(rk, rv, 4, 12, _order(4, 12),
+                                                    torch.float32, fill=None, seed=3)
+    want = oracle.paged_attention(q, kc2, vc2, tables2, ctx2, 0.25, lib=lib)
+    assert np.array_equal(got, want)
+
+
+def pin_stale_slots_unread(lib):
+    """NaN in the unfilled slots of last blocks, in table padding targets and in free
+    blocks changes nothing (only tokens below the context length are read)."""
+    lens = [7, 16, 2]
+    keys, values = _random_seqs(81, lens, 2, 8, torch.float32)
+    q = torch.randn(3, 4, 8, generator=torch.Generator().manual_seed(14))
+    a = paged_from_contiguous(keys, values, 4, 12, _order(6, 12), torch.float32, fill=0.0)
+    b = paged_from_contiguous(keys, values, 4, 12, _order(6, 12), torch.float32,
+                              fill=float("nan"))
+    ra = oracle.paged_attention(q, a[0], a[1], a[2], a[3], 0.3, lib=lib)
+    rb = oracle.paged_attention(q, b[0], b[1], b[2], b[3], 0.3, lib=lib)
+    assert np.all(np.isfinite(rb)) and np.array_equal(ra, rb)
+
+
+def pin_linearity_in_values(lib):
+    """The output is linear in V for fixed q and K."""
+    lens = [11, 5]
+    keys, v1 = _random_seqs(91, lens, 1, 8, torch.float64)
+    _, v2 = _random_seqs(92, lens, 1, 8, torch.float64)
+    q = torch.randn(2, 2, 8, generator=torch.Generator().manual_seed(15))
+    outs = []
+    for vals in (v1, v2, [a + 2.0 * b for a, b in zip(v1, v2)]):
+        kc, vc, tables, ctx = paged_from_contiguous(keys, vals, 4, 8, _order(7, 8),
+                                                    torch.float32, fill=None, seed=5)
+        outs.append(oracle.paged_attention(q, kc, vc, tables, ctx, 0.3, lib=lib))
+    # values were rounded to float32 when placed; compare in that precision
+    _close(outs[2], outs[0] + 2.0 * outs[1], 1e-5, "linearity")
+
+
+def pin_append_roundtrip(lib):
+    """Writing a sequence token by token through the slot mapping and reading it back
+    through the block table returns the sequence; nothing else in the pool changes;
+    negative slots write nothing."""
+    for dt in DTYPES:
+        bs, hkv, d, nb = 4, 3, 8, 16
+        gen = torch.Generator().manual_seed(17)
+        kc0 = torch.randn(nb, hkv, bs, d, generator=gen).to(dt)
+        vc0 = torch.randn(nb, hkv, bs, d, generator=gen).to(dt)
+        pool = BlockPool(nb, _order(8, nb))
+        seqs = [prefill(pool, 0, bs) for _ in range(3)]
+        lens = [6, 9, 4]
+        slots, toks = [], []
+        for step in range(max(lens)):
+            for i, s in enumerate(seqs):
+                if step < lens[i]:
+                    slots.append(append_token(pool, s, bs))
+                    toks.append((i, step))
+                    slots.append(-1)            # padding entry: must write nothing
+                    toks.append(None)
+        T = len(slots)
+        newk = torch.randn(T, hkv, d, generator=gen).to(dt)
+        newv = torch.randn(T, hkv, d, generator=gen).to(dt)
+        kc, vc = oracle.reshape_and_cache(newk, newv, kc0, vc0,
+                                          torch.tensor(slots, dtype=torch.int64), lib=lib)
+        written = torch.zeros(nb, bs, dtype=torch.bool)
+        for t, tok in enumerate(toks):
+            if tok is None:
+                continue
+            i, pos = tok
+            blk = seqs[i].table[pos // bs]
+            assert torch.equal(kc[blk, :, pos % bs], newk[t]), "K not readable at its position"
+            assert torch.equal(vc[blk, :, pos % bs], newv[t]), "V not readable at its position"
+            written[blk, pos % bs] = True
+        keep = ~written
+        assert torch.equal(kc.permute(0, 2, 1, 3)[keep], kc0.permute(0, 2, 1, 3)[keep])
+        assert torch.equal(vc.permute(0, 2, 1, 3)[keep], vc0.permute(0, 2, 1, 3)[keep])
+
+
+def pin_copy_on_write(lib):
+    """Copy-on-write through the block manager: two sequences share a partly filled
+    block; before the second one writes, the block is copied. Afterwards the first
+    sequence still sees its old tokens, the writer sees the shared prefix plus its
+    new token, and every other block is untouched."""
+    for dt in (torch.float32, torch.bfloat16):
+        bs, hkv, d, nb = 4, 2, 8, 10
+        gen = torch.Generator().manual_seed(19)
+        kc0 = torch.randn(nb, hkv, bs, d, generator=gen).to(dt)
+        pool = BlockPool(nb, _order(9, nb))
+        a = prefill(pool, 6, bs)
+        b = a.copy_shared(pool)
+        copies = []
+        slot = append_token(pool, b, bs, copies)
+        assert len(copies) == 1 and copies[0][0] == a.table[1] and b.table[1] == copies[0][1]
+        assert b.table[0] == a.table[0] and pool.refcount(a.table[0]) == 2
+        kc = oracle.copy_blocks(kc0, torch.tensor(copies, dtype=torch.int32), lib=lib)
+        src, dst = copies[0]
+        assert torch.equal(kc[dst], kc0[src]), "copy does not hold the source block"
+        others = [x for x in range(nb) if x != dst]
+        assert torch.equal(kc[others], kc0[others]), "copy touched another block"
+        newk = torch.randn(1, hkv, d, generator=gen).to(dt)
+        kc2, _ = oracle.reshape_and_cache(newk, newk, kc, kc.clone(),
+                                          torch.tensor([slot]), lib=lib)
+        for pos in range(6):   # the first sequence's view is unchanged
+            blk = a.table[pos // bs]
+            assert torch.equal(kc2[blk, :, pos % bs], kc0[blk, :, pos % bs])
+        for pos in range(6):   # the writer sees the same prefix ...
+            blk = b.table[pos // bs]
+            assert torch.equal(kc2[blk, :, pos % bs], kc0[a.table[pos // bs], :, pos % bs])
+        assert torch.equal(kc2[b.table[1], :, 6 % bs], newk[0])   # ... and its new token
+
+
+ALL_PINS = [pin_decoders, pin_sdpa_library, pin_dense_bruteforce, pin_worked_example,
+            pin_two_token_closed_form, pin_context_one, pin_uniform_scores, pin_zero_context,
+            pin_placement_permutation, pin_gqa_equals_repeated_mha, pin_stale_slots_unread,
+            pin_linearity_in_values, pin_append_roundtrip, pin_copy_on_write]

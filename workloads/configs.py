@@ -1,0 +1,289 @@
+"""Seeded synthetic decode workloads.
+
+Each builder returns the inputs of one decode step over a paged KV cache: the
+query, the K and V block pools, the block tables, the context lengths and the
+softmax scale, plus (where the workload has them) the new tokens to append with
+their slot mapping and the block-copy pairs of copy-on-write. Nothing here
+computes attention; placement comes from :mod:`workloads.blockmgr`.
+
+Value recipe (shared by every workload): float32 draws from N(0, 1) with a seeded
+``torch.Generator``, then cast to the KV dtype (round to nearest even). The whole
+pool is filled, used or not. Physical placement: a seeded random permutation of
+the pool is the free-list order, so consecutive logical blocks land on scattered
+physical blocks.
+
+The shapes follow the serving workloads the pages talk about (grouped-query
+heads, head_dim 128, block_size 16, variable context lengths); see the README of
+the design for the exact recipes. Random numbers for large pools can be drawn on
+the GPU (``gen_device``) so that multi-GiB pools are not generated on the host;
+block tables and lengths always come from a CPU generator.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional, Tuple
+
+import torch
+
+from .blockmgr import (BlockPool, Sequence_, append_token, blocks_needed, pack_tables,
+                       prefill)
+
+
+@dataclass
+class DecodeStep:
+    """All tensors of one decode step (plus optional append and copy work)."""
+
+    name: str
+    q: Optional[torch.Tensor]                 # [B, Hq, D]
+    k_cache: Optional[torch.Tensor]           # [num_blocks, Hkv, bs, D]
+    v_cache: Optional[torch.Tensor]           # [num_blocks, Hkv, bs, D]
+    block_tables: torch.Tensor                # int32 [B, max_blocks], -1 padded
+    context_lens: torch.Tensor                # int32 [B]
+    scale: float                              # an exact float32 value
+    block_size: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: torch.dtype
+    # optional append work (reshape_and_cache) that precedes the decode
+    new_k: Optional[torch.Tensor] = None      # [T, Hkv, D]
+    new_v: Optional[torch.Tensor] = None
+    slot_mapping: Optional[torch.Tensor] = None   # int64 [T]
+    # optional copy-on-write block copies that precede the append
+    copy_pairs: Optional[torch.Tensor] = None     # int32 [n, 2] (src, dst)
+    # context lengths before the append (for the pre-append decode of the tiny case)
+    context_lens_before: Optional[torch.Tensor] = None
+    block_tables_before: Optional[torch.Tensor] = None
+    partition_size: int = 0
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.numel())
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.extra["num_blocks"])
+
+    def kv_bytes(self) -> int:
+        """Bytes of K and V one decode step reads: sum(ctx) * Hkv * 2 * D * elt."""
+        elt = torch.empty((), dtype=self.dtype).element_size()
+        return int(self.context_lens.to(torch.int64).sum()) * self.num_kv_heads * 2 \
+            * self.head_dim * elt
+
+
+def fp32_scale(head_dim: int) -> float:
+    """1/sqrt(head_dim) rounded to float32 (both sides receive this exact value)."""
+    return float(torch.tensor(1.0 / math.sqrt(head_dim), dtype=torch.float32))
+
+
+def _normal(shape, dtype, gen: torch.Generator, device) -> torch.Tensor:
+    x = torch.randn(shape, generator=gen, dtype=torch.float32, device=device)
+    return x.to(dtype)
+
+
+def _gens(seed: int, gen_device) -> Tuple[torch.Generator, torch.Generator]:
+    """A CPU generator for structure and one on ``gen_device`` for values."""
+    g_cpu = torch.Generator(device="cpu").manual_seed(seed)
+    dev = torch.device(gen_device)
+    g_val = g_cpu if dev.type == "cpu" else torch.Generator(device=dev).manual_seed(seed)
+    return g_cpu, g_val
+
+
+def _fill_pools(num_blocks, hkv, bs, d, dtype, g_val, gen_device, device, materialize):
+    if not materialize:
+        return None, None
+    k = _normal((num_blocks, hkv, bs, d), dtype, g_val, gen_device).to(device)
+    v = _normal((num_blocks, hkv, bs, d), dtype, g_val, gen_device).to(device)
+    return k, v
+
+
+def tiny_fp32(seed: int = 1001, device="cpu", gen_device="cpu",
+              materialize: bool = True) -> DecodeStep:
+    """4 sequences, context lengths {7, 16, 33, 100}, block_size 4, 8 query heads =
+    8 KV heads, head_dim 64, float32, a pool of 64 physical blocks; plus one append
+    of 4 new tokens and one copy of 3 block pairs."""
+    B, H, HKV, D, BS, NP = 4, 8, 8, 64, 4, 64
+    ctx = [7, 16, 33, 100]
+    g_cpu, g_val = _gens(seed, gen_device)
+    perm = torch.randperm(NP, generator=g_cpu).tolist()
+    pool = BlockPool(NP, perm)
+    seqs = [prefill(pool, n, BS) for n in ctx]
+    width = blocks_needed(max(ctx) + 1, BS)
+    tables_before = torch.tensor(pack_tables(seqs, width), dtype=torch.int32)
+    ctx_before = torch.tensor(ctx, dtype=torch.int32)
+    slots = [append_token(pool, s, BS) for s in seqs]
+    tables = torch.tensor(pack_tables(seqs, width), dtype=torch.int32)
+    ctx_after = torch.tensor([s.num_tokens for s in seqs], dtype=torch.int32)
+    used = sorted({b for s in seqs for b in s.table})
+    free = sorted(set(range(NP)) - set(used))
+    pick = torch.randperm(len(used), generator=g_cpu)[:3].tolist()
+    pick_dst = torch.randperm(len(free), generator=g_cpu)[:3].tolist()
+    pairs = torch.tensor([[used[i], free[j]] for i, j in zip(pick, pick_dst)],
+                         dtype=torch.int32)
+    q = _normal((B, H, D), torch.float32, g_val, gen_device).to(device) if materialize else None
+    kc, vc = _fill_pools(NP, HKV, BS, D, torch.float32, g_val, gen_device, device, materialize)
+    nk = _normal((B, HKV, D), torch.float32, g_val, gen_device).to(device) if materialize else None
+    nv = _normal((B, HKV, D), torch.float32, g_val, gen_device).to(device) if materialize else None
+    return DecodeStep(
+        name="tiny_fp32", q=q, k_cache=kc, v_cache=vc,
+        block_tables=tables.to(device), context_lens=ctx_after.to(device),
+        scale=fp32_scale(D), block_size=BS, num_heads=H, num_kv_heads=HKV, head_dim=D,
+        dtype=torch.float32, new_k=nk, new_v=nv,
+        slot_mapping=torch.tensor(slots, dtype=torch.int64).to(device),
+        copy_pairs=pairs.to(device), context_lens_before=ctx_before.to(device),
+        block_tables_before=tables_before.to(device),
+        extra={"num_blocks": NP, "seed": seed})
+
+
+def _scattered_batch(name, seed, ctx: List[int], num_blocks: int, hq, hkv, d, bs, width,
+                     dtype, device, gen_device, materialize, partition_size=0):
+    g_cpu, g_val = _gens(seed, gen_device)
+    perm = torch.randperm(num_blocks, generator=g_cpu).tolist()
+    pool = BlockPool(num_blocks, perm)
+    seqs = [prefill(pool, n, bs) for n in ctx]
+    tables = torch.tensor(pack_tables(seqs, width), dtype=torch.int32)
+    q = _normal((len(ctx), hq, d), dtype, g_val, gen_device).to(device) if materialize else None
+    kc, vc = _fill_pools(num_blocks, hkv, bs, d, dtype, g_val, gen_device, device, materialize)
+    return DecodeStep(
+        name=name, q=q, k_cache=kc, v_cache=vc, block_tables=tables.to(device),
+        context_lens=torch.tensor(ctx, dtype=torch.int32).to(device), scale=fp32_scale(d),
+        block_size=bs, num_heads=hq, num_kv_heads=hkv, head_dim=d, dtype=dtype,
+        partition_size=partition_size,
+        extra={"num_blocks": num_blocks, "seed": seed})
+
+
+def llama3_8b_decode(seed: int = 1002, device="cpu", gen_device=None,
+                     materialize: bool = True, batch: int = 64) -> DecodeStep:
+    """Llama-3-8B-shaped single-layer decode: 64 sequences, 32 query / 8 KV heads,
+    head_dim 128, block_size 16, context lengths uniform in [128, 2048], blocks drawn
+    from a shuffled pool of 16384, bfloat16."""
+    gen_device = device if gen_device is None else gen_device
+    g = torch.Generator(device="cpu").manual_seed(seed + 7919)
+    ctx = torch.randint(128, 2049, (batch,), generator=g).tolist()
+    return _scattered_batch("llama3_8b_decode", seed, ctx, 16384, 32, 8, 128, 16, 128,
+                            torch.bfloat16, device, gen_device, materialize)
+
+
+def llama_70b_decode(seed: int = 1003, device="cpu", gen_device=None,
+                     materialize: bool = True) -> DecodeStep:
+    """70B-shaped decode batch on one GPU: 256 sequences, 64 query / 8 KV heads,
+    head_dim 128, block_size 16, context lengths log-normal (median 1024, sigma 0.8)
+    clipped to [16, 4096], a shuffled pool sized to 1.1x the blocks in use, bfloat16."""
+    gen_device = device if gen_device is None else gen_device
+    g = torch.Generator(device="cpu").manual_seed(seed + 7919)
+    z = torch.randn(256, generator=g, dtype=torch.float64)
+    ctx = torch.exp(math.log(1024.0) + 0.8 * z).round().clamp(16, 4096).to(torch.int64).tolist()
+    need = sum(blocks_needed(n, 16) for n in ctx)
+    return _scattered_batch("llama_70b_decode", seed, ctx, math.ceil(1.1 * need), 64, 8, 128,
+                            16, 256, torch.bfloat16, device, gen_device, materialize)
+
+
+def long_context_decode(seed: int = 1004, device="cpu", gen_device=None,
+                        materialize: bool = True) -> DecodeStep:
+    """Long-context decode for the split-K path: 8 sequences, 32 query / 8 KV heads,
+    head_dim 128, block_size 16, context lengths uniform in [32768, 131072], shuffled
+    pool of 1.1x the blocks in use, bfloat16, partitions of 512 tokens."""
+    gen_device = device if gen_device is None else gen_device
+    g = torch.Generator(device="cpu").manual_seed(seed + 7919)
+    ctx = torch.randint(32768, 131073, (8,), generator=g).tolist()
+    need = sum(blocks_needed(n, 16) for n in ctx)
+    return _scattered_batch("long_context_decode", seed, ctx, math.ceil(1.1 * need), 32, 8,
+                            128, 16, 8192, torch.bfloat16, device, gen_device, materialize,
+                            partition_size=512)
+
+
+def shared_prefix_cow(seed: int = 1005, device="cpu", gen_device=None,
+                      materialize: bool = True, prefix_tokens: int = 2048,
+                      prompts: int = 32, samples: int = 8) -> DecodeStep:
+    """Parallel sampling over shared prompts: 32 prompts x 8 samples (256 sequences),
+    each prompt's prefix stored once and referenced by all its samples, 1-256
+    divergent tokens per sample, 32 query / 8 KV heads, head_dim 128, block_size 16,
+    bfloat16.
+
+    Order of device work in the step: copy the last prefix block for every sample
+    but the first (copy_blocks, K and V pools), write every token placed after the
+    fork (the divergent tokens and the new one) with reshape_and_cache, then decode
+    with context = prefix + divergent + 1.
+
+    With ``prefix_tokens=2048`` the prefix fills its 128 blocks exactly, so the
+    first divergent token opens a fresh block; the last prefix block is still
+    copied for samples 1..7 before the first divergent write (the literal reading
+    of the workload's recipe). With a prefix that ends mid-block (e.g. 2040) the
+    copy is the genuine copy-on-write: the first divergent write lands in the
+    shared, partly filled block.
+    """
+    gen_device = device if gen_device is None else gen_device
+    BS, HQ, HKV, D = 16, 32, 8, 128
+    g_cpu, g_val = _gens(seed, gen_device)
+    g_len = torch.Generator(device="cpu").manual_seed(seed + 7919)
+    div = torch.randint(1, 257, (prompts * samples,), generator=g_len).tolist()
+    nb_prefix = blocks_needed(prefix_tokens, BS)
+    need = prompts * nb_prefix + prompts * (samples - 1) + sum(
+        blocks_needed(prefix_tokens + d + 1, BS) - nb_prefix + 1 for d in div)
+    num_blocks = math.ceil(1.1 * need)
+    perm = torch.randperm(num_blocks, generator=g_cpu).tolist()
+    pool = BlockPool(num_blocks, perm)
+    copies: List[Tuple[int, int]] = []
+    seqs: List[Sequence_] = []
+    for p in range(prompts):
+        root = prefill(pool, prefix_tokens, BS)
+        group = [root] + [root.copy_shared(pool) for _ in range(samples - 1)]
+        last = nb_prefix - 1
+        if prefix_tokens % BS == 0:
+            # full last block: copy it explicitly for samples 1.. (literal recipe)
+            for s in group[1:]:
+                old = s.table[last]
+                new = pool.allocate(1)[0]
+                copies.append((old, new))
+                pool.decref(old)
+                s.table[last] = new
+        seqs.extend(group)
+    slots: List[int] = []
+    for s, d in zip(seqs, div):
+        for _ in range(d + 1):  # divergent tokens, then the new token
+            slots.append(append_token(pool, s, BS, copies))
+    width = max(len(s.table) for s in seqs)
+    tables = torch.tensor(pack_tables(seqs, width), dtype=torch.int32)
+    ctx = torch.tensor([s.num_tokens for s in seqs], dtype=torch.int32)
+    T = len(slots)
+    q = _normal((len(seqs), HQ, D), torch.bfloat16, g_val, gen_device).to(device) \
+        if materialize else None
+    kc, vc = _fill_pools(num_blocks, HKV, BS, D, torch.bfloat16, g_val, gen_device, device,
+                         materialize)
+    nk = _normal((T, HKV, D), torch.bfloat16, g_val, gen_device).to(device) if materialize else None
+    nv = _normal((T, HKV, D), torch.bfloat16, g_val, gen_device).to(device) if materialize else None
+    return DecodeStep(
+        name="shared_prefix_cow" if prefix_tokens % BS == 0 else "shared_prefix_cow_partial",
+        q=q, k_cache=kc, v_cache=vc, block_tables=tables.to(device),
+        context_lens=ctx.to(device), scale=fp32_scale(D), block_size=BS, num_heads=HQ,
+        num_kv_heads=HKV, head_dim=D, dtype=torch.bfloat16, new_k=nk, new_v=nv,
+        slot_mapping=torch.tensor(slots, dtype=torch.int64).to(device),
+        copy_pairs=torch.tensor(copies, dtype=torch.int32).reshape(-1, 2).to(device),
+        extra={"num_blocks": num_blocks, "seed": seed, "prefix_tokens": prefix_tokens,
+               "divergent": div, "samples": samples, "prompts": prompts})
+
+
+def random_small(seed: int, *, batch: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                 block_size: int, max_ctx: int, dtype=torch.float32, min_ctx: int = 1,
+                 num_blocks: Optional[int] = None, device="cpu",
+                 gen_device="cpu") -> DecodeStep:
+    """A small random batch (for brute-force and parity sweeps): lengths uniform in
+    [min_ctx, max_ctx], blocks scattered over a shuffled pool with some spare."""
+    g = torch.Generator(device="cpu").manual_seed(seed + 7919)
+    ctx = torch.randint(min_ctx, max_ctx + 1, (batch,), generator=g).tolist()
+    need = sum(blocks_needed(n, block_size) for n in ctx)
+    nb = num_blocks if num_blocks is not None else need + 3 + need // 4
+    width = max(1, max(blocks_needed(n, block_size) for n in ctx))
+    return _scattered_batch(f"random_small_{seed}", seed, ctx, nb, num_heads, num_kv_heads,
+                            head_dim, block_size, width, dtype, device, gen_device, True)
+
+
+WORKLOADS = {
+    "tiny_fp32": tiny_fp32,
+    "llama3_8b_decode": llama3_8b_decode,
+    "llama_70b_decode": llama_70b_decode,
+    "long_context_decode": long_context_decode,
+    "shared_prefix_cow": shared_prefix_cow,
+}
