@@ -1,0 +1,178 @@
+/*
+ * pagedkv.h -- C ABI of the MI355X (gfx950) paged KV-cache library.
+ *
+ * Three operations form the decode hot path of a paged KV cache:
+ *   pkv_paged_attention_decode  single-query attention read through block tables
+ *   pkv_reshape_and_cache       write each new token's K/V into its slot
+ *   pkv_copy_blocks             copy whole blocks (copy-on-write)
+ * plus workspace sizing/initialisation, version and error strings.
+ *
+ * Pages cited (titles as published):
+ *   [P1] "vLLM 源码解析：PagedAttention 如何让大模型推理提速 10 倍"
+ *   [P2] "vLLM 核心源码深度解析：PagedAttention 的 KV Cache 管理、Scheduler 调度引擎与
+ *         Continuous Batching 实现全解"
+ *   [P3] "论文专题讲解：vLLM / PagedAttention：为什么 KV cache 需要分页管理"
+ *
+ * Common rules for every call:
+ *  - All array pointers are DEVICE memory owned by the caller; the library never
+ *    allocates, frees or retains them. Arrays are dense, row-major, contiguous.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and the
+ *    call returns before it completes. Nothing synchronises inside a call unless
+ *    the environment variable PKV_VALIDATE=1 is set (see below).
+ *  - Return value: PKV_OK (0), or a negative PKV_E_* code for errors the host can
+ *    see (NULL pointers, bad sizes, unsupported shapes, a too-small workspace, a
+ *    launch failure). Nothing is enqueued when a call returns an error.
+ *  - Contents of index arrays (block IDs, context lengths, slots, pairs) are the
+ *    caller's contract and are not checked on the host. The kernels never access
+ *    memory outside the arrays described by the size arguments: an out-of-range
+ *    block ID is skipped, a context longer than its table row is cut to the row,
+ *    a negative context counts as empty, an out-of-range slot or pair writes
+ *    nothing. Results for such inputs are unspecified.
+ *  - PKV_VALIDATE=1: before enqueuing, the index arrays are copied to the host
+ *    (a synchronising copy on `stream`) and checked; violations return
+ *    PKV_E_INDEX and enqueue nothing.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, out, k/v and the caches (all share one type). */
+typedef enum {
+    PKV_FLOAT32 = 0,
+    PKV_BFLOAT16 = 1,
+    PKV_FLOAT16 = 2
+} pkv_dtype;
+
+enum {
+    PKV_OK = 0,
+    PKV_E_NULL = -1,         /* a required pointer is NULL */
+    PKV_E_SHAPE = -2,        /* a size is negative/zero where it must be positive, or inconsistent */
+    PKV_E_HEADS = -3,        /* num_heads is not a multiple of num_kv_heads, or the group is too large */
+    PKV_E_UNSUPPORTED = -4,  /* dtype / head_dim / block_size combination not supported */
+    PKV_E_WORKSPACE = -5,    /* workspace NULL or smaller than pkv_paged_attention_workspace_size() */
+    PKV_E_LAUNCH = -6,       /* the HIP runtime reported an error when enqueuing */
+    PKV_E_INDEX = -7,        /* PKV_VALIDATE=1 only: an index array holds an out-of-range entry */
+    PKV_E_DEVICE = -8        /* no current HIP device could be queried */
+};
+
+/* A hipStream_t passed as an opaque pointer. */
+typedef void* pkv_stream_t;
+
+/* Library version string, e.g. "pagedkv 0.1.0 gfx950". Static storage. */
+const char* pkv_version(void);
+
+/* Human-readable text for a PKV_* code. Static storage; never NULL. */
+const char* pkv_strerror(int code);
+
+/*
+ * Bytes of device workspace pkv_paged_attention_decode needs for these sizes and
+ * this partition_size (same meaning as in the decode call). The value depends only
+ * on its arguments (no device query), so it can be computed once per shape bucket;
+ * it can be 0. Returns 0 for invalid sizes as well; the decode call then reports
+ * the error.
+ */
+size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                          int head_dim, int block_size,
+                                          int max_blocks_per_seq, int partition_size);
+
+/*
+ * Zero-fill a workspace with a kernel on `stream` (no memset node, so the call can
+ * sit inside a captured graph). A workspace must be zero-filled once before its
+ * first use; every decode call leaves its bookkeeping zeroed again on completion,
+ * so later calls need no re-initialisation. Decode calls that run concurrently must
+ * use distinct workspaces.
+ */
+int pkv_workspace_init(void* workspace, size_t workspace_bytes, pkv_stream_t stream);
+
+/*
+ * Paged decode attention (one query token per sequence).
+ *
+ * Defined by [P1] section 四 (the kernel walks, per query, the physical blocks of
+ * its page table, attends each block and merges the partial results) and [P3]
+ * section "PagedAttention：逻辑连续，物理不必连续" (the query at position i attends
+ * tokens 1..i; the keys/values of logical block j are tokens (j-1)B+1..jB). Token
+ * position t of sequence b is read from physical block block_tables[b][t / bs] at
+ * offset t % bs ([P2] section "Block Table 数据结构"). Per-block partial results are
+ * merged with an online softmax; long contexts are split into partitions whose
+ * (max, sum, output) are merged by a log-sum-exp reduction.
+ *
+ *   out[b,h,:] = sum_t softmax_t(scale * q[b,h,:] . K_b[t,:]) * V_b[t,:],
+ *   t = 0 .. context_lens[b]-1, K_b/V_b read from KV head h / (num_heads/num_kv_heads).
+ *
+ * out           [num_seqs, num_heads, head_dim]                 written
+ * q             [num_seqs, num_heads, head_dim]                 read
+ * k_cache       [num_blocks, num_kv_heads, block_size, head_dim] read
+ * v_cache       [num_blocks, num_kv_heads, block_size, head_dim] read
+ * block_tables  int32 [num_seqs, max_blocks_per_seq]; entries at or beyond
+ *               ceil(context_lens[b] / block_size) are never read (pad with -1)
+ * context_lens  int32 [num_seqs]; the tokens each query attends, the new token
+ *               included; 0 gives an all-zero output row
+ * scale         multiplier of q.k (typically 1/sqrt(head_dim))
+ * dtype         element type of out, q and the caches; accumulation is float32,
+ *               the output is rounded to nearest-even
+ * partition_size  0: the library chooses how to split the work (recommended);
+ *               >0: split every context into partitions of this many tokens
+ *               (a multiple of block_size), one partial result per partition,
+ *               merged by a separate reduction kernel
+ * workspace     device scratch of at least pkv_paged_attention_workspace_size()
+ *               bytes, zero-filled before first use (pkv_workspace_init); may be
+ *               NULL only when that size is 0
+ * Supported: head_dim in {64, 128, 256}; block_size in {1, 2, 4, 8, 16, 32};
+ * num_heads / num_kv_heads <= 16 (group sizes above 8 need bfloat16/float16,
+ * block_size 16, head_dim 64 or 128). Deterministic: the same inputs give
+ * bit-identical outputs.
+ */
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, float scale, int num_seqs,
+                               int num_heads, int num_kv_heads, int head_dim, int block_size,
+                               int max_blocks_per_seq, int num_blocks, pkv_dtype dtype,
+                               int partition_size, void* workspace, size_t workspace_bytes,
+                               pkv_stream_t stream);
+
+/*
+ * Slot-mapped append of new tokens' K and V ([P3] section "Block table：为什么它能
+ * 减少碎片": a decoded token goes into the free slot of its last block, or into a
+ * newly taken block; section "Continuous batching 为什么离不开内存管理": generated
+ * K/V are written back into their block).
+ *
+ * key, value    [num_tokens, num_kv_heads, head_dim] read
+ * k_cache, v_cache [num_blocks, num_kv_heads, block_size, head_dim] written at the
+ *               addressed slots only
+ * slot_mapping  int64 [num_tokens]; slot = physical_block * block_size + offset;
+ *               a negative slot skips the token. Two tokens with the same slot are a
+ *               caller error (which one lands is unspecified).
+ * The copy is bit-exact (no conversion). num_tokens may be 0 (nothing enqueued).
+ */
+int pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                          const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                          int head_dim, int block_size, int num_blocks, pkv_dtype dtype,
+                          pkv_stream_t stream);
+
+/*
+ * Whole-block copies inside one pool, as copy-on-write needs them ([P1] section 五:
+ * a shared block is copied to a newly allocated one before a writer changes it;
+ * [P3] section "共享前缀和 copy-on-write").
+ *
+ * cache         one pool of num_blocks blocks of block_bytes bytes each (call once
+ *               for the K pool and once for the V pool)
+ * src_dst_pairs int32 [num_pairs, 2] of (src, dst) block IDs. Destinations must be
+ *               distinct and no destination may also be a source (caller contract);
+ *               under that contract the result does not depend on the order.
+ * block_bytes   a multiple of 4 (16 for the vectorised path); num_pairs may be 0.
+ * Bit-exact.
+ */
+int pkv_copy_blocks(void* cache, const int32_t* src_dst_pairs, int num_pairs, int num_blocks,
+                    size_t block_bytes, pkv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,212 @@
+"""MI355X (gfx950) paged KV-cache decode attention.
+
+A thin binding over the C ABI of ``libpagedkv.so`` (declared in include/pagedkv.h).
+The functions here only marshal arguments: every step of the computation runs in
+the library's HIP kernels. PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is not built, or a tensor is not on a GPU,
+the call raises.
+
+    paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale)
+    reshape_and_cache(key, value, k_cache, v_cache, slot_mapping)
+    copy_blocks(caches, src_dst_pairs)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Iterable, Optional, Tuple, Union
+
+import torch
+
+__all__ = ["paged_attention_decode", "reshape_and_cache", "copy_blocks", "workspace_size",
+           "workspace_init", "version", "strerror", "PagedKVError", "library_path", "load"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+_lib = None
+
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+
+
+class PagedKVError(RuntimeError):
+    """A non-zero status from the library (the message is pkv_strerror's text)."""
+
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} (code {code})")
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libpagedkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.pkv_version.restype = ctypes.c_char_p
+    lib.pkv_version.argtypes = []
+    lib.pkv_strerror.restype = ctypes.c_char_p
+    lib.pkv_strerror.argtypes = [_I]
+    lib.pkv_paged_attention_workspace_size.restype = ctypes.c_size_t
+    lib.pkv_paged_attention_workspace_size.argtypes = [_I] * 7
+    lib.pkv_workspace_init.restype = _I
+    lib.pkv_workspace_init.argtypes = [_P, ctypes.c_size_t, _P]
+    lib.pkv_paged_attention_decode.restype = _I
+    lib.pkv_paged_attention_decode.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_float] + \
+        [_I] * 9 + [_P, ctypes.c_size_t, _P]
+    lib.pkv_reshape_and_cache.restype = _I
+    lib.pkv_reshape_and_cache.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
+    lib.pkv_copy_blocks.restype = _I
+    lib.pkv_copy_blocks.argtypes = [_P, _P, _I, _I, ctypes.c_size_t, _P]
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load().pkv_version().decode()
+
+
+def strerror(code: int) -> str:
+    return load().pkv_strerror(int(code)).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise PagedKVError(code, what)
+
+
+def _gpu(t: torch.Tensor, name: str, dtype=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                   block_size: int, max_blocks_per_seq: int, partition_size: int = 0) -> int:
+    return int(load().pkv_paged_attention_workspace_size(num_seqs, num_heads, num_kv_heads,
+                                                          head_dim, block_size,
+                                                          max_blocks_per_seq, partition_size))
+
+
+def workspace_init(workspace: torch.Tensor) -> None:
+    """Zero-fill a workspace on the current stream (needed once, before first use)."""
+    _gpu(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load().pkv_workspace_init(workspace.data_ptr(), nbytes, _stream(workspace.device)),
+           "pkv_workspace_init")
+
+
+# One zero-initialised workspace per (device, stream); the library leaves its
+# bookkeeping zeroed after every call, so a workspace can be reused by later calls
+# on the same stream.
+_WORKSPACES: Dict[Tuple[int, int], torch.Tensor] = {}
+
+
+def _workspace_for(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    key = (device.index if device.index is not None else torch.cuda.current_device(),
+           _stream(device))
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        workspace_init(ws)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                           v_cache: torch.Tensor, block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, scale: float, partition_size: int = 0,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[b,h,:] = attention of q[b,h,:] over the first context_lens[b] tokens that
+    block_tables[b] maps into the paged k_cache / v_cache ([num_blocks, Hkv, bs, D]).
+
+    ``workspace``: optional uint8 device tensor, zero-filled before its first use;
+    by default a cached per-(device, stream) workspace is used."""
+    for name, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _gpu(t, name, q.dtype)
+    _gpu(block_tables, "block_tables", torch.int32)
+    _gpu(context_lens, "context_lens", torch.int32)
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,Hq,D] and caches [num_blocks,Hkv,bs,D]")
+    B, Hq, D = q.shape
+    NB, Hkv, bs, D2 = k_cache.shape
+    if out.shape != q.shape or D2 != D:
+        raise ValueError("out must match q, and the caches' head_dim must match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    MB = block_tables.shape[1]
+    need = workspace_size(B, Hq, Hkv, D, bs, MB, partition_size)
+    if workspace is None:
+        workspace = _workspace_for(q.device, need)
+    else:
+        _gpu(workspace, "workspace")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = load().pkv_paged_attention_decode(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), B, Hq, Hkv, D, bs, MB,
+        NB, _DTYPES[q.dtype], int(partition_size), ws_ptr, ws_bytes, _stream(q.device))
+    _check(rc, "pkv_paged_attention_decode")
+    return out
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """Write key[t]/value[t] ([T, Hkv, D]) into the caches at slot_mapping[t]
+    (int64, physical_block * block_size + offset; negative = skip)."""
+    for name, t in (("key", key), ("value", value), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _gpu(t, name, key.dtype)
+    _gpu(slot_mapping, "slot_mapping", torch.int64)
+    if key.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {key.dtype}")
+    if key.dim() != 3 or value.shape != key.shape or k_cache.dim() != 4 or \
+            v_cache.shape != k_cache.shape:
+        raise ValueError("expected key/value [T,Hkv,D] and caches [num_blocks,Hkv,bs,D]")
+    T, Hkv, D = key.shape
+    NB, Hkv2, bs, D2 = k_cache.shape
+    if (Hkv2, D2) != (Hkv, D) or slot_mapping.shape != (T,):
+        raise ValueError("key/value and caches disagree on heads/head_dim, or slot_mapping != [T]")
+    rc = load().pkv_reshape_and_cache(key.data_ptr(), value.data_ptr(), k_cache.data_ptr(),
+                                      v_cache.data_ptr(), slot_mapping.data_ptr(), T, Hkv, D, bs,
+                                      NB, _DTYPES[key.dtype], _stream(key.device))
+    _check(rc, "pkv_reshape_and_cache")
+
+
+def copy_blocks(caches: Union[torch.Tensor, Iterable[torch.Tensor]],
+                src_dst_pairs: torch.Tensor) -> None:
+    """For each (src, dst) row of src_dst_pairs (int32 [n, 2] on the device), copy
+    block src to block dst in every pool of ``caches``."""
+    if isinstance(caches, torch.Tensor):
+        caches = [caches]
+    _gpu(src_dst_pairs, "src_dst_pairs", torch.int32)
+    if src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be [n, 2]")
+    n = src_dst_pairs.shape[0]
+    for c in caches:
+        _gpu(c, "cache")
+        nb = c.shape[0]
+        block_bytes = (c.numel() // nb) * c.element_size() if nb else 0
+        rc = load().pkv_copy_blocks(c.data_ptr(), src_dst_pairs.data_ptr(), n, nb, block_bytes,
+                                    _stream(c.device))
+        _check(rc, "pkv_copy_blocks")

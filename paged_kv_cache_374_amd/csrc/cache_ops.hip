@@ -1,0 +1,119 @@
+// Cache companions of paged decode attention: slot-mapped append and block copy.
+//
+// Both are pure data movement. Each thread moves one 16-byte (or 4-byte) chunk per
+// loop trip; consecutive threads take consecutive chunks of a row, so a wavefront's
+// stores cover contiguous runs of a KV row. Bounds are checked per chunk so that
+// no index array content can push an access outside the pools.
+#include "launchers.h"
+
+namespace pkv {
+
+namespace {
+
+// key/value [T, Hkv, D]; caches [num_blocks, Hkv, bs, D]; rows of row_chunks chunks.
+template <typename Chunk>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const Chunk* __restrict__ key, const Chunk* __restrict__ value, Chunk* __restrict__ k_cache,
+    Chunk* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int num_tokens,
+    int num_kv_heads, int row_chunks, int block_size, int num_blocks) {
+    const int64_t per_token = (int64_t)num_kv_heads * row_chunks;
+    const int64_t total = (int64_t)num_tokens * per_token;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = i / per_token;
+        const int64_t rem = i - t * per_token;          // h * row_chunks + c
+        const int64_t slot = slot_mapping[t];
+        if (slot < 0) continue;
+        const int64_t blk = slot / block_size;
+        if (blk >= num_blocks) continue;
+        const int64_t off = slot - blk * block_size;
+        const int64_t h = rem / row_chunks;
+        const int64_t c = rem - h * row_chunks;
+        const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_chunks + c;
+        k_cache[dst] = key[i];
+        v_cache[dst] = value[i];
+    }
+}
+
+// One block pair per grid row; threads stride over the block's chunks.
+template <typename Chunk>
+__global__ __launch_bounds__(256) void copy_blocks_kernel(Chunk* __restrict__ cache,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int num_pairs, int num_blocks,
+                                                          int64_t block_chunks) {
+    for (int pi = blockIdx.y; pi < num_pairs; pi += gridDim.y) {
+        const int src = pairs[2 * pi];
+        const int dst = pairs[2 * pi + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) continue;
+        const Chunk* s = cache + (int64_t)src * block_chunks;
+        Chunk* d = cache + (int64_t)dst * block_chunks;
+        for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < block_chunks;
+             c += (int64_t)gridDim.x * blockDim.x)
+            d[c] = s[c];
+    }
+}
+
+int grid_for(int64_t items, int threads, int cap) {
+    int64_t g = (items + threads - 1) / threads;
+    if (g < 1) g = 1;
+    return (int)(g > cap ? cap : g);
+}
+
+}  // namespace
+
+int launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                             const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                             int head_dim, int block_size, int num_blocks, int elt_bytes,
+                             hipStream_t stream) {
+    const int row_bytes = head_dim * elt_bytes;
+    const int64_t rows = (int64_t)num_tokens * num_kv_heads;
+    if (row_bytes % 16 == 0) {
+        const int rc = row_bytes / 16;
+        hipLaunchKernelGGL(reshape_and_cache_kernel<uint4>, dim3(grid_for(rows * rc, 256, 65536)),
+                           dim3(256), 0, stream, (const uint4*)key, (const uint4*)value,
+                           (uint4*)k_cache, (uint4*)v_cache, slot_mapping, num_tokens,
+                           num_kv_heads, rc, block_size, num_blocks);
+    } else {
+        const int rc = row_bytes / 4;
+        hipLaunchKernelGGL(reshape_and_cache_kernel<uint32_t>,
+                           dim3(grid_for(rows * rc, 256, 65536)), dim3(256), 0, stream,
+                           (const uint32_t*)key, (const uint32_t*)value, (uint32_t*)k_cache,
+                           (uint32_t*)v_cache, slot_mapping, num_tokens, num_kv_heads, rc,
+                           block_size, num_blocks);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_copy_blocks(void* cache, const int32_t* pairs, int num_pairs, int num_blocks,
+                       size_t block_bytes, hipStream_t stream) {
+    const int gy = num_pairs > 65535 ? 65535 : num_pairs;
+    if (block_bytes % 16 == 0) {
+        const int64_t chunks = (int64_t)(block_bytes / 16);
+        hipLaunchKernelGGL(copy_blocks_kernel<uint4>, dim3(grid_for(chunks, 256, 64), gy),
+                           dim3(256), 0, stream, (uint4*)cache, pairs, num_pairs, num_blocks,
+                           chunks);
+    } else {
+        const int64_t chunks = (int64_t)(block_bytes / 4);
+        hipLaunchKernelGGL(copy_blocks_kernel<uint32_t>, dim3(grid_for(chunks, 256, 64), gy),
+                           dim3(256), 0, stream, (uint32_t*)cache, pairs, num_pairs, num_blocks,
+                           chunks);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Zero-fill with a kernel (graph-capture friendly: no memset node).
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int64_t words) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+int launch_zero(void* p, size_t bytes, hipStream_t stream) {
+    const int64_t words = (int64_t)(bytes / 4);
+    if (words == 0) return 0;
+    hipLaunchKernelGGL(zero_kernel, dim3(grid_for(words, 256, 4096)), dim3(256), 0, stream,
+                       (uint32_t*)p, words);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace pkv

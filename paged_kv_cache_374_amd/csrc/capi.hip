@@ -1,0 +1,181 @@
+// C ABI of the paged KV-cache library: argument checks, optional index validation,
+// path selection and kernel launches. See include/pagedkv.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <vector>
+
+#include "launchers.h"
+#include "pagedkv.h"
+#include "plan.h"
+
+namespace {
+
+bool validate_enabled() {
+    static const int on = [] {
+        const char* e = std::getenv("PKV_VALIDATE");
+        return (e && e[0] == '1') ? 1 : 0;
+    }();
+    return on != 0;
+}
+
+// Compute units of the current device (cached per device ordinal).
+int current_device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return -1;
+    if (dev >= 0 && dev < 64) cache[dev] = n;
+    return n;
+}
+
+template <typename T>
+bool fetch(std::vector<T>& host, const T* dev, size_t n, hipStream_t stream) {
+    host.resize(n);
+    if (n == 0) return true;
+    if (hipMemcpyAsync(host.data(), dev, n * sizeof(T), hipMemcpyDeviceToHost, stream) !=
+        hipSuccess)
+        return false;
+    return hipStreamSynchronize(stream) == hipSuccess;
+}
+
+int validate_tables(const pkv::DecodeShape& s, const int32_t* tables, const int32_t* ctx,
+                    hipStream_t stream) {
+    std::vector<int32_t> ht, hc;
+    if (!fetch(hc, ctx, (size_t)s.num_seqs, stream) ||
+        !fetch(ht, tables, (size_t)s.num_seqs * s.max_blocks, stream))
+        return PKV_E_LAUNCH;
+    for (int b = 0; b < s.num_seqs; ++b) {
+        const long long n = hc[b];
+        if (n < 0 || n > (long long)s.max_blocks * s.block_size) return PKV_E_INDEX;
+        const long long nb = (n + s.block_size - 1) / s.block_size;
+        for (long long j = 0; j < nb; ++j) {
+            const int32_t p = ht[(size_t)b * s.max_blocks + j];
+            if (p < 0 || p >= s.num_blocks) return PKV_E_INDEX;
+        }
+    }
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_version(void) { return "pagedkv 0.1.0 (gfx950)"; }
+
+const char* pkv_strerror(int code) {
+    switch (code) {
+        case PKV_OK: return "success";
+        case PKV_E_NULL: return "a required pointer is NULL";
+        case PKV_E_SHAPE: return "invalid or inconsistent sizes";
+        case PKV_E_HEADS: return "num_heads must be a multiple of num_kv_heads within the supported group size";
+        case PKV_E_UNSUPPORTED: return "unsupported dtype / head_dim / block_size";
+        case PKV_E_WORKSPACE: return "workspace missing or too small";
+        case PKV_E_LAUNCH: return "the HIP runtime rejected a launch or copy";
+        case PKV_E_INDEX: return "an index array holds an out-of-range entry (PKV_VALIDATE)";
+        case PKV_E_DEVICE: return "no current HIP device";
+        default: return "unknown pagedkv error";
+    }
+}
+
+int pkv_workspace_init(void* workspace, size_t workspace_bytes, pkv_stream_t stream) {
+    if (workspace_bytes == 0) return PKV_OK;
+    if (!workspace) return PKV_E_NULL;
+    return pkv::launch_zero(workspace, workspace_bytes, (hipStream_t)stream) == 0 ? PKV_OK
+                                                                              : PKV_E_LAUNCH;
+}
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, float scale, int num_seqs,
+                               int num_heads, int num_kv_heads, int head_dim, int block_size,
+                               int max_blocks_per_seq, int num_blocks, pkv_dtype dtype,
+                               int partition_size, void* workspace, size_t workspace_bytes,
+                               pkv_stream_t stream) {
+    pkv::DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, num_blocks, (int)dtype, partition_size};
+    pkv::DecodePlan plan{};
+    const int rc = pkv::plan_decode(s, &plan);
+    if (rc != PKV_OK) return rc;
+    if (num_seqs == 0) return PKV_OK;
+    if (num_seqs > 65535) return PKV_E_SHAPE;
+    if (!out || !q || !context_lens) return PKV_E_NULL;
+    if (max_blocks_per_seq > 0 && (!k_cache || !v_cache || !block_tables)) return PKV_E_NULL;
+    if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes)) return PKV_E_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_enabled()) {
+        const int v = validate_tables(s, block_tables, context_lens, st);
+        if (v != PKV_OK) return v;
+    }
+    pkv::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, scale, s, workspace};
+    int lr;
+    if (plan.path == pkv::Path::Generic) {
+        lr = pkv::launch_decode_generic(a, plan, st);
+    } else {
+        const int cus = current_device_cus();
+        if (cus <= 0) return PKV_E_DEVICE;
+        lr = pkv::launch_decode_mfma(a, plan, cus, st);
+    }
+    return lr == 0 ? PKV_OK : PKV_E_LAUNCH;
+}
+
+int pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                          const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                          int head_dim, int block_size, int num_blocks, pkv_dtype dtype,
+                          pkv_stream_t stream) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks < 0)
+        return PKV_E_SHAPE;
+    int elt;
+    switch (dtype) {
+        case PKV_FLOAT32: elt = 4; break;
+        case PKV_BFLOAT16:
+        case PKV_FLOAT16: elt = 2; break;
+        default: return PKV_E_UNSUPPORTED;
+    }
+    if ((head_dim * elt) % 4 != 0) return PKV_E_UNSUPPORTED;
+    if (num_tokens == 0) return PKV_OK;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_E_NULL;
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_enabled()) {
+        std::vector<int64_t> hs;
+        if (!fetch(hs, slot_mapping, (size_t)num_tokens, st)) return PKV_E_LAUNCH;
+        for (int64_t x : hs)
+            if (x >= (int64_t)num_blocks * block_size) return PKV_E_INDEX;
+    }
+    return pkv::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_tokens,
+                                         num_kv_heads, head_dim, block_size, num_blocks, elt,
+                                         st) == 0
+               ? PKV_OK
+               : PKV_E_LAUNCH;
+}
+
+int pkv_copy_blocks(void* cache, const int32_t* src_dst_pairs, int num_pairs, int num_blocks,
+                    size_t block_bytes, pkv_stream_t stream) {
+    if (num_pairs < 0 || num_blocks < 0) return PKV_E_SHAPE;
+    if (block_bytes % 4 != 0) return PKV_E_UNSUPPORTED;
+    if (num_pairs == 0 || block_bytes == 0) return PKV_OK;
+    if (!cache || !src_dst_pairs) return PKV_E_NULL;
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_enabled()) {
+        std::vector<int32_t> hp;
+        if (!fetch(hp, src_dst_pairs, (size_t)num_pairs * 2, st)) return PKV_E_LAUNCH;
+        std::vector<char> role((size_t)num_blocks, 0);   // 1 = source, 2 = destination
+        for (int i = 0; i < num_pairs; ++i) {
+            const int32_t a = hp[2 * i], b = hp[2 * i + 1];
+            if (a < 0 || a >= num_blocks || b < 0 || b >= num_blocks) return PKV_E_INDEX;
+            if (role[b] != 0 || role[a] == 2) return PKV_E_INDEX;
+            role[a] = 1;
+            role[b] = 2;
+        }
+    }
+    return pkv::launch_copy_blocks(cache, src_dst_pairs, num_pairs, num_blocks, block_bytes,
+                                   st) == 0
+               ? PKV_OK
+               : PKV_E_LAUNCH;
+}
+
+}  // extern "C"

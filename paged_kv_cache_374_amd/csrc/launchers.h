@@ -1,0 +1,46 @@
+// Internal launch entry points (host functions that enqueue kernels). Each returns 0
+// on success or -1 if the HIP runtime rejected a launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+#include "plan.h"
+
+namespace pkv {
+
+int launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                             const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                             int head_dim, int block_size, int num_blocks, int elt_bytes,
+                             hipStream_t stream);
+
+int launch_copy_blocks(void* cache, const int32_t* pairs, int num_pairs, int num_blocks,
+                       size_t block_bytes, hipStream_t stream);
+
+int launch_zero(void* p, size_t bytes, hipStream_t stream);
+
+struct DecodeArgs {
+    void* out;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    float scale;
+    DecodeShape shape;
+    void* workspace;
+};
+
+// VALU kernel over fixed partitions (+ reduction when a context spans several).
+int launch_decode_generic(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+
+// Log-sum-exp merge of per-partition partial results (shared by the fixed-partition
+// paths).
+int launch_partition_reduce(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+
+// Matrix-core kernels (bfloat16/float16, block_size 16).
+int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
+                       hipStream_t stream);
+
+}  // namespace pkv

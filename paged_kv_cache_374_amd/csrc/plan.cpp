@@ -1,0 +1,89 @@
+// Host-side validation and launch planning for paged decode attention (no HIP calls).
+#include "plan.h"
+
+#include "pagedkv.h"
+
+namespace pkv {
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+
+// Switched on once the matrix-core kernel exists.
+constexpr bool kMfmaBuilt = false;
+
+bool block_size_ok(int bs) {
+    return bs == 1 || bs == 2 || bs == 4 || bs == 8 || bs == 16 || bs == 32;
+}
+
+}  // namespace
+
+bool mfma_eligible(int dtype, int head_dim, int block_size, int group) {
+    return kMfmaBuilt && (dtype == PKV_BFLOAT16 || dtype == PKV_FLOAT16) && block_size == 16 &&
+           (head_dim == 64 || head_dim == 128) && group >= 1 && group <= kMaxGroup;
+}
+
+int plan_decode(const DecodeShape& s, DecodePlan* plan) {
+    if (s.num_seqs < 0 || s.num_heads <= 0 || s.num_kv_heads <= 0 || s.head_dim <= 0 ||
+        s.block_size <= 0 || s.max_blocks < 0 || s.num_blocks < 0 || s.partition_size < 0)
+        return PKV_E_SHAPE;
+    if (s.num_heads % s.num_kv_heads != 0) return PKV_E_HEADS;
+    const int group = s.num_heads / s.num_kv_heads;
+    if (group > kMaxGroup) return PKV_E_HEADS;
+    if (s.dtype != PKV_FLOAT32 && s.dtype != PKV_BFLOAT16 && s.dtype != PKV_FLOAT16)
+        return PKV_E_UNSUPPORTED;
+    if (!head_dim_ok(s.head_dim) || !block_size_ok(s.block_size)) return PKV_E_UNSUPPORTED;
+    if (s.partition_size > 0 && s.partition_size % s.block_size != 0) return PKV_E_SHAPE;
+    const long long max_ctx = (long long)s.max_blocks * s.block_size;
+    if (max_ctx > (1LL << 30)) return PKV_E_SHAPE;
+
+    const bool mfma = mfma_eligible(s.dtype, s.head_dim, s.block_size, group);
+    if (!mfma && group > kMaxGroupGeneric) return PKV_E_HEADS;
+
+    DecodePlan p{};
+    p.group = group;
+    if (mfma && s.partition_size == 0 && s.num_seqs <= kMaxSeqsBalanced) {
+        p.path = Path::MfmaBalanced;
+        p.max_workers = kMaxWorkers;
+        const size_t counters = (size_t)s.num_seqs * s.num_kv_heads * sizeof(int32_t);
+        const size_t slot = (size_t)group * (s.head_dim + 2) * sizeof(float);
+        p.off_counters = 0;
+        p.off_partials = align_up(counters, 256);
+        p.bytes = p.off_partials + (size_t)2 * kMaxWorkers * slot;
+        if (s.num_seqs == 0) p.bytes = 0;
+    } else {
+        p.path = mfma ? Path::MfmaPartitioned : Path::Generic;
+        p.partition_tokens = s.partition_size > 0 ? s.partition_size : kDefaultPartition;
+        p.max_partitions = (int)((max_ctx + p.partition_tokens - 1) / p.partition_tokens);
+        if (p.max_partitions < 1) p.max_partitions = 1;
+        if (p.max_partitions > 1 && s.num_seqs > 0) {
+            const size_t rows = (size_t)s.num_seqs * s.num_heads * p.max_partitions;
+            p.off_m = 0;
+            p.off_l = align_up(rows * sizeof(float), 256);
+            p.off_o = p.off_l + align_up(rows * sizeof(float), 256);
+            p.bytes = p.off_o + rows * s.head_dim * sizeof(float);
+        }
+    }
+    *plan = p;
+    return PKV_OK;
+}
+
+}  // namespace pkv
+
+extern "C" size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads,
+                                                     int num_kv_heads, int head_dim,
+                                                     int block_size, int max_blocks_per_seq,
+                                                     int partition_size) {
+    // The dtype only matters for eligibility of the matrix-core path; size for the
+    // larger of the two layouts so one workspace serves every dtype.
+    size_t best = 0;
+    for (int dtype : {PKV_FLOAT32, PKV_BFLOAT16}) {
+        pkv::DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                           max_blocks_per_seq, 0, dtype, partition_size};
+        pkv::DecodePlan p{};
+        if (pkv::plan_decode(s, &p) == PKV_OK && p.bytes > best) best = p.bytes;
+    }
+    return best;
+}

@@ -1,0 +1,52 @@
+// Host-side validation and launch planning for paged decode attention.
+// Plain C++ (no HIP calls): every decision here depends only on sizes, so it can be
+// exercised without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace pkv {
+
+enum class Path {
+    Generic,          // VALU kernel, fixed partitions + reduction kernel
+    MfmaBalanced,     // matrix-core kernel, equal-share work split, in-kernel merge
+    MfmaPartitioned,  // matrix-core kernel, fixed partitions + reduction kernel
+};
+
+struct DecodeShape {
+    int num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks, num_blocks;
+    int dtype;           // pkv_dtype
+    int partition_size;  // 0 = library's choice
+};
+
+// Workspace layout (byte offsets into the caller's workspace).
+struct DecodePlan {
+    Path path;
+    int group;              // num_heads / num_kv_heads
+    int partition_tokens;   // fixed-partition paths: tokens per partition
+    int max_partitions;     // fixed-partition paths: ceil(max_blocks*block_size / partition)
+    int max_workers;        // balanced path: upper bound on workers (partial slots = 2 per worker)
+    size_t off_m, off_l, off_o;          // fixed-partition partial results
+    size_t off_counters, off_partials;   // balanced path
+    size_t bytes;                        // total workspace bytes
+};
+
+// Largest number of workers the balanced path launches; sizes its partial slots.
+constexpr int kMaxWorkers = 4096;
+// Partition length the generic path uses when the caller passes 0.
+constexpr int kDefaultPartition = 512;
+// Largest grouped-query factor any path supports.
+constexpr int kMaxGroup = 16;
+// Largest group the generic (VALU) kernel supports.
+constexpr int kMaxGroupGeneric = 8;
+// Sequences the balanced path scans in its prologue (LDS-resident prefix sums).
+constexpr int kMaxSeqsBalanced = 8192;
+
+// Validate sizes and choose a path. Returns 0 or a negative PKV_E_* code.
+int plan_decode(const DecodeShape& s, DecodePlan* plan);
+
+// True when the matrix-core kernel supports this dtype / head_dim / block_size / group.
+bool mfma_eligible(int dtype, int head_dim, int block_size, int group);
+
+}  // namespace pkv

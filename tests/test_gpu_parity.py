@@ -1,0 +1,238 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle.
+
+Bars: bit-exact for reshape_and_cache and copy_blocks (whole pools compared, the
+untouched bytes included); attention within max-abs 1e-5 for float32 KV and 2e-2
+for bfloat16 KV (float32 accumulation). float16 KV uses 5e-3: its 10-bit mantissa
+rounds the output 8x finer than bfloat16's 7 bits, so the bfloat16 bound scaled by
+that ratio is 2.5e-3; 5e-3 leaves a 2x margin.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_374_amd as pkv
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2, torch.float16: 5e-3}
+DEV = torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _max_err(got, want):
+    g = got.detach().cpu().to(torch.float64).numpy()
+    assert np.all(np.isfinite(g)), "non-finite output"
+    return float(np.max(np.abs(g - want))) if g.size else 0.0
+
+
+def decode(s, q=None, kc=None, vc=None, tables=None, ctx=None, partition_size=0):
+    q = s.q if q is None else q
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_decode(out, q, s.k_cache if kc is None else kc,
+                               s.v_cache if vc is None else vc,
+                               s.block_tables if tables is None else tables,
+                               s.context_lens if ctx is None else ctx, s.scale,
+                               partition_size=partition_size)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_decode(s, rows=None, kc=None, vc=None, ctx=None, tables=None):
+    return oracle.paged_attention(s.q, s.k_cache if kc is None else kc,
+                                  s.v_cache if vc is None else vc,
+                                  s.block_tables if tables is None else tables,
+                                  s.context_lens if ctx is None else ctx, s.scale, rows=rows)
+
+
+# ------------------------------------------------------------------ tiny float32 case
+def test_tiny_fp32_full_step():
+    _say("tiny_fp32: decode, copy_blocks, reshape_and_cache, decode")
+    s = W.tiny_fp32(device=DEV, gen_device="cpu")
+    out0 = decode(s, ctx=s.context_lens_before, tables=s.block_tables_before)
+    want0 = oracle_decode(s, ctx=s.context_lens_before, tables=s.block_tables_before)
+    assert _max_err(out0, want0) <= TOL[torch.float32]
+    kc, vc = s.k_cache.clone(), s.v_cache.clone()
+    pkv.copy_blocks([kc, vc], s.copy_pairs)
+    torch.cuda.synchronize()
+    ek = oracle.copy_blocks(s.k_cache, s.copy_pairs)
+    ev = oracle.copy_blocks(s.v_cache, s.copy_pairs)
+    assert torch.equal(kc.cpu(), ek) and torch.equal(vc.cpu(), ev)
+    pkv.reshape_and_cache(s.new_k, s.new_v, kc, vc, s.slot_mapping)
+    torch.cuda.synchronize()
+    ek, ev = oracle.reshape_and_cache(s.new_k, s.new_v, ek, ev, s.slot_mapping)
+    assert torch.equal(kc.cpu(), ek) and torch.equal(vc.cpu(), ev)
+    out1 = decode(s, kc=kc, vc=vc)
+    want1 = oracle_decode(s, kc=ek, vc=ev)
+    assert _max_err(out1, want1) <= TOL[torch.float32]
+    for part in (4, 8, 16, 64):          # forced split-K through the reduction kernel
+        outp = decode(s, kc=kc, vc=vc, partition_size=part)
+        assert _max_err(outp, want1) <= TOL[torch.float32], part
+
+
+# ------------------------------------------------------------------ random sweep
+SWEEP = []
+for dt in (torch.float32, torch.bfloat16, torch.float16):
+    for d in (64, 128, 256):
+        for bs, g in ((1, 1), (2, 2), (4, 4), (8, 8), (16, 1), (16, 4), (16, 8), (32, 2)):
+            SWEEP.append((dt, d, bs, g))
+
+
+@pytest.mark.parametrize("dt,d,bs,group", SWEEP,
+                         ids=[f"{str(a).split('.')[-1]}-d{b}-bs{c}-g{e}" for a, b, c, e in SWEEP])
+def test_random_batches(dt, d, bs, group):
+    seed = 300 + d + bs * 7 + group * 13 + TOL[dt].__hash__() % 17
+    _say(f"random batch {dt} d={d} bs={bs} g={group} seed={seed}")
+    s = W.random_small(seed, batch=5, num_heads=2 * group, num_kv_heads=2, head_dim=d,
+                       block_size=bs, max_ctx=600, min_ctx=1, dtype=dt, device=DEV)
+    want = oracle_decode(s)
+    for part in (0, 64 if bs <= 64 else bs):
+        part = (part // bs) * bs
+        out = decode(s, partition_size=part)
+        err = _max_err(out, want)
+        assert err <= TOL[dt], f"partition {part}: max err {err}"
+
+
+def test_ragged_edges_bf16():
+    """Lengths at 1, block boundaries +-1 and a partition boundary, one empty row."""
+    _say("ragged edges bf16")
+    lens = [1, 15, 16, 17, 31, 32, 33, 511, 512, 513, 0, 1024]
+    s = W.random_small(77, batch=len(lens), num_heads=8, num_kv_heads=2, head_dim=128,
+                       block_size=16, max_ctx=1024, dtype=torch.bfloat16, device=DEV)
+    ctx = torch.tensor(lens, dtype=torch.int32)
+    # rebuild tables for these lengths from a fresh shuffled pool
+    pool = W.BlockPool(s.num_blocks, torch.randperm(s.num_blocks,
+                                                    generator=torch.Generator().manual_seed(3)))
+    seqs = [W.prefill(pool, n, 16) for n in lens]
+    tables = torch.tensor(W.pack_tables(seqs, 64), dtype=torch.int32)
+    s.block_tables, s.context_lens = tables.to(DEV), ctx.to(DEV)
+    want = oracle_decode(s)
+    for part in (0, 512, 16):
+        out = decode(s, partition_size=part)
+        assert torch.all(out[10].float() == 0), "empty context must give zeros"
+        assert _max_err(out, want) <= TOL[torch.bfloat16], part
+
+
+# ------------------------------------------------------------------ invariants
+def test_context_one_returns_v0_bit_exact():
+    for dt in (torch.float32, torch.bfloat16):
+        _say(f"ctx=1 {dt}")
+        s = W.random_small(88, batch=4, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                           max_ctx=1, dtype=dt, device=DEV)
+        out = decode(s)
+        tb = s.block_tables.cpu()
+        for b in range(4):
+            for h in range(8):
+                v0 = s.v_cache[int(tb[b, 0]), h // 4, 0]
+                assert torch.equal(out[b, h], v0), (b, h)
+
+
+def test_placement_permutation_bit_identical():
+    _say("placement permutation bf16")
+    s = W.random_small(91, batch=6, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                       max_ctx=900, dtype=torch.bfloat16, device=DEV)
+    perm = torch.randperm(s.num_blocks, generator=torch.Generator().manual_seed(5)).to(DEV)
+    kc2 = torch.empty_like(s.k_cache)
+    vc2 = torch.empty_like(s.v_cache)
+    kc2[perm] = s.k_cache
+    vc2[perm] = s.v_cache
+    tb = s.block_tables.clone()
+    used = tb >= 0
+    tb[used] = perm[tb[used].long()].to(torch.int32)
+    a = decode(s)
+    b = decode(s, kc=kc2, vc=vc2, tables=tb)
+    assert torch.equal(a, b)
+
+
+def test_stale_slots_and_free_blocks_poisoned_with_nan():
+    _say("NaN poisoning bf16 and fp32")
+    for dt in (torch.bfloat16, torch.float32):
+        s = W.random_small(93, batch=6, num_heads=8, num_kv_heads=2, head_dim=128,
+                           block_size=16, max_ctx=500, dtype=dt, device=DEV)
+        a = decode(s)
+        kc, vc = s.k_cache.clone(), s.v_cache.clone()
+        tb, ctx = s.block_tables.cpu(), s.context_lens.cpu()
+        keep = torch.zeros(s.num_blocks, 16, dtype=torch.bool)
+        for b in range(tb.shape[0]):
+            for t in range(int(ctx[b])):
+                keep[int(tb[b, t // 16]), t % 16] = True
+        poison = (~keep).to(DEV)
+        kc.permute(0, 2, 1, 3)[poison] = float("nan")
+        vc.permute(0, 2, 1, 3)[poison] = float("nan")
+        for part in (0, 64):
+            b2 = decode(s, kc=kc, vc=vc, partition_size=part)
+            a2 = a if part == 0 else decode(s, partition_size=part)
+            assert torch.equal(a2, b2), (dt, part)
+
+
+def test_deterministic_across_runs():
+    _say("determinism")
+    s = W.random_small(95, batch=8, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                       max_ctx=2000, dtype=torch.bfloat16, device=DEV)
+    assert torch.equal(decode(s), decode(s))
+    assert torch.equal(decode(s, partition_size=256), decode(s, partition_size=256))
+
+
+# ------------------------------------------------------------------ serving-shape workloads
+def _sample_rows(B, H, n, seed):
+    g = torch.Generator().manual_seed(seed)
+    bs = torch.randint(0, B, (n,), generator=g)
+    hs = torch.randint(0, H, (n,), generator=g)
+    return [(int(b), int(h)) for b, h in zip(bs, hs)]
+
+
+def test_llama3_8b_decode_full():
+    _say("llama3_8b_decode: full output vs oracle")
+    s = W.llama3_8b_decode(device=DEV, gen_device=DEV)
+    want = oracle_decode(s)
+    out = decode(s)
+    assert _max_err(out, want) <= TOL[torch.bfloat16]
+
+
+def test_llama_70b_decode_sampled():
+    _say("llama_70b_decode: 512 sampled rows vs oracle")
+    s = W.llama_70b_decode(device=DEV, gen_device=DEV)
+    out = decode(s)
+    rows = _sample_rows(256, 64, 512, 1)
+    # always include the longest and shortest contexts
+    ctx = s.context_lens.cpu()
+    rows += [(int(ctx.argmax()), 0), (int(ctx.argmin()), 63)]
+    want = oracle_decode(s, rows=rows)
+    got = torch.stack([out[b, h] for b, h in rows])
+    assert _max_err(got, want) <= TOL[torch.bfloat16]
+
+
+def test_long_context_split_k_sampled():
+    _say("long_context_decode: sampled rows vs oracle, partitions of 512")
+    s = W.long_context_decode(device=DEV, gen_device=DEV)
+    rows = _sample_rows(8, 32, 24, 2)
+    want = oracle_decode(s, rows=rows)
+    for part in (512, 0):
+        out = decode(s, partition_size=part)
+        got = torch.stack([out[b, h] for b, h in rows])
+        assert _max_err(got, want) <= TOL[torch.bfloat16], part
+
+
+@pytest.mark.parametrize("prefix", [2048, 2040])
+def test_shared_prefix_cow_step(prefix):
+    _say(f"shared_prefix_cow prefix={prefix}: copy_blocks, reshape_and_cache, decode")
+    s = W.shared_prefix_cow(device=DEV, gen_device=DEV, prefix_tokens=prefix)
+    kc, vc = s.k_cache.clone(), s.v_cache.clone()
+    pkv.copy_blocks([kc, vc], s.copy_pairs)
+    pkv.reshape_and_cache(s.new_k, s.new_v, kc, vc, s.slot_mapping)
+    torch.cuda.synchronize()
+    ek = oracle.copy_blocks(s.k_cache, s.copy_pairs)
+    ev = oracle.copy_blocks(s.v_cache, s.copy_pairs)
+    ek, ev = oracle.reshape_and_cache(s.new_k, s.new_v, ek, ev, s.slot_mapping)
+    assert torch.equal(kc.cpu(), ek) and torch.equal(vc.cpu(), ev)
+    out = decode(s, kc=kc, vc=vc)
+    rows = _sample_rows(256, 32, 256, 3)
+    want = oracle_decode(s, rows=rows, kc=ek, vc=ev)
+    got = torch.stack([out[b, h] for b, h in rows])
+    assert _max_err(got, want) <= TOL[torch.bfloat16]
