@@ -19,7 +19,8 @@ from typing import Dict, Iterable, Optional, Tuple, Union
 import torch
 
 __all__ = ["paged_attention_decode", "reshape_and_cache", "copy_blocks", "workspace_size",
-           "workspace_init", "version", "strerror", "PagedKVError", "library_path", "load"]
+           "workspace_init", "version", "strerror", "PagedKVError", "library_path", "load",
+           "PreparedDecode", "PreparedReshapeAndCache"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
@@ -132,15 +133,10 @@ def _workspace_for(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
     return ws
 
 
-def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
-                           v_cache: torch.Tensor, block_tables: torch.Tensor,
-                           context_lens: torch.Tensor, scale: float, partition_size: int = 0,
-                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """out[b,h,:] = attention of q[b,h,:] over the first context_lens[b] tokens that
-    block_tables[b] maps into the paged k_cache / v_cache ([num_blocks, Hkv, bs, D]).
-
-    ``workspace``: optional uint8 device tensor, zero-filled before its first use;
-    by default a cached per-(device, stream) workspace is used."""
+def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, partition_size,
+                 workspace, own_workspace):
+    """Validate one decode call; returns (ctypes argument tuple without the stream,
+    the workspace tensor in use)."""
     for name, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _gpu(t, name, q.dtype)
     _gpu(block_tables, "block_tables", torch.int32)
@@ -158,23 +154,63 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
     MB = block_tables.shape[1]
     need = workspace_size(B, Hq, Hkv, D, bs, MB, partition_size)
     if workspace is None:
-        workspace = _workspace_for(q.device, need)
+        if own_workspace and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace_init(workspace)
+        else:
+            workspace = _workspace_for(q.device, need)
     else:
         _gpu(workspace, "workspace")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = load().pkv_paged_attention_decode(
-        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), B, Hq, Hkv, D, bs, MB,
-        NB, _DTYPES[q.dtype], int(partition_size), ws_ptr, ws_bytes, _stream(q.device))
-    _check(rc, "pkv_paged_attention_decode")
+    args = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), float(scale), B, Hq, Hkv, D, bs,
+            MB, NB, _DTYPES[q.dtype], int(partition_size), ws_ptr, ws_bytes)
+    return args, workspace
+
+
+def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                           v_cache: torch.Tensor, block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, scale: float, partition_size: int = 0,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[b,h,:] = attention of q[b,h,:] over the first context_lens[b] tokens that
+    block_tables[b] maps into the paged k_cache / v_cache ([num_blocks, Hkv, bs, D]).
+
+    ``workspace``: optional uint8 device tensor, zero-filled before its first use;
+    by default a cached per-(device, stream) workspace is used."""
+    args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                           partition_size, workspace, False)
+    _check(load().pkv_paged_attention_decode(*args, _stream(q.device)),
+           "pkv_paged_attention_decode")
     return out
 
 
-def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
-                      v_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
-    """Write key[t]/value[t] ([T, Hkv, D]) into the caches at slot_mapping[t]
-    (int64, physical_block * block_size + offset; negative = skip)."""
+class PreparedDecode:
+    """A decode call validated once for a fixed set of tensors, for loops that run
+    it many times (serving steps, HIP graph capture). It owns a zero-initialised
+    workspace unless one is passed. Calling it enqueues the decode on ``stream`` (a
+    raw hipStream_t handle) or on the current stream of the tensors' device."""
+
+    def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                 partition_size: int = 0, workspace: Optional[torch.Tensor] = None):
+        self._args, self.workspace = _decode_args(out, q, k_cache, v_cache, block_tables,
+                                                  context_lens, scale, partition_size,
+                                                  workspace, True)
+        self._fn = load().pkv_paged_attention_decode
+        self._device = q.device
+        self.out = out
+        # the raw pointers above stay valid only while these tensors are alive
+        self._keep = (out, q, k_cache, v_cache, block_tables, context_lens)
+
+    def __call__(self, stream: Optional[int] = None) -> torch.Tensor:
+        st = _stream(self._device) if stream is None else stream
+        rc = self._fn(*self._args, st)
+        if rc != 0:
+            raise PagedKVError(rc, "pkv_paged_attention_decode")
+        return self.out
+
+
+def _append_args(key, value, k_cache, v_cache, slot_mapping):
     for name, t in (("key", key), ("value", value), ("k_cache", k_cache), ("v_cache", v_cache)):
         _gpu(t, name, key.dtype)
     _gpu(slot_mapping, "slot_mapping", torch.int64)
@@ -187,10 +223,32 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
     NB, Hkv2, bs, D2 = k_cache.shape
     if (Hkv2, D2) != (Hkv, D) or slot_mapping.shape != (T,):
         raise ValueError("key/value and caches disagree on heads/head_dim, or slot_mapping != [T]")
-    rc = load().pkv_reshape_and_cache(key.data_ptr(), value.data_ptr(), k_cache.data_ptr(),
-                                      v_cache.data_ptr(), slot_mapping.data_ptr(), T, Hkv, D, bs,
-                                      NB, _DTYPES[key.dtype], _stream(key.device))
-    _check(rc, "pkv_reshape_and_cache")
+    return (key.data_ptr(), value.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            slot_mapping.data_ptr(), T, Hkv, D, bs, NB, _DTYPES[key.dtype])
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """Write key[t]/value[t] ([T, Hkv, D]) into the caches at slot_mapping[t]
+    (int64, physical_block * block_size + offset; negative = skip)."""
+    args = _append_args(key, value, k_cache, v_cache, slot_mapping)
+    _check(load().pkv_reshape_and_cache(*args, _stream(key.device)), "pkv_reshape_and_cache")
+
+
+class PreparedReshapeAndCache:
+    """reshape_and_cache validated once for a fixed set of tensors (see PreparedDecode)."""
+
+    def __init__(self, key, value, k_cache, v_cache, slot_mapping):
+        self._args = _append_args(key, value, k_cache, v_cache, slot_mapping)
+        self._fn = load().pkv_reshape_and_cache
+        self._device = key.device
+        self._keep = (key, value, k_cache, v_cache, slot_mapping)
+
+    def __call__(self, stream: Optional[int] = None) -> None:
+        st = _stream(self._device) if stream is None else stream
+        rc = self._fn(*self._args, st)
+        if rc != 0:
+            raise PagedKVError(rc, "pkv_reshape_and_cache")
 
 
 def copy_blocks(caches: Union[torch.Tensor, Iterable[torch.Tensor]],

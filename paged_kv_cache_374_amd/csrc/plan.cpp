@@ -11,8 +11,6 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 
-// Switched on once the matrix-core kernel exists.
-constexpr bool kMfmaBuilt = false;
 
 bool block_size_ok(int bs) {
     return bs == 1 || bs == 2 || bs == 4 || bs == 8 || bs == 16 || bs == 32;
@@ -21,8 +19,18 @@ bool block_size_ok(int bs) {
 }  // namespace
 
 bool mfma_eligible(int dtype, int head_dim, int block_size, int group) {
-    return kMfmaBuilt && (dtype == PKV_BFLOAT16 || dtype == PKV_FLOAT16) && block_size == 16 &&
-           (head_dim == 64 || head_dim == 128) && group >= 1 && group <= kMaxGroup;
+    return (dtype == PKV_BFLOAT16 || dtype == PKV_FLOAT16) && block_size == kMfmaBlockSize &&
+           head_dim == kMfmaHeadDim && group >= 1 && group <= kMaxGroup;
+}
+
+int balanced_workers(const DecodeShape& s, int num_cus, int wg_per_cu) {
+    if (num_cus <= 0 || wg_per_cu <= 0) return 0;
+    const long long blocks = (long long)s.num_seqs * s.num_kv_heads * s.max_blocks;
+    long long w = (long long)num_cus * wg_per_cu;
+    const long long need = (blocks + kShareMax - 1) / kShareMax;
+    if (need > w) w = need;
+    w = (w + 7) / 8 * 8;
+    return w > kMaxWorkers ? 0 : (int)w;
 }
 
 int plan_decode(const DecodeShape& s, DecodePlan* plan) {
@@ -44,24 +52,32 @@ int plan_decode(const DecodeShape& s, DecodePlan* plan) {
 
     DecodePlan p{};
     p.group = group;
-    if (mfma && s.partition_size == 0 && s.num_seqs <= kMaxSeqsBalanced) {
+    // The balanced path needs every sequence's length in LDS and at most kMaxWorkers
+    // workgroups of at most kShareMax blocks each.
+    const long long all_blocks = (long long)s.num_seqs * s.num_kv_heads * s.max_blocks;
+    const bool fits = s.num_seqs <= kMaxSeqsBalanced &&
+                      all_blocks <= (long long)kMaxWorkers * kShareMax &&
+                      (size_t)s.num_seqs * s.num_kv_heads * sizeof(int32_t) <= kCounterBytes;
+    if (mfma && s.partition_size == 0 && fits) {
         p.path = Path::MfmaBalanced;
         p.max_workers = kMaxWorkers;
-        const size_t counters = (size_t)s.num_seqs * s.num_kv_heads * sizeof(int32_t);
-        const size_t slot = (size_t)group * (s.head_dim + 2) * sizeof(float);
+        const size_t slot = (size_t)balanced_slot_floats(mfma_gmax(group)) * sizeof(float);
         p.off_counters = 0;
-        p.off_partials = align_up(counters, 256);
+        p.off_partials = kCounterBytes;
         p.bytes = p.off_partials + (size_t)2 * kMaxWorkers * slot;
         if (s.num_seqs == 0) p.bytes = 0;
     } else {
         p.path = mfma ? Path::MfmaPartitioned : Path::Generic;
         p.partition_tokens = s.partition_size > 0 ? s.partition_size : kDefaultPartition;
+        // the matrix-core partition kernel stages one partition's blocks in LDS
+        if (mfma && p.partition_tokens / s.block_size > kShareMax) p.path = Path::Generic;
+        if (p.path == Path::Generic && group > kMaxGroupGeneric) return PKV_E_HEADS;
         p.max_partitions = (int)((max_ctx + p.partition_tokens - 1) / p.partition_tokens);
         if (p.max_partitions < 1) p.max_partitions = 1;
         if (p.max_partitions > 1 && s.num_seqs > 0) {
             const size_t rows = (size_t)s.num_seqs * s.num_heads * p.max_partitions;
-            p.off_m = 0;
-            p.off_l = align_up(rows * sizeof(float), 256);
+            p.off_m = kCounterBytes;
+            p.off_l = p.off_m + align_up(rows * sizeof(float), 256);
             p.off_o = p.off_l + align_up(rows * sizeof(float), 256);
             p.bytes = p.off_o + rows * s.head_dim * sizeof(float);
         }

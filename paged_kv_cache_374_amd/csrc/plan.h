@@ -34,6 +34,17 @@ struct DecodePlan {
 
 // Largest number of workers the balanced path launches; sizes its partial slots.
 constexpr int kMaxWorkers = 4096;
+// Every workspace starts with this many bytes of merge counters, used only by the
+// balanced path and left zeroed by it; all other scratch lies above, so calls of any
+// path and shape can share one workspace without clobbering the counters.
+constexpr size_t kCounterBytes = size_t(1) << 20;
+// Largest share of blocks one balanced-path workgroup stages in LDS.
+constexpr int kShareMax = 2048;
+// Workgroups per compute unit the balanced path launches by default.
+constexpr int kWgPerCu = 2;
+// head_dim and block_size of the matrix-core kernels.
+constexpr int kMfmaHeadDim = 128;
+constexpr int kMfmaBlockSize = 16;
 // Partition length the generic path uses when the caller passes 0.
 constexpr int kDefaultPartition = 512;
 // Largest grouped-query factor any path supports.
@@ -41,12 +52,26 @@ constexpr int kMaxGroup = 16;
 // Largest group the generic (VALU) kernel supports.
 constexpr int kMaxGroupGeneric = 8;
 // Sequences the balanced path scans in its prologue (LDS-resident prefix sums).
-constexpr int kMaxSeqsBalanced = 8192;
+constexpr int kMaxSeqsBalanced = 4096;
 
 // Validate sizes and choose a path. Returns 0 or a negative PKV_E_* code.
 int plan_decode(const DecodeShape& s, DecodePlan* plan);
 
 // True when the matrix-core kernel supports this dtype / head_dim / block_size / group.
 bool mfma_eligible(int dtype, int head_dim, int block_size, int group);
+
+// Query heads per KV head that a matrix-core kernel instance is built for (4, 8, 16).
+constexpr int mfma_gmax(int group) { return group <= 4 ? 4 : group <= 8 ? 8 : 16; }
+
+// Floats of one balanced-path partial slot: o[gmax][128], m[gmax], l[gmax], padded to
+// a multiple of 64 floats.
+constexpr int balanced_slot_floats(int gmax) {
+    return ((gmax * kMfmaHeadDim + 2 * gmax) + 63) / 64 * 64;
+}
+
+// Workgroups the balanced path launches: wg_per_cu per compute unit, at least enough
+// that no share exceeds kShareMax blocks, rounded up to a multiple of 8 (one per
+// XCD). Returns 0 when that exceeds kMaxWorkers.
+int balanced_workers(const DecodeShape& s, int num_cus, int wg_per_cu);
 
 }  // namespace pkv

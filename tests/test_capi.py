@@ -47,7 +47,7 @@ def test_workspace_arithmetic_fixed_partitions():
     B, H, D, P = 8, 32, 128, 256
     rows = B * H * P
     align = lambda x: (x + 255) // 256 * 256
-    expect = align(rows * 4) * 2 + rows * D * 4
+    expect = (1 << 20) + align(rows * 4) * 2 + rows * D * 4   # counter region first
     assert pkv.workspace_size(B, H, 8, D, 16, 8192, 512) == expect
     # whole context in one partition: nothing to merge, no workspace
     assert pkv.workspace_size(4, 8, 8, 64, 4, 26, 0) == 0

@@ -236,3 +236,135 @@ def test_shared_prefix_cow_step(prefix):
     want = oracle_decode(s, rows=rows, kc=ek, vc=ev)
     got = torch.stack([out[b, h] for b, h in rows])
     assert _max_err(got, want) <= TOL[torch.bfloat16]
+
+
+# ------------------------------------------------------------------ matrix-core paths
+BAL = [(dt, hq, hkv, batch, max_ctx)
+       for dt in (torch.bfloat16, torch.float16)
+       for hq, hkv, batch, max_ctx in ((8, 8, 3, 40), (8, 4, 7, 300), (12, 4, 5, 1000),
+                                       (32, 8, 64, 2048), (40, 8, 9, 700), (64, 8, 33, 1500),
+                                       (32, 2, 4, 5000), (16, 1, 1, 20000), (4, 1, 300, 64))]
+
+
+@pytest.mark.parametrize("dt,hq,hkv,batch,max_ctx", BAL,
+                         ids=[f"{str(a).split('.')[-1]}-h{b}-kv{c}-B{d}-ctx{e}"
+                              for a, b, c, d, e in BAL])
+def test_mfma_balanced_and_partitioned(dt, hq, hkv, batch, max_ctx):
+    """Shares of a few blocks (many units cut between workgroups, merged by the last
+    one to finish), groups 1..16, and the fixed-partition kernel plus reduction."""
+    seed = 500 + hq + 3 * hkv + 7 * batch + max_ctx % 97
+    _say(f"mfma {dt} hq={hq} hkv={hkv} batch={batch} max_ctx={max_ctx} seed={seed}")
+    s = W.random_small(seed, batch=batch, num_heads=hq, num_kv_heads=hkv, head_dim=128,
+                       block_size=16, max_ctx=max_ctx, min_ctx=1, dtype=dt, device=DEV)
+    want = oracle_decode(s)
+    for part in (0, 512, 16):
+        out = decode(s, partition_size=part)
+        err = _max_err(out, want)
+        assert err <= TOL[dt], f"partition {part}: max err {err}"
+    # the balanced path leaves its counters zeroed: a second call agrees bit for bit
+    assert torch.equal(decode(s), decode(s))
+
+
+def test_mfma_empty_and_short_rows():
+    _say("mfma: empty rows mixed with one-token and block-boundary rows")
+    lens = [0, 1, 16, 0, 17, 2048, 0, 31, 33, 0]
+    s = W.random_small(611, batch=len(lens), num_heads=32, num_kv_heads=8, head_dim=128,
+                       block_size=16, max_ctx=2048, dtype=torch.bfloat16, device=DEV)
+    pool = W.BlockPool(s.num_blocks, torch.randperm(s.num_blocks,
+                                                    generator=torch.Generator().manual_seed(9)))
+    seqs = [W.prefill(pool, n, 16) for n in lens]
+    s.block_tables = torch.tensor(W.pack_tables(seqs, 128), dtype=torch.int32).to(DEV)
+    s.context_lens = torch.tensor(lens, dtype=torch.int32).to(DEV)
+    want = oracle_decode(s)
+    for part in (0, 512):
+        out = decode(s, partition_size=part)
+        for b, n in enumerate(lens):
+            if n == 0:
+                assert torch.all(out[b].float() == 0), (part, b)
+        assert _max_err(out, want) <= TOL[torch.bfloat16], part
+    allzero = torch.zeros_like(s.context_lens)
+    out = decode(s, ctx=allzero)
+    assert torch.all(out.float() == 0)
+
+
+def test_one_workspace_shared_by_every_path():
+    """A fixed-partition call must not disturb the balanced path's merge counters when
+    both use one workspace (regression: scratch used to overlap the counters)."""
+    _say("shared workspace: partitioned, balanced, generic, balanced")
+    s = W.random_small(701, batch=16, num_heads=32, num_kv_heads=8, head_dim=128,
+                       block_size=16, max_ctx=3000, dtype=torch.bfloat16, device=DEV)
+    MB = s.block_tables.shape[1]
+    need = max(pkv.workspace_size(16, 32, 8, 128, 16, MB, p) for p in (0, 512, 16))
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    pkv.workspace_init(ws)
+    want = oracle_decode(s)
+    outs = []
+    for part in (512, 0, 16, 0, 0):
+        out = torch.full_like(s.q, float("nan"))
+        pkv.paged_attention_decode(out, s.q, s.k_cache, s.v_cache, s.block_tables,
+                                   s.context_lens, s.scale, partition_size=part, workspace=ws)
+        torch.cuda.synchronize()
+        assert _max_err(out, want) <= TOL[torch.bfloat16], part
+        outs.append(out)
+    assert torch.equal(outs[1], outs[3]) and torch.equal(outs[3], outs[4])
+
+
+def test_prepared_calls_and_graph_replays():
+    """The prepared-call API and HIP-graph replays of it give the eager results on
+    every replay, with eager work and synchronisations between replays."""
+    _say("prepared calls + graph replays")
+    s = W.random_small(703, batch=24, num_heads=32, num_kv_heads=8, head_dim=128,
+                       block_size=16, max_ctx=2048, dtype=torch.bfloat16, device=DEV)
+    W.with_append(s, seed=703)
+    ref_k, ref_v = s.k_cache.clone(), s.v_cache.clone()
+    pkv.reshape_and_cache(s.new_k, s.new_v, ref_k, ref_v, s.slot_mapping)
+    ref = torch.empty_like(s.q)
+    pkv.paged_attention_decode(ref, s.q, ref_k, ref_v, s.block_tables, s.context_lens, s.scale)
+    torch.cuda.synchronize()
+    out = torch.full_like(s.q, float("nan"))
+    app = pkv.PreparedReshapeAndCache(s.new_k, s.new_v, s.k_cache, s.v_cache, s.slot_mapping)
+    dec = pkv.PreparedDecode(out, s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens,
+                             s.scale)
+    app()
+    dec()
+    torch.cuda.synchronize()
+    assert torch.equal(s.k_cache, ref_k) and torch.equal(s.v_cache, ref_v)
+    assert torch.equal(out, ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        app()
+        dec()
+    for i in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), i
+        assert torch.equal(s.k_cache, ref_k), i
+
+
+@pytest.mark.parametrize("hq,hkv,batch,max_ctx", [(32, 8, 6, 300), (16, 1, 2, 9000)])
+def test_balanced_merge_never_reads_stale_partials(hq, hkv, batch, max_ctx):
+    """Two batches of one shape alternate for many calls; every share is a few blocks,
+    so most units are merged across workgroups from partial slots that the previous
+    call filled with the other batch's data. Any stale read changes the output."""
+    _say(f"stale-partial stress hq={hq} hkv={hkv} batch={batch} max_ctx={max_ctx}")
+    sets = [W.random_small(800 + i, batch=batch, num_heads=hq, num_kv_heads=hkv, head_dim=128,
+                           block_size=16, max_ctx=max_ctx, min_ctx=max_ctx // 2,
+                           dtype=torch.bfloat16, device=DEV) for i in range(2)]
+    refs, decs = [], []
+    for s in sets:
+        want = oracle_decode(s)
+        out = torch.empty_like(s.q)
+        d = pkv.PreparedDecode(out, s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens,
+                               s.scale)
+        d()
+        torch.cuda.synchronize()
+        assert _max_err(out, want) <= TOL[torch.bfloat16]
+        refs.append(out.clone())
+        decs.append(d)
+    for it in range(300):
+        decs[it % 2]()
+        if it % 2 == 1:
+            torch.cuda.synchronize()
+            assert torch.equal(decs[0].out, refs[0]) and torch.equal(decs[1].out, refs[1]), it

@@ -287,3 +287,30 @@ WORKLOADS = {
     "long_context_decode": long_context_decode,
     "shared_prefix_cow": shared_prefix_cow,
 }
+
+
+def with_append(step: DecodeStep, seed: int = 0) -> DecodeStep:
+    """Turn a decode batch into a full decode step: the last token of every context
+    is the newly generated one, so its K/V are written into its slot first
+    (reshape_and_cache) and the decode then attends to it. New K/V values are drawn
+    like everything else (float32 N(0, 1), cast to the KV dtype); the slot of the
+    token at position ctx-1 is table[(ctx-1) // bs] * bs + (ctx-1) % bs."""
+    if step.new_k is not None:
+        return step
+    tables = step.block_tables.to("cpu")
+    ctx = step.context_lens.to("cpu").tolist()
+    bs = step.block_size
+    slots = []
+    for b, n in enumerate(ctx):
+        if n <= 0:
+            slots.append(-1)
+            continue
+        pos = n - 1
+        slots.append(int(tables[b, pos // bs]) * bs + pos % bs)
+    dev = step.block_tables.device
+    gen = torch.Generator(device=dev).manual_seed(seed + 104729)
+    shape = (len(ctx), step.num_kv_heads, step.head_dim)
+    step.new_k = _normal(shape, step.dtype, gen, dev)
+    step.new_v = _normal(shape, step.dtype, gen, dev)
+    step.slot_mapping = torch.tensor(slots, dtype=torch.int64).to(dev)
+    return step
