@@ -15,6 +15,7 @@ LIB = os.path.join(PKG, "libpagedkv.so")
 # Packed-FP32 vector ops are disabled for all device code (hipcc would otherwise
 # form them from ordinary float code).
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+               "-mllvm", "-amdgpu-mfma-vgpr-form=1",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-Wall", "-Wno-unused-command-line-argument"]
 

@@ -57,8 +57,11 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTabMax = kShareMax;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kLazy = 8.0f;    // rescale only when the max grows by more than 2^8
 constexpr uint32_t kNoTile = 0xffffffffu;
+// Register buffers per wave in the balanced kernel (blocks in flight + 1). Each block
+// is twelve loads; the hardware counts at most 63 outstanding, so deeper rings make
+// the compiler's wait counts lose track and drain the pipeline.
+constexpr int kRing = 4;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -111,10 +114,15 @@ __device__ __forceinline__ uint32_t pick(const uint4& a, const uint4& b) {
     return __builtin_amdgcn_perm(wb, wa, sel);
 }
 
-// One wave's KV registers for one block: K in QK operand order, V rows for PV.
+// One wave's registers for one block: K rows (line-coalesced), V rows for PV, and
+// the query of the block's unit in QK B-operand order (lane l: head l%16, dims
+// 32kk + 8(l/16) .. +7; zero for heads past the group). The query travels with every
+// block so the loop carries no per-unit registers (it is an L1/L2 hit after the first
+// block of a unit).
 struct BlockRegs {
     uint4 k[4];
     uint4 v[4];
+    uint4 q[4];
 };
 
 // Per-wave online-softmax state. Lane l: m, lsum for head l%16 (lsum over the tokens
@@ -132,34 +140,81 @@ __device__ __forceinline__ void reset(WaveState& s) {
     for (int n = 0; n < 8; ++n) s.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
+// Both tiles are fetched with whole 128-byte lines per instruction: K load i covers
+// rows 4i..4i+3 (one contiguous KiB; lane l takes row 4i + l/16, 16-byte chunk l%16),
+// V load r covers rows r, 4+r, 8+r, 12+r (lane l takes row 4(l/16)+r, chunk l%16).
+// (Loading K straight in MFMA operand order would touch 16 half lines per
+// instruction, which measured ~20% slower as a gather.)
+// Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-class parts.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int offset) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0));
+}
+
+// Issue the twelve 16-byte loads of one block. Every block issues exactly these
+// loads, with no branches: a block whose table entry is out of range gets a buffer
+// of zero records (the hardware returns zeros), and lanes past the query group read
+// past their buffer's end (zeros too). A fixed count lets the compiler wait for just
+// this block's loads while later blocks' loads stay in flight.
 template <typename T>
 __device__ __forceinline__ void issue_block(BlockRegs& r, const T* __restrict__ k_cache,
-                                            const T* __restrict__ v_cache, uint32_t tile,
-                                            int lane) {
-    if (tile == kNoTile) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            r.k[i] = make_uint4(0, 0, 0, 0);
-            r.v[i] = make_uint4(0, 0, 0, 0);
-        }
-        return;
-    }
-    const size_t base = (size_t)tile * kTile;
+                                            const T* __restrict__ v_cache,
+                                            const T* __restrict__ q, uint32_t tile, int qrow,
+                                            int group, int lane) {
+    tile = __builtin_amdgcn_readfirstlane(tile);
+    qrow = __builtin_amdgcn_readfirstlane(qrow);
+    const bool ok = tile != kNoTile;
+    const size_t base = (size_t)(ok ? tile : 0u) * kTile;
+    const int bytes = ok ? kTile * (int)sizeof(T) : 0;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(k_cache + base), 0, bytes, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + base), 0, bytes, kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(q + (size_t)qrow * kD), 0, group * kD * (int)sizeof(T), kRawBufferWord3);
     const int c = lane & 15, grp = lane >> 4;
-    const T* kp = k_cache + base + c * kD + 8 * grp;
-    const T* vp = v_cache + base + (4 * grp) * kD + 8 * c;
+    const int koff = (grp * kD + 8 * c) * (int)sizeof(T);
+    const int voff = (4 * grp * kD + 8 * c) * (int)sizeof(T);
+    const int qoff = (c * kD + 8 * grp) * (int)sizeof(T);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.k[i] = load16(kp + 32 * i);
+    for (int i = 0; i < 4; ++i) r.k[i] = buffer_load16(rk, koff + i * 4 * kD * (int)sizeof(T));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[i] = load16(vp + i * kD);
+    for (int i = 0; i < 4; ++i) r.v[i] = buffer_load16(rv, voff + i * kD * (int)sizeof(T));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.q[i] = buffer_load16(rq, qoff + 32 * i * (int)sizeof(T));
+}
+
+// Per-wave LDS tile that turns the line-coalesced K rows into MFMA operand order.
+// 16-byte chunk ch of token row t sits at slot ch ^ (t & 7) of the row, so both the
+// row-wise writes and the operand reads (16 rows, one chunk each) hit distinct banks.
+struct KTile {
+    uint4 chunk[kBS][kD / 8];
+};
+
+__device__ __forceinline__ void stage_k(KTile& kt, const BlockRegs& r, int lane) {
+    const int c = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = 4 * i + grp;
+        kt.chunk[t][c ^ (t & 7)] = r.k[i];
+    }
+}
+
+// A operand of QK product kk for lane l: token l%16, dims 32kk + 8(l/16) .. +7.
+__device__ __forceinline__ uint4 k_operand(const KTile& kt, int kk, int lane) {
+    const int c = lane & 15, grp = lane >> 4;
+    return kt.chunk[c][(4 * kk + grp) ^ (c & 7)];
 }
 
 // Fold one block into the wave's state. `valid` = tokens of the block that count
-// (0 masks the whole block); qop = the query in QK B-operand order.
+// (0 masks the whole block). The running max is updated every block (exact online
+// softmax), so the loop carries no conditionally updated state.
 template <typename T>
-__device__ __forceinline__ void fold_block(WaveState& s, BlockRegs& r, const uint4 (&qop)[4],
-                                           int valid, float scale_log2, int group, int lane) {
-    const int c = lane & 15, grp = lane >> 4;
+__device__ __forceinline__ void fold_block(WaveState& s, BlockRegs& r, KTile& kt, int valid,
+                                           float scale_log2, int lane) {
+    const int grp = lane >> 4;
+    stage_k(kt, r, lane);
     if (valid < kBS) {
         // Slots past the context hold stale data (possibly NaN); a zero weight does not
         // cancel a NaN inside the product, so their V rows are cleared. Their scores are
@@ -170,7 +225,7 @@ __device__ __forceinline__ void fold_block(WaveState& s, BlockRegs& r, const uin
     }
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc = Mma<T>::qk(r.k[i], qop[i], sc);
+    for (int i = 0; i < 4; ++i) sc = Mma<T>::qk(k_operand(kt, i, lane), r.q[i], sc);
     float x[4];
     float mb = kNegInf;
 #pragma unroll
@@ -180,26 +235,24 @@ __device__ __forceinline__ void fold_block(WaveState& s, BlockRegs& r, const uin
     }
     mb = fmaxf(mb, __shfl_xor(mb, 16));
     mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const bool raise = (c < group) && (mb > s.m + kLazy);
-    if (__any(raise)) {
-        const float mn = fmaxf(s.m, mb);
-        const float alpha = (s.m == kNegInf) ? 0.f : fast_exp2(s.m - mn);
-        s.lsum *= alpha;
-        s.m = mn;
-        // o[.][r] belongs to head 4(l/16)+r, whose factor lives in lane 4(l/16)+r.
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float a = __shfl(alpha, 4 * grp + e);
-#pragma unroll
-            for (int n = 0; n < 8; ++n) s.o[n][e] *= a;
-        }
-    }
-    const float mu = (s.m == kNegInf) ? 0.f : s.m;
+    const float mn = fmaxf(s.m, mb);
+    const float alpha = (s.m == kNegInf) ? 0.f : fast_exp2(s.m - mn);
+    const float mu = (mn == kNegInf) ? 0.f : mn;
     float p[4];
+    float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         p[e] = fast_exp2(x[e] - mu);
-        s.lsum += p[e];
+        ps += p[e];
+    }
+    s.lsum = s.lsum * alpha + ps;
+    s.m = mn;
+    // o[.][e] belongs to head 4(l/16)+e, whose factor lives in lane 4(l/16)+e.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float a = __shfl(alpha, 4 * grp + e);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) s.o[n][e] *= a;
     }
     const uint2 pa = make_uint2(Mma<T>::pack(p[0], p[1]), Mma<T>::pack(p[2], p[3]));
 #define PKV_PV_STEP(N)                                                                  \
@@ -210,74 +263,8 @@ __device__ __forceinline__ void fold_block(WaveState& s, BlockRegs& r, const uin
 #undef PKV_PV_STEP
 }
 
-template <typename T>
-__device__ __forceinline__ void load_query(uint4 (&qop)[4], const T* __restrict__ q, int b,
-                                           int g, int num_heads, int group, int lane) {
-    const int c = lane & 15, grp = lane >> 4;
-    if (c < group) {
-        const T* qp = q + ((size_t)b * num_heads + g * group + c) * kD + 8 * grp;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) qop[i] = load16(qp + 32 * i);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) qop[i] = make_uint4(0, 0, 0, 0);
-    }
-}
-
-// LDS used to merge the four waves' states of one unit.
-template <int GMAX>
-struct MergeLds {
-    float m[kWaves][GMAX];
-    float l[kWaves][GMAX];
-    float o[kWaves][GMAX][kD];
-};
-
-// Wave -> LDS (every wave calls it; caller syncs afterwards).
-template <int GMAX>
-__device__ __forceinline__ void stash_state(MergeLds<GMAX>& L, WaveState& s, int wave, int lane,
-                                            int group) {
-    const int c = lane & 15, grp = lane >> 4;
-    float ls = s.lsum;
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    if (grp == 0 && c < group) {
-        L.m[wave][c] = s.m;
-        L.l[wave][c] = ls;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int h = 4 * grp + e;
-        if (h < group) {
-            float4* dst = reinterpret_cast<float4*>(&L.o[wave][h][8 * c]);
-            dst[0] = make_float4(s.o[0][e], s.o[1][e], s.o[2][e], s.o[3][e]);
-            dst[1] = make_float4(s.o[4][e], s.o[5][e], s.o[6][e], s.o[7][e]);
-        }
-    }
-}
-
 __device__ __forceinline__ float weight(float m, float M) {
     return m == kNegInf ? 0.f : fast_exp2(m - M);
-}
-
-// Merge the four waves for head h, dims d0..d0+3: returns M, L and four o values.
-template <int GMAX>
-__device__ __forceinline__ void merge_waves(const MergeLds<GMAX>& L, int h, int d0, float& M,
-                                            float& Lsum, float4& o) {
-    M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, L.m[w][h]);
-    Lsum = 0.f;
-    o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const float wt = weight(L.m[w][h], M);
-        Lsum += L.l[w][h] * wt;
-        const float4 v = *reinterpret_cast<const float4*>(&L.o[w][h][d0]);
-        o.x += v.x * wt;
-        o.y += v.y * wt;
-        o.z += v.z * wt;
-        o.w += v.w * wt;
-    }
 }
 
 template <typename T>
@@ -288,39 +275,169 @@ __device__ __forceinline__ void store4(T* p, float4 v) {
     *reinterpret_cast<uint2*>(p) = w;
 }
 
-// Device-scope relaxed atomic store / load of one float (coherent across XCDs).
-__device__ __forceinline__ void publish(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Cache policy of the partial-result traffic between workgroups: the device-scope
+// coherence bit (sc1), as device-scope atomics use it, on plain wide accesses, so the
+// stores write through to the point of coherence shared by all XCDs and the loads
+// skip stale cache copies, while the compiler still batches them freely.
+constexpr int kCoherent = 16;
+
+__device__ __forceinline__ void publish4(__amdgpu_buffer_rsrc_t r, int byte_off, float4 v) {
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, byte_off, 0,
+                                           kCoherent);
 }
-__device__ __forceinline__ float fetch(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void publish1(__amdgpu_buffer_rsrc_t r, int byte_off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0,
+                                          kCoherent);
+}
+__device__ __forceinline__ float4 fetch4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(float4,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCoherent));
+}
+__device__ __forceinline__ float fetch1(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kCoherent));
 }
 
-// Partial-result slot of the balanced path: o[GMAX][D], then m[GMAX], l[GMAX].
+// Partial result of one unit: o[GMAX][D] (unnormalised), then m[GMAX], l[GMAX]. The
+// same layout serves a wave's piece in LDS and a workgroup's piece in the workspace.
 template <int GMAX>
-struct Slot {
+struct Part {
+    static constexpr int kM = GMAX * kD;
+    static constexpr int kL = GMAX * kD + GMAX;
     static constexpr int kFloats = balanced_slot_floats(GMAX);
 };
 
+// The wave's softmax denominator of head (lane & 15), in every lane of that head.
+__device__ __forceinline__ float head_lsum(const WaveState& s) {
+    float ls = s.lsum;
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    return ls;
+}
+
+// A wave's state -> partial record P (LDS).
+template <int GMAX>
+__device__ __forceinline__ void wave_to_part(float* P, const WaveState& s, int lane, int group) {
+    const int c = lane & 15, grp = lane >> 4;
+    const float ls = head_lsum(s);
+    if (grp == 0 && c < group) {
+        P[Part<GMAX>::kM + c] = s.m;
+        P[Part<GMAX>::kL + c] = ls;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int h = 4 * grp + e;
+        if (h < group) {
+            float4* dst = reinterpret_cast<float4*>(P + h * kD + 8 * c);
+            dst[0] = make_float4(s.o[0][e], s.o[1][e], s.o[2][e], s.o[3][e]);
+            dst[1] = make_float4(s.o[4][e], s.o[5][e], s.o[6][e], s.o[7][e]);
+        }
+    }
+}
+
+// A wave's state -> normalised output rows (the wave saw the whole unit). `rows`
+// points at head 0 of the unit's group; each lane stores 16 bytes per head.
+template <typename T>
+__device__ __forceinline__ void wave_to_out(T* rows, const WaveState& s, int lane, int group) {
+    const int c = lane & 15, grp = lane >> 4;
+    const float ls = head_lsum(s);
+    const float inv = ls > 0.f ? 1.f / ls : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int h = 4 * grp + e;
+        const float iv = __shfl(inv, h);
+        if (h < group) {
+            uint4 w;
+            w.x = Mma<T>::pack(s.o[0][e] * iv, s.o[1][e] * iv);
+            w.y = Mma<T>::pack(s.o[2][e] * iv, s.o[3][e] * iv);
+            w.z = Mma<T>::pack(s.o[4][e] * iv, s.o[5][e] * iv);
+            w.w = Mma<T>::pack(s.o[6][e] * iv, s.o[7][e] * iv);
+            *reinterpret_cast<uint4*>(rows + h * kD + 8 * c) = w;
+        }
+    }
+}
+
+// Merge n LDS partial records for head h, dims d0..d0+3. Records are addressed by
+// index into the LDS array (not through generic pointers, which would compile to
+// flat loads that also wait for outstanding global stores).
+template <int GMAX, int NREC>
+__device__ __forceinline__ void merge_parts(const float (&rec)[NREC][Part<GMAX>::kFloats],
+                                            const int* idx, int n, int h, int d0, float& M,
+                                            float& L, float4& o) {
+    M = kNegInf;
+    for (int i = 0; i < n; ++i) M = fmaxf(M, rec[idx[i]][Part<GMAX>::kM + h]);
+    L = 0.f;
+    o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < n; ++i) {
+        const float* r = rec[idx[i]];
+        const float wt = weight(r[Part<GMAX>::kM + h], M);
+        L += r[Part<GMAX>::kL + h] * wt;
+        const float4 v = *reinterpret_cast<const float4*>(r + h * kD + d0);
+        o.x += v.x * wt;
+        o.y += v.y * wt;
+        o.z += v.z * wt;
+        o.w += v.w * wt;
+    }
+}
+
+// A value every lane of the wave holds (read from LDS, say) moved to a scalar register,
+// so that branches on it are scalar and the compiler sees straight control flow.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Largest sequence b with Hkv * pref[b] <= x (x below the total; pref in LDS). Such a
+// sequence is never empty: an empty one shares its prefix with the next.
+__device__ __forceinline__ int seq_of(const int* pref, int num_seqs, int Hkv, int x) {
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (Hkv * uni(pref[mid]) <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// The unit after (b, g): next KV head, else the first KV head of the next non-empty
+// sequence.
+__device__ __forceinline__ void next_unit(const int* pref, int num_seqs, int Hkv, int b, int g,
+                                          int& bn, int& gn) {
+    bn = b;
+    gn = g + 1;
+    if (gn == Hkv) {
+        gn = 0;
+        ++bn;
+        while (bn < num_seqs && uni(pref[bn + 1]) == uni(pref[bn])) ++bn;
+    }
+}
+
 // ------------------------------------------------------------------ balanced kernel
-template <typename T, int GMAX>
+template <int GMAX, int NW>
 struct BalancedLds {
     int pref[kMaxSeqsBalanced + 1];   // blocks per sequence, exclusive prefix
     uint32_t tile[kTabMax];           // (physical block * Hkv + kv head), or kNoTile
+    int qrow[kTabMax];                // first query row of the block's unit
     uint8_t valid[kTabMax];           // tokens of the block inside the context
-    MergeLds<GMAX> merge;
-    int flag;
+    KTile ktile[NW];
+    float part[NW * 2][Part<GMAX>::kFloats];   // wave v: [2v] first, [2v+1] last unit piece
+    int flag[2];
 };
 
-template <typename T, int GMAX>
-__global__ __launch_bounds__(kThreads) void decode_mfma_balanced_kernel(
+// NW waves per workgroup, one workgroup per CU, one wave per SIMD. With two waves on
+// a SIMD the older one was measured to stream ~1.5x faster than the younger, which
+// breaks equal static shares; a lone wave per SIMD keeps kRing - 1 blocks in flight
+// instead.
+template <typename T, int GMAX, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
     T* __restrict__ out, const T* __restrict__ q, const T* __restrict__ k_cache,
     const T* __restrict__ v_cache, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx_lens, float scale_log2, int num_seqs, int num_heads,
     int num_kv_heads, int group, int max_blocks, int num_blocks, int32_t* __restrict__ counters,
     float* __restrict__ partials) {
-    __shared__ BalancedLds<T, GMAX> S;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ BalancedLds<GMAX, NW> S;
+    constexpr int kThreads = 64 * NW;
+    constexpr int kWaves = NW;
+    // wave index via readfirstlane: the compiler cannot tell that tid >> 6 is uniform,
+    // and everything derived from it (share bounds, loop counters) must be scalar
+    const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int W = gridDim.x;
     // Logical worker index: consecutive shares (which may cut one unit) go to
     // workgroups that the dispatcher places on the same XCD (round-robin over 8).
@@ -359,42 +476,34 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_balanced_kernel(
                 store4(o + i, make_float4(0.f, 0.f, 0.f, 0.f));
         }
     }
-    const long long total = (long long)Hkv * S.pref[num_seqs];
+    // Block indices of all units laid end to end fit in 32 bits: the plan admits at
+    // most kMaxWorkers * kShareMax blocks of tables.
+    const int total = Hkv * uni(S.pref[num_seqs]);
     if (total == 0) return;
-    const long long C = (total + W - 1) / W;
-    const long long x0 = (long long)w * C;
-    const long long x1 = x0 + C < total ? x0 + C : total;
+    const int C = (total + W - 1) / W;
+    const int x0 = (int)w * C;
+    const int x1 = x0 + C < total ? x0 + C : total;
     if (x0 >= x1) return;
-
-    // ---- first sequence of the share: largest b with Hkv * pref[b] <= x0
-    int b0;
-    {
-        int lo = 0, hi = num_seqs - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if ((long long)Hkv * S.pref[mid] <= x0) lo = mid; else hi = mid - 1;
-        }
-        b0 = lo;
-    }
 
     // ---- stage (tile, valid tokens) of every block of the share
     {
-        long long x = x0;
-        int b = b0;
+        int x = x0;
+        int b = seq_of(S.pref, num_seqs, Hkv, x0);
         while (x < x1) {
-            const long long base = (long long)Hkv * S.pref[b];
+            const int base = Hkv * S.pref[b];
             const int nb = S.pref[b + 1] - S.pref[b];
-            const long long end = base + (long long)Hkv * nb;
-            const long long stop = end < x1 ? end : x1;
+            const int end = base + Hkv * nb;
+            const int stop = end < x1 ? end : x1;
             int n = ctx_lens[b];
             n = n < 0 ? 0 : (n > cap ? cap : n);
-            for (long long xx = x + tid; xx < stop; xx += kThreads) {
+            for (int xx = x + tid; xx < stop; xx += kThreads) {
                 const int r = (int)(xx - base);
                 const int g = r / nb, j = r - g * nb;
                 const int phys = tables[(size_t)b * max_blocks + j];
                 const int left = n - j * kBS;
                 const bool ok = phys >= 0 && phys < num_blocks;
                 S.tile[xx - x0] = ok ? (uint32_t)phys * (uint32_t)Hkv + (uint32_t)g : kNoTile;
+                S.qrow[xx - x0] = b * num_heads + g * group;
                 S.valid[xx - x0] = (uint8_t)(ok ? (left < kBS ? left : kBS) : 0);
             }
             x = stop;
@@ -404,128 +513,180 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_balanced_kernel(
     }
     __syncthreads();
 
-    // ---- walk the units of the share
-    long long xw = x0 + wave;          // this wave's next block
-    BlockRegs cur;
-    if (xw < x1) issue_block(cur, k_cache, v_cache, S.tile[xw - x0], lane);
-    int b = b0;
-    long long ubase = (long long)Hkv * S.pref[b];
-    int nb = S.pref[b + 1] - S.pref[b];
-    int g = (int)((x0 - ubase) / nb);
-    uint4 qop[4];
-    load_query(qop, q, b, g, num_heads, group, lane);
-    long long x = x0;
-    WaveState st;
-    while (x < x1) {
-        const long long su = ubase + (long long)g * nb;   // first block of unit (b, g)
-        const long long ue = su + nb;
-        const long long stop = ue < x1 ? ue : x1;
+    // ---- each wave streams one contiguous quarter of the share; no barriers inside
+    const int Cw = (x1 - x0 + kWaves - 1) / kWaves;
+    const int xa = x0 + wave * Cw;
+    const int xb = xa + Cw < x1 ? xa + Cw : x1;
+    if (xa < xb) {
+        int b = seq_of(S.pref, num_seqs, Hkv, xa);
+        int nb = S.pref[b + 1] - S.pref[b];
+        int g = (xa - Hkv * S.pref[b]) / nb;
+        int su = Hkv * S.pref[b] + (int)g * nb;
+        int ue = su + nb;
+        int bn, gn;
+        next_unit(S.pref, num_seqs, Hkv, b, g, bn, gn);
+        // Two register buffers in fixed roles (the loop is unrolled by two), so a
+        // block's loads land where the fold reads them: no copies, no early waits.
+        // Every step issues one block (a zero-record buffer past the quarter's end), so
+        // the number of loads in flight never depends on the path taken.
+        auto issue = [&](BlockRegs& R, int xi) {
+            const int i = (int)((xi < xb ? xi : xb - 1) - x0);
+            issue_block(R, k_cache, v_cache, q, xi < xb ? S.tile[i] : kNoTile, S.qrow[i], group,
+                        lane);
+        };
+        // kRing register buffers in fixed roles (the loop is unrolled kRing times): a
+        // block's loads land where the fold reads them (no copies), and kRing - 1
+        // blocks stay in flight behind the one being folded.
+        BlockRegs R0, R1, R2, R3;
+        issue(R0, xa);
+        issue(R1, xa + 1);
+        issue(R2, xa + 2);
+        issue(R3, xa + 3);
+        WaveState st;
         reset(st);
-        // next unit (for the query prefetch)
-        int bn = b, gn = g + 1;
-        if (gn == Hkv) {
-            gn = 0;
-            ++bn;
-            while (bn < num_seqs && S.pref[bn + 1] == S.pref[bn]) ++bn;
-        }
-        uint4 qnext[4];
-        const bool more = stop < x1;
-        if (more) load_query(qnext, q, bn, gn, num_heads, group, lane);
-        while (xw < stop) {
-            const long long xn = xw + kWaves;
-            BlockRegs nxt;
-            if (xn < x1) issue_block(nxt, k_cache, v_cache, S.tile[xn - x0], lane);
-            fold_block<T>(st, cur, qop, S.valid[xw - x0], scale_log2, group, lane);
-            cur = nxt;
-            xw = xn;
-        }
-        // ---- merge the waves for unit (b, g)
-        stash_state(S.merge, st, wave, lane, group);
-        __syncthreads();
-        const bool whole = su >= x0 && ue <= x1;
-        const int u = b * Hkv + g;
-        if (whole) {
-            for (int i = tid; i < group * (kD / 4); i += kThreads) {
-                const int h = i / (kD / 4), d0 = (i % (kD / 4)) * 4;
-                float M, Ls;
-                float4 o;
-                merge_waves(S.merge, h, d0, M, Ls, o);
-                const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-                o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
-                store4(out + ((size_t)b * num_heads + g * group + h) * kD + d0, o);
-            }
-        } else {
-            // Publish this workgroup's partial. Every word goes out as a device-scope
-            // atomic store, coherent across the XCDs' L2s on its own, so no fence has to
-            // write back or invalidate whole caches (measured: such fences cost more than
-            // the attention itself). __syncthreads waits for those stores to complete
-            // before thread 0 bumps the unit's counter.
-            const int slot = 2 * w + (su <= x0 ? 0 : 1);
-            float* P = partials + (size_t)slot * Slot<GMAX>::kFloats;
-            for (int i = tid; i < group * (kD / 4); i += kThreads) {
-                const int h = i / (kD / 4), d0 = (i % (kD / 4)) * 4;
-                float M, Ls;
-                float4 o;
-                merge_waves(S.merge, h, d0, M, Ls, o);
-                publish(P + h * kD + d0, o.x);
-                publish(P + h * kD + d0 + 1, o.y);
-                publish(P + h * kD + d0 + 2, o.z);
-                publish(P + h * kD + d0 + 3, o.w);
-                if (d0 == 0) {
-                    publish(P + GMAX * kD + h, M);
-                    publish(P + GMAX * kD + GMAX + h, Ls);
-                }
-            }
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            const long long wf = su / C, wl = (ue - 1) / C;
-            if (tid == 0) {
-                const int done = __hip_atomic_fetch_add(&counters[u], 1, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT);
-                S.flag = (done == (int)(wl - wf));
-            }
-            __syncthreads();
-            if (S.flag) {
-                // Last contributor: read every partial back with device-scope atomic
-                // loads (they bypass stale cache copies) and merge in workgroup order.
-                for (int i = tid; i < group * (kD / 4); i += kThreads) {
-                    const int h = i / (kD / 4), d0 = (i % (kD / 4)) * 4;
-                    float M = kNegInf;
-                    for (long long v = wf; v <= wl; ++v) {
-                        const int sl = 2 * (int)v + ((v > wf || su == v * C) ? 0 : 1);
-                        const float* Q = partials + (size_t)sl * Slot<GMAX>::kFloats;
-                        M = fmaxf(M, fetch(Q + GMAX * kD + h));
-                    }
-                    float Ls = 0.f;
-                    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-                    for (long long v = wf; v <= wl; ++v) {
-                        const int sl = 2 * (int)v + ((v > wf || su == v * C) ? 0 : 1);
-                        const float* Q = partials + (size_t)sl * Slot<GMAX>::kFloats;
-                        const float wt = weight(fetch(Q + GMAX * kD + h), M);
-                        Ls += fetch(Q + GMAX * kD + GMAX + h) * wt;
-                        o.x += fetch(Q + h * kD + d0) * wt;
-                        o.y += fetch(Q + h * kD + d0 + 1) * wt;
-                        o.z += fetch(Q + h * kD + d0 + 2) * wt;
-                        o.w += fetch(Q + h * kD + d0 + 3) * wt;
-                    }
-                    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-                    o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
-                    store4(out + ((size_t)b * num_heads + g * group + h) * kD + d0, o);
-                }
-                if (tid == 0)
-                    __hip_atomic_store(&counters[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        __syncthreads();   // the merge LDS is reused by the next unit
-        x = stop;
-        if (more) {
+        int x = xa;
+        // Finish the current unit: the wave saw all of it -> output; else its piece
+        // goes to the wave's first (unit began at or before xa) or last LDS record.
+        auto flush = [&]() {
+            if (su >= xa && ue <= xb)
+                wave_to_out(out + ((size_t)b * num_heads + (size_t)g * group) * kD, st, lane,
+                            group);
+            else
+                wave_to_part<GMAX>(S.part[2 * wave + (su <= xa ? 0 : 1)], st, lane, group);
+        };
+        auto advance = [&]() {
+            flush();
             b = bn;
             g = gn;
-            ubase = (long long)Hkv * S.pref[b];
             nb = S.pref[b + 1] - S.pref[b];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) qop[i] = qnext[i];
+            su = Hkv * S.pref[b] + (int)g * nb;
+            ue = su + nb;
+            next_unit(S.pref, num_seqs, Hkv, b, g, bn, gn);
+            reset(st);
+        };
+#define PKV_STEP(R)                                                                       \
+        if (x >= xb) break;                                                               \
+        if (x >= ue) advance();                                                           \
+        fold_block<T>(st, R, S.ktile[wave], uni(S.valid[x - x0]), scale_log2, lane);      \
+        issue(R, x + kRing);                                                              \
+        ++x;
+        while (true) {
+            PKV_STEP(R0)
+            PKV_STEP(R1)
+            PKV_STEP(R2)
+            PKV_STEP(R3)
         }
+#undef PKV_STEP
+        flush();
+    }
+    __syncthreads();
+
+    // ---- units cut between waves or between workgroups. Each such unit contains the
+    // first block of some non-empty quarter or the share's last block. Units inside the
+    // share are merged from the LDS records and written; at most two (the share's first
+    // and last unit) cross its edges, and those go through one publish/count round
+    // together.
+    const __amdgpu_buffer_rsrc_t R = __builtin_amdgcn_make_buffer_rsrc(
+        partials, 0, 2 * kMaxWorkers * Part<GMAX>::kFloats * (int)sizeof(float),
+        kRawBufferWord3);
+    int ncross = 0;
+    int cb0 = 0, cg0 = 0, cb1 = 0, cg1 = 0;
+    int cs0 = 0, ce0 = 0, cs1 = 0, ce1 = 0;
+    int prev = -1;
+    for (int k = 0; k <= kWaves; ++k) {
+        const int pos = k < kWaves ? x0 + k * Cw : x1 - 1;
+        if (pos >= x1) continue;
+        const int b = seq_of(S.pref, num_seqs, Hkv, pos);
+        const int nb = S.pref[b + 1] - S.pref[b];
+        const int ub = Hkv * S.pref[b];
+        const int g = (pos - ub) / nb;
+        const int su = ub + (int)g * nb, ue = su + nb;
+        if (su == prev) continue;
+        prev = su;
+        const int lo = su > x0 ? su : x0, hi = ue < x1 ? ue : x1;
+        const int wlo = (lo - x0) / Cw, whi = (hi - 1 - x0) / Cw;
+        const bool crosses = su < x0 || ue > x1;
+        if (wlo == whi && !crosses) continue;   // one wave saw all of it: written
+        int P[kWaves];
+        int n = 0;
+        for (int v = wlo; v <= whi; ++v) P[n++] = 2 * v + (su <= x0 + v * Cw ? 0 : 1);
+        T* rows = out + ((size_t)b * num_heads + (size_t)g * group) * kD;
+        const int gslot = (2 * w + (su <= x0 ? 0 : 1)) * Part<GMAX>::kFloats;
+        for (int i = tid; i < group * (kD / 4); i += kThreads) {
+            const int h = i / (kD / 4), d0 = (i % (kD / 4)) * 4;
+            float M, Ls;
+            float4 o;
+            merge_parts<GMAX>(S.part, P, n, h, d0, M, Ls, o);
+            if (!crosses) {
+                const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+                store4(rows + h * kD + d0, make_float4(o.x * inv, o.y * inv, o.z * inv,
+                                                       o.w * inv));
+            } else {
+                // this workgroup's piece, with write-through stores (see kCoherent)
+                publish4(R, 4 * (gslot + h * kD + d0), o);
+                if (d0 == 0) {
+                    publish1(R, 4 * (gslot + Part<GMAX>::kM + h), M);
+                    publish1(R, 4 * (gslot + Part<GMAX>::kL + h), Ls);
+                }
+            }
+        }
+        if (crosses) {
+            if (ncross == 0) { cb0 = b; cg0 = g; cs0 = su; ce0 = ue; }
+            else { cb1 = b; cg1 = g; cs1 = su; ce1 = ue; }
+            ++ncross;
+        }
+    }
+    if (ncross == 0) return;
+    // The wait and barrier complete every published store before the counters move.
+    // (A release fence here would write back whole L2 caches: measured slower than the
+    // attention itself.) Wave k counts crossing unit k.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (lane == 0 && wave < ncross) {
+        const int su = wave ? cs1 : cs0, ue = wave ? ce1 : ce0;
+        const int u = (wave ? cb1 : cb0) * Hkv + (wave ? cg1 : cg0);
+        const int done = __hip_atomic_fetch_add(&counters[u], 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+        S.flag[wave] = (done == (ue - 1) / C - su / C);
+    }
+    __syncthreads();
+    // A last contributor reads every workgroup's piece back (coherent loads) and merges
+    // them in workgroup order; the two crossing units use separate thread halves.
+    const int span = kThreads / ncross;
+    const int k = tid / span, t = tid - k * span;
+    if (S.flag[k]) {
+        const int b = k ? cb1 : cb0, g = k ? cg1 : cg0;
+        const int su = k ? cs1 : cs0, ue = k ? ce1 : ce0;
+        const int wf = su / C, wl = (ue - 1) / C;
+        T* rows = out + ((size_t)b * num_heads + (size_t)g * group) * kD;
+        for (int i = t; i < group * (kD / 4); i += span) {
+            const int h = i / (kD / 4), d0 = (i % (kD / 4)) * 4;
+            float M = kNegInf;
+            for (int v = wf; v <= wl; ++v) {
+                const int sl = (2 * v + ((v > wf || su == v * C) ? 0 : 1)) *
+                               Part<GMAX>::kFloats;
+                M = fmaxf(M, fetch1(R, 4 * (sl + Part<GMAX>::kM + h)));
+            }
+            float Ls = 0.f;
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int v = wf; v <= wl; ++v) {
+                const int sl = (2 * v + ((v > wf || su == v * C) ? 0 : 1)) *
+                               Part<GMAX>::kFloats;
+                const float wt = weight(fetch1(R, 4 * (sl + Part<GMAX>::kM + h)), M);
+                Ls += fetch1(R, 4 * (sl + Part<GMAX>::kL + h)) * wt;
+                const float4 pv = fetch4(R, 4 * (sl + h * kD + d0));
+                o.x += pv.x * wt;
+                o.y += pv.y * wt;
+                o.z += pv.z * wt;
+                o.w += pv.w * wt;
+            }
+            const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+            store4(rows + h * kD + d0, make_float4(o.x * inv, o.y * inv, o.z * inv,
+                                                   o.w * inv));
+        }
+        if (t == 0)
+            __hip_atomic_store(&counters[b * Hkv + g], 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -534,7 +695,8 @@ template <int GMAX>
 struct PartLds {
     uint32_t tile[kTabMax];
     uint8_t valid[kTabMax];
-    MergeLds<GMAX> merge;
+    KTile ktile[kWaves];
+    float part[kWaves][Part<GMAX>::kFloats];
 };
 
 template <typename T, int GMAX>
@@ -546,7 +708,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
     __shared__ PartLds<GMAX> S;
     const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int cap = max_blocks * kBS;
     int n = ctx_lens[b];
     n = n < 0 ? 0 : (n > cap ? cap : n);
@@ -570,28 +732,40 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
         S.valid[j - j0] = (uint8_t)(ok ? (left < kBS ? left : kBS) : 0);
     }
     __syncthreads();
-    uint4 qop[4];
-    load_query(qop, q, b, g, num_heads, group, lane);
     WaveState st;
     reset(st);
-    int jw = j0 + wave;
-    BlockRegs cur;
-    if (jw < j1) issue_block(cur, k_cache, v_cache, S.tile[jw - j0], lane);
-    while (jw < j1) {
-        const int jn = jw + kWaves;
-        BlockRegs nxt;
-        if (jn < j1) issue_block(nxt, k_cache, v_cache, S.tile[jn - j0], lane);
-        fold_block<T>(st, cur, qop, S.valid[jw - j0], scale_log2, group, lane);
-        cur = nxt;
-        jw = jn;
+    // waves take every fourth block; two register buffers in fixed roles
+    const int qrow = b * num_heads + g * group;
+    int j = j0 + wave;
+    // every step issues one block (a zero-record buffer past the end): the loads in
+    // flight never depend on the path taken
+    auto issue = [&](BlockRegs& R, int ji) {
+        issue_block(R, k_cache, v_cache, q, ji < j1 ? S.tile[ji - j0] : kNoTile, qrow, group,
+                    lane);
+    };
+    BlockRegs A, B;
+    issue(A, j);
+    issue(B, j + kWaves);
+#define PKV_STEP(R)                                                                          \
+    if (j >= j1) break;                                                                      \
+    fold_block<T>(st, R, S.ktile[wave], S.valid[j - j0], scale_log2, lane);                  \
+    issue(R, j + 2 * kWaves);                                                                \
+    j += kWaves;
+    while (true) {
+        PKV_STEP(A)
+        PKV_STEP(B)
     }
-    stash_state(S.merge, st, wave, lane, group);
+#undef PKV_STEP
+
+    wave_to_part<GMAX>(S.part[wave], st, lane, group);
     __syncthreads();
+    int P[kWaves];
+    for (int v = 0; v < kWaves; ++v) P[v] = v;
     for (int i = tid; i < group * (kD / 4); i += kThreads) {
         const int h = i / (kD / 4), d0 = (i % (kD / 4)) * 4;
         float M, Ls;
         float4 o;
-        merge_waves(S.merge, h, d0, M, Ls, o);
+        merge_parts<GMAX>(S.part, P, kWaves, h, d0, M, Ls, o);
         const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
         o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
         const size_t hrow = (size_t)b * num_heads + g * group + h;
@@ -608,16 +782,26 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     }
 }
 
-template <typename T, int GMAX>
+// Workgroups per CU multiplier for experiments (PKV_WG_PER_CU, default 1).
+int wg_per_cu() {
+    static const int v = [] {
+        const char* e = std::getenv("PKV_WG_PER_CU");
+        const int n = e ? std::atoi(e) : 0;
+        return n > 0 && n <= 16 ? n : 1;
+    }();
+    return v;
+}
+
+template <typename T, int GMAX, int NW>
 int launch_balanced(const DecodeArgs& a, const DecodePlan& plan, int workers,
                     hipStream_t stream) {
     const DecodeShape& s = a.shape;
     char* ws = (char*)a.workspace;
-    hipLaunchKernelGGL((decode_mfma_balanced_kernel<T, GMAX>), dim3(workers), dim3(kThreads), 0,
-                       stream, (T*)a.out, (const T*)a.q, (const T*)a.k_cache,
-                       (const T*)a.v_cache, a.block_tables, a.context_lens, a.scale * kLog2e,
-                       s.num_seqs, s.num_heads, s.num_kv_heads, plan.group, s.max_blocks,
-                       s.num_blocks, (int32_t*)(ws + plan.off_counters),
+    hipLaunchKernelGGL((decode_mfma_balanced_kernel<T, GMAX, NW>), dim3(workers),
+                       dim3(64 * NW), 0, stream, (T*)a.out, (const T*)a.q,
+                       (const T*)a.k_cache, (const T*)a.v_cache, a.block_tables, a.context_lens,
+                       a.scale * kLog2e, s.num_seqs, s.num_heads, s.num_kv_heads, plan.group,
+                       s.max_blocks, s.num_blocks, (int32_t*)(ws + plan.off_counters),
                        (float*)(ws + plan.off_partials));
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -641,12 +825,15 @@ int launch_partitioned(const DecodeArgs& a, const DecodePlan& plan, hipStream_t 
 }
 
 template <typename T>
-int launch_typed(const DecodeArgs& a, const DecodePlan& plan, int workers, hipStream_t stream) {
+int launch_typed(const DecodeArgs& a, const DecodePlan& plan, int num_cus, hipStream_t stream) {
     const int G = plan.group;
     if (plan.path == Path::MfmaBalanced) {
-        if (G <= 4) return launch_balanced<T, 4>(a, plan, workers, stream);
-        if (G <= 8) return launch_balanced<T, 8>(a, plan, workers, stream);
-        return launch_balanced<T, 16>(a, plan, workers, stream);
+        const int per_cu = 1;
+        const int workers = balanced_workers(a.shape, num_cus, per_cu * wg_per_cu());
+        if (workers <= 0 || workers > plan.max_workers) return -1;
+        if (G <= 4) return launch_balanced<T, 4, 4>(a, plan, workers, stream);
+        if (G <= 8) return launch_balanced<T, 8, 4>(a, plan, workers, stream);
+        return launch_balanced<T, 16, 4>(a, plan, workers, stream);
     }
     if (G <= 4) return launch_partitioned<T, 4>(a, plan, stream);
     if (G <= 8) return launch_partitioned<T, 8>(a, plan, stream);
@@ -655,25 +842,11 @@ int launch_typed(const DecodeArgs& a, const DecodePlan& plan, int workers, hipSt
 
 }  // namespace
 
-int wg_per_cu() {
-    static const int v = [] {
-        const char* e = std::getenv("PKV_WG_PER_CU");
-        const int n = e ? std::atoi(e) : 0;
-        return n > 0 && n <= 16 ? n : kWgPerCu;
-    }();
-    return v;
-}
-
 int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
                        hipStream_t stream) {
-    int workers = 0;
-    if (plan.path == Path::MfmaBalanced) {
-        workers = balanced_workers(a.shape, num_cus, wg_per_cu());
-        if (workers <= 0 || workers > plan.max_workers) return -1;
-    }
     switch (a.shape.dtype) {
-        case PKV_BFLOAT16: return launch_typed<bf16_t>(a, plan, workers, stream);
-        case PKV_FLOAT16: return launch_typed<f16_t>(a, plan, workers, stream);
+        case PKV_BFLOAT16: return launch_typed<bf16_t>(a, plan, num_cus, stream);
+        case PKV_FLOAT16: return launch_typed<f16_t>(a, plan, num_cus, stream);
         default: return -1;
     }
 }

@@ -40,8 +40,6 @@ constexpr int kMaxWorkers = 4096;
 constexpr size_t kCounterBytes = size_t(1) << 20;
 // Largest share of blocks one balanced-path workgroup stages in LDS.
 constexpr int kShareMax = 2048;
-// Workgroups per compute unit the balanced path launches by default.
-constexpr int kWgPerCu = 2;
 // head_dim and block_size of the matrix-core kernels.
 constexpr int kMfmaHeadDim = 128;
 constexpr int kMfmaBlockSize = 16;
