@@ -63,8 +63,8 @@ def build_sets(name, rotate, dev):
 
 
 def prepare(pkv, s, graphs):
-    """Bind the step's two calls once; with ``graphs`` also capture each into a HIP
-    graph (append, decode) so a step costs two graph launches."""
+    """Bind the step's two calls once; with ``graphs`` also capture the step (append
+    then decode) into one HIP graph, so a step is one graph launch."""
     s.app = pkv.PreparedReshapeAndCache(s.new_k, s.new_v, s.k_cache, s.v_cache, s.slot_mapping)
     s.dec = pkv.PreparedDecode(s.out, s.q, s.k_cache, s.v_cache, s.block_tables,
                                s.context_lens, s.scale, partition_size=s.partition_size)
@@ -72,24 +72,44 @@ def prepare(pkv, s, graphs):
     s.dec()
     torch.cuda.synchronize()
     if graphs:
-        s.g_app, s.g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-        with torch.cuda.graph(s.g_app):
+        s.g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(s.g_step):
             s.app()
-        with torch.cuda.graph(s.g_dec):
             s.dec()
         torch.cuda.synchronize()
-        s.run_app, s.run_dec = s.g_app.replay, s.g_dec.replay
+        s.run = s.g_step.replay
     else:
-        s.run_app, s.run_dec = s.app, s.dec
+        def run(s=s):
+            s.app()
+            s.dec()
+        s.run = run
 
 
-def run_step(s, ev=None):
-    s.run_app()
-    if ev is not None:
-        ev[0].record()
-    s.run_dec()
-    if ev is not None:
-        ev[1].record()
+def time_decode_kernel(sets, graphs, per_set=4, reps=10):
+    """Mean duration of one decode launch: back-to-back decodes over the rotating pool
+    sets (captured in one graph unless --eager), bracketed by HIP events on the launch
+    stream. Returns microseconds."""
+    order = [s for _ in range(per_set) for s in sets]
+    if graphs:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in order:
+                s.dec()
+        torch.cuda.synchronize()
+        launch = g.replay
+    else:
+        def launch():
+            for s in order:
+                s.dec()
+    launch()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        launch()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * len(order))
 
 
 def cpu_baseline(s, seconds):
@@ -117,6 +137,38 @@ def cpu_baseline(s, seconds):
             "seqs_per_s": s.num_seqs * reps / t_total}, err
 
 
+CALIB_PAIRS, CALIB_BLOCK_BYTES = 4096, 8 * 16 * 128 * 2
+
+
+def calibrate(pkv, dev):
+    """copy_blocks over CALIB_PAIRS distinct 32 KiB blocks: reads and writes exactly
+    CALIB_PAIRS * CALIB_BLOCK_BYTES bytes per call; rocprofv3's FETCH_SIZE /
+    WRITE_SIZE readings of this kernel give the counters' byte scale."""
+    pool = torch.zeros(2 * CALIB_PAIRS, 8, 16, 128, dtype=torch.bfloat16, device=dev)
+    pairs = torch.stack([torch.arange(CALIB_PAIRS), torch.arange(CALIB_PAIRS) + CALIB_PAIRS],
+                        dim=1).to(torch.int32).to(dev)
+    for _ in range(5):
+        pkv.copy_blocks(pool, pairs)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration: copy_blocks moved {CALIB_PAIRS * CALIB_BLOCK_BYTES} bytes "
+        f"read + write per call")
+
+
+def traffic_per_launch(workload):
+    """Calibrated HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, if it was measured on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}.traffic.json")
+    try:
+        from paged_kv_cache_374_amd.rocprof_summary import sources_sha
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("source_sha") != sources_sha():
+            return None
+        return round(float(rec["traffic_bytes_per_launch"]))
+    except (OSError, ValueError, KeyError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +181,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch the prepared calls directly instead of replaying HIP graphs")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run copy_blocks on a known byte count (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -149,11 +203,9 @@ def main():
         prepare(pkv, s, graphs=not args.eager)
 
     for i in range(args.warmup):
-        run_step(sets[i % len(sets)])
+        sets[i % len(sets)].run()
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     kv_total = 0
     torch.cuda.synchronize()
@@ -161,21 +213,19 @@ def main():
     start.record()
     for i in range(args.steps):
         s = sets[i % len(sets)]
-        run_step(s, evs[i])
+        s.run()
         kv_total += s.kv
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = start.elapsed_time(stop)
-    ms = max(gpu_ms, 1e-9)
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    dec_mean = sum(dec_ms) / len(dec_ms)
-    dec_sorted = sorted(dec_ms)
-    kv_per_launch = kv_total / args.steps
-    achieved = kv_per_launch / (dec_mean * 1e-3) / 1e9
+    ms = max(start.elapsed_time(stop), 1e-9)
     value = kv_total / (ms * 1e-3) / 1e9
     s0 = sets[0]
     seqs_per_s = s0.num_seqs * args.steps / (ms * 1e-3)
+    # the dominant kernel on its own, back to back over the same pool sets
+    dec_us = time_decode_kernel(sets, graphs=not args.eager)
+    kv_per_launch = sum(s.kv for s in sets) / len(sets)
+    achieved = kv_per_launch / (dec_us * 1e-6) / 1e9
 
     cpu = None
     parity = None
@@ -183,6 +233,9 @@ def main():
         log("[bench] cpu baseline: oracle on the host cores")
         # the last step that used set 0 left its output in set 0's buffer
         cpu, parity = cpu_baseline(s0, args.cpu_seconds)
+
+    if args.calibrate:
+        calibrate(pkv, dev)
 
     elt = s0.q.element_size()
     dname = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[s0.dtype]
@@ -215,7 +268,7 @@ def main():
             "kv_bytes_per_step": int(kv_per_launch),
             "pool_sets": len(sets),
             "step": "reshape_and_cache(new token) + paged_attention_decode",
-            "launch": "eager" if args.eager else "hip_graph",
+            "launch": "eager" if args.eager else "one hip graph per step",
             "wall_s_timed": round(wall, 4),
         },
         "roofline": {
@@ -225,10 +278,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "launch_us_mean": round(dec_mean * 1e3, 3),
-            "launch_us_p10": round(dec_sorted[len(dec_sorted) // 10] * 1e3, 3),
-            "launch_us_p90": round(dec_sorted[(9 * len(dec_sorted)) // 10] * 1e3, 3),
+            "traffic": traffic_per_launch(s0.name),
+            "launch_us_mean": round(dec_us, 3),
+            "launch_timing": "back-to-back decode launches over the pool sets, HIP events",
         },
         "cpu_baseline": cpu,
     }

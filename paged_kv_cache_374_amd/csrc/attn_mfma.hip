@@ -148,8 +148,14 @@ __device__ __forceinline__ void reset(WaveState& s) {
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-class parts.
 constexpr int kRawBufferWord3 = 0x00020000;
 
+// Cache policy of the K/V loads: non-temporal. Every KV byte is read once per call,
+// and keeping it out of L2 and the Infinity Cache measured ~8% more gather bandwidth
+// (6.3 vs 5.8 TB/s for 285 MB of 4 KiB tiles).
+constexpr int kStream = 2;
+
+template <int AUX = 0>
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int offset) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, AUX));
 }
 
 // Issue the twelve 16-byte loads of one block. Every block issues exactly these
@@ -178,9 +184,11 @@ __device__ __forceinline__ void issue_block(BlockRegs& r, const T* __restrict__ 
     const int voff = (4 * grp * kD + 8 * c) * (int)sizeof(T);
     const int qoff = (c * kD + 8 * grp) * (int)sizeof(T);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.k[i] = buffer_load16(rk, koff + i * 4 * kD * (int)sizeof(T));
+    for (int i = 0; i < 4; ++i)
+        r.k[i] = buffer_load16<kStream>(rk, koff + i * 4 * kD * (int)sizeof(T));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[i] = buffer_load16(rv, voff + i * kD * (int)sizeof(T));
+    for (int i = 0; i < 4; ++i)
+        r.v[i] = buffer_load16<kStream>(rv, voff + i * kD * (int)sizeof(T));
 #pragma unroll
     for (int i = 0; i < 4; ++i) r.q[i] = buffer_load16(rq, qoff + 32 * i * (int)sizeof(T));
 }
@@ -418,6 +426,7 @@ struct BalancedLds {
     uint8_t valid[kTabMax];           // tokens of the block inside the context
     KTile ktile[NW];
     float part[NW * 2][Part<GMAX>::kFloats];   // wave v: [2v] first, [2v+1] last unit piece
+    int4 ends[NW][2];                          // wave v's first and last unit (b, g, su, ue)
     int flag[2];
 };
 
@@ -519,10 +528,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
     const int xb = xa + Cw < x1 ? xa + Cw : x1;
     if (xa < xb) {
         int b = seq_of(S.pref, num_seqs, Hkv, xa);
-        int nb = S.pref[b + 1] - S.pref[b];
-        int g = (xa - Hkv * S.pref[b]) / nb;
-        int su = Hkv * S.pref[b] + (int)g * nb;
+        int nb = uni(S.pref[b + 1]) - uni(S.pref[b]);
+        int g = (xa - Hkv * uni(S.pref[b])) / nb;
+        int su = Hkv * uni(S.pref[b]) + g * nb;
         int ue = su + nb;
+        if (lane == 0) S.ends[wave][0] = make_int4(b, g, su, ue);
         int bn, gn;
         next_unit(S.pref, num_seqs, Hkv, b, g, bn, gn);
         // Two register buffers in fixed roles (the loop is unrolled by two), so a
@@ -578,31 +588,26 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         }
 #undef PKV_STEP
         flush();
+        if (lane == 0) S.ends[wave][1] = make_int4(b, g, su, ue);
     }
     __syncthreads();
 
-    // ---- units cut between waves or between workgroups. Each such unit contains the
-    // first block of some non-empty quarter or the share's last block. Units inside the
-    // share are merged from the LDS records and written; at most two (the share's first
-    // and last unit) cross its edges, and those go through one publish/count round
-    // together.
+    // ---- units cut between waves or between workgroups. Each such unit is the first
+    // unit of some non-empty quarter or the share's last unit; the distinct ones are
+    // dealt out to the waves (wave j takes candidates j, j + NW, ...). Units inside
+    // the share are merged from the LDS records and written. At most two (the share's
+    // first and last unit) cross its edges: their merged pieces are published and go
+    // through one count round together below.
     const __amdgpu_buffer_rsrc_t R = __builtin_amdgcn_make_buffer_rsrc(
         partials, 0, 2 * kMaxWorkers * Part<GMAX>::kFloats * (int)sizeof(float),
         kRawBufferWord3);
-    int ncross = 0;
-    int cb0 = 0, cg0 = 0, cb1 = 0, cg1 = 0;
-    int cs0 = 0, ce0 = 0, cs1 = 0, ce1 = 0;
-    int prev = -1;
-    for (int k = 0; k <= kWaves; ++k) {
-        const int pos = k < kWaves ? x0 + k * Cw : x1 - 1;
-        if (pos >= x1) continue;
-        const int b = seq_of(S.pref, num_seqs, Hkv, pos);
-        const int nb = S.pref[b + 1] - S.pref[b];
-        const int ub = Hkv * S.pref[b];
-        const int g = (pos - ub) / nb;
-        const int su = ub + (int)g * nb, ue = su + nb;
-        if (su == prev) continue;
-        prev = su;
+    const int nq = (x1 - x0 + Cw - 1) / Cw;   // non-empty quarters
+    // candidate k: first unit of quarter k (k < nq), or the share's last unit (k = nq)
+    auto cand = [&](int k) { return k < nq ? S.ends[k][0] : S.ends[nq - 1][1]; };
+    for (int k = wave; k <= nq; k += kWaves) {
+        const int4 u = cand(k);
+        if (k > 0 && cand(k - 1).z == u.z) continue;   // same unit as the previous one
+        const int b = uni(u.x), g = uni(u.y), su = uni(u.z), ue = uni(u.w);
         const int lo = su > x0 ? su : x0, hi = ue < x1 ? ue : x1;
         const int wlo = (lo - x0) / Cw, whi = (hi - 1 - x0) / Cw;
         const bool crosses = su < x0 || ue > x1;
@@ -612,7 +617,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         for (int v = wlo; v <= whi; ++v) P[n++] = 2 * v + (su <= x0 + v * Cw ? 0 : 1);
         T* rows = out + ((size_t)b * num_heads + (size_t)g * group) * kD;
         const int gslot = (2 * w + (su <= x0 ? 0 : 1)) * Part<GMAX>::kFloats;
-        for (int i = tid; i < group * (kD / 4); i += kThreads) {
+        for (int i = lane; i < group * (kD / 4); i += 64) {
             const int h = i / (kD / 4), d0 = (i % (kD / 4)) * 4;
             float M, Ls;
             float4 o;
@@ -630,9 +635,20 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
                 }
             }
         }
-        if (crosses) {
-            if (ncross == 0) { cb0 = b; cg0 = g; cs0 = su; ce0 = ue; }
-            else { cb1 = b; cg1 = g; cs1 = su; ce1 = ue; }
+    }
+    // The crossing units: the first candidate if it starts before the share, the last
+    // if it ends after it (the same unit when it spans the whole share).
+    int ncross = 0;
+    int cb0 = 0, cg0 = 0, cs0 = 0, ce0 = 0, cb1 = 0, cg1 = 0, cs1 = 0, ce1 = 0;
+    {
+        const int4 f = cand(0), l = cand(nq);
+        if (f.z < x0 || f.w > x1) {
+            cb0 = uni(f.x); cg0 = uni(f.y); cs0 = uni(f.z); ce0 = uni(f.w);
+            ncross = 1;
+        }
+        if (l.z != f.z && l.w > x1) {
+            if (ncross == 0) { cb0 = uni(l.x); cg0 = uni(l.y); cs0 = uni(l.z); ce0 = uni(l.w); }
+            else { cb1 = uni(l.x); cg1 = uni(l.y); cs1 = uni(l.z); ce1 = uni(l.w); }
             ++ncross;
         }
     }
