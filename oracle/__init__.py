@@ -181,6 +181,36 @@ def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
     return kc, vc
 
 
+def context_end_slots(block_tables: torch.Tensor, context_lens: torch.Tensor,
+                      block_size: int) -> torch.Tensor:
+    """Slot of each sequence's newest token, the one at position n - 1 of a context
+    of n tokens. The block-table walk of [P2] section "Block Table 数据结构" gives
+    logical block (n - 1) // block_size at offset (n - 1) % block_size. The slot is
+    physical_block * block_size + offset, and -1 (write nothing) for an empty context.
+    Plain Python over lists."""
+    tables = block_tables.to("cpu").tolist()
+    slots = []
+    for b, n in enumerate(context_lens.to("cpu").tolist()):
+        if n <= 0:
+            slots.append(-1)
+            continue
+        pos = n - 1
+        slots.append(tables[b][pos // block_size] * block_size + pos % block_size)
+    return torch.tensor(slots, dtype=torch.int64)
+
+
+def decode_step(q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, scale,
+                lib=None):
+    """One decode step in the pages' order ([P3] section "Block table：为什么它能减少
+    碎片"). First the newest token's K and V go into its slot, the free slot of the
+    last block or the first slot of a newly taken one. Then every query attends over
+    its whole context, that token included. Returns (out fp64 [B, Hq, D], expected
+    k_cache, expected v_cache)."""
+    slots = context_end_slots(block_tables, context_lens, k_cache.shape[2])
+    kc, vc = reshape_and_cache(new_k, new_v, k_cache, v_cache, slots, lib=lib)
+    return paged_attention(q, kc, vc, block_tables, context_lens, scale, lib=lib), kc, vc
+
+
 def copy_blocks(cache: torch.Tensor, pairs: torch.Tensor, lib=None) -> torch.Tensor:
     """Expected pool after copying each (src, dst) block pair (a new CPU tensor)."""
     lib = lib or _load()

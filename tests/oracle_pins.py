@@ -187,6 +187,11 @@ def pin_worked_example(lib):
         assert slot == step["slot"], f"slot {slot} != {step['slot']}"
         assert seq.table == step["table_after"]
         pos = step["position"]
+        # the decode step's own slot rule: the walk to position ctx - 1
+        tb_now = torch.tensor([seq.table], dtype=torch.int32)
+        got_slot = oracle.context_end_slots(tb_now, torch.tensor([pos + 1]), bs)
+        assert got_slot.tolist() == [step["slot"]], f"context-end slot {got_slot.tolist()}"
+        assert step["logical_block"] == pos // bs and step["offset"] == pos % bs
         kc, vc = oracle.reshape_and_cache(K[pos:pos + 1], V[pos:pos + 1], kc, vc,
                                           torch.tensor([slot]), lib=lib)
         tb = torch.tensor([seq.table + [-1] * (3 - len(seq.table))], dtype=torch.int32)
@@ -379,7 +384,49 @@ def pin_copy_on_write(lib):
         assert torch.equal(kc2[b.table[1], :, 6 % bs], newk[0])   # ... and its new token
 
 
+def pin_decode_step_slots(lib):
+    """The decode step appends at the context end. For sequences grown token by token
+    through the block manager, whose allocation path is independent of the oracle,
+    the context-end slot of every sequence is the slot its last append returned.
+    Empty contexts write nothing. The composed step equals an explicit append
+    followed by attention over the contiguous tokens."""
+    bs, nb = 4, 24
+    pool = BlockPool(nb, _order(21, nb))
+    lens = [5, 8, 1, 0, 12, 9]
+    seqs, last = [], []
+    for n in lens:
+        s = prefill(pool, max(n - 1, 0), bs)
+        last.append(append_token(pool, s, bs) if n > 0 else -1)
+        seqs.append(s)
+    tables = torch.tensor(pack_tables(seqs, 4), dtype=torch.int32)
+    ctx = torch.tensor(lens, dtype=torch.int32)
+    assert oracle.context_end_slots(tables, ctx, bs).tolist() == last
+    hkv, hq, d = 2, 4, 8
+    gen = torch.Generator().manual_seed(23)
+    K = [torch.randn(n, hkv, d, generator=gen) for n in lens]
+    V = [torch.randn(n, hkv, d, generator=gen) for n in lens]
+    kc = torch.full((nb, hkv, bs, d), float("nan"))
+    vc = torch.full((nb, hkv, bs, d), float("nan"))
+    for i, s in enumerate(seqs):           # every token but the newest is already cached
+        for t in range(lens[i] - 1):
+            kc[s.table[t // bs], :, t % bs] = K[i][t]
+            vc[s.table[t // bs], :, t % bs] = V[i][t]
+    newk = torch.stack([K[i][-1] if lens[i] else torch.zeros(hkv, d) for i in range(len(lens))])
+    newv = torch.stack([V[i][-1] if lens[i] else torch.zeros(hkv, d) for i in range(len(lens))])
+    q = torch.randn(len(lens), hq, d, generator=gen)
+    out, ek, ev = oracle.decode_step(q, newk, newv, kc, vc, tables, ctx, 0.35, lib=lib)
+    want = sdpa_reference(q, K, V, 0.35)
+    _close(out, want, 1e-12, "decode step vs contiguous attention")
+    assert np.all(out[3] == 0), "empty context"
+    for i, s in enumerate(seqs):
+        if lens[i]:
+            p = lens[i] - 1
+            assert torch.equal(ek[s.table[p // bs], :, p % bs], K[i][-1])
+            assert torch.equal(ev[s.table[p // bs], :, p % bs], V[i][-1])
+
+
 ALL_PINS = [pin_decoders, pin_sdpa_library, pin_dense_bruteforce, pin_worked_example,
             pin_two_token_closed_form, pin_context_one, pin_uniform_scores, pin_zero_context,
             pin_placement_permutation, pin_gqa_equals_repeated_mha, pin_stale_slots_unread,
-            pin_linearity_in_values, pin_append_roundtrip, pin_copy_on_write]
+            pin_linearity_in_values, pin_append_roundtrip, pin_copy_on_write,
+            pin_decode_step_slots]
