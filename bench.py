@@ -2,12 +2,13 @@
 """Decode-step benchmark of the paged KV-cache library on one MI355X.
 
 One step is one decode iteration of a serving batch over a paged KV cache: the
-new token of every sequence is written into its slot (reshape_and_cache), then
-every query attends to its whole context through its block table
-(paged_attention_decode). The default workload is the Llama-3-8B-shaped layer:
-64 sequences, 32 query / 8 KV heads, head_dim 128, block_size 16, context
-lengths uniform in [128, 2048], bfloat16 KV scattered over a shuffled pool of
-16384 blocks. Its batches hold no shared blocks, so copy_blocks has no work in
+new token of every sequence is written into its slot, then every query attends to
+its whole context through its block table. By default the step is the fused call
+paged_attention_decode_append (one kernel); --unfused runs it as
+reshape_and_cache + paged_attention_decode. The default workload is the
+Llama-3-8B-shaped layer: 64 sequences, 32 query / 8 KV heads, head_dim 128,
+block_size 16, context lengths uniform in [128, 2048], bfloat16 KV scattered over a
+shuffled pool of 16384 blocks. Its batches hold no shared blocks, so copy_blocks has no work in
 this step; it is timed on the shared-prefix workload by the tests' cases only.
 
 Throughput = algorithmic KV bytes read per second: sum(ctx) * Hkv * 2 * D *
@@ -62,33 +63,44 @@ def build_sets(name, rotate, dev):
     return sets
 
 
-def prepare(pkv, s, graphs):
-    """Bind the step's two calls once; with ``graphs`` also capture the step (append
-    then decode) into one HIP graph, so a step is one graph launch."""
-    s.app = pkv.PreparedReshapeAndCache(s.new_k, s.new_v, s.k_cache, s.v_cache, s.slot_mapping)
-    s.dec = pkv.PreparedDecode(s.out, s.q, s.k_cache, s.v_cache, s.block_tables,
-                               s.context_lens, s.scale, partition_size=s.partition_size)
-    s.app()
-    s.dec()
+def prepare(pkv, s, graphs, fused):
+    """Bind the step once: by default the fused call (append at each context end, then
+    decode: one kernel on the matrix-core paths); with ``fused`` false the two calls
+    reshape_and_cache + paged_attention_decode. ``s.dec`` is the call that carries the
+    decode kernel. With ``graphs`` the step is captured into one HIP graph, so a step
+    is one graph launch."""
+    if fused:
+        s.dec = pkv.PreparedDecode(s.out, s.q, s.k_cache, s.v_cache, s.block_tables,
+                                   s.context_lens, s.scale, partition_size=s.partition_size,
+                                   new_k=s.new_k, new_v=s.new_v)
+        calls = [s.dec]
+    else:
+        app = pkv.PreparedReshapeAndCache(s.new_k, s.new_v, s.k_cache, s.v_cache,
+                                          s.slot_mapping)
+        s.dec = pkv.PreparedDecode(s.out, s.q, s.k_cache, s.v_cache, s.block_tables,
+                                   s.context_lens, s.scale, partition_size=s.partition_size)
+        calls = [app, s.dec]
+
+    def run(calls=calls):
+        for c in calls:
+            c()
+    run()
     torch.cuda.synchronize()
     if graphs:
         s.g_step = torch.cuda.CUDAGraph()
         with torch.cuda.graph(s.g_step):
-            s.app()
-            s.dec()
+            run()
         torch.cuda.synchronize()
         s.run = s.g_step.replay
     else:
-        def run(s=s):
-            s.app()
-            s.dec()
         s.run = run
 
 
 def time_decode_kernel(sets, graphs, per_set=4, reps=10):
-    """Mean duration of one decode launch: back-to-back decodes over the rotating pool
-    sets (captured in one graph unless --eager), bracketed by HIP events on the launch
-    stream. Returns microseconds."""
+    """Mean duration of one launch of the decode kernel (the fused call by default):
+    back-to-back calls over the rotating pool sets (captured in one graph with
+    --graphs), bracketed by HIP events on the launch stream. Repeated fused calls
+    rewrite the same rows into the same slots. Returns microseconds."""
     order = [s for _ in range(per_set) for s in sets]
     if graphs:
         g = torch.cuda.CUDAGraph()
@@ -179,8 +191,12 @@ def main():
                     help="independent pool sets the steps cycle through")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true",
-                    help="launch the prepared calls directly instead of replaying HIP graphs")
+    ap.add_argument("--graphs", action="store_true",
+                    help="capture each step in a HIP graph and replay it (default: launch the "
+                         "prepared call directly; for a one-kernel step a graph replay only "
+                         "adds a gap between steps)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the step as two calls (reshape_and_cache, then decode)")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run copy_blocks on a known byte count (counter calibration)")
     args = ap.parse_args()
@@ -200,7 +216,7 @@ def main():
     sets = build_sets(args.workload, max(1, args.rotate), dev)
     torch.cuda.synchronize()
     for s in sets:
-        prepare(pkv, s, graphs=not args.eager)
+        prepare(pkv, s, graphs=args.graphs, fused=not args.unfused)
 
     for i in range(args.warmup):
         sets[i % len(sets)].run()
@@ -223,7 +239,7 @@ def main():
     s0 = sets[0]
     seqs_per_s = s0.num_seqs * args.steps / (ms * 1e-3)
     # the dominant kernel on its own, back to back over the same pool sets
-    dec_us = time_decode_kernel(sets, graphs=not args.eager)
+    dec_us = time_decode_kernel(sets, graphs=args.graphs)
     kv_per_launch = sum(s.kv for s in sets) / len(sets)
     achieved = kv_per_launch / (dec_us * 1e-6) / 1e9
 
@@ -267,13 +283,16 @@ def main():
             "mean_context": round(float(s0.context_lens.float().mean()), 1),
             "kv_bytes_per_step": int(kv_per_launch),
             "pool_sets": len(sets),
-            "step": "reshape_and_cache(new token) + paged_attention_decode",
-            "launch": "eager" if args.eager else "one hip graph per step",
+            "step": ("reshape_and_cache(new token) + paged_attention_decode" if args.unfused
+                     else "paged_attention_decode_append (new token written at each "
+                          "context end, then attended; one kernel)"),
+            "launch": "one hip graph per step" if args.graphs else "direct (one call per step)",
             "wall_s_timed": round(wall, 4),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attention_decode",
+            "kernel": "paged_attention_decode" if args.unfused
+                      else "paged_attention_decode_append",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

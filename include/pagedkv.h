@@ -5,7 +5,8 @@
  *   pkv_paged_attention_decode  single-query attention read through block tables
  *   pkv_reshape_and_cache       write each new token's K/V into its slot
  *   pkv_copy_blocks             copy whole blocks (copy-on-write)
- * plus workspace sizing/initialisation, version and error strings.
+ * plus pkv_paged_attention_decode_append (a decode step's append and attention in
+ * one call), workspace sizing/initialisation, version and error strings.
  *
  * Pages cited (titles as published):
  *   [P1] "vLLM 源码解析：PagedAttention 如何让大模型推理提速 10 倍"
@@ -125,7 +126,7 @@ int pkv_workspace_init(void* workspace, size_t workspace_bytes, pkv_stream_t str
  *               NULL only when that size is 0
  * Supported: head_dim in {64, 128, 256}; block_size in {1, 2, 4, 8, 16, 32};
  * num_heads / num_kv_heads <= 16 (group sizes above 8 need bfloat16/float16,
- * block_size 16, head_dim 64 or 128). Deterministic: the same inputs give
+ * block_size 16, head_dim 128). Deterministic: the same inputs give
  * bit-identical outputs.
  */
 int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
@@ -135,6 +136,47 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                int max_blocks_per_seq, int num_blocks, pkv_dtype dtype,
                                int partition_size, void* workspace, size_t workspace_bytes,
                                pkv_stream_t stream);
+
+/*
+ * One whole decode step in one call: append each sequence's newest token, then attend.
+ * The step follows [P3] section "Block table：为什么它能减少碎片": the token just
+ * generated goes into the free slot of its sequence's last block, or into a newly
+ * taken block, and the query then attends over the context including that token. Its
+ * slot is the block-table walk of [P2] section "Block Table 数据结构" applied to
+ * position context_lens[b] - 1.
+ *
+ * The result is the same as two calls:
+ *   pkv_reshape_and_cache(new_k, new_v, k_cache, v_cache, slot_mapping, num_seqs, ...)
+ *   pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, ...)
+ * with slot_mapping[b] = block_tables[b][(n-1)/block_size] * block_size
+ * + (n-1) % block_size, where n = context_lens[b], and -1 (skip) when n == 0.
+ *
+ * On the matrix-core paths the append runs inside the decode kernel, so the step is
+ * one launch. The workgroup that reads a sequence's last block writes the new row
+ * before it loads that block. On other paths a small append kernel runs first.
+ *
+ * new_k, new_v  [num_seqs, num_kv_heads, head_dim], dtype; read. Must be non-NULL when
+ *               num_seqs > 0.
+ * k_cache, v_cache  read and written: only the slot at position context_lens[b] - 1
+ *               of each sequence changes, and it receives a bit-exact copy.
+ * All other arguments, the workspace rules and the errors are those of
+ * pkv_paged_attention_decode.
+ *
+ * Caller contract:
+ *  - No two sequences may append into the same slot.
+ *  - The slot a sequence writes must lie in a block that no other sequence of the
+ *    batch reads. Copy-on-write guarantees this: a shared block is copied before a
+ *    writer touches it. Where the contract is broken, the other sequence may see the
+ *    old or the new row.
+ */
+int pkv_paged_attention_decode_append(void* out, const void* q, const void* new_k,
+                                      const void* new_v, void* k_cache, void* v_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      float scale, int num_seqs, int num_heads,
+                                      int num_kv_heads, int head_dim, int block_size,
+                                      int max_blocks_per_seq, int num_blocks, pkv_dtype dtype,
+                                      int partition_size, void* workspace,
+                                      size_t workspace_bytes, pkv_stream_t stream);
 
 /*
  * Slot-mapped append of new tokens' K and V ([P3] section "Block table：为什么它能

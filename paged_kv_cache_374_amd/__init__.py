@@ -7,6 +7,8 @@ There is no fallback: if the library is not built, or a tensor is not on a GPU,
 the call raises.
 
     paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale)
+    paged_attention_decode_append(out, q, new_k, new_v, k_cache, v_cache, block_tables,
+                                  context_lens, scale)
     reshape_and_cache(key, value, k_cache, v_cache, slot_mapping)
     copy_blocks(caches, src_dst_pairs)
 """
@@ -18,7 +20,7 @@ from typing import Dict, Iterable, Optional, Tuple, Union
 
 import torch
 
-__all__ = ["paged_attention_decode", "reshape_and_cache", "copy_blocks", "workspace_size",
+__all__ = ["paged_attention_decode", "paged_attention_decode_append", "reshape_and_cache", "copy_blocks", "workspace_size",
            "workspace_init", "version", "strerror", "PagedKVError", "library_path", "load",
            "PreparedDecode", "PreparedReshapeAndCache"]
 
@@ -62,6 +64,9 @@ def load():
     lib.pkv_workspace_init.argtypes = [_P, ctypes.c_size_t, _P]
     lib.pkv_paged_attention_decode.restype = _I
     lib.pkv_paged_attention_decode.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_float] + \
+        [_I] * 9 + [_P, ctypes.c_size_t, _P]
+    lib.pkv_paged_attention_decode_append.restype = _I
+    lib.pkv_paged_attention_decode_append.argtypes = [_P] * 8 + [ctypes.c_float] + \
         [_I] * 9 + [_P, ctypes.c_size_t, _P]
     lib.pkv_reshape_and_cache.restype = _I
     lib.pkv_reshape_and_cache.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
@@ -169,6 +174,20 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, pa
     return args, workspace
 
 
+def _new_rows(new_k, new_v, q, k_cache):
+    for name, t in (("new_k", new_k), ("new_v", new_v)):
+        _gpu(t, name, q.dtype)
+    want = (q.shape[0], k_cache.shape[1], q.shape[2])
+    if tuple(new_k.shape) != want or tuple(new_v.shape) != want:
+        raise ValueError(f"new_k/new_v must be [num_seqs, num_kv_heads, head_dim] = {want}")
+    return new_k.data_ptr(), new_v.data_ptr()
+
+
+def _fused(args, rows):
+    """Argument tuple of pkv_paged_attention_decode_append from a decode tuple."""
+    return args[:2] + rows + args[2:]
+
+
 def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
                            v_cache: torch.Tensor, block_tables: torch.Tensor,
                            context_lens: torch.Tensor, scale: float, partition_size: int = 0,
@@ -185,28 +204,54 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
     return out
 
 
+def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, new_k: torch.Tensor,
+                                  new_v: torch.Tensor, k_cache: torch.Tensor,
+                                  v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, scale: float,
+                                  partition_size: int = 0,
+                                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step: new_k[b]/new_v[b] ([B, Hkv, D]) are written at position
+    context_lens[b] - 1 of sequence b (the slot its block table gives), then q attends
+    over all context_lens[b] tokens. On the matrix-core paths this is one kernel."""
+    args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                           partition_size, workspace, False)
+    rows = _new_rows(new_k, new_v, q, k_cache)
+    _check(load().pkv_paged_attention_decode_append(*_fused(args, rows), _stream(q.device)),
+           "pkv_paged_attention_decode_append")
+    return out
+
+
 class PreparedDecode:
     """A decode call validated once for a fixed set of tensors, for loops that run
     it many times (serving steps, HIP graph capture). It owns a zero-initialised
     workspace unless one is passed. Calling it enqueues the decode on ``stream`` (a
-    raw hipStream_t handle) or on the current stream of the tensors' device."""
+    raw hipStream_t handle) or on the current stream of the tensors' device. With
+    ``new_k``/``new_v`` it is the fused step of paged_attention_decode_append."""
 
     def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                 partition_size: int = 0, workspace: Optional[torch.Tensor] = None):
+                 partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
+                 new_k: Optional[torch.Tensor] = None, new_v: Optional[torch.Tensor] = None):
         self._args, self.workspace = _decode_args(out, q, k_cache, v_cache, block_tables,
                                                   context_lens, scale, partition_size,
                                                   workspace, True)
-        self._fn = load().pkv_paged_attention_decode
+        if (new_k is None) != (new_v is None):
+            raise ValueError("pass both new_k and new_v, or neither")
+        if new_k is not None:
+            self._args = _fused(self._args, _new_rows(new_k, new_v, q, k_cache))
+            self._name = "pkv_paged_attention_decode_append"
+        else:
+            self._name = "pkv_paged_attention_decode"
+        self._fn = getattr(load(), self._name)
         self._device = q.device
         self.out = out
         # the raw pointers above stay valid only while these tensors are alive
-        self._keep = (out, q, k_cache, v_cache, block_tables, context_lens)
+        self._keep = (out, q, k_cache, v_cache, block_tables, context_lens, new_k, new_v)
 
     def __call__(self, stream: Optional[int] = None) -> torch.Tensor:
         st = _stream(self._device) if stream is None else stream
         rc = self._fn(*self._args, st)
         if rc != 0:
-            raise PagedKVError(rc, "pkv_paged_attention_decode")
+            raise PagedKVError(rc, self._name)
         return self.out
 
 

@@ -11,10 +11,10 @@
 //
 // Mapping onto CDNA4 (one wavefront = one 16-token KV block at a time):
 //   * QK^T of a block is one 16x16 tile: rows = the block's 16 tokens, columns = the
-//     query heads of the KV head (G <= 16, unused columns see a zero query). K is
-//     loaded straight from HBM into the A operand of v_mfma_f32_16x16x32 (16-byte
-//     loads; lane l holds token l%16, dims 32kk + 8(l/16) .. +7), Q sits in the B
-//     operand with the same dim assignment, so the contraction pairs equal dims.
+//     query heads of the KV head (G <= 16, unused columns see a zero query). K arrives
+//     in whole 128-byte lines and passes through a per-wave LDS tile (chunk c of row t
+//     stored at slot c ^ (t & 7): conflict-free writes and operand reads) into the A
+//     operand of v_mfma_f32_16x16x32; Q is the B operand with the same dim assignment.
 //   * The score tile comes out with lane l holding tokens 4(l/16)+r (r = 0..3) of
 //     head l%16, which is exactly the A-operand layout of v_mfma_f32_16x16x16 for
 //     P (rows = heads, k = tokens). The probabilities are rounded to the KV type.
@@ -22,23 +22,23 @@
 //     16x16x16 products takes element n of those four rows as its B operand, so
 //     output column j of product n is dim 8j + n; the repack is a byte permute per
 //     register, no LDS transpose.
-//   * Online softmax per head in base-2 units (scale * log2 e folded in). The running
-//     max is raised lazily: the accumulators are rescaled only when a block's max
-//     exceeds the running max by more than 2^8, so most blocks skip the rescale.
+//   * Exact online softmax per head in base-2 units (scale * log2 e folded in).
 //
 // Work split ("balanced" path): all (sequence, KV head) units are laid end to end as
-// one list of blocks, and every workgroup takes an equal contiguous share of it
-// (the grid is a fixed multiple of the CU count). Its four waves take every fourth
-// block of the share, each keeping its own softmax state, merged through LDS at each
-// unit boundary. A unit covered by one workgroup is written out directly; a unit cut
-// by share boundaries leaves one partial (m, l, unnormalised o) per workgroup, and
-// the last workgroup to finish it (atomic counter) merges them:
+// one list of blocks, and every workgroup (one per CU, one wave per SIMD) takes an
+// equal contiguous share of it. Each wave streams one contiguous quarter of the share
+// through a ring of register buffers. A unit a wave sees whole is written out by that
+// wave; pieces cut between waves merge through LDS; a unit cut by share boundaries
+// leaves one partial (m, l, unnormalised o) per workgroup, and the last workgroup to
+// finish it (atomic counter) merges them:
 //   M = max_w m_w,  L = sum_w l_w 2^(m_w - M),  out = sum_w o_w 2^(m_w - M) / L,
 // in fixed workgroup order (deterministic), and zeroes the counter for the next call.
 //
 // "Partitioned" path (caller asks for a partition size): one workgroup per
 // (partition, KV head, sequence); each leaves (m, l, o/l) per partition for the
 // shared reduction kernel, or writes the output when the context has one partition.
+//
+// Both kernels can also perform the append of a decode step (see "fused append").
 #include <cstdlib>
 
 #include "device_common.h"
@@ -58,10 +58,11 @@ constexpr int kTabMax = kShareMax;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr uint32_t kNoTile = 0xffffffffu;
-// Register buffers per wave in the balanced kernel (blocks in flight + 1). Each block
-// is twelve loads; the hardware counts at most 63 outstanding, so deeper rings make
-// the compiler's wait counts lose track and drain the pipeline.
-constexpr int kRing = 4;
+// Register buffers per wave in the balanced kernel: while one block is folded, the
+// next one is in flight. Measured on the Llama-3-8B-shaped batch (four waves per CU):
+// 2 buffers 53.6 us, 3 buffers 55.7, 4 buffers 56.4, 6 buffers 58. The memory
+// system is saturated either way, and more outstanding requests only add contention.
+constexpr int kRing = 2;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -164,8 +165,7 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int off
 // past their buffer's end (zeros too). A fixed count lets the compiler wait for just
 // this block's loads while later blocks' loads stay in flight.
 template <typename T>
-__device__ __forceinline__ void issue_block(BlockRegs& r, const T* __restrict__ k_cache,
-                                            const T* __restrict__ v_cache,
+__device__ __forceinline__ void issue_block(BlockRegs& r, const T* k_cache, const T* v_cache,
                                             const T* __restrict__ q, uint32_t tile, int qrow,
                                             int group, int lane) {
     tile = __builtin_amdgcn_readfirstlane(tile);
@@ -177,8 +177,11 @@ __device__ __forceinline__ void issue_block(BlockRegs& r, const T* __restrict__ 
         __builtin_amdgcn_make_buffer_rsrc((void*)(k_cache + base), 0, bytes, kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + base), 0, bytes, kRawBufferWord3);
+    // A padding block (past the wave's range) reads no query either: its loads are all
+    // zero-record, so none of them waits on memory when the wave drains its ring.
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(q + (size_t)qrow * kD), 0, group * kD * (int)sizeof(T), kRawBufferWord3);
+        (void*)(q + (size_t)qrow * kD), 0, ok ? group * kD * (int)sizeof(T) : 0,
+        kRawBufferWord3);
     const int c = lane & 15, grp = lane >> 4;
     const int koff = (grp * kD + 8 * c) * (int)sizeof(T);
     const int voff = (4 * grp * kD + 8 * c) * (int)sizeof(T);
@@ -366,26 +369,37 @@ __device__ __forceinline__ void wave_to_out(T* rows, const WaveState& s, int lan
     }
 }
 
-// Merge n LDS partial records for head h, dims d0..d0+3. Records are addressed by
-// index into the LDS array (not through generic pointers, which would compile to
-// flat loads that also wait for outstanding global stores).
-template <int GMAX, int NREC>
+// Merge n (1 <= n <= NMAX) LDS partial records for head h, dims d0..d0+3. Records are
+// addressed by index into the LDS array (not through generic pointers, which would
+// compile to flat loads that also wait for outstanding global stores). The trip count
+// is fixed and records past n are masked, so every LDS read of a call is independent
+// of the others and they all go out before the first wait.
+template <int GMAX, int NREC, int NMAX>
 __device__ __forceinline__ void merge_parts(const float (&rec)[NREC][Part<GMAX>::kFloats],
                                             const int* idx, int n, int h, int d0, float& M,
                                             float& L, float4& o) {
-    M = kNegInf;
-    for (int i = 0; i < n; ++i) M = fmaxf(M, rec[idx[i]][Part<GMAX>::kM + h]);
+    float m[NMAX], l[NMAX];
+    float4 v[NMAX];
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+        const float* r = rec[idx[i < n ? i : 0]];
+        m[i] = i < n ? r[Part<GMAX>::kM + h] : kNegInf;
+        l[i] = r[Part<GMAX>::kL + h];
+        v[i] = *reinterpret_cast<const float4*>(r + h * kD + d0);
+    }
+    M = m[0];
+#pragma unroll
+    for (int i = 1; i < NMAX; ++i) M = fmaxf(M, m[i]);
     L = 0.f;
     o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = 0; i < n; ++i) {
-        const float* r = rec[idx[i]];
-        const float wt = weight(r[Part<GMAX>::kM + h], M);
-        L += r[Part<GMAX>::kL + h] * wt;
-        const float4 v = *reinterpret_cast<const float4*>(r + h * kD + d0);
-        o.x += v.x * wt;
-        o.y += v.y * wt;
-        o.z += v.z * wt;
-        o.w += v.w * wt;
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+        const float wt = weight(m[i], M);
+        L += l[i] * wt;
+        o.x += v[i].x * wt;
+        o.y += v[i].y * wt;
+        o.z += v[i].z * wt;
+        o.w += v[i].w * wt;
     }
 }
 
@@ -417,10 +431,77 @@ __device__ __forceinline__ void next_unit(const int* pref, int num_seqs, int Hkv
     }
 }
 
+// ------------------------------------------------------------------ fused append
+// A decode step first writes each sequence's newest token (position n - 1) into the
+// free slot of its last block, then attends over all n tokens ([P3] section "Block
+// table：为什么它能减少碎片": a decoded token fills the last block's free slot or a
+// newly taken block; the slot is found by the block-table walk of [P2] section
+// "Block Table 数据结构"). Fused into the decode, the workgroup that reads a unit's
+// last block writes that unit's new K and V rows during staging; the workgroup
+// barrier before its waves start loading orders those stores before the loads.
+constexpr int kRowChunks = kD * 2 / 16;   // 16-byte chunks of one bf16/f16 row
+
+// Copy chunk `c` of the new K (kind 0) or V (kind 1) row of unit (b, g) into
+// position n - 1 of the sequence (table row `table`). The source chunk is loaded
+// before the table entry is checked, so the two loads overlap.
+template <typename T>
+__device__ __forceinline__ void append_chunk(T* k_cache, T* v_cache,
+                                             const T* __restrict__ new_k,
+                                             const T* __restrict__ new_v,
+                                             const int32_t* __restrict__ table, int b, int g,
+                                             int Hkv, int n, int num_blocks, int kind, int c) {
+    const int j = (n - 1) / kBS;
+    const size_t src = ((size_t)b * Hkv + g) * kD;
+    const uint4 val = reinterpret_cast<const uint4*>((kind ? new_v : new_k) + src)[c];
+    const int phys = table[j];
+    if (phys < 0 || phys >= num_blocks) return;
+    const size_t dst = (((size_t)phys * Hkv + g) * kBS + (n - 1 - j * kBS)) * kD;
+    reinterpret_cast<uint4*>((kind ? v_cache : k_cache) + dst)[c] = val;
+}
+
 // ------------------------------------------------------------------ balanced kernel
+// Shares of the block list, laid out in logical worker order (XCD-major: the `per`
+// workers of XCD 0, then XCD 1, ...). Without skew every share has C = ceil(total/W)
+// blocks. With a skew of s per mille, shares on odd XCDs shrink to C(1 - s/1000) and
+// those on even XCDs grow to cover the rest. (On MI355X the odd-numbered XCDs were
+// measured to stream a few per cent slower than the even ones.) Every workgroup
+// derives the same map from `total`, so share boundaries, and with them the results,
+// do not depend on scheduling.
+struct ShareMap {
+    int per, ce, co, total;
+    __device__ ShareMap(int total_, int W, int skew) : total(total_) {
+        const int C = (total + W - 1) / W;
+        per = W % 8 == 0 ? W / 8 : W;
+        ce = co = C;
+        if (W % 8 == 0 && skew > 0 && skew < 1000) {
+            const int half = W / 2;
+            const int lo = (int)((long long)C * (1000 - skew) / 1000);
+            const int hi = (total - half * lo + half - 1) / half;
+            if (lo >= 1 && hi >= lo && hi <= kShareMax) {
+                co = lo;
+                ce = hi;
+            }
+        }
+    }
+    // First block of worker w's share (w = W gives the end of the list).
+    __device__ int start(int w) const {
+        const int x = w / per, i = w - x * per;
+        const long long s = (long long)(x / 2) * per * (ce + co) + (x & 1) * per * ce +
+                            (long long)i * ((x & 1) ? co : ce);
+        return s < total ? (int)s : total;
+    }
+    // The worker whose share holds block t (0 <= t < total).
+    __device__ int owner(int t) const {
+        const int pair = per * (ce + co);
+        const int p = t / pair, r = t - p * pair;
+        return r < per * ce ? 2 * p * per + r / ce : (2 * p + 1) * per + (r - per * ce) / co;
+    }
+};
+
 template <int GMAX, int NW>
 struct BalancedLds {
     int pref[kMaxSeqsBalanced + 1];   // blocks per sequence, exclusive prefix
+    int ctx[kMaxSeqsBalanced];        // context length per sequence (clipped to the table)
     uint32_t tile[kTabMax];           // (physical block * Hkv + kv head), or kNoTile
     int qrow[kTabMax];                // first query row of the block's unit
     uint8_t valid[kTabMax];           // tokens of the block inside the context
@@ -432,15 +513,15 @@ struct BalancedLds {
 
 // NW waves per workgroup, one workgroup per CU, one wave per SIMD. With two waves on
 // a SIMD the older one was measured to stream ~1.5x faster than the younger, which
-// breaks equal static shares; a lone wave per SIMD keeps kRing - 1 blocks in flight
-// instead.
+// breaks equal static shares. Eight waves per CU were also slower overall (54.7 vs
+// 53.6 us on the 8B-shaped batch).
 template <typename T, int GMAX, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
-    T* __restrict__ out, const T* __restrict__ q, const T* __restrict__ k_cache,
-    const T* __restrict__ v_cache, const int32_t* __restrict__ tables,
+    T* __restrict__ out, const T* __restrict__ q, T* k_cache, T* v_cache,
+    const T* __restrict__ new_k, const T* __restrict__ new_v, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx_lens, float scale_log2, int num_seqs, int num_heads,
     int num_kv_heads, int group, int max_blocks, int num_blocks, int32_t* __restrict__ counters,
-    float* __restrict__ partials) {
+    float* __restrict__ partials, int xcd_skew) {
     __shared__ BalancedLds<GMAX, NW> S;
     constexpr int kThreads = 64 * NW;
     constexpr int kWaves = NW;
@@ -454,10 +535,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
     const int cap = max_blocks * kBS;
     const int Hkv = num_kv_heads;
 
-    // ---- prologue: blocks per sequence and their prefix sums
+    // ---- prologue: context lengths, blocks per sequence and their prefix sums
     for (int i = tid; i < num_seqs; i += kThreads) {
         int n = ctx_lens[i];
         n = n < 0 ? 0 : (n > cap ? cap : n);
+        S.ctx[i] = n;
         S.pref[i + 1] = (n + kBS - 1) / kBS;
     }
     if (tid == 0) S.pref[0] = 0;
@@ -489,35 +571,47 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
     // most kMaxWorkers * kShareMax blocks of tables.
     const int total = Hkv * uni(S.pref[num_seqs]);
     if (total == 0) return;
-    const int C = (total + W - 1) / W;
-    const int x0 = (int)w * C;
-    const int x1 = x0 + C < total ? x0 + C : total;
+    const ShareMap shares(total, W, xcd_skew);
+    const int x0 = shares.start(w);
+    const int x1 = shares.start(w + 1);
     if (x0 >= x1) return;
 
-    // ---- stage (tile, valid tokens) of every block of the share
-    {
-        int x = x0;
-        int b = seq_of(S.pref, num_seqs, Hkv, x0);
-        while (x < x1) {
-            const int base = Hkv * S.pref[b];
+    // ---- stage (tile, query row, valid tokens) of every block of the share. Each
+    // thread finds its block's sequence by binary search over the prefix sums, so the
+    // table loads of the whole share go out together.
+    for (int xx = x0 + tid; xx < x1; xx += kThreads) {
+        int lo = 0, hi = num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (Hkv * S.pref[mid] <= xx) lo = mid; else hi = mid - 1;
+        }
+        // the largest such sequence is never empty (an empty one shares its prefix
+        // with the next), so nb > 0
+        const int b = lo;
+        const int nb = S.pref[b + 1] - S.pref[b];
+        const int r = xx - Hkv * S.pref[b];
+        const int g = r / nb, j = r - g * nb;
+        const int phys = tables[(size_t)b * max_blocks + j];
+        const int left = S.ctx[b] - j * kBS;
+        const bool ok = phys >= 0 && phys < num_blocks;
+        S.tile[xx - x0] = ok ? (uint32_t)phys * (uint32_t)Hkv + (uint32_t)g : kNoTile;
+        S.qrow[xx - x0] = b * num_heads + g * group;
+        S.valid[xx - x0] = (uint8_t)(ok ? (left < kBS ? left : kBS) : 0);
+    }
+    // Fused append: the units whose last block lies in the share belong to the
+    // sequences from that of the share's first block to that of its last one.
+    if (new_k != nullptr) {
+        const int b0 = seq_of(S.pref, num_seqs, Hkv, x0);
+        const int b1 = seq_of(S.pref, num_seqs, Hkv, x1 - 1);
+        const int items = (b1 - b0 + 1) * Hkv * 2 * kRowChunks;
+        for (int it = tid; it < items; it += kThreads) {
+            const int u = it / (2 * kRowChunks);
+            const int b = b0 + u / Hkv, g = u - (u / Hkv) * Hkv;
             const int nb = S.pref[b + 1] - S.pref[b];
-            const int end = base + Hkv * nb;
-            const int stop = end < x1 ? end : x1;
-            int n = ctx_lens[b];
-            n = n < 0 ? 0 : (n > cap ? cap : n);
-            for (int xx = x + tid; xx < stop; xx += kThreads) {
-                const int r = (int)(xx - base);
-                const int g = r / nb, j = r - g * nb;
-                const int phys = tables[(size_t)b * max_blocks + j];
-                const int left = n - j * kBS;
-                const bool ok = phys >= 0 && phys < num_blocks;
-                S.tile[xx - x0] = ok ? (uint32_t)phys * (uint32_t)Hkv + (uint32_t)g : kNoTile;
-                S.qrow[xx - x0] = b * num_heads + g * group;
-                S.valid[xx - x0] = (uint8_t)(ok ? (left < kBS ? left : kBS) : 0);
-            }
-            x = stop;
-            ++b;
-            while (b < num_seqs && S.pref[b + 1] == S.pref[b]) ++b;
+            const int last = Hkv * S.pref[b] + (g + 1) * nb - 1;
+            if (nb == 0 || last < x0 || last >= x1) continue;
+            append_chunk(k_cache, v_cache, new_k, new_v, tables + (size_t)b * max_blocks, b, g,
+                         Hkv, S.ctx[b], num_blocks, (it / kRowChunks) & 1, it % kRowChunks);
         }
     }
     __syncthreads();
@@ -535,8 +629,6 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         if (lane == 0) S.ends[wave][0] = make_int4(b, g, su, ue);
         int bn, gn;
         next_unit(S.pref, num_seqs, Hkv, b, g, bn, gn);
-        // Two register buffers in fixed roles (the loop is unrolled by two), so a
-        // block's loads land where the fold reads them: no copies, no early waits.
         // Every step issues one block (a zero-record buffer past the quarter's end), so
         // the number of loads in flight never depends on the path taken.
         auto issue = [&](BlockRegs& R, int xi) {
@@ -547,11 +639,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         // kRing register buffers in fixed roles (the loop is unrolled kRing times): a
         // block's loads land where the fold reads them (no copies), and kRing - 1
         // blocks stay in flight behind the one being folded.
-        BlockRegs R0, R1, R2, R3;
+        static_assert(kRing == 2, "the loop below is unrolled for two buffers");
+        BlockRegs R0, R1;
         issue(R0, xa);
         issue(R1, xa + 1);
-        issue(R2, xa + 2);
-        issue(R3, xa + 3);
         WaveState st;
         reset(st);
         int x = xa;
@@ -583,8 +674,6 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         while (true) {
             PKV_STEP(R0)
             PKV_STEP(R1)
-            PKV_STEP(R2)
-            PKV_STEP(R3)
         }
 #undef PKV_STEP
         flush();
@@ -621,7 +710,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
             const int h = i / (kD / 4), d0 = (i % (kD / 4)) * 4;
             float M, Ls;
             float4 o;
-            merge_parts<GMAX>(S.part, P, n, h, d0, M, Ls, o);
+            merge_parts<GMAX, NW * 2, NW>(S.part, P, n, h, d0, M, Ls, o);
             if (!crosses) {
                 const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
                 store4(rows + h * kD + d0, make_float4(o.x * inv, o.y * inv, o.z * inv,
@@ -663,7 +752,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         const int u = (wave ? cb1 : cb0) * Hkv + (wave ? cg1 : cg0);
         const int done = __hip_atomic_fetch_add(&counters[u], 1, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
-        S.flag[wave] = (done == (ue - 1) / C - su / C);
+        S.flag[wave] = (done == shares.owner(ue - 1) - shares.owner(su));
     }
     __syncthreads();
     // A last contributor reads every workgroup's piece back (coherent loads) and merges
@@ -673,28 +762,29 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
     if (S.flag[k]) {
         const int b = k ? cb1 : cb0, g = k ? cg1 : cg0;
         const int su = k ? cs1 : cs0, ue = k ? ce1 : ce0;
-        const int wf = su / C, wl = (ue - 1) / C;
+        const int wf = shares.owner(su), wl = shares.owner(ue - 1);
         T* rows = out + ((size_t)b * num_heads + (size_t)g * group) * kD;
         for (int i = t; i < group * (kD / 4); i += span) {
             const int h = i / (kD / 4), d0 = (i % (kD / 4)) * 4;
-            float M = kNegInf;
-            for (int v = wf; v <= wl; ++v) {
-                const int sl = (2 * v + ((v > wf || su == v * C) ? 0 : 1)) *
-                               Part<GMAX>::kFloats;
-                M = fmaxf(M, fetch1(R, 4 * (sl + Part<GMAX>::kM + h)));
-            }
-            float Ls = 0.f;
+            // Online merge in workgroup order. The loads of unrolled iterations do not
+            // depend on the running state, so they go out together: one round trip.
+            float M = kNegInf, Ls = 0.f;
             float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
             for (int v = wf; v <= wl; ++v) {
-                const int sl = (2 * v + ((v > wf || su == v * C) ? 0 : 1)) *
+                const int sl = (2 * v + ((v > wf || su == shares.start(v)) ? 0 : 1)) *
                                Part<GMAX>::kFloats;
-                const float wt = weight(fetch1(R, 4 * (sl + Part<GMAX>::kM + h)), M);
-                Ls += fetch1(R, 4 * (sl + Part<GMAX>::kL + h)) * wt;
+                const float m = fetch1(R, 4 * (sl + Part<GMAX>::kM + h));
+                const float l = fetch1(R, 4 * (sl + Part<GMAX>::kL + h));
                 const float4 pv = fetch4(R, 4 * (sl + h * kD + d0));
-                o.x += pv.x * wt;
-                o.y += pv.y * wt;
-                o.z += pv.z * wt;
-                o.w += pv.w * wt;
+                const float Mn = fmaxf(M, m);
+                const float a = weight(M, Mn), c = weight(m, Mn);
+                Ls = Ls * a + l * c;
+                o.x = o.x * a + pv.x * c;
+                o.y = o.y * a + pv.y * c;
+                o.z = o.z * a + pv.z * c;
+                o.w = o.w * a + pv.w * c;
+                M = Mn;
             }
             const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
             store4(rows + h * kD + d0, make_float4(o.x * inv, o.y * inv, o.z * inv,
@@ -717,8 +807,8 @@ struct PartLds {
 
 template <typename T, int GMAX>
 __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
-    T* __restrict__ out, const T* __restrict__ q, const T* __restrict__ k_cache,
-    const T* __restrict__ v_cache, const int32_t* __restrict__ tables,
+    T* __restrict__ out, const T* __restrict__ q, T* k_cache, T* v_cache,
+    const T* __restrict__ new_k, const T* __restrict__ new_v, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx_lens, float scale_log2, int num_heads, int num_kv_heads,
     int group, int max_blocks, int num_blocks, int part_blocks, int max_parts,
     float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
@@ -747,6 +837,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
         S.tile[j - j0] = ok ? (uint32_t)phys * (uint32_t)num_kv_heads + (uint32_t)g : kNoTile;
         S.valid[j - j0] = (uint8_t)(ok ? (left < kBS ? left : kBS) : 0);
     }
+    // fused append: the partition holding the newest token writes its K and V rows
+    // (the barrier below orders the stores before this workgroup's loads)
+    if (new_k != nullptr && (n - 1) / kBS >= j0 && (n - 1) / kBS < j1 &&
+        tid < 2 * kRowChunks)
+        append_chunk(k_cache, v_cache, new_k, new_v, tables + (size_t)b * max_blocks, b, g,
+                     num_kv_heads, n, num_blocks, tid / kRowChunks, tid % kRowChunks);
     __syncthreads();
     WaveState st;
     reset(st);
@@ -781,7 +877,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
         const int h = i / (kD / 4), d0 = (i % (kD / 4)) * 4;
         float M, Ls;
         float4 o;
-        merge_parts<GMAX>(S.part, P, kWaves, h, d0, M, Ls, o);
+        merge_parts<GMAX, kWaves, kWaves>(S.part, P, kWaves, h, d0, M, Ls, o);
         const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
         o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
         const size_t hrow = (size_t)b * num_heads + g * group + h;
@@ -808,17 +904,28 @@ int wg_per_cu() {
     return v;
 }
 
+// Share skew between XCD parities, per mille (see ShareMap); PKV_XCD_SKEW overrides.
+constexpr int kXcdSkew = 0;
+int xcd_skew_permille() {
+    static const int v = [] {
+        const char* e = std::getenv("PKV_XCD_SKEW");
+        const int n = e ? std::atoi(e) : kXcdSkew;
+        return n >= 0 && n <= 300 ? n : kXcdSkew;
+    }();
+    return v;
+}
+
 template <typename T, int GMAX, int NW>
 int launch_balanced(const DecodeArgs& a, const DecodePlan& plan, int workers,
                     hipStream_t stream) {
     const DecodeShape& s = a.shape;
     char* ws = (char*)a.workspace;
     hipLaunchKernelGGL((decode_mfma_balanced_kernel<T, GMAX, NW>), dim3(workers),
-                       dim3(64 * NW), 0, stream, (T*)a.out, (const T*)a.q,
-                       (const T*)a.k_cache, (const T*)a.v_cache, a.block_tables, a.context_lens,
-                       a.scale * kLog2e, s.num_seqs, s.num_heads, s.num_kv_heads, plan.group,
+                       dim3(64 * NW), 0, stream, (T*)a.out, (const T*)a.q, (T*)a.k_cache,
+                       (T*)a.v_cache, (const T*)a.new_k, (const T*)a.new_v, a.block_tables,
+                       a.context_lens, a.scale * kLog2e, s.num_seqs, s.num_heads, s.num_kv_heads, plan.group,
                        s.max_blocks, s.num_blocks, (int32_t*)(ws + plan.off_counters),
-                       (float*)(ws + plan.off_partials));
+                       (float*)(ws + plan.off_partials), xcd_skew_permille());
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -829,8 +936,9 @@ int launch_partitioned(const DecodeArgs& a, const DecodePlan& plan, hipStream_t 
     const bool split = plan.max_partitions > 1;
     hipLaunchKernelGGL((decode_mfma_partition_kernel<T, GMAX>),
                        dim3(plan.max_partitions, s.num_kv_heads, s.num_seqs), dim3(kThreads), 0,
-                       stream, (T*)a.out, (const T*)a.q, (const T*)a.k_cache,
-                       (const T*)a.v_cache, a.block_tables, a.context_lens, a.scale * kLog2e,
+                       stream, (T*)a.out, (const T*)a.q, (T*)a.k_cache, (T*)a.v_cache,
+                       (const T*)a.new_k, (const T*)a.new_v, a.block_tables, a.context_lens,
+                       a.scale * kLog2e,
                        s.num_heads, s.num_kv_heads, plan.group, s.max_blocks, s.num_blocks,
                        plan.partition_tokens / kBS, plan.max_partitions,
                        split ? (float*)(ws + plan.off_m) : nullptr,

@@ -1,10 +1,13 @@
-// Cache companions of paged decode attention: slot-mapped append and block copy.
+// Cache companions of paged decode attention: slot-mapped append, the decode step's
+// append at each context end (for paths whose decode kernel does not fuse it) and
+// block copy.
 //
 // Both are pure data movement. Each thread moves one 16-byte (or 4-byte) chunk per
 // loop trip; consecutive threads take consecutive chunks of a row, so a wavefront's
 // stores cover contiguous runs of a KV row. Bounds are checked per chunk so that
 // no index array content can push an access outside the pools.
 #include "launchers.h"
+#include "pagedkv.h"
 
 namespace pkv {
 
@@ -29,6 +32,38 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
         const int64_t off = slot - blk * block_size;
         const int64_t h = rem / row_chunks;
         const int64_t c = rem - h * row_chunks;
+        const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_chunks + c;
+        k_cache[dst] = key[i];
+        v_cache[dst] = value[i];
+    }
+}
+
+// The append of a decode step with slots taken from the block tables: row (b, h) of
+// key/value goes to position context_lens[b] - 1 of sequence b, i.e. physical block
+// tables[b][(n - 1) / block_size] at offset (n - 1) % block_size. Empty contexts and
+// out-of-range table entries write nothing.
+template <typename Chunk>
+__global__ __launch_bounds__(256) void append_at_context_end_kernel(
+    const Chunk* __restrict__ key, const Chunk* __restrict__ value, Chunk* __restrict__ k_cache,
+    Chunk* __restrict__ v_cache, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ ctx_lens, int num_seqs, int num_kv_heads, int row_chunks,
+    int block_size, int max_blocks, int num_blocks) {
+    const int64_t per_seq = (int64_t)num_kv_heads * row_chunks;
+    const int64_t total = (int64_t)num_seqs * per_seq;
+    const int64_t cap = (int64_t)max_blocks * block_size;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t b = i / per_seq;
+        int64_t n = ctx_lens[b];
+        n = n > cap ? cap : n;
+        if (n <= 0) continue;
+        const int64_t j = (n - 1) / block_size;
+        const int64_t blk = tables[b * max_blocks + j];
+        if (blk < 0 || blk >= num_blocks) continue;
+        const int64_t rem = i - b * per_seq;            // h * row_chunks + c
+        const int64_t h = rem / row_chunks;
+        const int64_t c = rem - h * row_chunks;
+        const int64_t off = (n - 1) - j * block_size;
         const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_chunks + c;
         k_cache[dst] = key[i];
         v_cache[dst] = value[i];
@@ -80,6 +115,31 @@ int launch_reshape_and_cache(const void* key, const void* value, void* k_cache, 
                            (const uint32_t*)key, (const uint32_t*)value, (uint32_t*)k_cache,
                            (uint32_t*)v_cache, slot_mapping, num_tokens, num_kv_heads, rc,
                            block_size, num_blocks);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_append_at_context_end(const DecodeArgs& a, hipStream_t stream) {
+    const DecodeShape& s = a.shape;
+    const int elt = s.dtype == PKV_FLOAT32 ? 4 : 2;
+    const int row_bytes = s.head_dim * elt;
+    const int64_t rows = (int64_t)s.num_seqs * s.num_kv_heads;
+    if (rows == 0 || s.max_blocks == 0) return 0;
+    if (row_bytes % 16 == 0) {
+        const int rc = row_bytes / 16;
+        hipLaunchKernelGGL(append_at_context_end_kernel<uint4>,
+                           dim3(grid_for(rows * rc, 256, 65536)), dim3(256), 0, stream,
+                           (const uint4*)a.new_k, (const uint4*)a.new_v, (uint4*)a.k_cache,
+                           (uint4*)a.v_cache, a.block_tables, a.context_lens, s.num_seqs,
+                           s.num_kv_heads, rc, s.block_size, s.max_blocks, s.num_blocks);
+    } else {
+        const int rc = row_bytes / 4;
+        hipLaunchKernelGGL(append_at_context_end_kernel<uint32_t>,
+                           dim3(grid_for(rows * rc, 256, 65536)), dim3(256), 0, stream,
+                           (const uint32_t*)a.new_k, (const uint32_t*)a.new_v,
+                           (uint32_t*)a.k_cache, (uint32_t*)a.v_cache, a.block_tables,
+                           a.context_lens, s.num_seqs, s.num_kv_heads, rc, s.block_size,
+                           s.max_blocks, s.num_blocks);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -88,13 +88,18 @@ int pkv_workspace_init(void* workspace, size_t workspace_bytes, pkv_stream_t str
                                                                               : PKV_E_LAUNCH;
 }
 
-int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
-                               const void* v_cache, const int32_t* block_tables,
-                               const int32_t* context_lens, float scale, int num_seqs,
-                               int num_heads, int num_kv_heads, int head_dim, int block_size,
-                               int max_blocks_per_seq, int num_blocks, pkv_dtype dtype,
-                               int partition_size, void* workspace, size_t workspace_bytes,
-                               pkv_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the plain and the fused (append + decode) entry points; new_k/new_v are
+// NULL for the plain decode.
+int decode_call(void* out, const void* q, const void* new_k, const void* new_v,
+                const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                const int32_t* context_lens, float scale, int num_seqs, int num_heads,
+                int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                int num_blocks, pkv_dtype dtype, int partition_size, void* workspace,
+                size_t workspace_bytes, pkv_stream_t stream) {
     pkv::DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        max_blocks_per_seq, num_blocks, (int)dtype, partition_size};
     pkv::DecodePlan plan{};
@@ -111,15 +116,51 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
         if (v != PKV_OK) return v;
     }
     pkv::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, scale, s, workspace};
+    a.new_k = new_k;
+    a.new_v = new_v;
     int lr;
     if (plan.path == pkv::Path::Generic) {
-        lr = pkv::launch_decode_generic(a, plan, st);
+        // the VALU kernel does not fuse the append: run it as its own kernel first
+        lr = new_k ? pkv::launch_append_at_context_end(a, st) : 0;
+        if (lr == 0) lr = pkv::launch_decode_generic(a, plan, st);
     } else {
         const int cus = current_device_cus();
         if (cus <= 0) return PKV_E_DEVICE;
         lr = pkv::launch_decode_mfma(a, plan, cus, st);
     }
     return lr == 0 ? PKV_OK : PKV_E_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, float scale, int num_seqs,
+                               int num_heads, int num_kv_heads, int head_dim, int block_size,
+                               int max_blocks_per_seq, int num_blocks, pkv_dtype dtype,
+                               int partition_size, void* workspace, size_t workspace_bytes,
+                               pkv_stream_t stream) {
+    return decode_call(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens,
+                       scale, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, num_blocks, dtype, partition_size, workspace,
+                       workspace_bytes, stream);
+}
+
+int pkv_paged_attention_decode_append(void* out, const void* q, const void* new_k,
+                                      const void* new_v, void* k_cache, void* v_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      float scale, int num_seqs, int num_heads,
+                                      int num_kv_heads, int head_dim, int block_size,
+                                      int max_blocks_per_seq, int num_blocks, pkv_dtype dtype,
+                                      int partition_size, void* workspace,
+                                      size_t workspace_bytes, pkv_stream_t stream) {
+    if (num_seqs > 0 && (!new_k || !new_v)) return PKV_E_NULL;
+    return decode_call(out, q, new_k, new_v, k_cache, v_cache, block_tables, context_lens,
+                       scale, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, num_blocks, dtype, partition_size, workspace,
+                       workspace_bytes, stream);
 }
 
 int pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,

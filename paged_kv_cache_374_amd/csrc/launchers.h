@@ -30,7 +30,15 @@ struct DecodeArgs {
     float scale;
     DecodeShape shape;
     void* workspace;
+    // Fused append (both NULL for a plain decode): new K/V rows [num_seqs, Hkv, D]
+    // written at each sequence's last context position before it is attended.
+    const void* new_k = nullptr;
+    const void* new_v = nullptr;
 };
+
+// The append half of a fused decode step as its own kernel (paths whose decode kernel
+// does not fuse it): new_k/new_v[b] go to position context_lens[b] - 1 of sequence b.
+int launch_append_at_context_end(const DecodeArgs& a, hipStream_t stream);
 
 // VALU kernel over fixed partitions (+ reduction when a context spans several).
 int launch_decode_generic(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);

@@ -5,6 +5,6 @@ holds none of the attention arithmetic.
 """
 from .blockmgr import (BlockPool, OutOfBlocks, Sequence_, append_token, blocks_needed,
                        locate, pack_tables, prefill, release, slot_of)
-from .configs import (WORKLOADS, DecodeStep, fp32_scale, llama3_8b_decode, llama_70b_decode,
+from .configs import (WORKLOADS, DecodeStep, batch_with_lengths, fp32_scale, llama3_8b_decode, llama_70b_decode,
                       long_context_decode, random_small, shared_prefix_cow, tiny_fp32,
                       with_append)

@@ -13,8 +13,8 @@ the pool is the free-list order, so consecutive logical blocks land on scattered
 physical blocks.
 
 The shapes follow the serving workloads the pages talk about (grouped-query
-heads, head_dim 128, block_size 16, variable context lengths); see the README of
-the design for the exact recipes. Random numbers for large pools can be drawn on
+heads, head_dim 128, block_size 16, variable context lengths); each builder's
+docstring gives its exact recipe. Random numbers for large pools can be drawn on
 the GPU (``gen_device``) so that multi-GiB pools are not generated on the host;
 block tables and lengths always come from a CPU generator.
 """
@@ -278,6 +278,18 @@ def random_small(seed: int, *, batch: int, num_heads: int, num_kv_heads: int, he
     width = max(1, max(blocks_needed(n, block_size) for n in ctx))
     return _scattered_batch(f"random_small_{seed}", seed, ctx, nb, num_heads, num_kv_heads,
                             head_dim, block_size, width, dtype, device, gen_device, True)
+
+
+def batch_with_lengths(seed: int, lens: List[int], *, num_heads: int, num_kv_heads: int,
+                       head_dim: int, block_size: int, dtype=torch.float32, spare: int = 5,
+                       device="cpu", gen_device="cpu") -> DecodeStep:
+    """A batch with exactly these context lengths (edge-case tests), blocks scattered
+    over a shuffled pool with ``spare`` unused blocks."""
+    need = sum(blocks_needed(n, block_size) for n in lens)
+    width = max(1, max(blocks_needed(n, block_size) for n in lens))
+    return _scattered_batch(f"lengths_{seed}", seed, list(lens), need + spare, num_heads,
+                            num_kv_heads, head_dim, block_size, width, dtype, device,
+                            gen_device, True)
 
 
 WORKLOADS = {
