@@ -58,9 +58,38 @@ def build_sets(name, rotate, dev):
         W.with_append(s, seed=base + 100 * i)
         s.out = torch.empty_like(s.q)
         s.kv = s.kv_bytes()          # computed once: no device sync inside the timed loop
+        # distinct physical blocks the decode reads (whole blocks), for batches that
+        # share prefix blocks between sequences
+        bs, tb = s.block_size, s.block_tables.cpu()
+        used = {int(tb[b, j]) for b, n in enumerate(s.context_lens.cpu().tolist())
+                for j in range((n + bs - 1) // bs)}
+        s.kv_unique = len(used) * s.num_kv_heads * 2 * bs * s.head_dim * s.q.element_size()
         sets.append(s)
         log(f"[bench] built {name} set {i}: batch {s.num_seqs}, kv bytes {s.kv_bytes()}")
     return sets
+
+
+def older_tokens_to_setup(pkv, s):
+    """A batch whose append holds several tokens per sequence (the shared-prefix
+    batch writes every token placed after the fork): the tokens before each
+    sequence's newest are written once here, untimed, as earlier decode steps would
+    have written them. The timed step appends only the newest token of each sequence,
+    the one at position ctx - 1."""
+    bs = s.block_size
+    tables = s.block_tables.cpu().tolist()
+    ctx = s.context_lens.cpu().tolist()
+    slots = s.slot_mapping.cpu().tolist()
+    where = {slot: t for t, slot in enumerate(slots)}
+    newest = [where[tables[b][(n - 1) // bs] * bs + (n - 1) % bs] for b, n in enumerate(ctx)]
+    keep = set(newest)
+    older = torch.tensor([t for t in range(len(slots)) if t not in keep], device=s.q.device)
+    newest = torch.tensor(newest, device=s.q.device)
+    pkv.reshape_and_cache(s.new_k[older].contiguous(), s.new_v[older].contiguous(),
+                          s.k_cache, s.v_cache, s.slot_mapping[older].contiguous())
+    s.new_k = s.new_k[newest].contiguous()
+    s.new_v = s.new_v[newest].contiguous()
+    s.slot_mapping = s.slot_mapping[newest].contiguous()
+    torch.cuda.synchronize()
 
 
 def prepare(pkv, s, graphs, fused):
@@ -69,7 +98,18 @@ def prepare(pkv, s, graphs, fused):
     reshape_and_cache + paged_attention_decode. ``s.dec`` is the call that carries the
     decode kernel. With ``graphs`` the step is captured into one HIP graph, so a step
     is one graph launch."""
-    if fused:
+    copy = None
+    if s.copy_pairs is not None and s.copy_pairs.numel() > 0:
+        copy = pkv.PreparedCopyBlocks([s.k_cache, s.v_cache], s.copy_pairs)
+        copy()                       # copy-on-write before any write after the fork
+        # Repeating the copies in every step is harmless only while no written token
+        # sits in a copied block, i.e. when the prefix ends on a block boundary.
+        if s.extra.get("prefix_tokens", 0) % s.block_size != 0:
+            copy = None
+    if s.new_k.shape[0] != s.num_seqs:
+        older_tokens_to_setup(pkv, s)
+    s.fused = fused
+    if s.fused:
         s.dec = pkv.PreparedDecode(s.out, s.q, s.k_cache, s.v_cache, s.block_tables,
                                    s.context_lens, s.scale, partition_size=s.partition_size,
                                    new_k=s.new_k, new_v=s.new_v)
@@ -80,6 +120,8 @@ def prepare(pkv, s, graphs, fused):
         s.dec = pkv.PreparedDecode(s.out, s.q, s.k_cache, s.v_cache, s.block_tables,
                                    s.context_lens, s.scale, partition_size=s.partition_size)
         calls = [app, s.dec]
+    if copy is not None:
+        calls.insert(0, copy)
 
     def run(calls=calls):
         for c in calls:
@@ -282,17 +324,21 @@ def main():
             "element_bytes": elt,
             "mean_context": round(float(s0.context_lens.float().mean()), 1),
             "kv_bytes_per_step": int(kv_per_launch),
+            "kv_unique_block_bytes_per_step": int(sum(x.kv_unique for x in sets) / len(sets)),
+            "partition_size": s0.partition_size,
             "pool_sets": len(sets),
-            "step": ("reshape_and_cache(new token) + paged_attention_decode" if args.unfused
-                     else "paged_attention_decode_append (new token written at each "
-                          "context end, then attended; one kernel)"),
+            "step": ("copy_blocks(K, V) + " if s0.copy_pairs is not None and
+                     s0.extra.get("prefix_tokens", 0) % s0.block_size == 0 else "") +
+                    ("paged_attention_decode_append (new token written at each context end, "
+                     "then attended; one kernel)" if s0.fused else
+                     "reshape_and_cache(new token) + paged_attention_decode"),
             "launch": "one hip graph per step" if args.graphs else "direct (one call per step)",
             "wall_s_timed": round(wall, 4),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attention_decode" if args.unfused
-                      else "paged_attention_decode_append",
+            "kernel": "paged_attention_decode_append" if s0.fused
+                      else "paged_attention_decode",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

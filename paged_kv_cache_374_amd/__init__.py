@@ -22,7 +22,7 @@ import torch
 
 __all__ = ["paged_attention_decode", "paged_attention_decode_append", "reshape_and_cache", "copy_blocks", "workspace_size",
            "workspace_init", "version", "strerror", "PagedKVError", "library_path", "load",
-           "PreparedDecode", "PreparedReshapeAndCache"]
+           "PreparedDecode", "PreparedReshapeAndCache", "PreparedCopyBlocks"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
@@ -296,20 +296,43 @@ class PreparedReshapeAndCache:
             raise PagedKVError(rc, "pkv_reshape_and_cache")
 
 
-def copy_blocks(caches: Union[torch.Tensor, Iterable[torch.Tensor]],
-                src_dst_pairs: torch.Tensor) -> None:
-    """For each (src, dst) row of src_dst_pairs (int32 [n, 2] on the device), copy
-    block src to block dst in every pool of ``caches``."""
+def _copy_args(caches, src_dst_pairs):
     if isinstance(caches, torch.Tensor):
         caches = [caches]
     _gpu(src_dst_pairs, "src_dst_pairs", torch.int32)
     if src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
         raise ValueError("src_dst_pairs must be [n, 2]")
     n = src_dst_pairs.shape[0]
+    args = []
     for c in caches:
         _gpu(c, "cache")
         nb = c.shape[0]
         block_bytes = (c.numel() // nb) * c.element_size() if nb else 0
-        rc = load().pkv_copy_blocks(c.data_ptr(), src_dst_pairs.data_ptr(), n, nb, block_bytes,
-                                    _stream(c.device))
-        _check(rc, "pkv_copy_blocks")
+        args.append((c.data_ptr(), src_dst_pairs.data_ptr(), n, nb, block_bytes))
+    return list(caches), args
+
+
+def copy_blocks(caches: Union[torch.Tensor, Iterable[torch.Tensor]],
+                src_dst_pairs: torch.Tensor) -> None:
+    """For each (src, dst) row of src_dst_pairs (int32 [n, 2] on the device), copy
+    block src to block dst in every pool of ``caches``."""
+    caches, args = _copy_args(caches, src_dst_pairs)
+    for c, a in zip(caches, args):
+        _check(load().pkv_copy_blocks(*a, _stream(c.device)), "pkv_copy_blocks")
+
+
+class PreparedCopyBlocks:
+    """copy_blocks validated once for fixed pools and pairs (see PreparedDecode)."""
+
+    def __init__(self, caches, src_dst_pairs):
+        caches, self._args = _copy_args(caches, src_dst_pairs)
+        self._fn = load().pkv_copy_blocks
+        self._device = src_dst_pairs.device
+        self._keep = (caches, src_dst_pairs)
+
+    def __call__(self, stream: Optional[int] = None) -> None:
+        st = _stream(self._device) if stream is None else stream
+        for a in self._args:
+            rc = self._fn(*a, st)
+            if rc != 0:
+                raise PagedKVError(rc, "pkv_copy_blocks")

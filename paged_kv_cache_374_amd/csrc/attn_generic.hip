@@ -183,14 +183,24 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
     }
 }
 
-// One wavefront per (query head, sequence): merge that row's partitions.
+// One workgroup per (query head, sequence) merges that row's partitions:
+//   M = max_p m_p,  w_p = l_p 2^(m_p - M),  out = sum_p w_p o_p / sum_p w_p
+// (o_p is partition p's normalised output). Threads split the partitions into
+// interleaved sets and the dims into float4 columns, so every load of a thread is
+// independent of the others; the sets are then added in LDS in a fixed order
+// (deterministic).
+constexpr int kReduceThreads = 256;
+
 template <typename T>
-__global__ __launch_bounds__(64) void partition_reduce_kernel(
+__global__ __launch_bounds__(kReduceThreads) void partition_reduce_kernel(
     T* __restrict__ out, const int32_t* __restrict__ ctx_lens, int num_heads, int head_dim,
     int max_blocks, int block_size, int part_tokens, int max_parts,
     const float* __restrict__ ws_m, const float* __restrict__ ws_l,
     const float* __restrict__ ws_o) {
-    const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    __shared__ float4 acc_s[kReduceThreads];
+    __shared__ float w_s[kReduceThreads];
+    __shared__ float max_s[kReduceThreads / 64];
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int cap = max_blocks * block_size;
     int ctx = ctx_lens[b];
     ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
@@ -201,18 +211,48 @@ __global__ __launch_bounds__(64) void partition_reduce_kernel(
     const float* l = ws_l + row * max_parts;
     const float* o = ws_o + row * max_parts * head_dim;
     float M = kNegInf;
-    for (int p = lane; p < nparts; p += 64) M = fmaxf(M, m[p]);
+    for (int p = tid; p < nparts; p += kReduceThreads) M = fmaxf(M, m[p]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float W = 0.f;
-    for (int p = lane; p < nparts; p += 64) W += l[p] * merge_weight(m[p], M);
+    if ((tid & 63) == 0) max_s[tid >> 6] = M;
+    __syncthreads();
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) W += __shfl_xor(W, off);
-    const float inv = W > 0.f ? 1.f / W : 0.f;
-    for (int d = lane; d < head_dim; d += 64) {
-        float acc = 0.f;
-        for (int p = 0; p < nparts; ++p) acc += l[p] * merge_weight(m[p], M) * o[p * head_dim + d];
-        out[row * head_dim + d] = Elt<T>::from_float(acc * inv);
+    for (int i = 0; i < kReduceThreads / 64; ++i) M = fmaxf(M, max_s[i]);
+    const int cols = head_dim / 4;               // 16, 32 or 64
+    const int sets = kReduceThreads / cols;      // 16, 8 or 4
+    const int c = tid % cols, set = tid / cols;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float W = 0.f;
+#pragma unroll 4
+    for (int p = set; p < nparts; p += sets) {
+        const float w = l[p] * merge_weight(m[p], M);
+        const float4 v = reinterpret_cast<const float4*>(o + (size_t)p * head_dim)[c];
+        acc.x += w * v.x;
+        acc.y += w * v.y;
+        acc.z += w * v.z;
+        acc.w += w * v.w;
+        W += w;
+    }
+    acc_s[tid] = acc;
+    w_s[tid] = W;
+    __syncthreads();
+    if (set == 0) {
+        float4 t = acc;
+        float wt = W;
+        for (int k = 1; k < sets; ++k) {
+            const float4 u = acc_s[k * cols + c];
+            t.x += u.x;
+            t.y += u.y;
+            t.z += u.z;
+            t.w += u.w;
+            wt += w_s[k * cols];
+        }
+        const float inv = wt > 0.f ? 1.f / wt : 0.f;
+        T* dst = out + row * head_dim + 4 * c;
+        dst[0] = Elt<T>::from_float(t.x * inv);
+        dst[1] = Elt<T>::from_float(t.y * inv);
+        dst[2] = Elt<T>::from_float(t.z * inv);
+        dst[3] = Elt<T>::from_float(t.w * inv);
     }
 }
 
@@ -238,7 +278,8 @@ template <typename T>
 int launch_reduce_typed(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
     const DecodeShape& s = a.shape;
     const char* ws = (const char*)a.workspace;
-    hipLaunchKernelGGL(partition_reduce_kernel<T>, dim3(s.num_heads, s.num_seqs), dim3(64), 0,
+    hipLaunchKernelGGL(partition_reduce_kernel<T>, dim3(s.num_heads, s.num_seqs),
+                       dim3(kReduceThreads), 0,
                        stream, (T*)a.out, a.context_lens, s.num_heads, s.head_dim, s.max_blocks,
                        s.block_size, plan.partition_tokens, plan.max_partitions,
                        (const float*)(ws + plan.off_m), (const float*)(ws + plan.off_l),

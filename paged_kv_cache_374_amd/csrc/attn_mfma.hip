@@ -460,42 +460,21 @@ __device__ __forceinline__ void append_chunk(T* k_cache, T* v_cache,
 }
 
 // ------------------------------------------------------------------ balanced kernel
-// Shares of the block list, laid out in logical worker order (XCD-major: the `per`
-// workers of XCD 0, then XCD 1, ...). Without skew every share has C = ceil(total/W)
-// blocks. With a skew of s per mille, shares on odd XCDs shrink to C(1 - s/1000) and
-// those on even XCDs grow to cover the rest. (On MI355X the odd-numbered XCDs were
-// measured to stream a few per cent slower than the even ones.) Every workgroup
-// derives the same map from `total`, so share boundaries, and with them the results,
-// do not depend on scheduling.
+// Equal shares of the block list: worker w (logical index) covers [w*C, (w+1)*C)
+// clipped to the list, C = ceil(total / W). Every workgroup derives the same map from
+// `total`, so share boundaries, and with them the results, do not depend on scheduling.
+// (Per-XCD streaming speeds differ by a few per cent, but the pattern changes from
+// machine to machine; a fixed skew between XCDs did not shorten the kernel.)
 struct ShareMap {
-    int per, ce, co, total;
-    __device__ ShareMap(int total_, int W, int skew) : total(total_) {
-        const int C = (total + W - 1) / W;
-        per = W % 8 == 0 ? W / 8 : W;
-        ce = co = C;
-        if (W % 8 == 0 && skew > 0 && skew < 1000) {
-            const int half = W / 2;
-            const int lo = (int)((long long)C * (1000 - skew) / 1000);
-            const int hi = (total - half * lo + half - 1) / half;
-            if (lo >= 1 && hi >= lo && hi <= kShareMax) {
-                co = lo;
-                ce = hi;
-            }
-        }
-    }
+    int C, total;
+    __device__ ShareMap(int total_, int W) : C((total_ + W - 1) / W), total(total_) {}
     // First block of worker w's share (w = W gives the end of the list).
     __device__ int start(int w) const {
-        const int x = w / per, i = w - x * per;
-        const long long s = (long long)(x / 2) * per * (ce + co) + (x & 1) * per * ce +
-                            (long long)i * ((x & 1) ? co : ce);
+        const long long s = (long long)w * C;
         return s < total ? (int)s : total;
     }
     // The worker whose share holds block t (0 <= t < total).
-    __device__ int owner(int t) const {
-        const int pair = per * (ce + co);
-        const int p = t / pair, r = t - p * pair;
-        return r < per * ce ? 2 * p * per + r / ce : (2 * p + 1) * per + (r - per * ce) / co;
-    }
+    __device__ int owner(int t) const { return t / C; }
 };
 
 template <int GMAX, int NW>
@@ -521,7 +500,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
     const T* __restrict__ new_k, const T* __restrict__ new_v, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx_lens, float scale_log2, int num_seqs, int num_heads,
     int num_kv_heads, int group, int max_blocks, int num_blocks, int32_t* __restrict__ counters,
-    float* __restrict__ partials, int xcd_skew) {
+    float* __restrict__ partials) {
     __shared__ BalancedLds<GMAX, NW> S;
     constexpr int kThreads = 64 * NW;
     constexpr int kWaves = NW;
@@ -571,7 +550,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
     // most kMaxWorkers * kShareMax blocks of tables.
     const int total = Hkv * uni(S.pref[num_seqs]);
     if (total == 0) return;
-    const ShareMap shares(total, W, xcd_skew);
+    const ShareMap shares(total, W);
     const int x0 = shares.start(w);
     const int x1 = shares.start(w + 1);
     if (x0 >= x1) return;
@@ -904,17 +883,6 @@ int wg_per_cu() {
     return v;
 }
 
-// Share skew between XCD parities, per mille (see ShareMap); PKV_XCD_SKEW overrides.
-constexpr int kXcdSkew = 0;
-int xcd_skew_permille() {
-    static const int v = [] {
-        const char* e = std::getenv("PKV_XCD_SKEW");
-        const int n = e ? std::atoi(e) : kXcdSkew;
-        return n >= 0 && n <= 300 ? n : kXcdSkew;
-    }();
-    return v;
-}
-
 template <typename T, int GMAX, int NW>
 int launch_balanced(const DecodeArgs& a, const DecodePlan& plan, int workers,
                     hipStream_t stream) {
@@ -925,7 +893,7 @@ int launch_balanced(const DecodeArgs& a, const DecodePlan& plan, int workers,
                        (T*)a.v_cache, (const T*)a.new_k, (const T*)a.new_v, a.block_tables,
                        a.context_lens, a.scale * kLog2e, s.num_seqs, s.num_heads, s.num_kv_heads, plan.group,
                        s.max_blocks, s.num_blocks, (int32_t*)(ws + plan.off_counters),
-                       (float*)(ws + plan.off_partials), xcd_skew_permille());
+                       (float*)(ws + plan.off_partials));
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -219,12 +219,34 @@ def test_long_context_split_k_sampled():
         assert _max_err(got, want) <= TOL[torch.bfloat16], part
 
 
+REDUCE = [(torch.float32, 64, 32), (torch.float32, 256, 32), (torch.bfloat16, 128, 16),
+          (torch.float16, 64, 16)]
+
+
+@pytest.mark.parametrize("dt,d,part", REDUCE,
+                         ids=[f"{str(a).split('.')[-1]}-d{b}-p{c}" for a, b, c in REDUCE])
+def test_reduce_many_partitions(dt, d, part):
+    """Contexts cut into hundreds of partitions (up to 512), one empty row and one
+    single-partition row: the reduction kernel against the oracle."""
+    _say(f"reduce over many partitions {dt} d={d} partition={part}")
+    lens = [8192, 5000, 0, part, 7777, 1]
+    s = W.batch_with_lengths(1200 + d + part, lens, num_heads=8, num_kv_heads=2, head_dim=d,
+                             block_size=16, dtype=dt, device=DEV)
+    want = oracle_decode(s)
+    out = decode(s, partition_size=part)
+    assert torch.all(out[2].float() == 0), "empty context must give zeros"
+    assert _max_err(out, want) <= TOL[dt]
+
+
 @pytest.mark.parametrize("prefix", [2048, 2040])
 def test_shared_prefix_cow_step(prefix):
     _say(f"shared_prefix_cow prefix={prefix}: copy_blocks, reshape_and_cache, decode")
     s = W.shared_prefix_cow(device=DEV, gen_device=DEV, prefix_tokens=prefix)
     kc, vc = s.k_cache.clone(), s.v_cache.clone()
-    pkv.copy_blocks([kc, vc], s.copy_pairs)
+    if prefix == 2048:
+        pkv.copy_blocks([kc, vc], s.copy_pairs)
+    else:                                   # the prepared form of the same call
+        pkv.PreparedCopyBlocks([kc, vc], s.copy_pairs)()
     pkv.reshape_and_cache(s.new_k, s.new_v, kc, vc, s.slot_mapping)
     torch.cuda.synchronize()
     ek = oracle.copy_blocks(s.k_cache, s.copy_pairs)
