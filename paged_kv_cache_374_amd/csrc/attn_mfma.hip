@@ -63,6 +63,9 @@ constexpr uint32_t kNoTile = 0xffffffffu;
 // 2 buffers 53.6 us, 3 buffers 55.7, 4 buffers 56.4, 6 buffers 58. The memory
 // system is saturated either way, and more outstanding requests only add contention.
 constexpr int kRing = 2;
+// s_waitcnt immediate that waits for vmcnt == 0 only (expcnt 7 and lgkmcnt 15 are the
+// "don't wait" values of their fields on gfx9-class parts).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -378,11 +381,13 @@ template <int GMAX, int NREC, int NMAX>
 __device__ __forceinline__ void merge_parts(const float (&rec)[NREC][Part<GMAX>::kFloats],
                                             const int* idx, int n, int h, int d0, float& M,
                                             float& L, float4& o) {
+    // idx[i] must be a valid record for every i < NMAX (callers repeat a valid one
+    // past n), so the reads need no branch and all go out together.
     float m[NMAX], l[NMAX];
     float4 v[NMAX];
 #pragma unroll
     for (int i = 0; i < NMAX; ++i) {
-        const float* r = rec[idx[i < n ? i : 0]];
+        const float* r = rec[idx[i]];
         m[i] = i < n ? r[Part<GMAX>::kM + h] : kNegInf;
         l[i] = r[Part<GMAX>::kL + h];
         v[i] = *reinterpret_cast<const float4*>(r + h * kD + d0);
@@ -477,6 +482,16 @@ struct ShareMap {
     __device__ int owner(int t) const { return t / C; }
 };
 
+// How the workgroup finishes one unit that its waves saw in pieces: merge LDS records
+// rec[0..n-1] (n = 0: nothing to do), then write query rows row.. of the output, or,
+// when the unit crosses the share's edge, publish the merged piece at float offset
+// `slot` of the partials.
+template <int NW>
+struct MergePlan {
+    int rec[NW];
+    int n, cross, row, slot;
+};
+
 template <int GMAX, int NW>
 struct BalancedLds {
     int pref[kMaxSeqsBalanced + 1];   // blocks per sequence, exclusive prefix
@@ -487,6 +502,8 @@ struct BalancedLds {
     KTile ktile[NW];
     float part[NW * 2][Part<GMAX>::kFloats];   // wave v: [2v] first, [2v+1] last unit piece
     int4 ends[NW][2];                          // wave v's first and last unit (b, g, su, ue)
+    MergePlan<NW> plan[NW + 1];                // candidate units of the end phase
+    int nplan;                                 // how many of them have work
     int flag[2];
 };
 
@@ -655,57 +672,29 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
             PKV_STEP(R1)
         }
 #undef PKV_STEP
+        // Retire the padding loads still in flight before the last unit's stores go
+        // out. Their registers are reused below, and the memory counter retires loads
+        // and stores in order, so waiting after the stores would also wait for the
+        // stores to complete (slow while other workgroups saturate the memory system).
+        // The padding loads touch no memory, so this wait is short.
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         flush();
         if (lane == 0) S.ends[wave][1] = make_int4(b, g, su, ue);
     }
     __syncthreads();
 
     // ---- units cut between waves or between workgroups. Each such unit is the first
-    // unit of some non-empty quarter or the share's last unit; the distinct ones are
-    // dealt out to the waves (wave j takes candidates j, j + NW, ...). Units inside
-    // the share are merged from the LDS records and written. At most two (the share's
-    // first and last unit) cross its edges: their merged pieces are published and go
-    // through one count round together below.
+    // unit of some non-empty quarter or the share's last unit. At most two of them (the
+    // share's first and last unit) cross its edges; all other pieces of those belong to
+    // other workgroups.
     const __amdgpu_buffer_rsrc_t R = __builtin_amdgcn_make_buffer_rsrc(
         partials, 0, 2 * kMaxWorkers * Part<GMAX>::kFloats * (int)sizeof(float),
         kRawBufferWord3);
     const int nq = (x1 - x0 + Cw - 1) / Cw;   // non-empty quarters
     // candidate k: first unit of quarter k (k < nq), or the share's last unit (k = nq)
     auto cand = [&](int k) { return k < nq ? S.ends[k][0] : S.ends[nq - 1][1]; };
-    for (int k = wave; k <= nq; k += kWaves) {
-        const int4 u = cand(k);
-        if (k > 0 && cand(k - 1).z == u.z) continue;   // same unit as the previous one
-        const int b = uni(u.x), g = uni(u.y), su = uni(u.z), ue = uni(u.w);
-        const int lo = su > x0 ? su : x0, hi = ue < x1 ? ue : x1;
-        const int wlo = (lo - x0) / Cw, whi = (hi - 1 - x0) / Cw;
-        const bool crosses = su < x0 || ue > x1;
-        if (wlo == whi && !crosses) continue;   // one wave saw all of it: written
-        int P[kWaves];
-        int n = 0;
-        for (int v = wlo; v <= whi; ++v) P[n++] = 2 * v + (su <= x0 + v * Cw ? 0 : 1);
-        T* rows = out + ((size_t)b * num_heads + (size_t)g * group) * kD;
-        const int gslot = (2 * w + (su <= x0 ? 0 : 1)) * Part<GMAX>::kFloats;
-        for (int i = lane; i < group * (kD / 4); i += 64) {
-            const int h = i / (kD / 4), d0 = (i % (kD / 4)) * 4;
-            float M, Ls;
-            float4 o;
-            merge_parts<GMAX, NW * 2, NW>(S.part, P, n, h, d0, M, Ls, o);
-            if (!crosses) {
-                const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-                store4(rows + h * kD + d0, make_float4(o.x * inv, o.y * inv, o.z * inv,
-                                                       o.w * inv));
-            } else {
-                // this workgroup's piece, with write-through stores (see kCoherent)
-                publish4(R, 4 * (gslot + h * kD + d0), o);
-                if (d0 == 0) {
-                    publish1(R, 4 * (gslot + Part<GMAX>::kM + h), M);
-                    publish1(R, 4 * (gslot + Part<GMAX>::kL + h), Ls);
-                }
-            }
-        }
-    }
-    // The crossing units: the first candidate if it starts before the share, the last
-    // if it ends after it (the same unit when it spans the whole share).
+    // The crossing units: the first candidate if it starts before the share or ends
+    // after it, the last if it differs and ends after it.
     int ncross = 0;
     int cb0 = 0, cg0 = 0, cs0 = 0, ce0 = 0, cb1 = 0, cg1 = 0, cs1 = 0, ce1 = 0;
     {
@@ -718,6 +707,56 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
             if (ncross == 0) { cb0 = uni(l.x); cg0 = uni(l.y); cs0 = uni(l.z); ce0 = uni(l.w); }
             else { cb1 = uni(l.x); cg1 = uni(l.y); cs1 = uni(l.z); ce1 = uni(l.w); }
             ++ncross;
+        }
+    }
+    // Lane k of wave 0 writes the merge plan of candidate k; then every thread of the
+    // workgroup takes (candidate, dims) items, so the merges run on all waves at once.
+    // A unit inside the share is written out; a crossing unit's merged piece is
+    // published for the count round below.
+    if (tid <= nq) {
+        const int k = tid;
+        const int4 u = cand(k);
+        MergePlan<NW> pl;
+        const int su = u.z, ue = u.w;
+        const int lo = su > x0 ? su : x0, hi = ue < x1 ? ue : x1;
+        const int wlo = (lo - x0) / Cw, whi = (hi - 1 - x0) / Cw;
+        const bool crosses = su < x0 || ue > x1;
+        pl.cross = crosses;
+        // same unit as the previous candidate, or one wave saw all of it (written)
+        pl.n = ((k > 0 && cand(k - 1).z == su) || (wlo == whi && !crosses))
+                   ? 0 : whi - wlo + 1;
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            const int v = wlo + j < whi ? wlo + j : whi;
+            pl.rec[j] = 2 * v + (su <= x0 + v * Cw ? 0 : 1);
+        }
+        pl.row = u.x * num_heads + u.y * group;
+        pl.slot = (2 * w + (su <= x0 ? 0 : 1)) * Part<GMAX>::kFloats;
+        // keep only the candidates with work, packed to the front
+        const unsigned long long act = __ballot(pl.n > 0);
+        if (pl.n > 0) S.plan[__popcll(act & ((1ull << k) - 1))] = pl;
+        if (k == 0) S.nplan = __popcll(act);
+    }
+    __syncthreads();
+    constexpr int kCols = kD / 4;   // float4 columns of a head's row
+    for (int it = tid; it < S.nplan * group * kCols; it += kThreads) {
+        const int k = it / (group * kCols), i = it - k * (group * kCols);
+        const MergePlan<NW> pl = S.plan[k];   // one copy: all fields load together
+        const int h = i / kCols, d0 = (i % kCols) * 4;
+        float M, Ls;
+        float4 o;
+        merge_parts<GMAX, NW * 2, NW>(S.part, pl.rec, pl.n, h, d0, M, Ls, o);
+        if (!pl.cross) {
+            const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+            store4(out + ((size_t)pl.row + h) * kD + d0,
+                   make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv));
+        } else {
+            // this workgroup's piece, with write-through stores (see kCoherent)
+            publish4(R, 4 * (pl.slot + h * kD + d0), o);
+            if (d0 == 0) {
+                publish1(R, 4 * (pl.slot + Part<GMAX>::kM + h), M);
+                publish1(R, 4 * (pl.slot + Part<GMAX>::kL + h), Ls);
+            }
         }
     }
     if (ncross == 0) return;
@@ -743,8 +782,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         const int su = k ? cs1 : cs0, ue = k ? ce1 : ce0;
         const int wf = shares.owner(su), wl = shares.owner(ue - 1);
         T* rows = out + ((size_t)b * num_heads + (size_t)g * group) * kD;
-        for (int i = t; i < group * (kD / 4); i += span) {
-            const int h = i / (kD / 4), d0 = (i % (kD / 4)) * 4;
+        for (int i = t; i < group * kCols; i += span) {
+            const int h = i / kCols, d0 = (i % kCols) * 4;
             // Online merge in workgroup order. The loads of unrolled iterations do not
             // depend on the running state, so they go out together: one round trip.
             float M = kNegInf, Ls = 0.f;

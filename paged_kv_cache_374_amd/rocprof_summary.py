@@ -39,10 +39,11 @@ def sources_sha() -> str:
 
 
 def _one(pattern: str) -> str:
-    hits = sorted(glob.glob(pattern, recursive=True))
+    """The newest file matching `pattern` (an output folder may hold several runs)."""
+    hits = glob.glob(pattern, recursive=True)
     if not hits:
         raise FileNotFoundError(pattern)
-    return hits[0]
+    return max(hits, key=os.path.getmtime)
 
 
 def kernel_stats(trace_dir: str):
@@ -100,6 +101,7 @@ def main():
     achieved = args.bytes_per_launch / (d["avg_us"] * 1e-6) / 1e9
     lines = [f"# rocprofv3 summary: {args.kernel}", "",
              f"Command: `{args.command}`", "",
+             f"Trace file: `{os.path.basename(tpath)}`", "",
              f"Source hash (kernel sources): `{sources_sha()}`", "",
              "| kernel | calls | avg us | min us | max us | % of GPU time |",
              "|---|---|---|---|---|---|"]
@@ -122,6 +124,7 @@ def main():
         wb = write[kw] * 1024.0 * w_factor
         traffic = fb + wb
         lines += ["", f"PMC command: `{args.pmc_command}`", "",
+                  f"Counter files: `{os.path.basename(fpath)}`, `{os.path.basename(wpath)}`", "",
                   "| counter | calibration kernel reading (KiB) | true bytes | factor | "
                   "decode reading (KiB) | decode bytes/launch |", "|---|---|---|---|---|---|",
                   f"| FETCH_SIZE | {fetch[cf]:.0f} | {args.calib_read_bytes:.0f} | "
