@@ -33,6 +33,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+FP8 = 3   # uint8 tensors holding OCP FP8 E4M3 codes
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -60,6 +61,15 @@ def _bind(lib):
     lib.oracle_copy_blocks.argtypes = [_P, _P, _I, _I, ctypes.c_long]
     lib.oracle_decode.restype = _I
     lib.oracle_decode.argtypes = [_P, _P, ctypes.c_long, _I]
+    lib.oracle_quantize_fp8.restype = _I
+    lib.oracle_quantize_fp8.argtypes = [_P, _P, ctypes.c_long, _I, ctypes.c_float]
+    lib.oracle_paged_attention_kv.restype = _I
+    lib.oracle_paged_attention_kv.argtypes = [_P, _P, _I, _P, _P, _I, ctypes.c_double,
+                                              ctypes.c_double, _P, _P, ctypes.c_double, _I,
+                                              _I, _I, _I, _I, _I, _I, _P, _I, _I]
+    lib.oracle_reshape_and_cache_fp8.restype = _I
+    lib.oracle_reshape_and_cache_fp8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                                 ctypes.c_float, ctypes.c_float]
     lib.oracle_max_threads.restype = _I
     return lib
 
@@ -159,6 +169,110 @@ class PreparedAttention:
         if rc != 0:
             raise ValueError(f"oracle_paged_attention rejected its inputs ({rc})")
         return out
+
+
+# ------------------------------------------------------------------ 8-bit KV cache
+def inv_scale(scale: float) -> float:
+    """The binary32 reciprocal of a cache scale (one IEEE division in float32), the
+    multiplier the quantising append applies."""
+    return float(np.float32(1.0) / np.float32(scale))
+
+
+def fp8_decode(codes: torch.Tensor, lib=None) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (a uint8 tensor) as float64 (C decoder)."""
+    lib = lib or _load()
+    raw = np.ascontiguousarray(codes.detach().to("cpu", torch.uint8).numpy())
+    out = np.empty(raw.size, dtype=np.float64)
+    if lib.oracle_decode(_ptr(out), _ptr(raw), raw.size, FP8) != 0:
+        raise ValueError("oracle_decode failed")
+    return out.reshape(tuple(codes.shape))
+
+
+def fp8_quantize(x: torch.Tensor, inv: float, lib=None) -> torch.Tensor:
+    """E4M3 codes of float32(x) * inv (binary32 product), nearest with ties to even,
+    saturating at 448 (a uint8 CPU tensor shaped like x)."""
+    lib = lib or _load()
+    raw = _raw(x)
+    out = np.empty(raw.size, dtype=np.uint8)
+    if lib.oracle_quantize_fp8(_ptr(out), _ptr(raw), raw.size, DTYPE_CODE[x.dtype],
+                               float(inv)) != 0:
+        raise ValueError("oracle_quantize_fp8 failed")
+    return torch.from_numpy(out.reshape(tuple(x.shape)))
+
+
+def paged_attention_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        k_scale: float, v_scale: float, block_tables: torch.Tensor,
+                        context_lens: torch.Tensor, scale: float,
+                        rows: Optional[Sequence[Tuple[int, int]]] = None, threads: int = 0,
+                        lib=None) -> np.ndarray:
+    """fp64 paged decode attention over 8-bit caches (uint8 E4M3 codes): key =
+    decode(code) * k_scale, value = decode(code) * v_scale; q in its own dtype."""
+    lib = lib or _load()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,Hq,D] and caches [num_blocks,Hkv,bs,D]")
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise ValueError("8-bit caches are uint8 tensors of E4M3 codes")
+    B, Hq, D = q.shape
+    NB, Hkv, bs, D2 = k_cache.shape
+    if D2 != D:
+        raise ValueError("head_dim mismatch")
+    qa = _raw(q)
+    ka = np.ascontiguousarray(k_cache.detach().cpu().numpy())
+    va = np.ascontiguousarray(v_cache.detach().cpu().numpy())
+    tables = np.ascontiguousarray(block_tables.to("cpu", torch.int32).numpy())
+    ctx = np.ascontiguousarray(context_lens.to("cpu", torch.int32).numpy())
+    mb = tables.shape[1] if tables.ndim == 2 else 0
+    if rows is not None:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
+        out = np.zeros((r.shape[0], D), dtype=np.float64)
+        rp, nr = _ptr(r), r.shape[0]
+    else:
+        out = np.zeros((B, Hq, D), dtype=np.float64)
+        rp, nr = None, 0
+    rc = lib.oracle_paged_attention_kv(_ptr(out), _ptr(qa), DTYPE_CODE[q.dtype], _ptr(ka),
+                                       _ptr(va), FP8, float(k_scale), float(v_scale),
+                                       _ptr(tables), _ptr(ctx), float(scale), B, Hq, Hkv, D,
+                                       bs, mb, NB, rp, nr, int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_paged_attention_kv rejected its inputs ({rc})")
+    return out
+
+
+def reshape_and_cache_fp8(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float,
+                          v_scale: float, lib=None):
+    """Expected 8-bit pools (new uint8 CPU tensors) after the quantising append of
+    k, v ([T, Hkv, D], float32/bfloat16/float16) at their slots."""
+    lib = lib or _load()
+    T, Hkv, D = k.shape
+    NB, Hkv2, bs, D2 = k_cache.shape
+    if (Hkv2, D2) != (Hkv, D) or v.shape != k.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    kc = k_cache.detach().to("cpu").clone().contiguous()
+    vc = v_cache.detach().to("cpu").clone().contiguous()
+    ka, va = _raw(k), _raw(v)
+    kca, vca = kc.numpy(), vc.numpy()   # views of kc/vc's storage
+    slots = np.ascontiguousarray(slot_mapping.to("cpu", torch.int64).numpy())
+    rc = lib.oracle_reshape_and_cache_fp8(_ptr(ka), _ptr(va), _ptr(kca), _ptr(vca),
+                                          _ptr(slots), T, Hkv, D, bs, NB,
+                                          DTYPE_CODE[k.dtype], inv_scale(k_scale),
+                                          inv_scale(v_scale))
+    if rc != 0:
+        raise ValueError(f"oracle_reshape_and_cache_fp8 rejected its inputs ({rc})")
+    return kc, vc
+
+
+def decode_step_fp8(q, new_k, new_v, k_cache, v_cache, k_scale, v_scale, block_tables,
+                    context_lens, scale, lib=None):
+    """decode_step over 8-bit caches: the newest tokens' rows are quantised into their
+    slots, then every query attends over its whole context. Returns (out fp64, expected
+    k_cache, expected v_cache)."""
+    slots = context_end_slots(block_tables, context_lens, k_cache.shape[2])
+    kc, vc = reshape_and_cache_fp8(new_k, new_v, k_cache, v_cache, slots, k_scale, v_scale,
+                                   lib=lib)
+    out = paged_attention_fp8(q, kc, vc, k_scale, v_scale, block_tables, context_lens, scale,
+                              lib=lib)
+    return out, kc, vc
 
 
 def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,

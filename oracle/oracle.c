@@ -35,6 +35,16 @@
  * flat slot encoding block * bs + offset is the reading taken for the mapping).
  * copy_blocks: each (src, dst) pair copies a whole block ([P1] section 五,
  * copy-on-write copies the shared block to the new one before the write).
+ *
+ * 8-bit KV cache. [P2] lists an FP8 KV cache among the engine's milestones
+ * ("vLLM 的发展里程碑"), and [P3]'s KV-size formula notes that quantisation lowers
+ * the bytes per element. The format and scales are a reading, since the pages fix
+ * neither. Elements are OCP FP8 E4M3 (1 sign bit, 4 exponent bits with bias 7, 3
+ * mantissa bits; no infinities; S.1111.111 is NaN; largest finite 448). Each cache
+ * has one scale: value = decode(code) * scale. Appending a value x stores
+ * code = round_e4m3(float(x) * inv_scale). The multiply is a binary32 product, and
+ * rounding goes to nearest with ties to an even mantissa; magnitudes of 448 or more
+ * (infinity included) saturate to 448, and NaN stays NaN.
  */
 #include <math.h>
 #include <stdint.h>
@@ -44,7 +54,7 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F16 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F16 = 2, ORACLE_FP8 = 3 };
 
 /* IEEE 754 binary16 -> double, from the format's definition. */
 static double half_to_double(uint16_t h) {
@@ -70,24 +80,73 @@ static double bf16_to_double(uint16_t b) {
     return (double)f;
 }
 
+/* OCP FP8 E4M3 -> double, from the format's definition. */
+static double fp8_to_double(uint8_t c) {
+    int sign = c >> 7, expo = (c >> 3) & 15, mant = c & 7;
+    double v;
+    if (expo == 15 && mant == 7) {
+        v = NAN;
+    } else if (expo == 0) {
+        v = ldexp((double)mant, -9);                 /* subnormal: mant/8 * 2^(1-7) */
+    } else {
+        v = ldexp(8.0 + (double)mant, expo - 10);    /* (1 + mant/8) * 2^(expo-7) */
+    }
+    return sign ? -v : v;
+}
+
+/* binary32 -> OCP FP8 E4M3: nearest, ties to even mantissa, saturating at 448. */
+static uint8_t fp8_from_float(float y) {
+    const uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    const double a = fabs((double)y);
+    if (isnan(y)) return sign | 0x7F;
+    if (a >= 448.0) return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: multiples of 2^-9; a result of 8 is the code of 2^-6,
+           the smallest normal value */
+        return sign | (uint8_t)nearbyint(ldexp(a, 9));
+    }
+    int e;
+    const double f = frexp(a, &e);                   /* a = f * 2^e, 0.5 <= f < 1 */
+    int expo = e - 1;                                /* a = (1 + mant/8) * 2^expo */
+    int mant = (int)nearbyint((2.0 * f - 1.0) * 8.0);
+    if (mant == 8) {
+        mant = 0;
+        expo += 1;
+    }
+    return sign | (uint8_t)(((expo + 7) << 3) | mant);
+}
+
 static double elem(const void* base, size_t i, int dtype) {
     if (dtype == ORACLE_F32) return (double)((const float*)base)[i];
+    if (dtype == ORACLE_FP8) return fp8_to_double(((const uint8_t*)base)[i]);
     uint16_t bits = ((const uint16_t*)base)[i];
     return dtype == ORACLE_BF16 ? bf16_to_double(bits) : half_to_double(bits);
 }
 
 /* Exposed for the tests: decode n raw elements to double. */
 int oracle_decode(double* out, const void* src, long n, int dtype) {
-    if (dtype < 0 || dtype > 2) return -1;
+    if (dtype < 0 || dtype > 3) return -1;
     for (long i = 0; i < n; ++i) out[i] = elem(src, (size_t)i, dtype);
+    return 0;
+}
+
+/* Exposed for the tests: quantise n elements (dtype F32, BF16 or F16) to E4M3 codes,
+   code[i] = fp8_from_float(float(src[i]) * inv_scale). */
+int oracle_quantize_fp8(uint8_t* out, const void* src, long n, int dtype, float inv_scale) {
+    if (dtype < 0 || dtype > 2) return -1;
+    for (long i = 0; i < n; ++i) {
+        const float x = (float)elem(src, (size_t)i, dtype);   /* exact widening */
+        const float y = x * inv_scale;                        /* one binary32 product */
+        out[i] = fp8_from_float(y);
+    }
     return 0;
 }
 
 /*
  * out:          double [B, Hq, D]
- * q:            [B, Hq, D]            (dtype)
- * k_cache:      [num_blocks, Hkv, bs, D]
- * v_cache:      [num_blocks, Hkv, bs, D]
+ * q:            [B, Hq, D]            (q_dtype)
+ * k_cache:      [num_blocks, Hkv, bs, D]   (kv_dtype; key = element * k_scale)
+ * v_cache:      [num_blocks, Hkv, bs, D]   (kv_dtype; value = element * v_scale)
  * block_tables: int32 [B, max_blocks]
  * context_lens: int32 [B]
  * rows:         optional int32 [num_rows, 2] of (b, h) to evaluate; NULL = all.
@@ -95,13 +154,14 @@ int oracle_decode(double* out, const void* src, long n, int dtype) {
  * Returns 0, or -1 for inconsistent sizes, -2 for a table entry outside the pool
  * inside the used part of a table, -3 for a context longer than its table.
  */
-int oracle_paged_attention(double* out, const void* q, const void* k_cache,
-                           const void* v_cache, int dtype, const int32_t* block_tables,
-                           const int32_t* context_lens, double scale, int B, int Hq,
-                           int Hkv, int D, int bs, int max_blocks, int num_blocks,
-                           const int32_t* rows, int num_rows, int nthreads) {
+int oracle_paged_attention_kv(double* out, const void* q, int q_dtype, const void* k_cache,
+                              const void* v_cache, int kv_dtype, double k_scale,
+                              double v_scale, const int32_t* block_tables,
+                              const int32_t* context_lens, double scale, int B, int Hq,
+                              int Hkv, int D, int bs, int max_blocks, int num_blocks,
+                              const int32_t* rows, int num_rows, int nthreads) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || Hq % Hkv != 0) return -1;
-    if (dtype < 0 || dtype > 2) return -1;
+    if (q_dtype < 0 || q_dtype > 2 || kv_dtype < 0 || kv_dtype > 3) return -1;
     const int G = Hq / Hkv;
     for (int b = 0; b < B; ++b) {
         int n = context_lens[b];
@@ -137,7 +197,7 @@ int oracle_paged_attention(double* out, const void* q, const void* k_cache,
             at[t] = (((size_t)phys * Hkv + g) * bs + (size_t)(t % bs)) * D;
             double acc = 0.0;
             for (int d = 0; d < D; ++d)
-                acc += elem(q, qoff + d, dtype) * elem(k_cache, at[t] + d, dtype);
+                acc += elem(q, qoff + d, q_dtype) * (elem(k_cache, at[t] + d, kv_dtype) * k_scale);
             s[t] = scale * acc;
             if (s[t] > mx) mx = s[t];
         }
@@ -148,12 +208,25 @@ int oracle_paged_attention(double* out, const void* q, const void* k_cache,
             denom += s[t];
         }
         for (int t = 0; t < n; ++t)
-            for (int d = 0; d < D; ++d) o[d] += s[t] * elem(v_cache, at[t] + d, dtype);
+            for (int d = 0; d < D; ++d)
+                o[d] += s[t] * (elem(v_cache, at[t] + d, kv_dtype) * v_scale);
         for (int d = 0; d < D; ++d) o[d] /= denom;
         free(s);
         free(at);
     }
     return status;
+}
+
+/* The same walk with q and the caches in one 16/32-bit type and unit scales. */
+int oracle_paged_attention(double* out, const void* q, const void* k_cache,
+                           const void* v_cache, int dtype, const int32_t* block_tables,
+                           const int32_t* context_lens, double scale, int B, int Hq,
+                           int Hkv, int D, int bs, int max_blocks, int num_blocks,
+                           const int32_t* rows, int num_rows, int nthreads) {
+    if (dtype < 0 || dtype > 2) return -1;
+    return oracle_paged_attention_kv(out, q, dtype, k_cache, v_cache, dtype, 1.0, 1.0,
+                                     block_tables, context_lens, scale, B, Hq, Hkv, D, bs,
+                                     max_blocks, num_blocks, rows, num_rows, nthreads);
 }
 
 /*
@@ -186,6 +259,36 @@ int oracle_reshape_and_cache(const void* k, const void* v, void* k_cache, void* 
  * pairs: int32 [n, 2] of (src, dst), applied in order.
  * Returns 0, or -2 for an ID outside the pool.
  */
+/*
+ * The append into an 8-bit cache: the same slot walk, each element quantised.
+ * k, v:          [T, Hkv, D] elements of src_dtype (F32, BF16 or F16)
+ * k_cache, v_cache: uint8 [num_blocks, Hkv, bs, D] E4M3 codes, updated in place
+ * k_inv_scale, v_inv_scale: the binary32 reciprocals of the caches' scales
+ */
+int oracle_reshape_and_cache_fp8(const void* k, const void* v, uint8_t* k_cache,
+                                 uint8_t* v_cache, const int64_t* slot_mapping, int T,
+                                 int Hkv, int D, int bs, int num_blocks, int src_dtype,
+                                 float k_inv_scale, float v_inv_scale) {
+    if (src_dtype < 0 || src_dtype > 2) return -1;
+    for (int t = 0; t < T; ++t) {
+        const int64_t slot = slot_mapping[t];
+        if (slot >= (int64_t)num_blocks * bs) return -2;
+        if (slot >= 0) for (int h = 0; h < Hkv; ++h) {
+            /* slot = block * bs + offset */
+            const int64_t block = slot / bs, offset = slot - block * bs;
+            size_t dst = (((size_t)block * Hkv + h) * bs + (size_t)offset) * D;
+            size_t src = ((size_t)t * Hkv + h) * D;
+            for (int d = 0; d < D; ++d) {
+                k_cache[dst + d] =
+                    fp8_from_float((float)elem(k, src + d, src_dtype) * k_inv_scale);
+                v_cache[dst + d] =
+                    fp8_from_float((float)elem(v, src + d, src_dtype) * v_inv_scale);
+            }
+        }
+    }
+    return 0;
+}
+
 int oracle_copy_blocks(void* cache, const int32_t* pairs, int n, int num_blocks,
                        long block_bytes) {
     for (int i = 0; i < n; ++i) {

@@ -425,8 +425,126 @@ def pin_decode_step_slots(lib):
             assert torch.equal(ev[s.table[p // bs], :, p % bs], V[i][-1])
 
 
+# ------------------------------------------------------------------ 8-bit KV cache
+def _fp8_values(codes):
+    """Values of E4M3 codes through torch's float8_e4m3fn type (a library routine)."""
+    return codes.view(torch.float8_e4m3fn).to(torch.float64)
+
+
+def _random_codes(shape, gen):
+    """Random finite E4M3 codes (both signs, NaN codes excluded)."""
+    mag = torch.randint(0, 0x7F, shape, generator=gen, dtype=torch.int32)
+    sign = torch.randint(0, 2, shape, generator=gen, dtype=torch.int32) * 0x80
+    return (mag | sign).to(torch.uint8)
+
+
+def pin_fp8_decode(lib):
+    """Every OCP E4M3 code decodes to the value torch's float8_e4m3fn type gives it
+    (NaN codes included); closed forms: 448 is the largest finite value, 2^-9 the
+    smallest subnormal, 0x38 is one."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    got = oracle.fp8_decode(codes, lib=lib)
+    want = _fp8_values(codes).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(want)), "NaN codes"
+    fin = ~np.isnan(want)
+    assert np.array_equal(got[fin], want[fin]), "decoded values"
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6 and got[0x38] == 1.0
+
+
+def pin_fp8_quantize(lib):
+    """Quantisation to E4M3: every finite code round-trips; a value midway between
+    neighbouring codes goes to the one with the even mantissa; random in-range values
+    (normal and subnormal) match torch's conversion; 448 and beyond (infinity too)
+    saturate to 448, NaN stays NaN; the scale enters as one binary32 product."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    vals = _fp8_values(codes).to(torch.float32)
+    fin = ~torch.isnan(vals)
+    assert torch.equal(oracle.fp8_quantize(vals[fin], 1.0, lib=lib), codes[fin]), "round trip"
+    for sign in (1.0, -1.0):
+        pos = vals[:0x7F].double() * sign
+        mids = ((pos[:-1] + pos[1:]) / 2).to(torch.float32)   # exact in float32
+        lo = torch.arange(0, 0x7E, dtype=torch.int32)
+        even = torch.where(lo % 2 == 0, lo, lo + 1) | (0x80 if sign < 0 else 0)
+        got = oracle.fp8_quantize(mids, 1.0, lib=lib).to(torch.int32)
+        assert torch.equal(got, even), f"ties to even ({sign:+.0f})"
+    g = torch.Generator().manual_seed(31)
+    for x in ((torch.rand(20000, generator=g) * 2 - 1) * 447.0,
+              torch.randn(20000, generator=g) * 0.02,            # subnormal range too
+              torch.randn(20000, generator=g) * 3.0):
+        want = x.to(torch.float8_e4m3fn).view(torch.uint8)
+        assert torch.equal(oracle.fp8_quantize(x, 1.0, lib=lib), want), "vs torch"
+    # [464, 480) would round up to the NaN code without saturation
+    sat = torch.tensor([448.0, 449.0, 463.9, 464.0, 470.0, 479.99, 1e6, float("inf"),
+                        -448.0, -470.0, -1e6, -float("inf")])
+    assert oracle.fp8_quantize(sat, 1.0, lib=lib).tolist() == [0x7E] * 8 + [0xFE] * 4
+    nan = oracle.fp8_quantize(torch.tensor([float("nan")]), 1.0, lib=lib)
+    assert int(nan[0]) & 0x7F == 0x7F, "NaN"
+    xb = torch.randn(5000, generator=g).to(torch.bfloat16)
+    inv = oracle.inv_scale(0.0123)
+    prod = xb.to(torch.float32) * torch.tensor(inv, dtype=torch.float32)
+    assert torch.equal(oracle.fp8_quantize(xb, inv, lib=lib),
+                       oracle.fp8_quantize(prod, 1.0, lib=lib)), "binary32 product"
+
+
+def pin_fp8_attention(lib):
+    """Attention over 8-bit caches equals the plain definition on the dequantised
+    values (torch's float8 decode times the scales, then the NumPy brute force)."""
+    bs, hkv, hq, d, nb = 4, 2, 4, 16, 24
+    g = torch.Generator().manual_seed(37)
+    kc = _random_codes((nb, hkv, bs, d), g)
+    vc = _random_codes((nb, hkv, bs, d), g)
+    ks, vs = 0.0173, 0.25
+    pool = BlockPool(nb, _order(39, nb))
+    lens = [7, 1, 0, 16, 21]
+    seqs = [prefill(pool, n, bs) for n in lens]
+    tables = torch.tensor(pack_tables(seqs, 6), dtype=torch.int32)
+    ctx = torch.tensor(lens, dtype=torch.int32)
+    q = torch.randn(len(lens), hq, d, generator=g).to(torch.bfloat16)
+    got = oracle.paged_attention_fp8(q, kc, vc, ks, vs, tables, ctx, 0.3, lib=lib)
+    want = oracle.dense_attention(q, _fp8_values(kc) * ks, _fp8_values(vc) * vs, tables, ctx,
+                                  0.3)
+    _close(got, want, 1e-12, "fp8 attention vs dequantised brute force")
+
+
+def pin_fp8_append(lib):
+    """The quantising append writes, at each token's slot, torch's E4M3 conversion of
+    float32(x) * float32(1/scale) (K and V with their own scales), and changes nothing
+    else; negative slots write nothing."""
+    bs, hkv, d, nb = 4, 3, 8, 12
+    g = torch.Generator().manual_seed(41)
+    kc0, vc0 = _random_codes((nb, hkv, bs, d), g), _random_codes((nb, hkv, bs, d), g)
+    pool = BlockPool(nb, _order(43, nb))
+    seq = prefill(pool, 0, bs)
+    slots = [append_token(pool, seq, bs) for _ in range(6)] + [-1]
+    T = len(slots)
+    newk = torch.randn(T, hkv, d, generator=g).to(torch.bfloat16)
+    newv = (torch.randn(T, hkv, d, generator=g) * 5).to(torch.bfloat16)
+    ks, vs = 0.011, 0.07
+    kc, vc = oracle.reshape_and_cache_fp8(newk, newv, kc0, vc0,
+                                          torch.tensor(slots, dtype=torch.int64), ks, vs,
+                                          lib=lib)
+
+    def conv(x, scale):
+        inv = torch.tensor(oracle.inv_scale(scale), dtype=torch.float32)
+        return (x.to(torch.float32) * inv).to(torch.float8_e4m3fn).view(torch.uint8)
+
+    touched = torch.zeros(nb, bs, dtype=torch.bool)
+    for t, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        blk, off = slot // bs, slot % bs
+        assert torch.equal(kc[blk, :, off], conv(newk[t], ks)), "K codes"
+        assert torch.equal(vc[blk, :, off], conv(newv[t], vs)), "V codes"
+        touched[blk, off] = True
+    keep = ~touched
+    assert torch.equal(kc.permute(0, 2, 1, 3)[keep], kc0.permute(0, 2, 1, 3)[keep])
+    assert torch.equal(vc.permute(0, 2, 1, 3)[keep], vc0.permute(0, 2, 1, 3)[keep])
+
+
 ALL_PINS = [pin_decoders, pin_sdpa_library, pin_dense_bruteforce, pin_worked_example,
             pin_two_token_closed_form, pin_context_one, pin_uniform_scores, pin_zero_context,
             pin_placement_permutation, pin_gqa_equals_repeated_mha, pin_stale_slots_unread,
             pin_linearity_in_values, pin_append_roundtrip, pin_copy_on_write,
-            pin_decode_step_slots]
+            pin_decode_step_slots, pin_fp8_decode, pin_fp8_quantize, pin_fp8_attention,
+            pin_fp8_append]

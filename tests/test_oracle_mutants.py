@@ -28,8 +28,8 @@ MUTANTS = {
     "softmax_sign": ("s[t] = exp(s[t] - mx);", "s[t] = exp(mx - s[t]);"),
     "normaliser_wrong": ("o[d] /= denom;", "o[d] /= denom + 1.0;"),
     "first_token_dropped_from_sum": ("denom += s[t];", "denom += t ? s[t] : 0.0;"),
-    "keys_and_values_swapped": ("elem(q, qoff + d, dtype) * elem(k_cache",
-                                "elem(q, qoff + d, dtype) * elem(v_cache"),
+    "keys_and_values_swapped": ("elem(q, qoff + d, q_dtype) * (elem(k_cache",
+                                "elem(q, qoff + d, q_dtype) * (elem(v_cache"),
     "last_token_skipped": ("for (int t = 0; t < n; ++t) {\n            int phys",
                            "for (int t = 0; t < n - 1; ++t) {\n            int phys"),
     "slot_block_offset_swapped": ("int64_t blk = slot / bs, off = slot % bs;",
@@ -39,6 +39,21 @@ MUTANTS = {
                                 "int dst = pairs[2 * i], src = pairs[2 * i + 1];"),
     "bf16_shift_wrong": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
     "f16_bias_wrong": ("expo - 25", "expo - 24"),
+    # 8-bit cache: decoder, quantiser, scales, quantising append
+    "fp8_bias_wrong": ("expo - 10", "expo - 9"),
+    "fp8_subnormal_step_wrong": ("ldexp((double)mant, -9)", "ldexp((double)mant, -10)"),
+    "fp8_ties_away_from_zero": ("(int)nearbyint((2.0 * f - 1.0) * 8.0)",
+                                "(int)round((2.0 * f - 1.0) * 8.0)"),
+    "fp8_no_saturation": ("if (a >= 448.0) return sign | 0x7E;",
+                          "if (a >= 480.0) return sign | 0x7E;"),
+    "fp8_subnormal_bound_wrong": ("if (a < ldexp(1.0, -6)) {", "if (a < ldexp(1.0, -7)) {"),
+    "fp8_key_scale_dropped": ("(elem(k_cache, at[t] + d, kv_dtype) * k_scale)",
+                              "elem(k_cache, at[t] + d, kv_dtype)"),
+    "fp8_value_scale_dropped": ("(elem(v_cache, at[t] + d, kv_dtype) * v_scale)",
+                                "elem(v_cache, at[t] + d, kv_dtype)"),
+    "fp8_append_scales_swapped": ("(float)elem(k, src + d, src_dtype) * k_inv_scale",
+                                  "(float)elem(k, src + d, src_dtype) * v_inv_scale"),
+    "fp8_append_offset_wrong": ("offset = slot - block * bs;", "offset = slot - block;"),
 }
 
 
