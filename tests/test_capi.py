@@ -24,7 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("pkv_paged_attention_decode", "pkv_reshape_and_cache", "pkv_copy_blocks",
+    for n in ("pkv_paged_attention_decode", "pkv_paged_attention_decode_append",
+              "pkv_reshape_and_cache", "pkv_copy_blocks",
               "pkv_paged_attention_workspace_size", "pkv_workspace_init", "pkv_version",
               "pkv_strerror"):
         assert n in names
@@ -84,6 +85,30 @@ def test_decode_rejects_bad_arguments_on_the_host():
     assert _decode(lib, MB=64, part=16, ws=1, ws_bytes=16) == E["WORKSPACE"]
     # empty batch: nothing to do, success without any device work
     assert _decode(lib, B=0, out=None, q=None) == E["OK"]
+
+
+def _fused(lib, **kw):
+    a = dict(out=1, q=1, nk=1, nv=1, k=1, v=1, tables=1, ctx=1, scale=1.0, B=2, Hq=8, Hkv=2,
+             D=128, bs=16, MB=4, NB=16, dtype=BF16, part=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.pkv_paged_attention_decode_append(
+        a["out"], a["q"], a["nk"], a["nv"], a["k"], a["v"], a["tables"], a["ctx"], a["scale"],
+        a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"], a["dtype"], a["part"],
+        a["ws"], a["ws_bytes"], None)
+
+
+def test_fused_step_rejects_bad_arguments_on_the_host():
+    lib = pkv.load()
+    assert _fused(lib, nk=None) == E["NULL"]
+    assert _fused(lib, nv=None) == E["NULL"]
+    assert _fused(lib, Hq=6, Hkv=4) == E["HEADS"]
+    assert _fused(lib, D=96) == E["UNSUPPORTED"]
+    assert _fused(lib, B=-1) == E["SHAPE"]
+    assert _fused(lib, k=None) == E["NULL"]
+    # the balanced path needs its workspace (counters and partial slots)
+    assert _fused(lib) == E["WORKSPACE"]
+    # empty batch: nothing to do
+    assert _fused(lib, B=0, out=None, q=None, nk=None, nv=None) == E["OK"]
 
 
 def test_cache_ops_reject_bad_arguments_on_the_host():
