@@ -47,8 +47,9 @@ def log(msg):
 def build_sets(name, rotate, dev):
     import workloads as W
     builder = W.WORKLOADS[name]
-    base = {"tiny_fp32": 1001, "llama3_8b_decode": 1002, "llama_70b_decode": 1003,
-            "long_context_decode": 1004, "shared_prefix_cow": 1005}[name]
+    base = {"tiny_fp32": 1001, "llama3_8b_decode": 1002, "llama3_8b_decode_fp8": 1002,
+            "llama_70b_decode": 1003, "long_context_decode": 1004,
+            "shared_prefix_cow": 1005}[name]
     sets = []
     for i in range(rotate):
         kw = {"device": dev}
@@ -63,7 +64,8 @@ def build_sets(name, rotate, dev):
         bs, tb = s.block_size, s.block_tables.cpu()
         used = {int(tb[b, j]) for b, n in enumerate(s.context_lens.cpu().tolist())
                 for j in range((n + bs - 1) // bs)}
-        s.kv_unique = len(used) * s.num_kv_heads * 2 * bs * s.head_dim * s.q.element_size()
+        s.kv_unique = len(used) * s.num_kv_heads * 2 * bs * s.head_dim * \
+            s.k_cache.element_size()
         sets.append(s)
         log(f"[bench] built {name} set {i}: batch {s.num_seqs}, kv bytes {s.kv_bytes()}")
     return sets
@@ -84,8 +86,12 @@ def older_tokens_to_setup(pkv, s):
     keep = set(newest)
     older = torch.tensor([t for t in range(len(slots)) if t not in keep], device=s.q.device)
     newest = torch.tensor(newest, device=s.q.device)
-    pkv.reshape_and_cache(s.new_k[older].contiguous(), s.new_v[older].contiguous(),
-                          s.k_cache, s.v_cache, s.slot_mapping[older].contiguous())
+    rows = (s.new_k[older].contiguous(), s.new_v[older].contiguous(), s.k_cache, s.v_cache,
+            s.slot_mapping[older].contiguous())
+    if s.kv_scales is not None:
+        pkv.reshape_and_cache_fp8(*rows, *s.kv_scales)
+    else:
+        pkv.reshape_and_cache(*rows)
     s.new_k = s.new_k[newest].contiguous()
     s.new_v = s.new_v[newest].contiguous()
     s.slot_mapping = s.slot_mapping[newest].contiguous()
@@ -109,16 +115,23 @@ def prepare(pkv, s, graphs, fused):
     if s.new_k.shape[0] != s.num_seqs:
         older_tokens_to_setup(pkv, s)
     s.fused = fused
+    ks, vs = s.kv_scales if s.kv_scales is not None else (None, None)
     if s.fused:
         s.dec = pkv.PreparedDecode(s.out, s.q, s.k_cache, s.v_cache, s.block_tables,
                                    s.context_lens, s.scale, partition_size=s.partition_size,
-                                   new_k=s.new_k, new_v=s.new_v)
+                                   new_k=s.new_k, new_v=s.new_v, k_scale=ks, v_scale=vs)
         calls = [s.dec]
     else:
-        app = pkv.PreparedReshapeAndCache(s.new_k, s.new_v, s.k_cache, s.v_cache,
-                                          s.slot_mapping)
+        if s.kv_scales is not None:
+            def app(s=s):
+                pkv.reshape_and_cache_fp8(s.new_k, s.new_v, s.k_cache, s.v_cache,
+                                          s.slot_mapping, *s.kv_scales)
+        else:
+            app = pkv.PreparedReshapeAndCache(s.new_k, s.new_v, s.k_cache, s.v_cache,
+                                              s.slot_mapping)
         s.dec = pkv.PreparedDecode(s.out, s.q, s.k_cache, s.v_cache, s.block_tables,
-                                   s.context_lens, s.scale, partition_size=s.partition_size)
+                                   s.context_lens, s.scale, partition_size=s.partition_size,
+                                   k_scale=ks, v_scale=vs)
         calls = [app, s.dec]
     if copy is not None:
         calls.insert(0, copy)
@@ -171,7 +184,7 @@ def cpu_baseline(s, seconds):
     import numpy as np
     import oracle
     prep = oracle.PreparedAttention(s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens,
-                                    s.scale)
+                                    s.scale, kv_scales=s.kv_scales)
     threads = oracle.max_threads()
     reps, t_total, want = 0, 0.0, None
     while True:
@@ -295,8 +308,10 @@ def main():
     if args.calibrate:
         calibrate(pkv, dev)
 
-    elt = s0.q.element_size()
+    elt = s0.k_cache.element_size()
     dname = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[s0.dtype]
+    kv_dname = "fp8_e4m3" if s0.kv_scales is not None else dname
+    fp8 = "_fp8" if s0.kv_scales is not None else ""
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -320,7 +335,7 @@ def main():
             "head_dim": s0.head_dim,
             "block_size": s0.block_size,
             "num_blocks": s0.num_blocks,
-            "kv_dtype": dname,
+            "kv_dtype": kv_dname,
             "element_bytes": elt,
             "mean_context": round(float(s0.context_lens.float().mean()), 1),
             "kv_bytes_per_step": int(kv_per_launch),
@@ -337,8 +352,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attention_decode_append" if s0.fused
-                      else "paged_attention_decode",
+            "kernel": ("paged_attention_decode_append" if s0.fused
+                       else "paged_attention_decode") + fp8,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -6,7 +6,8 @@
  *   pkv_reshape_and_cache       write each new token's K/V into its slot
  *   pkv_copy_blocks             copy whole blocks (copy-on-write)
  * plus pkv_paged_attention_decode_append (a decode step's append and attention in
- * one call), workspace sizing/initialisation, version and error strings.
+ * one call), the same calls over 8-bit (FP8 E4M3) caches, workspace sizing and
+ * initialisation, version and error strings.
  *
  * Pages cited (titles as published):
  *   [P1] "vLLM 源码解析：PagedAttention 如何让大模型推理提速 10 倍"
@@ -43,7 +44,8 @@
 extern "C" {
 #endif
 
-/* Element type of q, out, k/v and the caches (all share one type). */
+/* Element type of q, out, k/v and the caches (all share one type, except in the
+ * *_fp8 calls, whose caches hold OCP FP8 E4M3 codes). */
 typedef enum {
     PKV_FLOAT32 = 0,
     PKV_BFLOAT16 = 1,
@@ -177,6 +179,61 @@ int pkv_paged_attention_decode_append(void* out, const void* q, const void* new_
                                       int max_blocks_per_seq, int num_blocks, pkv_dtype dtype,
                                       int partition_size, void* workspace,
                                       size_t workspace_bytes, pkv_stream_t stream);
+
+/*
+ * 8-bit KV caches. [P2] lists an FP8 KV cache among the engine's milestones (section
+ * "vLLM 的发展里程碑"), and [P3]'s KV-size formula notes that quantisation lowers the
+ * bytes per element. The format and the scales are this library's reading, since the
+ * pages fix neither.
+ *  - Each cache element is one byte, an OCP FP8 E4M3 code: 1 sign bit, 4 exponent bits
+ *    with bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN, largest finite 448.
+ *  - Each cache has one scale, so key = decode(code) * k_scale and
+ *    value = decode(code) * v_scale. Both scales must be positive and finite
+ *    (PKV_E_SHAPE otherwise).
+ *  - Appending stores code = E4M3(float(x) * (1.0f / scale)): one binary32 product with
+ *    the binary32 reciprocal, rounded to the nearest code (ties to an even mantissa).
+ *    Magnitudes of 448 or more saturate to +-448; NaN stays NaN.
+ *  - q, out and the appended rows keep their 16-bit dtype. Every E4M3 value is exact
+ *    in bfloat16 and float16, so the attention arithmetic is that of the 16-bit calls.
+ *  - Supported: dtype bfloat16/float16, head_dim 128, block_size 16 (the matrix-core
+ *    kernels); other shapes return PKV_E_UNSUPPORTED.
+ * Caches are [num_blocks, num_kv_heads, block_size, head_dim] bytes. pkv_copy_blocks
+ * serves them unchanged, with block_bytes = num_kv_heads * block_size * head_dim.
+ */
+
+/* pkv_paged_attention_decode over 8-bit caches (arguments as there, plus the scales). */
+int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_cache,
+                                   const void* v_cache, float k_scale, float v_scale,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   float scale, int num_seqs, int num_heads, int num_kv_heads,
+                                   int head_dim, int block_size, int max_blocks_per_seq,
+                                   int num_blocks, pkv_dtype dtype, int partition_size,
+                                   void* workspace, size_t workspace_bytes,
+                                   pkv_stream_t stream);
+
+/* pkv_paged_attention_decode_append over 8-bit caches: new_k/new_v ([num_seqs,
+ * num_kv_heads, head_dim], dtype) are quantised as described above into the slot of
+ * each sequence's last context position, then attended. Same caller contract. */
+int pkv_paged_attention_decode_append_fp8(void* out, const void* q, const void* new_k,
+                                          const void* new_v, void* k_cache, void* v_cache,
+                                          float k_scale, float v_scale,
+                                          const int32_t* block_tables,
+                                          const int32_t* context_lens, float scale,
+                                          int num_seqs, int num_heads, int num_kv_heads,
+                                          int head_dim, int block_size, int max_blocks_per_seq,
+                                          int num_blocks, pkv_dtype dtype, int partition_size,
+                                          void* workspace, size_t workspace_bytes,
+                                          pkv_stream_t stream);
+
+/* pkv_reshape_and_cache into 8-bit caches: key/value ([num_tokens, num_kv_heads,
+ * head_dim] of dtype float32, bfloat16 or float16) are quantised as described above.
+ * head_dim must be a multiple of 16 (PKV_E_UNSUPPORTED otherwise). Slots as in
+ * pkv_reshape_and_cache. */
+int pkv_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                              void* v_cache, const int64_t* slot_mapping, float k_scale,
+                              float v_scale, int num_tokens, int num_kv_heads, int head_dim,
+                              int block_size, int num_blocks, pkv_dtype dtype,
+                              pkv_stream_t stream);
 
 /*
  * Slot-mapped append of new tokens' K and V ([P3] section "Block table：为什么它能

@@ -140,13 +140,21 @@ class PreparedAttention:
     """Host copies of one decode step's inputs, marshalled once, so that repeated
     oracle evaluations (the benchmark's CPU baseline) time only the C walk."""
 
-    def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, lib=None):
+    def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, lib=None,
+                 kv_scales: Optional[Tuple[float, float]] = None):
         self.lib = lib or _load()
         B, Hq, D = q.shape
         NB, Hkv, bs, _ = k_cache.shape
         self.dims = (B, Hq, Hkv, D, bs, NB)
         self.dtype = DTYPE_CODE[q.dtype]
-        self.qa, self.ka, self.va = _raw(q), _raw(k_cache), _raw(v_cache)
+        # 8-bit caches: uint8 E4M3 codes with their two scales
+        self.kv_scales = None if kv_scales is None else tuple(float(x) for x in kv_scales)
+        self.qa = _raw(q)
+        if self.kv_scales is None:
+            self.ka, self.va = _raw(k_cache), _raw(v_cache)
+        else:
+            self.ka = np.ascontiguousarray(k_cache.detach().cpu().numpy())
+            self.va = np.ascontiguousarray(v_cache.detach().cpu().numpy())
         self.tables = np.ascontiguousarray(block_tables.to("cpu", torch.int32).numpy())
         self.ctx = np.ascontiguousarray(context_lens.to("cpu", torch.int32).numpy())
         self.scale = float(scale)
@@ -162,10 +170,17 @@ class PreparedAttention:
         else:
             out = np.zeros((B, Hq, D), dtype=np.float64)
             rp, nr = None, 0
-        rc = self.lib.oracle_paged_attention(_ptr(out), _ptr(self.qa), _ptr(self.ka),
-                                             _ptr(self.va), self.dtype, _ptr(self.tables),
-                                             _ptr(self.ctx), self.scale, B, Hq, Hkv, D, bs, mb,
-                                             NB, rp, nr, int(threads))
+        if self.kv_scales is None:
+            rc = self.lib.oracle_paged_attention(_ptr(out), _ptr(self.qa), _ptr(self.ka),
+                                                 _ptr(self.va), self.dtype, _ptr(self.tables),
+                                                 _ptr(self.ctx), self.scale, B, Hq, Hkv, D, bs,
+                                                 mb, NB, rp, nr, int(threads))
+        else:
+            rc = self.lib.oracle_paged_attention_kv(_ptr(out), _ptr(self.qa), self.dtype,
+                                                    _ptr(self.ka), _ptr(self.va), FP8,
+                                                    *self.kv_scales, _ptr(self.tables),
+                                                    _ptr(self.ctx), self.scale, B, Hq, Hkv, D,
+                                                    bs, mb, NB, rp, nr, int(threads))
         if rc != 0:
             raise ValueError(f"oracle_paged_attention rejected its inputs ({rc})")
         return out

@@ -10,6 +10,8 @@ the call raises.
     paged_attention_decode_append(out, q, new_k, new_v, k_cache, v_cache, block_tables,
                                   context_lens, scale)
     reshape_and_cache(key, value, k_cache, v_cache, slot_mapping)
+    ..._fp8 variants of the three: caches are uint8 tensors of OCP FP8 E4M3 codes with
+    one scale each (key = code value * k_scale, value = code value * v_scale)
     copy_blocks(caches, src_dst_pairs)
 """
 from __future__ import annotations
@@ -20,7 +22,9 @@ from typing import Dict, Iterable, Optional, Tuple, Union
 
 import torch
 
-__all__ = ["paged_attention_decode", "paged_attention_decode_append", "reshape_and_cache", "copy_blocks", "workspace_size",
+__all__ = ["paged_attention_decode", "paged_attention_decode_append", "reshape_and_cache",
+           "paged_attention_decode_fp8", "paged_attention_decode_append_fp8",
+           "reshape_and_cache_fp8", "copy_blocks", "workspace_size",
            "workspace_init", "version", "strerror", "PagedKVError", "library_path", "load",
            "PreparedDecode", "PreparedReshapeAndCache", "PreparedCopyBlocks"]
 
@@ -68,6 +72,15 @@ def load():
     lib.pkv_paged_attention_decode_append.restype = _I
     lib.pkv_paged_attention_decode_append.argtypes = [_P] * 8 + [ctypes.c_float] + \
         [_I] * 9 + [_P, ctypes.c_size_t, _P]
+    _F = ctypes.c_float
+    lib.pkv_paged_attention_decode_fp8.restype = _I
+    lib.pkv_paged_attention_decode_fp8.argtypes = [_P] * 4 + [_F, _F, _P, _P, _F] + \
+        [_I] * 9 + [_P, ctypes.c_size_t, _P]
+    lib.pkv_paged_attention_decode_append_fp8.restype = _I
+    lib.pkv_paged_attention_decode_append_fp8.argtypes = [_P] * 6 + [_F, _F, _P, _P, _F] + \
+        [_I] * 9 + [_P, ctypes.c_size_t, _P]
+    lib.pkv_reshape_and_cache_fp8.restype = _I
+    lib.pkv_reshape_and_cache_fp8.argtypes = [_P] * 5 + [_F, _F] + [_I] * 6 + [_P]
     lib.pkv_reshape_and_cache.restype = _I
     lib.pkv_reshape_and_cache.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
     lib.pkv_copy_blocks.restype = _I
@@ -139,11 +152,13 @@ def _workspace_for(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
 
 
 def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, partition_size,
-                 workspace, own_workspace):
+                 workspace, own_workspace, kv_fp8=False):
     """Validate one decode call; returns (ctypes argument tuple without the stream,
-    the workspace tensor in use)."""
-    for name, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+    the workspace tensor in use). With kv_fp8 the caches are uint8 E4M3 codes."""
+    for name, t in (("out", out), ("q", q)):
         _gpu(t, name, q.dtype)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _gpu(t, name, torch.uint8 if kv_fp8 else q.dtype)
     _gpu(block_tables, "block_tables", torch.int32)
     _gpu(context_lens, "context_lens", torch.int32)
     if q.dtype not in _DTYPES:
@@ -221,6 +236,45 @@ def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, new_k: tor
     return out
 
 
+def _with_scales(args, at, k_scale, v_scale):
+    """Insert the two cache scales into a ctypes argument tuple at position `at`."""
+    if not (float(k_scale) > 0 and float(v_scale) > 0):
+        raise ValueError("cache scales must be positive")
+    return args[:at] + (float(k_scale), float(v_scale)) + args[at:]
+
+
+def paged_attention_decode_fp8(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                               v_cache: torch.Tensor, k_scale: float, v_scale: float,
+                               block_tables: torch.Tensor, context_lens: torch.Tensor,
+                               scale: float, partition_size: int = 0,
+                               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """paged_attention_decode over 8-bit caches: k_cache/v_cache are uint8 tensors of
+    OCP FP8 E4M3 codes [num_blocks, Hkv, bs, D]; key = code value * k_scale, value =
+    code value * v_scale. q/out are bfloat16 or float16."""
+    args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                           partition_size, workspace, False, kv_fp8=True)
+    _check(load().pkv_paged_attention_decode_fp8(*_with_scales(args, 4, k_scale, v_scale),
+                                                 _stream(q.device)),
+           "pkv_paged_attention_decode_fp8")
+    return out
+
+
+def paged_attention_decode_append_fp8(out, q, new_k, new_v, k_cache, v_cache, k_scale,
+                                      v_scale, block_tables, context_lens, scale,
+                                      partition_size: int = 0,
+                                      workspace: Optional[torch.Tensor] = None):
+    """paged_attention_decode_append over 8-bit caches: new_k/new_v (q's dtype) are
+    quantised (float32(x) * float32(1/scale), nearest E4M3, saturating at 448) into
+    each sequence's context-end slot, then attended."""
+    args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                           partition_size, workspace, False, kv_fp8=True)
+    fused = _fused(args, _new_rows(new_k, new_v, q, k_cache))
+    _check(load().pkv_paged_attention_decode_append_fp8(
+        *_with_scales(fused, 6, k_scale, v_scale), _stream(q.device)),
+        "pkv_paged_attention_decode_append_fp8")
+    return out
+
+
 class PreparedDecode:
     """A decode call validated once for a fixed set of tensors, for loops that run
     it many times (serving steps, HIP graph capture). It owns a zero-initialised
@@ -230,17 +284,26 @@ class PreparedDecode:
 
     def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, scale,
                  partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
-                 new_k: Optional[torch.Tensor] = None, new_v: Optional[torch.Tensor] = None):
+                 new_k: Optional[torch.Tensor] = None, new_v: Optional[torch.Tensor] = None,
+                 k_scale: Optional[float] = None, v_scale: Optional[float] = None):
+        fp8 = k_cache.dtype == torch.uint8
+        if fp8 and (k_scale is None or v_scale is None):
+            raise ValueError("8-bit caches need k_scale and v_scale")
         self._args, self.workspace = _decode_args(out, q, k_cache, v_cache, block_tables,
                                                   context_lens, scale, partition_size,
-                                                  workspace, True)
+                                                  workspace, True, kv_fp8=fp8)
         if (new_k is None) != (new_v is None):
             raise ValueError("pass both new_k and new_v, or neither")
         if new_k is not None:
             self._args = _fused(self._args, _new_rows(new_k, new_v, q, k_cache))
             self._name = "pkv_paged_attention_decode_append"
+            at = 6
         else:
             self._name = "pkv_paged_attention_decode"
+            at = 4
+        if fp8:
+            self._args = _with_scales(self._args, at, k_scale, v_scale)
+            self._name += "_fp8"
         self._fn = getattr(load(), self._name)
         self._device = q.device
         self.out = out
@@ -270,6 +333,32 @@ def _append_args(key, value, k_cache, v_cache, slot_mapping):
         raise ValueError("key/value and caches disagree on heads/head_dim, or slot_mapping != [T]")
     return (key.data_ptr(), value.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             slot_mapping.data_ptr(), T, Hkv, D, bs, NB, _DTYPES[key.dtype])
+
+
+def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float,
+                          v_scale: float) -> None:
+    """Quantising slot-mapped append into 8-bit caches (uint8 E4M3 codes): key/value
+    ([T, Hkv, D], float32/bfloat16/float16) at slot_mapping[t]."""
+    for name, t in (("key", key), ("value", value)):
+        _gpu(t, name, key.dtype)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _gpu(t, name, torch.uint8)
+    _gpu(slot_mapping, "slot_mapping", torch.int64)
+    if key.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {key.dtype}")
+    if key.dim() != 3 or value.shape != key.shape or k_cache.dim() != 4 or \
+            v_cache.shape != k_cache.shape:
+        raise ValueError("expected key/value [T,Hkv,D] and caches [num_blocks,Hkv,bs,D]")
+    T, Hkv, D = key.shape
+    NB, Hkv2, bs, D2 = k_cache.shape
+    if (Hkv2, D2) != (Hkv, D) or slot_mapping.shape != (T,):
+        raise ValueError("key/value and caches disagree on heads/head_dim, or slot_mapping != [T]")
+    args = (key.data_ptr(), value.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            slot_mapping.data_ptr(), float(k_scale), float(v_scale), T, Hkv, D, bs, NB,
+            _DTYPES[key.dtype])
+    _check(load().pkv_reshape_and_cache_fp8(*args, _stream(key.device)),
+           "pkv_reshape_and_cache_fp8")
 
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,

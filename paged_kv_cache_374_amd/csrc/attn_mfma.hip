@@ -39,8 +39,6 @@
 // shared reduction kernel, or writes the output when the context has one partition.
 //
 // Both kernels can also perform the append of a decode step (see "fused append").
-#include <cstdlib>
-
 #include "device_common.h"
 #include "launchers.h"
 #include "pagedkv.h"
@@ -118,17 +116,6 @@ __device__ __forceinline__ uint32_t pick(const uint4& a, const uint4& b) {
     return __builtin_amdgcn_perm(wb, wa, sel);
 }
 
-// One wave's registers for one block: K rows (line-coalesced), V rows for PV, and
-// the query of the block's unit in QK B-operand order (lane l: head l%16, dims
-// 32kk + 8(l/16) .. +7; zero for heads past the group). The query travels with every
-// block so the loop carries no per-unit registers (it is an L1/L2 hit after the first
-// block of a unit).
-struct BlockRegs {
-    uint4 k[4];
-    uint4 v[4];
-    uint4 q[4];
-};
-
 // Per-wave online-softmax state. Lane l: m, lsum for head l%16 (lsum over the tokens
 // this lane saw); o[n][r] = unnormalised output of head 4(l/16)+r, dim 8(l%16)+n.
 struct WaveState {
@@ -144,11 +131,6 @@ __device__ __forceinline__ void reset(WaveState& s) {
     for (int n = 0; n < 8; ++n) s.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
-// Both tiles are fetched with whole 128-byte lines per instruction: K load i covers
-// rows 4i..4i+3 (one contiguous KiB; lane l takes row 4i + l/16, 16-byte chunk l%16),
-// V load r covers rows r, 4+r, 8+r, 12+r (lane l takes row 4(l/16)+r, chunk l%16).
-// (Loading K straight in MFMA operand order would touch 16 half lines per
-// instruction, which measured ~20% slower as a gather.)
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-class parts.
 constexpr int kRawBufferWord3 = 0x00020000;
 
@@ -161,42 +143,9 @@ template <int AUX = 0>
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int offset) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, AUX));
 }
-
-// Issue the twelve 16-byte loads of one block. Every block issues exactly these
-// loads, with no branches: a block whose table entry is out of range gets a buffer
-// of zero records (the hardware returns zeros), and lanes past the query group read
-// past their buffer's end (zeros too). A fixed count lets the compiler wait for just
-// this block's loads while later blocks' loads stay in flight.
-template <typename T>
-__device__ __forceinline__ void issue_block(BlockRegs& r, const T* k_cache, const T* v_cache,
-                                            const T* __restrict__ q, uint32_t tile, int qrow,
-                                            int group, int lane) {
-    tile = __builtin_amdgcn_readfirstlane(tile);
-    qrow = __builtin_amdgcn_readfirstlane(qrow);
-    const bool ok = tile != kNoTile;
-    const size_t base = (size_t)(ok ? tile : 0u) * kTile;
-    const int bytes = ok ? kTile * (int)sizeof(T) : 0;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(k_cache + base), 0, bytes, kRawBufferWord3);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + base), 0, bytes, kRawBufferWord3);
-    // A padding block (past the wave's range) reads no query either: its loads are all
-    // zero-record, so none of them waits on memory when the wave drains its ring.
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(q + (size_t)qrow * kD), 0, ok ? group * kD * (int)sizeof(T) : 0,
-        kRawBufferWord3);
-    const int c = lane & 15, grp = lane >> 4;
-    const int koff = (grp * kD + 8 * c) * (int)sizeof(T);
-    const int voff = (4 * grp * kD + 8 * c) * (int)sizeof(T);
-    const int qoff = (c * kD + 8 * grp) * (int)sizeof(T);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        r.k[i] = buffer_load16<kStream>(rk, koff + i * 4 * kD * (int)sizeof(T));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        r.v[i] = buffer_load16<kStream>(rv, voff + i * kD * (int)sizeof(T));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.q[i] = buffer_load16(rq, qoff + 32 * i * (int)sizeof(T));
+template <int AUX = 0>
+__device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int offset) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, offset, 0, AUX));
 }
 
 // Per-wave LDS tile that turns the line-coalesced K rows into MFMA operand order.
@@ -206,14 +155,199 @@ struct KTile {
     uint4 chunk[kBS][kD / 8];
 };
 
-__device__ __forceinline__ void stage_k(KTile& kt, const BlockRegs& r, int lane) {
-    const int c = lane & 15, grp = lane >> 4;
+// The query of the block's unit in QK B-operand order (lane l: head l%16, dims
+// 32kk + 8(l/16) .. +7; zero for heads past the group). It travels with every block so
+// the loop carries no per-unit registers (an L1/L2 hit after a unit's first block). A
+// padding block (past the wave's range) reads no query either: its loads are all
+// zero-record, so none of them waits on memory when the wave drains its ring.
+template <typename T>
+__device__ __forceinline__ void issue_query(uint4 (&qv)[4], const T* __restrict__ q, bool ok,
+                                            int qrow, int group, int lane) {
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(q + (size_t)qrow * kD), 0, ok ? group * kD * (int)sizeof(T) : 0,
+        kRawBufferWord3);
+    const int qoff = ((lane & 15) * kD + 8 * (lane >> 4)) * (int)sizeof(T);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = 4 * i + grp;
-        kt.chunk[t][c ^ (t & 7)] = r.k[i];
-    }
+    for (int i = 0; i < 4; ++i) qv[i] = buffer_load16(rq, qoff + 32 * i * (int)sizeof(T));
 }
+
+// ---- KV formats: how one (block, KV head) tile of K and V is fetched and widened to
+// the MFMA type T. Every block issues exactly the format's loads, with no branches: a
+// block whose table entry is out of range gets buffers of zero records (the hardware
+// returns zeros). A fixed count lets the compiler wait for just this block's loads
+// while later blocks' loads stay in flight.
+
+// Caches of T itself (bfloat16 / float16). Both tiles come in whole 128-byte lines: K
+// load i covers rows 4i..4i+3 (one contiguous KiB; lane l takes row 4i + l/16, 16-byte
+// chunk l%16), V load r covers rows r, 4+r, 8+r, 12+r (lane l takes row 4(l/16)+r,
+// chunk l%16). (Loading K straight in MFMA operand order would touch 16 half lines per
+// instruction, which measured ~20% slower as a gather.)
+template <typename T>
+struct KvNative {
+    using Elem = T;
+    struct Regs {
+        uint4 k[4];
+        uint4 v[4];
+        uint4 q[4];
+    };
+    static __device__ __forceinline__ void issue(Regs& r, const T* k_cache, const T* v_cache,
+                                                 const T* __restrict__ q, uint32_t tile,
+                                                 int qrow, int group, int lane) {
+        tile = __builtin_amdgcn_readfirstlane(tile);
+        qrow = __builtin_amdgcn_readfirstlane(qrow);
+        const bool ok = tile != kNoTile;
+        const size_t base = (size_t)(ok ? tile : 0u) * kTile;
+        const int bytes = ok ? kTile * (int)sizeof(T) : 0;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(k_cache + base), 0, bytes, kRawBufferWord3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(v_cache + base), 0, bytes, kRawBufferWord3);
+        const int c = lane & 15, grp = lane >> 4;
+        const int koff = (grp * kD + 8 * c) * (int)sizeof(T);
+        const int voff = (4 * grp * kD + 8 * c) * (int)sizeof(T);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r.k[i] = buffer_load16<kStream>(rk, koff + i * 4 * kD * (int)sizeof(T));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r.v[i] = buffer_load16<kStream>(rv, voff + i * kD * (int)sizeof(T));
+        issue_query(r.q, q, ok, qrow, group, lane);
+    }
+    static __device__ __forceinline__ void stage_k(KTile& kt, const Regs& r, int lane) {
+        const int c = lane & 15, grp = lane >> 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * i + grp;
+            kt.chunk[t][c ^ (t & 7)] = r.k[i];
+        }
+    }
+    static __device__ __forceinline__ void widen_v(const Regs& r, uint4 (&v)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = r.v[e];
+    }
+    // Append: chunk c (16 bytes) of the new K (kind 0) or V (kind 1) row of unit (b, g)
+    // goes to position n - 1 of the sequence (table row `table`), bit for bit. The source
+    // is loaded before the table entry is checked, so the two loads overlap.
+    static constexpr int kAppendChunks = kD * (int)sizeof(T) / 16;
+    static __device__ __forceinline__ void append(T* k_cache, T* v_cache,
+                                                  const T* __restrict__ new_k,
+                                                  const T* __restrict__ new_v,
+                                                  const int32_t* __restrict__ table, int b,
+                                                  int g, int Hkv, int n, int num_blocks,
+                                                  int kind, int c, float, float) {
+        const int j = (n - 1) / kBS;
+        const size_t src = ((size_t)b * Hkv + g) * kD;
+        const uint4 val = reinterpret_cast<const uint4*>((kind ? new_v : new_k) + src)[c];
+        const int phys = table[j];
+        if (phys < 0 || phys >= num_blocks) return;
+        const size_t dst = (((size_t)phys * Hkv + g) * kBS + (n - 1 - j * kBS)) * kD;
+        reinterpret_cast<uint4*>((kind ? v_cache : k_cache) + dst)[c] = val;
+    }
+};
+
+// Two E4M3 codes (the low or the high byte pair of a word) widened exactly to T,
+// packed low/high (the lower byte becomes the lower element).
+template <typename T> struct WidenFp8;
+template <> struct WidenFp8<bf16_t> {
+    template <bool HI>
+    static __device__ __forceinline__ uint32_t pair(uint32_t w) {
+        return __builtin_bit_cast(uint32_t,
+                                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+    }
+};
+template <> struct WidenFp8<f16_t> {
+    template <bool HI>
+    static __device__ __forceinline__ uint32_t pair(uint32_t w) {
+        return __builtin_bit_cast(uint32_t,
+                                  __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HI));
+    }
+};
+template <typename T>
+__device__ __forceinline__ uint4 widen8(uint32_t lo, uint32_t hi) {   // 8 codes -> 8 T
+    using W = WidenFp8<T>;
+    return make_uint4(W::template pair<false>(lo), W::template pair<true>(lo),
+                      W::template pair<false>(hi), W::template pair<true>(hi));
+}
+
+// 8-bit caches (OCP FP8 E4M3 codes, one byte per element). Every E4M3 value is exact
+// in bfloat16 and float16, so widening loses nothing; the caches' scales are applied
+// outside the tile (the key scale folds into the softmax scale, the value scale into
+// the final normalisation). K load i covers rows 8i..8i+7 (one contiguous KiB; lane l
+// takes row 8i + l/8, codes 16(l%8) .. +15); V load r covers rows r, 4+r, 8+r, 12+r
+// (lane l takes row 4(l/16)+r, codes 8(l%16) .. +7: 8 bytes, four half lines per
+// instruction).
+template <typename T>
+struct KvFp8 {
+    using Elem = uint8_t;
+    struct Regs {
+        uint4 k[2];
+        uint2 v[4];
+        uint4 q[4];
+    };
+    static __device__ __forceinline__ void issue(Regs& r, const uint8_t* k_cache,
+                                                 const uint8_t* v_cache,
+                                                 const T* __restrict__ q, uint32_t tile,
+                                                 int qrow, int group, int lane) {
+        tile = __builtin_amdgcn_readfirstlane(tile);
+        qrow = __builtin_amdgcn_readfirstlane(qrow);
+        const bool ok = tile != kNoTile;
+        const size_t base = (size_t)(ok ? tile : 0u) * kTile;
+        const int bytes = ok ? kTile : 0;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(k_cache + base), 0, bytes, kRawBufferWord3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(v_cache + base), 0, bytes, kRawBufferWord3);
+        const int koff = (lane >> 3) * kD + 16 * (lane & 7);
+        const int voff = 4 * (lane >> 4) * kD + 8 * (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) r.k[i] = buffer_load16<kStream>(rk, koff + i * 8 * kD);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.v[i] = buffer_load8<kStream>(rv, voff + i * kD);
+        issue_query(r.q, q, ok, qrow, group, lane);
+    }
+    static __device__ __forceinline__ void stage_k(KTile& kt, const Regs& r, int lane) {
+        const int c2 = 2 * (lane & 7);   // the lane's first 8-dim chunk
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = 8 * i + (lane >> 3);
+            kt.chunk[t][c2 ^ (t & 7)] = widen8<T>(r.k[i].x, r.k[i].y);
+            kt.chunk[t][(c2 + 1) ^ (t & 7)] = widen8<T>(r.k[i].z, r.k[i].w);
+        }
+    }
+    static __device__ __forceinline__ void widen_v(const Regs& r, uint4 (&v)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = widen8<T>(r.v[e].x, r.v[e].y);
+    }
+    // Append: chunk c (16 elements) of the new K or V row is quantised (binary32 product
+    // with the reciprocal scale, then E4M3 nearest-even, saturating) into 16 codes at
+    // position n - 1 of the sequence.
+    static constexpr int kAppendChunks = kD / 16;
+    static __device__ __forceinline__ void append(uint8_t* k_cache, uint8_t* v_cache,
+                                                  const T* __restrict__ new_k,
+                                                  const T* __restrict__ new_v,
+                                                  const int32_t* __restrict__ table, int b,
+                                                  int g, int Hkv, int n, int num_blocks,
+                                                  int kind, int c, float k_inv, float v_inv) {
+        const int j = (n - 1) / kBS;
+        const uint4* src = reinterpret_cast<const uint4*>((kind ? new_v : new_k) +
+                                                          ((size_t)b * Hkv + g) * kD + 16 * c);
+        float f[16];
+        Vec16<T>::unpack(src[0], f);
+        Vec16<T>::unpack(src[1], f + 8);
+        const float inv = kind ? v_inv : k_inv;
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = fp8_e4m3_code(f[4 * i] * inv) | fp8_e4m3_code(f[4 * i + 1] * inv) << 8 |
+                   fp8_e4m3_code(f[4 * i + 2] * inv) << 16 |
+                   fp8_e4m3_code(f[4 * i + 3] * inv) << 24;
+        const int phys = table[j];
+        if (phys < 0 || phys >= num_blocks) return;
+        const size_t dst = (((size_t)phys * Hkv + g) * kBS + (n - 1 - j * kBS)) * kD + 16 * c;
+        *reinterpret_cast<uint4*>((kind ? v_cache : k_cache) + dst) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+    }
+};
 
 // A operand of QK product kk for lane l: token l%16, dims 32kk + 8(l/16) .. +7.
 __device__ __forceinline__ uint4 k_operand(const KTile& kt, int kk, int lane) {
@@ -224,18 +358,20 @@ __device__ __forceinline__ uint4 k_operand(const KTile& kt, int kk, int lane) {
 // Fold one block into the wave's state. `valid` = tokens of the block that count
 // (0 masks the whole block). The running max is updated every block (exact online
 // softmax), so the loop carries no conditionally updated state.
-template <typename T>
-__device__ __forceinline__ void fold_block(WaveState& s, BlockRegs& r, KTile& kt, int valid,
-                                           float scale_log2, int lane) {
+template <typename T, typename KV>
+__device__ __forceinline__ void fold_block(WaveState& s, typename KV::Regs& r, KTile& kt,
+                                           int valid, float scale_log2, int lane) {
     const int grp = lane >> 4;
-    stage_k(kt, r, lane);
+    KV::stage_k(kt, r, lane);
+    uint4 v[4];
+    KV::widen_v(r, v);
     if (valid < kBS) {
         // Slots past the context hold stale data (possibly NaN); a zero weight does not
         // cancel a NaN inside the product, so their V rows are cleared. Their scores are
         // replaced by -inf below (a select), so stale K never reaches the softmax.
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (4 * grp + e >= valid) r.v[e] = make_uint4(0, 0, 0, 0);
+            if (4 * grp + e >= valid) v[e] = make_uint4(0, 0, 0, 0);
     }
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -270,8 +406,7 @@ __device__ __forceinline__ void fold_block(WaveState& s, BlockRegs& r, KTile& kt
     }
     const uint2 pa = make_uint2(Mma<T>::pack(p[0], p[1]), Mma<T>::pack(p[2], p[3]));
 #define PKV_PV_STEP(N)                                                                  \
-    s.o[N] = Mma<T>::pv(pa, make_uint2(pick<N>(r.v[0], r.v[1]), pick<N>(r.v[2], r.v[3])), \
-                        s.o[N]);
+    s.o[N] = Mma<T>::pv(pa, make_uint2(pick<N>(v[0], v[1]), pick<N>(v[2], v[3])), s.o[N]);
     PKV_PV_STEP(0) PKV_PV_STEP(1) PKV_PV_STEP(2) PKV_PV_STEP(3)
     PKV_PV_STEP(4) PKV_PV_STEP(5) PKV_PV_STEP(6) PKV_PV_STEP(7)
 #undef PKV_PV_STEP
@@ -353,10 +488,11 @@ __device__ __forceinline__ void wave_to_part(float* P, const WaveState& s, int l
 // A wave's state -> normalised output rows (the wave saw the whole unit). `rows`
 // points at head 0 of the unit's group; each lane stores 16 bytes per head.
 template <typename T>
-__device__ __forceinline__ void wave_to_out(T* rows, const WaveState& s, int lane, int group) {
+__device__ __forceinline__ void wave_to_out(T* rows, const WaveState& s, int lane, int group,
+                                            float out_scale) {
     const int c = lane & 15, grp = lane >> 4;
     const float ls = head_lsum(s);
-    const float inv = ls > 0.f ? 1.f / ls : 0.f;
+    const float inv = ls > 0.f ? out_scale / ls : 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int h = 4 * grp + e;
@@ -444,26 +580,6 @@ __device__ __forceinline__ void next_unit(const int* pref, int num_seqs, int Hkv
 // "Block Table 数据结构"). Fused into the decode, the workgroup that reads a unit's
 // last block writes that unit's new K and V rows during staging; the workgroup
 // barrier before its waves start loading orders those stores before the loads.
-constexpr int kRowChunks = kD * 2 / 16;   // 16-byte chunks of one bf16/f16 row
-
-// Copy chunk `c` of the new K (kind 0) or V (kind 1) row of unit (b, g) into
-// position n - 1 of the sequence (table row `table`). The source chunk is loaded
-// before the table entry is checked, so the two loads overlap.
-template <typename T>
-__device__ __forceinline__ void append_chunk(T* k_cache, T* v_cache,
-                                             const T* __restrict__ new_k,
-                                             const T* __restrict__ new_v,
-                                             const int32_t* __restrict__ table, int b, int g,
-                                             int Hkv, int n, int num_blocks, int kind, int c) {
-    const int j = (n - 1) / kBS;
-    const size_t src = ((size_t)b * Hkv + g) * kD;
-    const uint4 val = reinterpret_cast<const uint4*>((kind ? new_v : new_k) + src)[c];
-    const int phys = table[j];
-    if (phys < 0 || phys >= num_blocks) return;
-    const size_t dst = (((size_t)phys * Hkv + g) * kBS + (n - 1 - j * kBS)) * kD;
-    reinterpret_cast<uint4*>((kind ? v_cache : k_cache) + dst)[c] = val;
-}
-
 // ------------------------------------------------------------------ balanced kernel
 // Equal shares of the block list: worker w (logical index) covers [w*C, (w+1)*C)
 // clipped to the list, C = ceil(total / W). Every workgroup derives the same map from
@@ -511,11 +627,16 @@ struct BalancedLds {
 // a SIMD the older one was measured to stream ~1.5x faster than the younger, which
 // breaks equal static shares. Eight waves per CU were also slower overall (54.7 vs
 // 53.6 us on the 8B-shaped batch).
-template <typename T, int GMAX, int NW>
+//
+// KV: the cache format (KvNative<T> or KvFp8<T>). scale_log2 = scale * key scale *
+// log2(e); out_scale = value scale (1 for native caches) multiplies each normalised
+// output; k_inv, v_inv are the reciprocal scales an 8-bit append quantises with.
+template <typename T, typename KV, int GMAX, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
-    T* __restrict__ out, const T* __restrict__ q, T* k_cache, T* v_cache,
-    const T* __restrict__ new_k, const T* __restrict__ new_v, const int32_t* __restrict__ tables,
-    const int32_t* __restrict__ ctx_lens, float scale_log2, int num_seqs, int num_heads,
+    T* __restrict__ out, const T* __restrict__ q, typename KV::Elem* k_cache,
+    typename KV::Elem* v_cache, const T* __restrict__ new_k, const T* __restrict__ new_v,
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ ctx_lens, float scale_log2,
+    float out_scale, float k_inv, float v_inv, int num_seqs, int num_heads,
     int num_kv_heads, int group, int max_blocks, int num_blocks, int32_t* __restrict__ counters,
     float* __restrict__ partials) {
     __shared__ BalancedLds<GMAX, NW> S;
@@ -599,15 +720,16 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
     if (new_k != nullptr) {
         const int b0 = seq_of(S.pref, num_seqs, Hkv, x0);
         const int b1 = seq_of(S.pref, num_seqs, Hkv, x1 - 1);
-        const int items = (b1 - b0 + 1) * Hkv * 2 * kRowChunks;
+        const int items = (b1 - b0 + 1) * Hkv * 2 * KV::kAppendChunks;
         for (int it = tid; it < items; it += kThreads) {
-            const int u = it / (2 * kRowChunks);
+            const int u = it / (2 * KV::kAppendChunks);
             const int b = b0 + u / Hkv, g = u - (u / Hkv) * Hkv;
             const int nb = S.pref[b + 1] - S.pref[b];
             const int last = Hkv * S.pref[b] + (g + 1) * nb - 1;
             if (nb == 0 || last < x0 || last >= x1) continue;
-            append_chunk(k_cache, v_cache, new_k, new_v, tables + (size_t)b * max_blocks, b, g,
-                         Hkv, S.ctx[b], num_blocks, (it / kRowChunks) & 1, it % kRowChunks);
+            KV::append(k_cache, v_cache, new_k, new_v, tables + (size_t)b * max_blocks, b, g,
+                       Hkv, S.ctx[b], num_blocks, (it / KV::kAppendChunks) & 1,
+                       it % KV::kAppendChunks, k_inv, v_inv);
         }
     }
     __syncthreads();
@@ -627,16 +749,16 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         next_unit(S.pref, num_seqs, Hkv, b, g, bn, gn);
         // Every step issues one block (a zero-record buffer past the quarter's end), so
         // the number of loads in flight never depends on the path taken.
-        auto issue = [&](BlockRegs& R, int xi) {
+        auto issue = [&](typename KV::Regs& R, int xi) {
             const int i = (int)((xi < xb ? xi : xb - 1) - x0);
-            issue_block(R, k_cache, v_cache, q, xi < xb ? S.tile[i] : kNoTile, S.qrow[i], group,
-                        lane);
+            KV::issue(R, k_cache, v_cache, q, xi < xb ? S.tile[i] : kNoTile, S.qrow[i], group,
+                      lane);
         };
         // kRing register buffers in fixed roles (the loop is unrolled kRing times): a
         // block's loads land where the fold reads them (no copies), and kRing - 1
         // blocks stay in flight behind the one being folded.
         static_assert(kRing == 2, "the loop below is unrolled for two buffers");
-        BlockRegs R0, R1;
+        typename KV::Regs R0, R1;
         issue(R0, xa);
         issue(R1, xa + 1);
         WaveState st;
@@ -647,7 +769,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         auto flush = [&]() {
             if (su >= xa && ue <= xb)
                 wave_to_out(out + ((size_t)b * num_heads + (size_t)g * group) * kD, st, lane,
-                            group);
+                            group, out_scale);
             else
                 wave_to_part<GMAX>(S.part[2 * wave + (su <= xa ? 0 : 1)], st, lane, group);
         };
@@ -664,7 +786,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
 #define PKV_STEP(R)                                                                       \
         if (x >= xb) break;                                                               \
         if (x >= ue) advance();                                                           \
-        fold_block<T>(st, R, S.ktile[wave], uni(S.valid[x - x0]), scale_log2, lane);      \
+        fold_block<T, KV>(st, R, S.ktile[wave], uni(S.valid[x - x0]), scale_log2, lane);  \
         issue(R, x + kRing);                                                              \
         ++x;
         while (true) {
@@ -747,7 +869,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         float4 o;
         merge_parts<GMAX, NW * 2, NW>(S.part, pl.rec, pl.n, h, d0, M, Ls, o);
         if (!pl.cross) {
-            const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+            const float inv = Ls > 0.f ? out_scale / Ls : 0.f;
             store4(out + ((size_t)pl.row + h) * kD + d0,
                    make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv));
         } else {
@@ -804,7 +926,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
                 o.w = o.w * a + pv.w * c;
                 M = Mn;
             }
-            const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+            const float inv = Ls > 0.f ? out_scale / Ls : 0.f;
             store4(rows + h * kD + d0, make_float4(o.x * inv, o.y * inv, o.z * inv,
                                                    o.w * inv));
         }
@@ -823,11 +945,12 @@ struct PartLds {
     float part[kWaves][Part<GMAX>::kFloats];
 };
 
-template <typename T, int GMAX>
+template <typename T, typename KV, int GMAX>
 __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
-    T* __restrict__ out, const T* __restrict__ q, T* k_cache, T* v_cache,
-    const T* __restrict__ new_k, const T* __restrict__ new_v, const int32_t* __restrict__ tables,
-    const int32_t* __restrict__ ctx_lens, float scale_log2, int num_heads, int num_kv_heads,
+    T* __restrict__ out, const T* __restrict__ q, typename KV::Elem* k_cache,
+    typename KV::Elem* v_cache, const T* __restrict__ new_k, const T* __restrict__ new_v,
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ ctx_lens, float scale_log2,
+    float out_scale, float k_inv, float v_inv, int num_heads, int num_kv_heads,
     int group, int max_blocks, int num_blocks, int part_blocks, int max_parts,
     float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
     __shared__ PartLds<GMAX> S;
@@ -858,9 +981,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     // fused append: the partition holding the newest token writes its K and V rows
     // (the barrier below orders the stores before this workgroup's loads)
     if (new_k != nullptr && (n - 1) / kBS >= j0 && (n - 1) / kBS < j1 &&
-        tid < 2 * kRowChunks)
-        append_chunk(k_cache, v_cache, new_k, new_v, tables + (size_t)b * max_blocks, b, g,
-                     num_kv_heads, n, num_blocks, tid / kRowChunks, tid % kRowChunks);
+        tid < 2 * KV::kAppendChunks)
+        KV::append(k_cache, v_cache, new_k, new_v, tables + (size_t)b * max_blocks, b, g,
+                   num_kv_heads, n, num_blocks, tid / KV::kAppendChunks,
+                   tid % KV::kAppendChunks, k_inv, v_inv);
     __syncthreads();
     WaveState st;
     reset(st);
@@ -869,16 +993,16 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     int j = j0 + wave;
     // every step issues one block (a zero-record buffer past the end): the loads in
     // flight never depend on the path taken
-    auto issue = [&](BlockRegs& R, int ji) {
-        issue_block(R, k_cache, v_cache, q, ji < j1 ? S.tile[ji - j0] : kNoTile, qrow, group,
-                    lane);
+    auto issue = [&](typename KV::Regs& R, int ji) {
+        KV::issue(R, k_cache, v_cache, q, ji < j1 ? S.tile[ji - j0] : kNoTile, qrow, group,
+                  lane);
     };
-    BlockRegs A, B;
+    typename KV::Regs A, B;
     issue(A, j);
     issue(B, j + kWaves);
 #define PKV_STEP(R)                                                                          \
     if (j >= j1) break;                                                                      \
-    fold_block<T>(st, R, S.ktile[wave], S.valid[j - j0], scale_log2, lane);                  \
+    fold_block<T, KV>(st, R, S.ktile[wave], S.valid[j - j0], scale_log2, lane);              \
     issue(R, j + 2 * kWaves);                                                                \
     j += kWaves;
     while (true) {
@@ -896,7 +1020,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
         float M, Ls;
         float4 o;
         merge_parts<GMAX, kWaves, kWaves>(S.part, P, kWaves, h, d0, M, Ls, o);
-        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+        const float inv = Ls > 0.f ? out_scale / Ls : 0.f;
         o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
         const size_t hrow = (size_t)b * num_heads + g * group + h;
         if (nparts == 1) {
@@ -912,40 +1036,47 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     }
 }
 
-// Workgroups per CU multiplier for experiments (PKV_WG_PER_CU, default 1).
-int wg_per_cu() {
-    static const int v = [] {
-        const char* e = std::getenv("PKV_WG_PER_CU");
-        const int n = e ? std::atoi(e) : 0;
-        return n > 0 && n <= 16 ? n : 1;
-    }();
-    return v;
+// Scale arguments of a launch: the key scale folds into the softmax scale, the value
+// scale into the output normalisation; reciprocals (one binary32 division each) for
+// the 8-bit append.
+struct Scales {
+    float scale_log2, out_scale, k_inv, v_inv;
+};
+inline Scales scales_of(const DecodeArgs& a) {
+    const bool fp8 = a.kv_fp8 != 0;
+    return Scales{a.scale * (fp8 ? a.k_scale : 1.f) * kLog2e, fp8 ? a.v_scale : 1.f,
+                  fp8 ? 1.f / a.k_scale : 1.f, fp8 ? 1.f / a.v_scale : 1.f};
 }
 
-template <typename T, int GMAX, int NW>
+template <typename T, typename KV, int GMAX, int NW>
 int launch_balanced(const DecodeArgs& a, const DecodePlan& plan, int workers,
                     hipStream_t stream) {
     const DecodeShape& s = a.shape;
     char* ws = (char*)a.workspace;
-    hipLaunchKernelGGL((decode_mfma_balanced_kernel<T, GMAX, NW>), dim3(workers),
-                       dim3(64 * NW), 0, stream, (T*)a.out, (const T*)a.q, (T*)a.k_cache,
-                       (T*)a.v_cache, (const T*)a.new_k, (const T*)a.new_v, a.block_tables,
-                       a.context_lens, a.scale * kLog2e, s.num_seqs, s.num_heads, s.num_kv_heads, plan.group,
+    using E = typename KV::Elem;
+    const Scales sc = scales_of(a);
+    hipLaunchKernelGGL((decode_mfma_balanced_kernel<T, KV, GMAX, NW>), dim3(workers),
+                       dim3(64 * NW), 0, stream, (T*)a.out, (const T*)a.q, (E*)a.k_cache,
+                       (E*)a.v_cache, (const T*)a.new_k, (const T*)a.new_v, a.block_tables,
+                       a.context_lens, sc.scale_log2, sc.out_scale, sc.k_inv, sc.v_inv,
+                       s.num_seqs, s.num_heads, s.num_kv_heads, plan.group,
                        s.max_blocks, s.num_blocks, (int32_t*)(ws + plan.off_counters),
                        (float*)(ws + plan.off_partials));
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-template <typename T, int GMAX>
+template <typename T, typename KV, int GMAX>
 int launch_partitioned(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
     const DecodeShape& s = a.shape;
     char* ws = (char*)a.workspace;
     const bool split = plan.max_partitions > 1;
-    hipLaunchKernelGGL((decode_mfma_partition_kernel<T, GMAX>),
+    using E = typename KV::Elem;
+    const Scales sc = scales_of(a);
+    hipLaunchKernelGGL((decode_mfma_partition_kernel<T, KV, GMAX>),
                        dim3(plan.max_partitions, s.num_kv_heads, s.num_seqs), dim3(kThreads), 0,
-                       stream, (T*)a.out, (const T*)a.q, (T*)a.k_cache, (T*)a.v_cache,
+                       stream, (T*)a.out, (const T*)a.q, (E*)a.k_cache, (E*)a.v_cache,
                        (const T*)a.new_k, (const T*)a.new_v, a.block_tables, a.context_lens,
-                       a.scale * kLog2e,
+                       sc.scale_log2, sc.out_scale, sc.k_inv, sc.v_inv,
                        s.num_heads, s.num_kv_heads, plan.group, s.max_blocks, s.num_blocks,
                        plan.partition_tokens / kBS, plan.max_partitions,
                        split ? (float*)(ws + plan.off_m) : nullptr,
@@ -955,20 +1086,27 @@ int launch_partitioned(const DecodeArgs& a, const DecodePlan& plan, hipStream_t 
     return split ? launch_partition_reduce(a, plan, stream) : 0;
 }
 
-template <typename T>
-int launch_typed(const DecodeArgs& a, const DecodePlan& plan, int num_cus, hipStream_t stream) {
+template <typename T, typename KV>
+int launch_format(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
+                  hipStream_t stream) {
     const int G = plan.group;
     if (plan.path == Path::MfmaBalanced) {
-        const int per_cu = 1;
-        const int workers = balanced_workers(a.shape, num_cus, per_cu * wg_per_cu());
+        // one workgroup per CU
+        const int workers = balanced_workers(a.shape, num_cus, 1);
         if (workers <= 0 || workers > plan.max_workers) return -1;
-        if (G <= 4) return launch_balanced<T, 4, 4>(a, plan, workers, stream);
-        if (G <= 8) return launch_balanced<T, 8, 4>(a, plan, workers, stream);
-        return launch_balanced<T, 16, 4>(a, plan, workers, stream);
+        if (G <= 4) return launch_balanced<T, KV, 4, 4>(a, plan, workers, stream);
+        if (G <= 8) return launch_balanced<T, KV, 8, 4>(a, plan, workers, stream);
+        return launch_balanced<T, KV, 16, 4>(a, plan, workers, stream);
     }
-    if (G <= 4) return launch_partitioned<T, 4>(a, plan, stream);
-    if (G <= 8) return launch_partitioned<T, 8>(a, plan, stream);
-    return launch_partitioned<T, 16>(a, plan, stream);
+    if (G <= 4) return launch_partitioned<T, KV, 4>(a, plan, stream);
+    if (G <= 8) return launch_partitioned<T, KV, 8>(a, plan, stream);
+    return launch_partitioned<T, KV, 16>(a, plan, stream);
+}
+
+template <typename T>
+int launch_typed(const DecodeArgs& a, const DecodePlan& plan, int num_cus, hipStream_t stream) {
+    return a.kv_fp8 ? launch_format<T, KvFp8<T>>(a, plan, num_cus, stream)
+                    : launch_format<T, KvNative<T>>(a, plan, num_cus, stream);
 }
 
 }  // namespace

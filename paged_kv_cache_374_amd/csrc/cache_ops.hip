@@ -1,11 +1,12 @@
-// Cache companions of paged decode attention: slot-mapped append, the decode step's
-// append at each context end (for paths whose decode kernel does not fuse it) and
-// block copy.
+// Cache companions of paged decode attention: slot-mapped append (into 16/32-bit
+// caches, or quantising into 8-bit ones), the decode step's append at each context end
+// (for paths whose decode kernel does not fuse it) and block copy.
 //
 // Both are pure data movement. Each thread moves one 16-byte (or 4-byte) chunk per
 // loop trip; consecutive threads take consecutive chunks of a row, so a wavefront's
 // stores cover contiguous runs of a KV row. Bounds are checked per chunk so that
 // no index array content can push an access outside the pools.
+#include "device_common.h"
 #include "launchers.h"
 #include "pagedkv.h"
 
@@ -35,6 +36,50 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
         const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_chunks + c;
         k_cache[dst] = key[i];
         v_cache[dst] = value[i];
+    }
+}
+
+// Slot-mapped append into 8-bit caches: each thread takes 16 consecutive elements of a
+// K or V row (bf16/f16/f32 source S) and stores their 16 E4M3 codes with one 16-byte
+// store: code = E4M3(float(x) * inv_scale), nearest-even, saturating at 448.
+template <typename S>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const S* __restrict__ key, const S* __restrict__ value, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int num_tokens,
+    int num_kv_heads, int head_dim, int block_size, int num_blocks, float k_inv, float v_inv) {
+    constexpr int kPer = Vec16<S>::N;            // source elements per 16-byte load
+    const int chunks = head_dim / 16;
+    const int64_t per_token = (int64_t)num_kv_heads * chunks;
+    const int64_t total = (int64_t)num_tokens * per_token;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = i / per_token;
+        const int64_t rem = i - t * per_token;   // h * chunks + c
+        const int64_t slot = slot_mapping[t];
+        if (slot < 0) continue;
+        const int64_t blk = slot / block_size;
+        if (blk >= num_blocks) continue;
+        const int64_t off = slot - blk * block_size;
+        const int64_t h = rem / chunks;
+        const int64_t c = rem - h * chunks;
+        const int64_t src = (t * num_kv_heads + h) * head_dim + 16 * c;
+        const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * head_dim + 16 * c;
+#pragma unroll
+        for (int kind = 0; kind < 2; ++kind) {
+            const uint4* sp = reinterpret_cast<const uint4*>((kind ? value : key) + src);
+            const float inv = kind ? v_inv : k_inv;
+            float f[16];
+#pragma unroll
+            for (int k = 0; k < 16 / kPer; ++k) Vec16<S>::unpack(sp[k], f + k * kPer);
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                w[k] = fp8_e4m3_code(f[4 * k] * inv) | fp8_e4m3_code(f[4 * k + 1] * inv) << 8 |
+                       fp8_e4m3_code(f[4 * k + 2] * inv) << 16 |
+                       fp8_e4m3_code(f[4 * k + 3] * inv) << 24;
+            *reinterpret_cast<uint4*>((kind ? v_cache : k_cache) + dst) =
+                make_uint4(w[0], w[1], w[2], w[3]);
+        }
     }
 }
 
@@ -115,6 +160,38 @@ int launch_reshape_and_cache(const void* key, const void* value, void* k_cache, 
                            (const uint32_t*)key, (const uint32_t*)value, (uint32_t*)k_cache,
                            (uint32_t*)v_cache, slot_mapping, num_tokens, num_kv_heads, rc,
                            block_size, num_blocks);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                                 void* v_cache, const int64_t* slot_mapping, int num_tokens,
+                                 int num_kv_heads, int head_dim, int block_size,
+                                 int num_blocks, int src_dtype, float k_inv, float v_inv,
+                                 hipStream_t stream) {
+    const int64_t items = (int64_t)num_tokens * num_kv_heads * (head_dim / 16);
+    const dim3 grid(grid_for(items, 256, 65536)), block(256);
+    switch (src_dtype) {
+        case PKV_FLOAT32:
+            hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<float>, grid, block, 0, stream,
+                               (const float*)key, (const float*)value, (uint8_t*)k_cache,
+                               (uint8_t*)v_cache, slot_mapping, num_tokens, num_kv_heads,
+                               head_dim, block_size, num_blocks, k_inv, v_inv);
+            break;
+        case PKV_BFLOAT16:
+            hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<bf16_t>, grid, block, 0, stream,
+                               (const bf16_t*)key, (const bf16_t*)value, (uint8_t*)k_cache,
+                               (uint8_t*)v_cache, slot_mapping, num_tokens, num_kv_heads,
+                               head_dim, block_size, num_blocks, k_inv, v_inv);
+            break;
+        case PKV_FLOAT16:
+            hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<f16_t>, grid, block, 0, stream,
+                               (const f16_t*)key, (const f16_t*)value, (uint8_t*)k_cache,
+                               (uint8_t*)v_cache, slot_mapping, num_tokens, num_kv_heads,
+                               head_dim, block_size, num_blocks, k_inv, v_inv);
+            break;
+        default:
+            return -1;
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

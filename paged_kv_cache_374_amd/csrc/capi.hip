@@ -42,6 +42,9 @@ bool fetch(std::vector<T>& host, const T* dev, size_t n, hipStream_t stream) {
     return hipStreamSynchronize(stream) == hipSuccess;
 }
 
+// A cache scale must be a positive, finite binary32 value.
+bool scale_ok(float s) { return s > 0.f && s <= 3.4028235e38f; }
+
 int validate_tables(const pkv::DecodeShape& s, const int32_t* tables, const int32_t* ctx,
                     hipStream_t stream) {
     std::vector<int32_t> ht, hc;
@@ -94,17 +97,22 @@ namespace {
 
 // Shared by the plain and the fused (append + decode) entry points; new_k/new_v are
 // NULL for the plain decode.
+// kv_fp8: the caches hold E4M3 codes with scales k_scale / v_scale.
 int decode_call(void* out, const void* q, const void* new_k, const void* new_v,
-                const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                const int32_t* context_lens, float scale, int num_seqs, int num_heads,
-                int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
-                int num_blocks, pkv_dtype dtype, int partition_size, void* workspace,
-                size_t workspace_bytes, pkv_stream_t stream) {
+                const void* k_cache, const void* v_cache, int kv_fp8, float k_scale,
+                float v_scale, const int32_t* block_tables, const int32_t* context_lens,
+                float scale, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                int block_size, int max_blocks_per_seq, int num_blocks, pkv_dtype dtype,
+                int partition_size, void* workspace, size_t workspace_bytes,
+                pkv_stream_t stream) {
     pkv::DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        max_blocks_per_seq, num_blocks, (int)dtype, partition_size};
     pkv::DecodePlan plan{};
     const int rc = pkv::plan_decode(s, &plan);
     if (rc != PKV_OK) return rc;
+    // 8-bit caches run on the matrix-core kernels only
+    if (kv_fp8 && plan.path == pkv::Path::Generic) return PKV_E_UNSUPPORTED;
+    if (kv_fp8 && !(scale_ok(k_scale) && scale_ok(v_scale))) return PKV_E_SHAPE;
     if (num_seqs == 0) return PKV_OK;
     if (num_seqs > 65535) return PKV_E_SHAPE;
     if (!out || !q || !context_lens) return PKV_E_NULL;
@@ -118,6 +126,9 @@ int decode_call(void* out, const void* q, const void* new_k, const void* new_v,
     pkv::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, scale, s, workspace};
     a.new_k = new_k;
     a.new_v = new_v;
+    a.kv_fp8 = kv_fp8;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
     int lr;
     if (plan.path == pkv::Path::Generic) {
         // the VALU kernel does not fuse the append: run it as its own kernel first
@@ -142,10 +153,10 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                int max_blocks_per_seq, int num_blocks, pkv_dtype dtype,
                                int partition_size, void* workspace, size_t workspace_bytes,
                                pkv_stream_t stream) {
-    return decode_call(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens,
-                       scale, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                       max_blocks_per_seq, num_blocks, dtype, partition_size, workspace,
-                       workspace_bytes, stream);
+    return decode_call(out, q, nullptr, nullptr, k_cache, v_cache, 0, 1.f, 1.f, block_tables,
+                       context_lens, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                       block_size, max_blocks_per_seq, num_blocks, dtype, partition_size,
+                       workspace, workspace_bytes, stream);
 }
 
 int pkv_paged_attention_decode_append(void* out, const void* q, const void* new_k,
@@ -157,10 +168,41 @@ int pkv_paged_attention_decode_append(void* out, const void* q, const void* new_
                                       int partition_size, void* workspace,
                                       size_t workspace_bytes, pkv_stream_t stream) {
     if (num_seqs > 0 && (!new_k || !new_v)) return PKV_E_NULL;
-    return decode_call(out, q, new_k, new_v, k_cache, v_cache, block_tables, context_lens,
-                       scale, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                       max_blocks_per_seq, num_blocks, dtype, partition_size, workspace,
-                       workspace_bytes, stream);
+    return decode_call(out, q, new_k, new_v, k_cache, v_cache, 0, 1.f, 1.f, block_tables,
+                       context_lens, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                       block_size, max_blocks_per_seq, num_blocks, dtype, partition_size,
+                       workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attention_decode_fp8(void* out, const void* q, const void* k_cache,
+                                   const void* v_cache, float k_scale, float v_scale,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   float scale, int num_seqs, int num_heads, int num_kv_heads,
+                                   int head_dim, int block_size, int max_blocks_per_seq,
+                                   int num_blocks, pkv_dtype dtype, int partition_size,
+                                   void* workspace, size_t workspace_bytes,
+                                   pkv_stream_t stream) {
+    return decode_call(out, q, nullptr, nullptr, k_cache, v_cache, 1, k_scale, v_scale,
+                       block_tables, context_lens, scale, num_seqs, num_heads, num_kv_heads,
+                       head_dim, block_size, max_blocks_per_seq, num_blocks, dtype,
+                       partition_size, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attention_decode_append_fp8(void* out, const void* q, const void* new_k,
+                                          const void* new_v, void* k_cache, void* v_cache,
+                                          float k_scale, float v_scale,
+                                          const int32_t* block_tables,
+                                          const int32_t* context_lens, float scale,
+                                          int num_seqs, int num_heads, int num_kv_heads,
+                                          int head_dim, int block_size, int max_blocks_per_seq,
+                                          int num_blocks, pkv_dtype dtype, int partition_size,
+                                          void* workspace, size_t workspace_bytes,
+                                          pkv_stream_t stream) {
+    if (num_seqs > 0 && (!new_k || !new_v)) return PKV_E_NULL;
+    return decode_call(out, q, new_k, new_v, k_cache, v_cache, 1, k_scale, v_scale,
+                       block_tables, context_lens, scale, num_seqs, num_heads, num_kv_heads,
+                       head_dim, block_size, max_blocks_per_seq, num_blocks, dtype,
+                       partition_size, workspace, workspace_bytes, stream);
 }
 
 int pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
@@ -190,6 +232,34 @@ int pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, voi
     return pkv::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_tokens,
                                          num_kv_heads, head_dim, block_size, num_blocks, elt,
                                          st) == 0
+               ? PKV_OK
+               : PKV_E_LAUNCH;
+}
+
+int pkv_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                              void* v_cache, const int64_t* slot_mapping, float k_scale,
+                              float v_scale, int num_tokens, int num_kv_heads, int head_dim,
+                              int block_size, int num_blocks, pkv_dtype dtype,
+                              pkv_stream_t stream) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks < 0 || !scale_ok(k_scale) || !scale_ok(v_scale))
+        return PKV_E_SHAPE;
+    if ((dtype != PKV_FLOAT32 && dtype != PKV_BFLOAT16 && dtype != PKV_FLOAT16) ||
+        head_dim % 16 != 0)
+        return PKV_E_UNSUPPORTED;
+    if (num_tokens == 0) return PKV_OK;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_E_NULL;
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_enabled()) {
+        std::vector<int64_t> hs;
+        if (!fetch(hs, slot_mapping, (size_t)num_tokens, st)) return PKV_E_LAUNCH;
+        for (int64_t x : hs)
+            if (x >= (int64_t)num_blocks * block_size) return PKV_E_INDEX;
+    }
+    return pkv::launch_reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping,
+                                             num_tokens, num_kv_heads, head_dim, block_size,
+                                             num_blocks, (int)dtype, 1.f / k_scale,
+                                             1.f / v_scale, st) == 0
                ? PKV_OK
                : PKV_E_LAUNCH;
 }

@@ -34,7 +34,20 @@ struct DecodeArgs {
     // written at each sequence's last context position before it is attended.
     const void* new_k = nullptr;
     const void* new_v = nullptr;
+    // 8-bit caches (OCP FP8 E4M3 codes): key = code value * k_scale, value = code value
+    // * v_scale; q, out and appended rows keep the 16-bit dtype of `shape`.
+    int kv_fp8 = 0;
+    float k_scale = 1.f;
+    float v_scale = 1.f;
 };
+
+// Slot-mapped append into 8-bit caches: each element of key/value (elt_bytes 2 or 4,
+// dtype bf16/f16/f32) becomes the E4M3 code of float(x) * inv_scale.
+int launch_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                                 void* v_cache, const int64_t* slot_mapping, int num_tokens,
+                                 int num_kv_heads, int head_dim, int block_size,
+                                 int num_blocks, int src_dtype, float k_inv, float v_inv,
+                                 hipStream_t stream);
 
 // The append half of a fused decode step as its own kernel (paths whose decode kernel
 // does not fuse it): new_k/new_v[b] go to position context_lens[b] - 1 of sequence b.

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("pkv_paged_attention_decode", "pkv_paged_attention_decode_append",
-              "pkv_reshape_and_cache", "pkv_copy_blocks",
+              "pkv_paged_attention_decode_fp8", "pkv_paged_attention_decode_append_fp8",
+              "pkv_reshape_and_cache", "pkv_reshape_and_cache_fp8", "pkv_copy_blocks",
               "pkv_paged_attention_workspace_size", "pkv_workspace_init", "pkv_version",
               "pkv_strerror"):
         assert n in names
@@ -109,6 +110,53 @@ def test_fused_step_rejects_bad_arguments_on_the_host():
     assert _fused(lib) == E["WORKSPACE"]
     # empty batch: nothing to do
     assert _fused(lib, B=0, out=None, q=None, nk=None, nv=None) == E["OK"]
+
+
+def _decode_fp8(lib, fused=False, **kw):
+    a = dict(out=1, q=1, nk=1, nv=1, k=1, v=1, ks=0.5, vs=0.25, tables=1, ctx=1, scale=1.0,
+             B=2, Hq=8, Hkv=2, D=128, bs=16, MB=4, NB=16, dtype=BF16, part=0, ws=None,
+             ws_bytes=0)
+    a.update(kw)
+    tail = (a["tables"], a["ctx"], a["scale"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+            a["MB"], a["NB"], a["dtype"], a["part"], a["ws"], a["ws_bytes"], None)
+    if fused:
+        return lib.pkv_paged_attention_decode_append_fp8(a["out"], a["q"], a["nk"], a["nv"],
+                                                         a["k"], a["v"], a["ks"], a["vs"],
+                                                         *tail)
+    return lib.pkv_paged_attention_decode_fp8(a["out"], a["q"], a["k"], a["v"], a["ks"],
+                                              a["vs"], *tail)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_fp8_decode_rejects_bad_arguments_on_the_host(fused):
+    lib = pkv.load()
+    # 8-bit caches run on the matrix-core kernels only: float32 queries, head_dim other
+    # than 128, block_size other than 16 are refused
+    assert _decode_fp8(lib, fused, dtype=F32) == E["UNSUPPORTED"]
+    assert _decode_fp8(lib, fused, D=64) == E["UNSUPPORTED"]
+    assert _decode_fp8(lib, fused, bs=8) == E["UNSUPPORTED"]
+    # scales must be positive and finite
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert _decode_fp8(lib, fused, ks=bad) == E["SHAPE"]
+        assert _decode_fp8(lib, fused, vs=bad) == E["SHAPE"]
+    assert _decode_fp8(lib, fused, Hq=6, Hkv=4) == E["HEADS"]
+    assert _decode_fp8(lib, fused, q=None) == E["NULL"]
+    assert _decode_fp8(lib, fused) == E["WORKSPACE"]
+    assert _decode_fp8(lib, fused, B=0, out=None, q=None, nk=None, nv=None) == E["OK"]
+    if fused:
+        assert _decode_fp8(lib, fused, nk=None) == E["NULL"]
+
+
+def test_fp8_append_rejects_bad_arguments_on_the_host():
+    lib = pkv.load()
+    f = lib.pkv_reshape_and_cache_fp8
+    assert f(1, 1, 1, 1, 1, 0.0, 0.5, 4, 8, 64, 16, 16, BF16, None) == E["SHAPE"]
+    assert f(1, 1, 1, 1, 1, 0.5, float("nan"), 4, 8, 64, 16, 16, BF16, None) == E["SHAPE"]
+    assert f(1, 1, 1, 1, 1, 0.5, 0.5, -1, 8, 64, 16, 16, BF16, None) == E["SHAPE"]
+    assert f(1, 1, 1, 1, 1, 0.5, 0.5, 4, 8, 72, 16, 16, BF16, None) == E["UNSUPPORTED"]
+    assert f(1, 1, 1, 1, 1, 0.5, 0.5, 4, 8, 64, 16, 16, 9, None) == E["UNSUPPORTED"]
+    assert f(None, 1, 1, 1, 1, 0.5, 0.5, 4, 8, 64, 16, 16, F32, None) == E["NULL"]
+    assert f(None, None, None, None, None, 0.5, 0.5, 0, 8, 64, 16, 16, F16, None) == E["OK"]
 
 
 def test_cache_ops_reject_bad_arguments_on_the_host():

@@ -56,6 +56,8 @@ class DecodeStep:
     context_lens_before: Optional[torch.Tensor] = None
     block_tables_before: Optional[torch.Tensor] = None
     partition_size: int = 0
+    # 8-bit caches: k_cache/v_cache hold OCP FP8 E4M3 codes (uint8) with these scales
+    kv_scales: Optional[Tuple[float, float]] = None
     extra: dict = field(default_factory=dict)
 
     @property
@@ -67,8 +69,10 @@ class DecodeStep:
         return int(self.extra["num_blocks"])
 
     def kv_bytes(self) -> int:
-        """Bytes of K and V one decode step reads: sum(ctx) * Hkv * 2 * D * elt."""
-        elt = torch.empty((), dtype=self.dtype).element_size()
+        """Bytes of K and V one decode step reads: sum(ctx) * Hkv * 2 * D * elt, with
+        elt the cache element size (1 for 8-bit caches)."""
+        elt = 1 if self.kv_scales is not None else \
+            torch.empty((), dtype=self.dtype).element_size()
         return int(self.context_lens.to(torch.int64).sum()) * self.num_kv_heads * 2 \
             * self.head_dim * elt
 
@@ -292,13 +296,39 @@ def batch_with_lengths(seed: int, lens: List[int], *, num_heads: int, num_kv_hea
                             gen_device, True)
 
 
+def llama3_8b_decode_fp8(seed: int = 1002, device="cpu", gen_device=None,
+                         materialize: bool = True) -> DecodeStep:
+    """The Llama-3-8B-shaped batch with 8-bit (E4M3) caches, scales FP8_SCALES."""
+    return with_fp8(llama3_8b_decode(seed, device, gen_device, materialize))
+
+
 WORKLOADS = {
     "tiny_fp32": tiny_fp32,
     "llama3_8b_decode": llama3_8b_decode,
+    "llama3_8b_decode_fp8": llama3_8b_decode_fp8,
     "llama_70b_decode": llama_70b_decode,
     "long_context_decode": long_context_decode,
     "shared_prefix_cow": shared_prefix_cow,
 }
+
+
+FP8_SCALES = (0.0137, 0.0211)
+
+
+def with_fp8(step: DecodeStep, scales: Tuple[float, float] = FP8_SCALES) -> DecodeStep:
+    """8-bit copy of a batch's caches: each pool value x becomes the OCP FP8 E4M3 code of
+    clamp(x / scale, -448, 448) through torch's float8_e4m3fn conversion, so the cache
+    holds scale * E4M3(...) (inputs only; the library's own quantising append is tested
+    separately). With N(0, 1) values and scales near 1/73 the codes span most of the
+    E4M3 range. q and any rows to append keep their dtype."""
+    def codes(x, scale):
+        y = (x.float() / scale).clamp_(-448.0, 448.0)
+        return y.to(torch.float8_e4m3fn).view(torch.uint8)
+    step.k_cache = codes(step.k_cache, scales[0])
+    step.v_cache = codes(step.v_cache, scales[1])
+    step.kv_scales = (float(scales[0]), float(scales[1]))
+    step.name = step.name + "_fp8"
+    return step
 
 
 def with_append(step: DecodeStep, seed: int = 0) -> DecodeStep:
