@@ -185,6 +185,7 @@ __device__ __forceinline__ void issue_query(uint4 (&qv)[4], const T* __restrict_
 template <typename T>
 struct KvNative {
     using Elem = T;
+    static constexpr int kWaves = 4;   // balanced-kernel waves per workgroup
     struct Regs {
         uint4 k[4];
         uint4 v[4];
@@ -279,6 +280,9 @@ __device__ __forceinline__ uint4 widen8(uint32_t lo, uint32_t hi) {   // 8 codes
 template <typename T>
 struct KvFp8 {
     using Elem = uint8_t;
+    // Two waves per SIMD: with half the bytes per block the fold's own latency weighs
+    // more, and a second wave hides it (35.1 vs 37.8 us on the 8B-shaped batch).
+    static constexpr int kWaves = 8;
     struct Regs {
         uint4 k[2];
         uint2 v[4];
@@ -623,10 +627,10 @@ struct BalancedLds {
     int flag[2];
 };
 
-// NW waves per workgroup, one workgroup per CU, one wave per SIMD. With two waves on
-// a SIMD the older one was measured to stream ~1.5x faster than the younger, which
-// breaks equal static shares. Eight waves per CU were also slower overall (54.7 vs
-// 53.6 us on the 8B-shaped batch).
+// NW waves per workgroup, one workgroup per CU. 16-bit caches use one wave per SIMD:
+// with two waves on a SIMD the older one was measured to stream ~1.5x faster than the
+// younger, which breaks equal static shares, and eight waves per CU were no faster
+// (52.9 vs 53.0 us on the 8B-shaped batch). 8-bit caches use two waves per SIMD.
 //
 // KV: the cache format (KvNative<T> or KvFp8<T>). scale_log2 = scale * key scale *
 // log2(e); out_scale = value scale (1 for native caches) multiplies each normalised
@@ -1094,8 +1098,11 @@ int launch_format(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
         // one workgroup per CU
         const int workers = balanced_workers(a.shape, num_cus, 1);
         if (workers <= 0 || workers > plan.max_workers) return -1;
-        if (G <= 4) return launch_balanced<T, KV, 4, 4>(a, plan, workers, stream);
-        if (G <= 8) return launch_balanced<T, KV, 8, 4>(a, plan, workers, stream);
+        // Waves per workgroup: KV::kWaves (two per SIMD for 8-bit caches) while the
+        // merge records fit in LDS (groups up to 8), else four.
+        constexpr int NW = KV::kWaves;
+        if (G <= 4) return launch_balanced<T, KV, 4, NW>(a, plan, workers, stream);
+        if (G <= 8) return launch_balanced<T, KV, 8, NW>(a, plan, workers, stream);
         return launch_balanced<T, KV, 16, 4>(a, plan, workers, stream);
     }
     if (G <= 4) return launch_partitioned<T, KV, 4>(a, plan, stream);
