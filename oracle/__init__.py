@@ -26,7 +26,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 import torch
 
-from .dense import dense_attention  # noqa: F401
+from .dense import dense_attention, dense_chunk_attention  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
@@ -67,6 +67,10 @@ def _bind(lib):
     lib.oracle_paged_attention_kv.argtypes = [_P, _P, _I, _P, _P, _I, ctypes.c_double,
                                               ctypes.c_double, _P, _P, ctypes.c_double, _I,
                                               _I, _I, _I, _I, _I, _I, _P, _I, _I]
+    lib.oracle_paged_attention_chunk.restype = _I
+    lib.oracle_paged_attention_chunk.argtypes = [_P, _P, _I, _P, _P, _I, ctypes.c_double,
+                                                 ctypes.c_double, _P, _P, _P, ctypes.c_double,
+                                                 _I, _I, _I, _I, _I, _I, _I, _I, _I]
     lib.oracle_reshape_and_cache_fp8.restype = _I
     lib.oracle_reshape_and_cache_fp8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                                  ctypes.c_float, ctypes.c_float]
@@ -288,6 +292,47 @@ def decode_step_fp8(q, new_k, new_v, k_cache, v_cache, k_scale, v_scale, block_t
     out = paged_attention_fp8(q, kc, vc, k_scale, v_scale, block_tables, context_lens, scale,
                               lib=lib)
     return out, kc, vc
+
+
+def paged_attention_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          block_tables: torch.Tensor, context_lens: torch.Tensor,
+                          query_start: torch.Tensor, scale: float,
+                          kv_scales: Optional[Tuple[float, float]] = None, threads: int = 0,
+                          lib=None) -> np.ndarray:
+    """fp64 attention of several new query tokens per sequence (causal within the
+    chunk): q [NQ, Hq, D]; rows query_start[b] .. query_start[b+1]-1 are the last
+    tokens of sequence b, and row query_start[b] + j attends the first
+    context_lens[b] - T_b + j + 1 tokens. kv_scales: 8-bit (E4M3) caches with these
+    scales; otherwise the caches share q's dtype. Returns [NQ, Hq, D]."""
+    lib = lib or _load()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [NQ,Hq,D] and caches [num_blocks,Hkv,bs,D]")
+    NQ, Hq, D = q.shape
+    NB, Hkv, bs, D2 = k_cache.shape
+    if D2 != D:
+        raise ValueError("head_dim mismatch")
+    qa = _raw(q)
+    if kv_scales is None:
+        ka, va, kvt, ks, vs = _raw(k_cache), _raw(v_cache), DTYPE_CODE[k_cache.dtype], 1.0, 1.0
+    else:
+        ka = np.ascontiguousarray(k_cache.detach().cpu().numpy())
+        va = np.ascontiguousarray(v_cache.detach().cpu().numpy())
+        kvt, ks, vs = FP8, float(kv_scales[0]), float(kv_scales[1])
+    tables = np.ascontiguousarray(block_tables.to("cpu", torch.int32).numpy())
+    ctx = np.ascontiguousarray(context_lens.to("cpu", torch.int32).numpy())
+    qs = np.ascontiguousarray(query_start.to("cpu", torch.int32).numpy())
+    B = ctx.shape[0]
+    if qs.shape != (B + 1,):
+        raise ValueError("query_start must be [num_seqs + 1]")
+    mb = tables.shape[1] if tables.ndim == 2 else 0
+    out = np.zeros((NQ, Hq, D), dtype=np.float64)
+    rc = lib.oracle_paged_attention_chunk(_ptr(out), _ptr(qa), DTYPE_CODE[q.dtype], _ptr(ka),
+                                          _ptr(va), kvt, ks, vs, _ptr(tables), _ptr(ctx),
+                                          _ptr(qs), float(scale), B, NQ, Hq, Hkv, D, bs, mb, NB,
+                                          int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_paged_attention_chunk rejected its inputs ({rc})")
+    return out
 
 
 def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,

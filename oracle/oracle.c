@@ -154,6 +154,59 @@ int oracle_quantize_fp8(uint8_t* out, const void* src, long n, int dtype, float 
  * Returns 0, or -1 for inconsistent sizes, -2 for a table entry outside the pool
  * inside the used part of a table, -3 for a context longer than its table.
  */
+/* Attention of one query row against the first n tokens of sequence b through KV head
+ * g: the two-pass walk described at the top. qoff is the element offset of the row's D
+ * values in q. Writes o[0..D-1]; returns 0, or -1 when scratch memory runs out. */
+static int attend_row(double* o, const void* q, size_t qoff, int q_dtype,
+                      const void* k_cache, const void* v_cache, int kv_dtype, double k_scale,
+                      double v_scale, const int32_t* block_tables, int b, int g, int n,
+                      double scale, int Hkv, int D, int bs, int max_blocks) {
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    if (n <= 0) return 0;
+    double* s = (double*)malloc(sizeof(double) * (size_t)n);
+    size_t* at = (size_t*)malloc(sizeof(size_t) * (size_t)n);
+    if (!s || !at) { free(s); free(at); return -1; }
+    /* pass 1: scores, token by token through the block table */
+    double mx = -INFINITY;
+    for (int t = 0; t < n; ++t) {
+        int phys = block_tables[(long)b * max_blocks + t / bs];
+        at[t] = (((size_t)phys * Hkv + g) * bs + (size_t)(t % bs)) * D;
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d)
+            acc += elem(q, qoff + d, q_dtype) * (elem(k_cache, at[t] + d, kv_dtype) * k_scale);
+        s[t] = scale * acc;
+        if (s[t] > mx) mx = s[t];
+    }
+    /* pass 2: normalised weights applied to the values */
+    double denom = 0.0;
+    for (int t = 0; t < n; ++t) {
+        s[t] = exp(s[t] - mx);
+        denom += s[t];
+    }
+    for (int t = 0; t < n; ++t)
+        for (int d = 0; d < D; ++d)
+            o[d] += s[t] * (elem(v_cache, at[t] + d, kv_dtype) * v_scale);
+    for (int d = 0; d < D; ++d) o[d] /= denom;
+    free(s);
+    free(at);
+    return 0;
+}
+
+/* Checks shared by the attention entry points: sizes, contexts within their tables,
+ * table entries inside the pool over the used part. */
+static int check_tables(const int32_t* block_tables, const int32_t* context_lens, int B,
+                        int max_blocks, int num_blocks, int bs) {
+    for (int b = 0; b < B; ++b) {
+        int n = context_lens[b];
+        if (n < 0 || (long)n > (long)max_blocks * bs) return -3;
+        for (int j = 0; j < (n + bs - 1) / bs; ++j) {
+            int p = block_tables[(long)b * max_blocks + j];
+            if (p < 0 || p >= num_blocks) return -2;
+        }
+    }
+    return 0;
+}
+
 int oracle_paged_attention_kv(double* out, const void* q, int q_dtype, const void* k_cache,
                               const void* v_cache, int kv_dtype, double k_scale,
                               double v_scale, const int32_t* block_tables,
@@ -163,14 +216,8 @@ int oracle_paged_attention_kv(double* out, const void* q, int q_dtype, const voi
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || Hq % Hkv != 0) return -1;
     if (q_dtype < 0 || q_dtype > 2 || kv_dtype < 0 || kv_dtype > 3) return -1;
     const int G = Hq / Hkv;
-    for (int b = 0; b < B; ++b) {
-        int n = context_lens[b];
-        if (n < 0 || (long)n > (long)max_blocks * bs) return -3;
-        for (int j = 0; j < (n + bs - 1) / bs; ++j) {
-            int p = block_tables[(long)b * max_blocks + j];
-            if (p < 0 || p >= num_blocks) return -2;
-        }
-    }
+    const int bad = check_tables(block_tables, context_lens, B, max_blocks, num_blocks, bs);
+    if (bad) return bad;
     const long work = rows ? num_rows : (long)B * Hq;
     int status = 0;
 #ifdef _OPENMP
@@ -180,39 +227,61 @@ int oracle_paged_attention_kv(double* out, const void* q, int q_dtype, const voi
     for (long w = 0; w < work; ++w) {
         int b = rows ? rows[2 * w] : (int)(w / Hq);
         int h = rows ? rows[2 * w + 1] : (int)(w % Hq);
-        double* o = out + w * D;
         if (b < 0 || b >= B || h < 0 || h >= Hq) { status = -1; continue; }
         int g = h / G;
-        int n = context_lens[b];
-        for (int d = 0; d < D; ++d) o[d] = 0.0;
-        if (n == 0) continue;
-        double* s = (double*)malloc(sizeof(double) * (size_t)n);
-        size_t* at = (size_t*)malloc(sizeof(size_t) * (size_t)n);
-        if (!s || !at) { free(s); free(at); status = -1; continue; }
-        const size_t qoff = ((size_t)b * Hq + h) * D;
-        /* pass 1: scores, token by token through the block table */
-        double mx = -INFINITY;
-        for (int t = 0; t < n; ++t) {
-            int phys = block_tables[(long)b * max_blocks + t / bs];
-            at[t] = (((size_t)phys * Hkv + g) * bs + (size_t)(t % bs)) * D;
-            double acc = 0.0;
-            for (int d = 0; d < D; ++d)
-                acc += elem(q, qoff + d, q_dtype) * (elem(k_cache, at[t] + d, kv_dtype) * k_scale);
-            s[t] = scale * acc;
-            if (s[t] > mx) mx = s[t];
-        }
-        /* pass 2: normalised weights applied to the values */
-        double denom = 0.0;
-        for (int t = 0; t < n; ++t) {
-            s[t] = exp(s[t] - mx);
-            denom += s[t];
-        }
-        for (int t = 0; t < n; ++t)
-            for (int d = 0; d < D; ++d)
-                o[d] += s[t] * (elem(v_cache, at[t] + d, kv_dtype) * v_scale);
-        for (int d = 0; d < D; ++d) o[d] /= denom;
-        free(s);
-        free(at);
+        if (attend_row(out + w * D, q, ((size_t)b * Hq + h) * D, q_dtype, k_cache, v_cache,
+                       kv_dtype, k_scale, v_scale, block_tables, b, g, context_lens[b],
+                       scale, Hkv, D, bs, max_blocks))
+            status = -1;
+    }
+    return status;
+}
+
+/*
+ * Several new query tokens per sequence (a prefill chunk, or draft tokens to verify):
+ * [P3] "PagedAttention：逻辑连续，物理不必连续" states that the query at position i
+ * attends tokens 1..i, read block by block. Sequence b owns query rows
+ * query_start[b] .. query_start[b+1]-1, which are its last T_b = query_start[b+1] -
+ * query_start[b] tokens: row query_start[b] + j sits at position
+ * context_lens[b] - T_b + j (0-based) and so attends the first
+ * context_lens[b] - T_b + j + 1 tokens (none if that count is not positive).
+ *
+ * out: double [NQ, Hq, D]; q: [NQ, Hq, D] (q_dtype); query_start: int32 [B + 1] with
+ * query_start[0] = 0, non-decreasing, query_start[B] = NQ. The caches' new tokens are
+ * already written. Returns 0, or the codes of oracle_paged_attention_kv, or -4 for an
+ * inconsistent query_start.
+ */
+int oracle_paged_attention_chunk(double* out, const void* q, int q_dtype,
+                                 const void* k_cache, const void* v_cache, int kv_dtype,
+                                 double k_scale, double v_scale, const int32_t* block_tables,
+                                 const int32_t* context_lens, const int32_t* query_start,
+                                 double scale, int B, int NQ, int Hq, int Hkv, int D, int bs,
+                                 int max_blocks, int num_blocks, int nthreads) {
+    if (B < 0 || NQ < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || Hq % Hkv != 0)
+        return -1;
+    if (q_dtype < 0 || q_dtype > 2 || kv_dtype < 0 || kv_dtype > 3) return -1;
+    if (query_start[0] != 0 || query_start[B] != NQ) return -4;
+    for (int b = 0; b < B; ++b)
+        if (query_start[b + 1] < query_start[b]) return -4;
+    const int bad = check_tables(block_tables, context_lens, B, max_blocks, num_blocks, bs);
+    if (bad) return bad;
+    const int G = Hq / Hkv;
+    int status = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (long w = 0; w < (long)NQ * Hq; ++w) {
+        const int r = (int)(w / Hq), h = (int)(w % Hq);
+        int b = 0;                                  /* the sequence that owns row r */
+        while (query_start[b + 1] <= r) ++b;
+        const int T = query_start[b + 1] - query_start[b];
+        const int j = r - query_start[b];
+        const int n = context_lens[b] - T + j + 1;  /* tokens 0 .. position */
+        if (attend_row(out + w * D, q, ((size_t)r * Hq + h) * D, q_dtype, k_cache, v_cache,
+                       kv_dtype, k_scale, v_scale, block_tables, b, h / G, n, scale, Hkv, D,
+                       bs, max_blocks))
+            status = -1;
     }
     return status;
 }

@@ -542,9 +542,110 @@ def pin_fp8_append(lib):
     assert torch.equal(vc.permute(0, 2, 1, 3)[keep], vc0.permute(0, 2, 1, 3)[keep])
 
 
+# ----------------------------------------------------------------------------- chunks
+def _chunk_case(seed, lens, tlens, hq, hkv, d, bs, dt):
+    """Contiguous sequences of lengths `lens` placed in a paged pool (random filler
+    elsewhere), plus tlens[b] query rows per sequence. Returns the pieces for both the
+    paged oracle and library references."""
+    keys, values = _random_seqs(seed, lens, hkv, d, dt)
+    need = sum(blocks_needed(n, bs) for n in lens) + 4
+    kc, vc, tables, ctx = paged_from_contiguous(keys, values, bs, need, _order(seed, need), dt,
+                                                fill=None, seed=seed)
+    qs = torch.tensor([0] + list(np.cumsum(tlens)), dtype=torch.int32)
+    g = torch.Generator().manual_seed(seed + 1)
+    q = torch.randn(int(qs[-1]), hq, d, generator=g).to(dt)
+    return keys, values, kc, vc, tables, ctx, qs, q
+
+
+def pin_chunk_causal_sdpa(lib):
+    """Several query tokens per sequence == library attention with an explicit causal
+    mask on the contiguous sequence: row j of a T-token chunk (position n - T + j) keeps
+    the tokens at positions <= n - T + j. Covers single-token chunks, whole prompts
+    (T = n), empty chunks, block sizes 1/4/16 and grouped heads."""
+    cases = [(4, 8, 2, 16, [9, 16, 33, 5], [3, 1, 33, 0]),
+             (16, 4, 4, 32, [40, 17], [16, 5]),
+             (1, 6, 3, 8, [6, 2, 11], [6, 2, 4])]
+    for i, (bs, hq, hkv, d, lens, tl) in enumerate(cases):
+        for dt in DTYPES:
+            keys, values, kc, vc, tables, ctx, qs, q = _chunk_case(300 + i, lens, tl, hq, hkv,
+                                                                   d, bs, dt)
+            scale = 1.0 / math.sqrt(d)
+            got = oracle.paged_attention_chunk(q, kc, vc, tables, ctx, qs, scale, lib=lib)
+            want = np.zeros_like(got)
+            for b, (n, T) in enumerate(zip(lens, tl)):
+                if T == 0:
+                    continue
+                r0 = int(qs[b])
+                K = keys[b].to(torch.float64).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+                V = values[b].to(torch.float64).permute(1, 0, 2).repeat_interleave(hq // hkv, 0)
+                Q = q[r0:r0 + T].to(torch.float64).permute(1, 0, 2)          # [Hq, T, D]
+                keep = torch.arange(n)[None, :] <= (n - T + torch.arange(T))[:, None]
+                o = F.scaled_dot_product_attention(Q, K, V, attn_mask=keep, scale=scale)
+                want[r0:r0 + T] = o.permute(1, 0, 2).numpy()
+            _close(got, want, 1e-12, f"chunk sdpa case {i} {dt}")
+
+
+def pin_chunk_dense(lib):
+    """Chunk walk == the NumPy masked dense form on random batches, including rows
+    whose position falls before the context (more query rows than tokens): zero."""
+    from workloads import random_small
+    g = torch.Generator().manual_seed(77)
+    for i, (B, hq, hkv, d, bs, mx) in enumerate([(4, 8, 2, 16, 4, 40), (3, 4, 4, 8, 16, 50),
+                                                 (5, 2, 1, 8, 2, 9)]):
+        for dt in DTYPES:
+            s = random_small(400 + i, batch=B, num_heads=hq, num_kv_heads=hkv, head_dim=d,
+                             block_size=bs, max_ctx=mx, dtype=dt)
+            ctx = s.context_lens.tolist()
+            tl = [int(torch.randint(0, n + 1, (1,), generator=g)) for n in ctx]
+            tl[0] = ctx[0] + 2                       # two rows before the context starts
+            qs = torch.tensor([0] + list(np.cumsum(tl)), dtype=torch.int32)
+            q = torch.randn(int(qs[-1]), hq, d, generator=g).to(dt)
+            got = oracle.paged_attention_chunk(q, s.k_cache, s.v_cache, s.block_tables,
+                                               s.context_lens, qs, s.scale, lib=lib)
+            want = oracle.dense_chunk_attention(q, s.k_cache, s.v_cache, s.block_tables,
+                                                s.context_lens, qs, s.scale)
+            assert np.all(got[:2] == 0.0), "rows before the context must be zero"
+            _close(got, want, 1e-12, f"chunk dense case {i} {dt}")
+
+
+def pin_chunk_causality(lib):
+    """Changing the key and value of the token at position p leaves every query row at
+    a position < p bit for bit unchanged, and changes the rows at positions >= p."""
+    bs, hq, hkv, d = 4, 4, 2, 8
+    lens, tl = [13, 9], [6, 9]
+    keys, values, kc, vc, tables, ctx, qs, q = _chunk_case(500, lens, tl, hq, hkv, d, bs,
+                                                           torch.float32)
+    base = oracle.paged_attention_chunk(q, kc, vc, tables, ctx, qs, 0.4, lib=lib)
+    for b, p in ((0, 10), (1, 4)):
+        kc2, vc2 = kc.clone(), vc.clone()
+        blk = int(tables[b, p // bs])
+        kc2[blk, :, p % bs] += 3.0
+        vc2[blk, :, p % bs] -= 2.0
+        got = oracle.paged_attention_chunk(q, kc2, vc2, tables, ctx, qs, 0.4, lib=lib)
+        r0, n, T = int(qs[b]), lens[b], tl[b]
+        for j in range(T):
+            pos = n - T + j
+            same = np.array_equal(got[r0 + j], base[r0 + j])
+            assert same == (pos < p), f"seq {b} row {j} (position {pos}) vs change at {p}"
+
+
+def pin_chunk_last_row_is_decode(lib):
+    """The last row of each chunk sits at the context's end: it equals the decode of
+    that row over the whole context."""
+    bs, hq, hkv, d = 4, 8, 2, 16
+    lens, tl = [21, 7, 30], [5, 7, 1]
+    for dt in DTYPES:
+        _, _, kc, vc, tables, ctx, qs, q = _chunk_case(600, lens, tl, hq, hkv, d, bs, dt)
+        got = oracle.paged_attention_chunk(q, kc, vc, tables, ctx, qs, 0.25, lib=lib)
+        last = (qs[1:] - 1).long()
+        want = oracle.paged_attention(q[last].contiguous(), kc, vc, tables, ctx, 0.25, lib=lib)
+        _close(got[last.numpy()], want, 0.0, f"last rows {dt}")
+
+
 ALL_PINS = [pin_decoders, pin_sdpa_library, pin_dense_bruteforce, pin_worked_example,
             pin_two_token_closed_form, pin_context_one, pin_uniform_scores, pin_zero_context,
             pin_placement_permutation, pin_gqa_equals_repeated_mha, pin_stale_slots_unread,
             pin_linearity_in_values, pin_append_roundtrip, pin_copy_on_write,
             pin_decode_step_slots, pin_fp8_decode, pin_fp8_quantize, pin_fp8_attention,
-            pin_fp8_append]
+            pin_fp8_append, pin_chunk_causal_sdpa, pin_chunk_dense, pin_chunk_causality,
+            pin_chunk_last_row_is_decode]

@@ -30,8 +30,8 @@ MUTANTS = {
     "first_token_dropped_from_sum": ("denom += s[t];", "denom += t ? s[t] : 0.0;"),
     "keys_and_values_swapped": ("elem(q, qoff + d, q_dtype) * (elem(k_cache",
                                 "elem(q, qoff + d, q_dtype) * (elem(v_cache"),
-    "last_token_skipped": ("for (int t = 0; t < n; ++t) {\n            int phys",
-                           "for (int t = 0; t < n - 1; ++t) {\n            int phys"),
+    "last_token_skipped": ("for (int t = 0; t < n; ++t) {\n        int phys",
+                           "for (int t = 0; t < n - 1; ++t) {\n        int phys"),
     "slot_block_offset_swapped": ("int64_t blk = slot / bs, off = slot % bs;",
                                   "int64_t blk = slot % bs, off = slot / bs;"),
     "negative_slot_written": ("if (slot < 0) continue;", "if (slot < 0) slot = 0;"),
@@ -40,6 +40,15 @@ MUTANTS = {
     "bf16_shift_wrong": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
     "f16_bias_wrong": ("expo - 25", "expo - 24"),
     # 8-bit cache: decoder, quantiser, scales, quantising append
+    "chunk_causal_off_by_one": ("const int n = context_lens[b] - T + j + 1;",
+                                "const int n = context_lens[b] - T + j;"),
+    "chunk_not_causal": ("const int n = context_lens[b] - T + j + 1;",
+                         "const int n = context_lens[b];"),
+    "chunk_rows_reversed": ("const int j = r - query_start[b];",
+                            "const int j = query_start[b + 1] - 1 - r;"),
+    "chunk_query_row_of_sequence": ("((size_t)r * Hq + h) * D", "((size_t)b * Hq + h) * D"),
+    "chunk_row_owner_wrong": ("while (query_start[b + 1] <= r) ++b;",
+                              "while (query_start[b + 1] < r) ++b;"),
     "fp8_bias_wrong": ("expo - 10", "expo - 9"),
     "fp8_subnormal_step_wrong": ("ldexp((double)mant, -9)", "ldexp((double)mant, -10)"),
     "fp8_ties_away_from_zero": ("(int)nearbyint((2.0 * f - 1.0) * 8.0)",
