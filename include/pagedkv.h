@@ -236,6 +236,52 @@ int pkv_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
                               pkv_stream_t stream);
 
 /*
+ * Attention of several new query tokens per sequence: a prefill chunk, or draft tokens
+ * verified in one pass. [P3] section "PagedAttention：逻辑连续，物理不必连续" states
+ * that the query at position i attends tokens 1..i, read block by block through the
+ * block table; [P2] section "vLLM 的发展里程碑" names chunked prefill and speculative
+ * decoding, the two users of such a call.
+ *
+ * Sequence b owns query rows query_start[b] .. query_start[b+1]-1 (T_b rows). They are
+ * the LAST T_b tokens of its context of n = context_lens[b] tokens, which already hold
+ * their K and V (written by pkv_reshape_and_cache). Row query_start[b] + j sits at
+ * position n - T_b + j and attends the first n - T_b + j + 1 tokens. A row whose
+ * position is negative (T_b > n) attends nothing and gets a zero output.
+ *
+ * out, q        [num_query_tokens, num_heads, head_dim], dtype bfloat16 or float16;
+ *               out written (only rows owned by a sequence), q read.
+ * k_cache, v_cache, block_tables, context_lens, scale: as in pkv_paged_attention_decode.
+ * query_start   int32 [num_seqs + 1] on the device: query_start[0] = 0, non-decreasing,
+ *               query_start[num_seqs] = num_query_tokens.
+ * max_query_len host value >= every T_b; sizes the launch (one workgroup per 16 / G
+ *               query tokens, KV head and sequence, G = num_heads / num_kv_heads).
+ * Supported: bfloat16/float16, head_dim 128, block_size 16, G <= 16
+ * (PKV_E_UNSUPPORTED / PKV_E_HEADS otherwise); no workspace.
+ * Errors: PKV_E_SHAPE for negative sizes, PKV_E_NULL for missing pointers. Under
+ * PKV_VALIDATE=1 a query_start that breaks the rules above, or a T_b above
+ * max_query_len, returns PKV_E_INDEX. Without it the kernel skips a sequence whose
+ * query_start entries fall outside [0, num_query_tokens] or decrease, and rows past
+ * max_query_len are not written.
+ */
+int pkv_paged_attention_chunk(void* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, const int32_t* query_start,
+                              float scale, int num_seqs, int num_query_tokens,
+                              int max_query_len, int num_heads, int num_kv_heads, int head_dim,
+                              int block_size, int max_blocks_per_seq, int num_blocks,
+                              pkv_dtype dtype, pkv_stream_t stream);
+
+/* pkv_paged_attention_chunk over 8-bit (E4M3) caches with their scales. */
+int pkv_paged_attention_chunk_fp8(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, float k_scale, float v_scale,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* query_start, float scale, int num_seqs,
+                                  int num_query_tokens, int max_query_len, int num_heads,
+                                  int num_kv_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int num_blocks, pkv_dtype dtype,
+                                  pkv_stream_t stream);
+
+/*
  * Slot-mapped append of new tokens' K and V ([P3] section "Block table：为什么它能
  * 减少碎片": a decoded token goes into the free slot of its last block, or into a
  * newly taken block; section "Continuous batching 为什么离不开内存管理": generated

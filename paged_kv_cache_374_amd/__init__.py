@@ -79,6 +79,11 @@ def load():
     lib.pkv_paged_attention_decode_append_fp8.restype = _I
     lib.pkv_paged_attention_decode_append_fp8.argtypes = [_P] * 6 + [_F, _F, _P, _P, _F] + \
         [_I] * 9 + [_P, ctypes.c_size_t, _P]
+    lib.pkv_paged_attention_chunk.restype = _I
+    lib.pkv_paged_attention_chunk.argtypes = [_P] * 7 + [_F] + [_I] * 10 + [_P]
+    lib.pkv_paged_attention_chunk_fp8.restype = _I
+    lib.pkv_paged_attention_chunk_fp8.argtypes = [_P] * 4 + [_F, _F] + [_P] * 3 + [_F] + \
+        [_I] * 10 + [_P]
     lib.pkv_reshape_and_cache_fp8.restype = _I
     lib.pkv_reshape_and_cache_fp8.argtypes = [_P] * 5 + [_F, _F] + [_I] * 6 + [_P]
     lib.pkv_reshape_and_cache.restype = _I
@@ -272,6 +277,62 @@ def paged_attention_decode_append_fp8(out, q, new_k, new_v, k_cache, v_cache, k_
     _check(load().pkv_paged_attention_decode_append_fp8(
         *_with_scales(fused, 6, k_scale, v_scale), _stream(q.device)),
         "pkv_paged_attention_decode_append_fp8")
+    return out
+
+
+def _chunk_args(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                max_query_len, kv_fp8):
+    for name, t in (("out", out), ("q", q)):
+        _gpu(t, name, q.dtype)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _gpu(t, name, torch.uint8 if kv_fp8 else q.dtype)
+    for name, t in (("block_tables", block_tables), ("context_lens", context_lens),
+                    ("query_start", query_start)):
+        _gpu(t, name, torch.int32)
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if q.dim() != 3 or out.shape != q.shape or k_cache.dim() != 4 or \
+            v_cache.shape != k_cache.shape or k_cache.shape[3] != q.shape[2]:
+        raise ValueError("expected q/out [num_query_tokens,Hq,D] and caches "
+                         "[num_blocks,Hkv,bs,D] with the same D")
+    B = context_lens.shape[0]
+    if context_lens.dim() != 1 or query_start.shape != (B + 1,) or block_tables.dim() != 2 \
+            or block_tables.shape[0] != B:
+        raise ValueError("context_lens [B], query_start [B + 1], block_tables [B, max_blocks]")
+    if max_query_len is None:
+        max_query_len = int((query_start[1:] - query_start[:-1]).max()) if B else 0
+    NQ, Hq, D = q.shape
+    NB, Hkv, bs, _ = k_cache.shape
+    return (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(),
+            float(scale), B, NQ, int(max_query_len), Hq, Hkv, D, bs, block_tables.shape[1], NB,
+            _DTYPES[q.dtype])
+
+
+def paged_attention_chunk(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, block_tables: torch.Tensor,
+                          context_lens: torch.Tensor, query_start: torch.Tensor, scale: float,
+                          max_query_len: Optional[int] = None, k_scale: Optional[float] = None,
+                          v_scale: Optional[float] = None) -> torch.Tensor:
+    """Attention of several new query tokens per sequence (causal within the chunk).
+
+    q/out [num_query_tokens, Hq, D]; sequence b owns rows query_start[b] ..
+    query_start[b+1]-1, its last T_b context tokens (their K/V already in the cache);
+    row j attends the first context_lens[b] - T_b + j + 1 tokens. ``max_query_len``
+    (>= every T_b) is read from query_start when not given (a device sync).
+    With uint8 caches (E4M3 codes) pass k_scale and v_scale."""
+    fp8 = k_cache.dtype == torch.uint8
+    args = _chunk_args(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                       scale, max_query_len, fp8)
+    if fp8:
+        if k_scale is None or v_scale is None:
+            raise ValueError("8-bit caches need k_scale and v_scale")
+        _check(load().pkv_paged_attention_chunk_fp8(*_with_scales(args, 4, k_scale, v_scale),
+                                                    _stream(q.device)),
+               "pkv_paged_attention_chunk_fp8")
+    else:
+        _check(load().pkv_paged_attention_chunk(*args, _stream(q.device)),
+               "pkv_paged_attention_chunk")
     return out
 
 

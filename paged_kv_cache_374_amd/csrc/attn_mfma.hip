@@ -155,18 +155,21 @@ struct KTile {
     uint4 chunk[kBS][kD / 8];
 };
 
-// The query of the block's unit in QK B-operand order (lane l: head l%16, dims
-// 32kk + 8(l/16) .. +7; zero for heads past the group). It travels with every block so
-// the loop carries no per-unit registers (an L1/L2 hit after a unit's first block). A
-// padding block (past the wave's range) reads no query either: its loads are all
+// The query of the block's unit in QK B-operand order (lane l: column l%16, dims
+// 32kk + 8(l/16) .. +7). It travels with every block so the loop carries no per-unit
+// registers (an L1/L2 hit after a unit's first block). `qrow` is the unit's first query
+// row, `qbytes` the size of the buffer over its rows and `qlane` the byte offset of the
+// lane's column row from the first; columns past the unit fall outside the buffer and
+// read zeros. A padding block (past the wave's range) passes qbytes 0: its loads are all
 // zero-record, so none of them waits on memory when the wave drains its ring.
+//   decode: column c is head c of the group: qlane = c * D * elt, qbytes = G * D * elt.
+//   query chunks: column c is token c / G, head c % G of the chunk's rows.
 template <typename T>
-__device__ __forceinline__ void issue_query(uint4 (&qv)[4], const T* __restrict__ q, bool ok,
-                                            int qrow, int group, int lane) {
+__device__ __forceinline__ void issue_query(uint4 (&qv)[4], const T* __restrict__ q, int qrow,
+                                            int qbytes, int qlane, int lane) {
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(q + (size_t)qrow * kD), 0, ok ? group * kD * (int)sizeof(T) : 0,
-        kRawBufferWord3);
-    const int qoff = ((lane & 15) * kD + 8 * (lane >> 4)) * (int)sizeof(T);
+        (void*)(q + (size_t)qrow * kD), 0, qbytes, kRawBufferWord3);
+    const int qoff = qlane + 8 * (lane >> 4) * (int)sizeof(T);
 #pragma unroll
     for (int i = 0; i < 4; ++i) qv[i] = buffer_load16(rq, qoff + 32 * i * (int)sizeof(T));
 }
@@ -193,7 +196,7 @@ struct KvNative {
     };
     static __device__ __forceinline__ void issue(Regs& r, const T* k_cache, const T* v_cache,
                                                  const T* __restrict__ q, uint32_t tile,
-                                                 int qrow, int group, int lane) {
+                                                 int qrow, int qbytes, int qlane, int lane) {
         tile = __builtin_amdgcn_readfirstlane(tile);
         qrow = __builtin_amdgcn_readfirstlane(qrow);
         const bool ok = tile != kNoTile;
@@ -212,7 +215,7 @@ struct KvNative {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             r.v[i] = buffer_load16<kStream>(rv, voff + i * kD * (int)sizeof(T));
-        issue_query(r.q, q, ok, qrow, group, lane);
+        issue_query(r.q, q, qrow, ok ? qbytes : 0, qlane, lane);
     }
     static __device__ __forceinline__ void stage_k(KTile& kt, const Regs& r, int lane) {
         const int c = lane & 15, grp = lane >> 4;
@@ -291,7 +294,7 @@ struct KvFp8 {
     static __device__ __forceinline__ void issue(Regs& r, const uint8_t* k_cache,
                                                  const uint8_t* v_cache,
                                                  const T* __restrict__ q, uint32_t tile,
-                                                 int qrow, int group, int lane) {
+                                                 int qrow, int qbytes, int qlane, int lane) {
         tile = __builtin_amdgcn_readfirstlane(tile);
         qrow = __builtin_amdgcn_readfirstlane(qrow);
         const bool ok = tile != kNoTile;
@@ -307,7 +310,7 @@ struct KvFp8 {
         for (int i = 0; i < 2; ++i) r.k[i] = buffer_load16<kStream>(rk, koff + i * 8 * kD);
 #pragma unroll
         for (int i = 0; i < 4; ++i) r.v[i] = buffer_load8<kStream>(rv, voff + i * kD);
-        issue_query(r.q, q, ok, qrow, group, lane);
+        issue_query(r.q, q, qrow, ok ? qbytes : 0, qlane, lane);
     }
     static __device__ __forceinline__ void stage_k(KTile& kt, const Regs& r, int lane) {
         const int c2 = 2 * (lane & 7);   // the lane's first 8-dim chunk
@@ -359,12 +362,14 @@ __device__ __forceinline__ uint4 k_operand(const KTile& kt, int kk, int lane) {
     return kt.chunk[c][(4 * kk + grp) ^ (c & 7)];
 }
 
-// Fold one block into the wave's state. `valid` = tokens of the block that count
-// (0 masks the whole block). The running max is updated every block (exact online
-// softmax), so the loop carries no conditionally updated state.
+// Fold one block into the wave's state. `valid` = tokens of the block inside the
+// context (0 masks the whole block); `lim` <= valid = tokens that count for the lane's
+// column (decode: lim = valid; query chunks: the column's causal limit). The running
+// max is updated every block (exact online softmax), so the loop carries no
+// conditionally updated state.
 template <typename T, typename KV>
 __device__ __forceinline__ void fold_block(WaveState& s, typename KV::Regs& r, KTile& kt,
-                                           int valid, float scale_log2, int lane) {
+                                           int valid, int lim, float scale_log2, int lane) {
     const int grp = lane >> 4;
     KV::stage_k(kt, r, lane);
     uint4 v[4];
@@ -384,7 +389,7 @@ __device__ __forceinline__ void fold_block(WaveState& s, typename KV::Regs& r, K
     float mb = kNegInf;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        x[e] = (4 * grp + e < valid) ? sc[e] * scale_log2 : kNegInf;
+        x[e] = (4 * grp + e < lim) ? sc[e] * scale_log2 : kNegInf;
         mb = fmaxf(mb, x[e]);
     }
     mb = fmaxf(mb, __shfl_xor(mb, 16));
@@ -753,10 +758,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         next_unit(S.pref, num_seqs, Hkv, b, g, bn, gn);
         // Every step issues one block (a zero-record buffer past the quarter's end), so
         // the number of loads in flight never depends on the path taken.
+        const int qbytes = group * kD * (int)sizeof(T), qlane = (lane & 15) * kD * (int)sizeof(T);
         auto issue = [&](typename KV::Regs& R, int xi) {
             const int i = (int)((xi < xb ? xi : xb - 1) - x0);
-            KV::issue(R, k_cache, v_cache, q, xi < xb ? S.tile[i] : kNoTile, S.qrow[i], group,
-                      lane);
+            KV::issue(R, k_cache, v_cache, q, xi < xb ? S.tile[i] : kNoTile, S.qrow[i], qbytes,
+                      qlane, lane);
         };
         // kRing register buffers in fixed roles (the loop is unrolled kRing times): a
         // block's loads land where the fold reads them (no copies), and kRing - 1
@@ -790,7 +796,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
 #define PKV_STEP(R)                                                                       \
         if (x >= xb) break;                                                               \
         if (x >= ue) advance();                                                           \
-        fold_block<T, KV>(st, R, S.ktile[wave], uni(S.valid[x - x0]), scale_log2, lane);  \
+        {                                                                                 \
+            const int vd = uni(S.valid[x - x0]);                                          \
+            fold_block<T, KV>(st, R, S.ktile[wave], vd, vd, scale_log2, lane);            \
+        }                                                                                 \
         issue(R, x + kRing);                                                              \
         ++x;
         while (true) {
@@ -997,16 +1006,18 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     int j = j0 + wave;
     // every step issues one block (a zero-record buffer past the end): the loads in
     // flight never depend on the path taken
+    const int qbytes = group * kD * (int)sizeof(T), qlane = (lane & 15) * kD * (int)sizeof(T);
     auto issue = [&](typename KV::Regs& R, int ji) {
-        KV::issue(R, k_cache, v_cache, q, ji < j1 ? S.tile[ji - j0] : kNoTile, qrow, group,
-                  lane);
+        KV::issue(R, k_cache, v_cache, q, ji < j1 ? S.tile[ji - j0] : kNoTile, qrow, qbytes,
+                  qlane, lane);
     };
     typename KV::Regs A, B;
     issue(A, j);
     issue(B, j + kWaves);
 #define PKV_STEP(R)                                                                          \
     if (j >= j1) break;                                                                      \
-    fold_block<T, KV>(st, R, S.ktile[wave], S.valid[j - j0], scale_log2, lane);              \
+    fold_block<T, KV>(st, R, S.ktile[wave], S.valid[j - j0], S.valid[j - j0], scale_log2,    \
+                      lane);                                                                 \
     issue(R, j + 2 * kWaves);                                                                \
     j += kWaves;
     while (true) {
@@ -1037,6 +1048,126 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
                 ws_l[pr] = Ls;
             }
         }
+    }
+}
+
+// ------------------------------------------------------------------ query chunks
+// Several new query tokens per sequence: a prefill chunk, or draft tokens to verify in
+// one pass. The query at position i attends tokens 1..i, read block by block ([P3]
+// section "PagedAttention：逻辑连续，物理不必连续"). Sequence b's query rows
+// query_start[b] .. query_start[b+1]-1 are its last T tokens, so its row j sits at
+// position n - T + j of an n-token context.
+//
+// The 16 MFMA columns of a wave hold TQ = 16 / G query tokens times the G heads of one
+// KV head: column c is token c / G, head c % G. One workgroup per (tile of TQ tokens,
+// KV head, sequence) streams the blocks its last row can see; its four waves take
+// every fourth block, and their pieces merge through LDS. Each lane masks the scores of
+// its own column: token t of a block that starts at position s counts for column c
+// when s + t <= (position of the tile's first row) + c / G. Tables are staged in
+// windows of kTabMax blocks, so the context length is not limited by LDS.
+struct ChunkLds {
+    uint32_t tile[kTabMax];
+    uint8_t valid[kTabMax];
+    int8_t rel[kTabMax];   // first row's position minus the block's start, clipped
+    KTile ktile[kWaves];
+    float part[kWaves][Part<16>::kFloats];
+};
+
+template <typename T, typename KV>
+__global__ __launch_bounds__(kThreads) void chunk_mfma_kernel(
+    T* __restrict__ out, const T* __restrict__ q, const typename KV::Elem* k_cache,
+    const typename KV::Elem* v_cache, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ query_start,
+    float scale_log2, float out_scale, int num_query_tokens, int num_heads, int num_kv_heads,
+    int group, int tq, int max_blocks, int num_blocks) {
+    __shared__ ChunkLds S;
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+    const int r0 = query_start[b], r1 = query_start[b + 1];
+    // rows outside the query array or a decreasing start: nothing is read or written
+    if (r0 < 0 || r1 < r0 || r1 > num_query_tokens) return;
+    const int T_b = r1 - r0;
+    const int tok0 = blockIdx.x * tq;
+    if (tok0 >= T_b) return;
+    const int ntok = min(tq, T_b - tok0);
+    const int cap = max_blocks * kBS;
+    int n = ctx_lens[b];
+    n = n < 0 ? 0 : (n > cap ? cap : n);
+    const int first = n - T_b + tok0;              // position of the tile's first row
+    const int last = first + ntok - 1;             // position of its last row
+    const int nbv = last < 0 ? 0 : last / kBS + 1; // blocks the last row sees
+    const int ncols = ntok * group;
+    const int row0 = (r0 + tok0) * num_heads + g * group;   // query/output row of column 0
+    constexpr int kCols = kD / 4;                  // float4 columns of a row
+    auto row_of = [&](int c) { return row0 + (c / group) * num_heads + c % group; };
+    if (nbv == 0) {
+        // every row of the tile lies before the context: zero output
+        for (int i = tid; i < ncols * kCols; i += kThreads)
+            store4(out + (size_t)row_of(i / kCols) * kD + (i % kCols) * 4,
+                   make_float4(0.f, 0.f, 0.f, 0.f));
+        return;
+    }
+    // The lane's column: token ctok, head c % G. Columns past the tile (c >= ncols)
+    // point past the query buffer and read zeros; they are never written.
+    const int c = lane & 15, ctok = c / group;
+    const int qlane = (ctok * num_heads + c % group) * kD * (int)sizeof(T);
+    const int qbytes = ((ntok - 1) * num_heads + group) * kD * (int)sizeof(T);
+
+    WaveState st;
+    reset(st);
+    for (int w0 = 0; w0 < nbv; w0 += kTabMax) {
+        const int w1 = min(nbv, w0 + kTabMax);
+        __syncthreads();   // the previous window's entries are no longer read
+        for (int j = w0 + tid; j < w1; j += kThreads) {
+            const int phys = tables[(size_t)b * max_blocks + j];
+            const bool ok = phys >= 0 && phys < num_blocks;
+            const int left = n - j * kBS;
+            int rel = first - j * kBS;
+            rel = rel < -kBS - 1 ? -kBS - 1 : (rel > kBS ? kBS : rel);
+            S.tile[j - w0] = ok ? (uint32_t)phys * (uint32_t)num_kv_heads + (uint32_t)g
+                                : kNoTile;
+            S.valid[j - w0] = (uint8_t)(ok ? (left < kBS ? left : kBS) : 0);
+            S.rel[j - w0] = (int8_t)rel;
+        }
+        __syncthreads();
+        // every step issues one block (a zero-record buffer past the window), so the
+        // loads in flight never depend on the path taken
+        auto issue = [&](typename KV::Regs& R, int ji) {
+            KV::issue(R, k_cache, v_cache, q, ji < w1 ? S.tile[ji - w0] : kNoTile, row0,
+                      qbytes, qlane, lane);
+        };
+        int j = w0 + wave;
+        typename KV::Regs A, B;
+        issue(A, j);
+        issue(B, j + kWaves);
+#define PKV_STEP(R)                                                                          \
+        if (j >= w1) break;                                                                  \
+        {                                                                                    \
+            const int vd = S.valid[j - w0];                                                  \
+            int lim = S.rel[j - w0] + ctok + 1;                                              \
+            lim = lim < 0 ? 0 : (lim > vd ? vd : lim);                                       \
+            fold_block<T, KV>(st, R, S.ktile[wave], vd, lim, scale_log2, lane);              \
+        }                                                                                    \
+        issue(R, j + 2 * kWaves);                                                            \
+        j += kWaves;
+        while (true) {
+            PKV_STEP(A)
+            PKV_STEP(B)
+        }
+#undef PKV_STEP
+    }
+    wave_to_part<16>(S.part[wave], st, lane, ncols);
+    __syncthreads();
+    int P[kWaves];
+    for (int v = 0; v < kWaves; ++v) P[v] = v;
+    for (int i = tid; i < ncols * kCols; i += kThreads) {
+        const int h = i / kCols, d0 = (i % kCols) * 4;
+        float M, Ls;
+        float4 o;
+        merge_parts<16, kWaves, kWaves>(S.part, P, kWaves, h, d0, M, Ls, o);
+        const float inv = Ls > 0.f ? out_scale / Ls : 0.f;
+        store4(out + (size_t)row_of(h) * kD + d0,
+               make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv));
     }
 }
 
@@ -1091,6 +1222,25 @@ int launch_partitioned(const DecodeArgs& a, const DecodePlan& plan, hipStream_t 
 }
 
 template <typename T, typename KV>
+int launch_chunk(const ChunkArgs& a, hipStream_t stream) {
+    const int G = a.num_heads / a.num_kv_heads;
+    const int tq = 16 / G;   // query tokens per workgroup (G <= 16)
+    const int tiles = (a.max_query_len + tq - 1) / tq;
+    if (tiles == 0 || a.num_seqs == 0) return 0;
+    using E = typename KV::Elem;
+    const bool fp8 = a.kv_fp8 != 0;
+    const float scale_log2 = a.scale * (fp8 ? a.k_scale : 1.f) * kLog2e;
+    const float out_scale = fp8 ? a.v_scale : 1.f;
+    hipLaunchKernelGGL((chunk_mfma_kernel<T, KV>), dim3(tiles, a.num_kv_heads, a.num_seqs),
+                       dim3(kThreads), 0, stream, (T*)a.out, (const T*)a.q,
+                       (const E*)a.k_cache, (const E*)a.v_cache, a.block_tables,
+                       a.context_lens, a.query_start, scale_log2, out_scale,
+                       a.num_query_tokens, a.num_heads, a.num_kv_heads, G, tq, a.max_blocks,
+                       a.num_blocks);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <typename T, typename KV>
 int launch_format(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
                   hipStream_t stream) {
     const int G = plan.group;
@@ -1117,6 +1267,16 @@ int launch_typed(const DecodeArgs& a, const DecodePlan& plan, int num_cus, hipSt
 }
 
 }  // namespace
+
+int launch_chunk_mfma(const ChunkArgs& a, hipStream_t stream) {
+    if (a.dtype == PKV_BFLOAT16)
+        return a.kv_fp8 ? launch_chunk<bf16_t, KvFp8<bf16_t>>(a, stream)
+                        : launch_chunk<bf16_t, KvNative<bf16_t>>(a, stream);
+    if (a.dtype == PKV_FLOAT16)
+        return a.kv_fp8 ? launch_chunk<f16_t, KvFp8<f16_t>>(a, stream)
+                        : launch_chunk<f16_t, KvNative<f16_t>>(a, stream);
+    return -1;
+}
 
 int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
                        hipStream_t stream) {

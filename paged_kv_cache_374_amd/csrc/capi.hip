@@ -142,6 +142,49 @@ int decode_call(void* out, const void* q, const void* new_k, const void* new_v,
     return lr == 0 ? PKV_OK : PKV_E_LAUNCH;
 }
 
+// Shared by the 16-bit and 8-bit chunk entry points.
+int chunk_call(void* out, const void* q, const void* k_cache, const void* v_cache, int kv_fp8,
+               float k_scale, float v_scale, const int32_t* block_tables,
+               const int32_t* context_lens, const int32_t* query_start, float scale,
+               int num_seqs, int num_query_tokens, int max_query_len, int num_heads,
+               int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+               int num_blocks, pkv_dtype dtype, pkv_stream_t stream) {
+    if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || num_heads <= 0 ||
+        num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq < 0 ||
+        num_blocks < 0)
+        return PKV_E_SHAPE;
+    if (num_heads % num_kv_heads != 0 || num_heads / num_kv_heads > pkv::kMaxGroup)
+        return PKV_E_HEADS;
+    // matrix-core kernel only: bfloat16/float16 queries, head_dim 128, block_size 16
+    if (!pkv::mfma_eligible((int)dtype, head_dim, block_size, num_heads / num_kv_heads))
+        return PKV_E_UNSUPPORTED;
+    if (kv_fp8 && !(scale_ok(k_scale) && scale_ok(v_scale))) return PKV_E_SHAPE;
+    if (num_seqs > 65535 || num_kv_heads > 65535) return PKV_E_SHAPE;
+    if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PKV_OK;
+    if ((long long)num_query_tokens * num_heads * head_dim > 0x7fffffffLL) return PKV_E_SHAPE;
+    if (!out || !q || !context_lens || !query_start) return PKV_E_NULL;
+    if (max_blocks_per_seq > 0 && (!k_cache || !v_cache || !block_tables)) return PKV_E_NULL;
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_enabled()) {
+        pkv::DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                           max_blocks_per_seq, num_blocks, (int)dtype, 0};
+        const int v = validate_tables(s, block_tables, context_lens, st);
+        if (v != PKV_OK) return v;
+        std::vector<int32_t> hq;
+        if (!fetch(hq, query_start, (size_t)num_seqs + 1, st)) return PKV_E_LAUNCH;
+        if (hq[0] != 0 || hq[num_seqs] != num_query_tokens) return PKV_E_INDEX;
+        for (int b = 0; b < num_seqs; ++b)
+            if (hq[b + 1] < hq[b] || hq[b + 1] - hq[b] > max_query_len) return PKV_E_INDEX;
+    }
+    pkv::ChunkArgs a{out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                     num_seqs, num_query_tokens, max_query_len, num_heads, num_kv_heads,
+                     head_dim, block_size, max_blocks_per_seq, num_blocks, (int)dtype};
+    a.kv_fp8 = kv_fp8;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    return pkv::launch_chunk_mfma(a, st) == 0 ? PKV_OK : PKV_E_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -203,6 +246,33 @@ int pkv_paged_attention_decode_append_fp8(void* out, const void* q, const void* 
                        block_tables, context_lens, scale, num_seqs, num_heads, num_kv_heads,
                        head_dim, block_size, max_blocks_per_seq, num_blocks, dtype,
                        partition_size, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attention_chunk(void* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, const int32_t* query_start,
+                              float scale, int num_seqs, int num_query_tokens,
+                              int max_query_len, int num_heads, int num_kv_heads, int head_dim,
+                              int block_size, int max_blocks_per_seq, int num_blocks,
+                              pkv_dtype dtype, pkv_stream_t stream) {
+    return chunk_call(out, q, k_cache, v_cache, 0, 1.f, 1.f, block_tables, context_lens,
+                      query_start, scale, num_seqs, num_query_tokens, max_query_len, num_heads,
+                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, dtype,
+                      stream);
+}
+
+int pkv_paged_attention_chunk_fp8(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, float k_scale, float v_scale,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* query_start, float scale, int num_seqs,
+                                  int num_query_tokens, int max_query_len, int num_heads,
+                                  int num_kv_heads, int head_dim, int block_size,
+                                  int max_blocks_per_seq, int num_blocks, pkv_dtype dtype,
+                                  pkv_stream_t stream) {
+    return chunk_call(out, q, k_cache, v_cache, 1, k_scale, v_scale, block_tables,
+                      context_lens, query_start, scale, num_seqs, num_query_tokens,
+                      max_query_len, num_heads, num_kv_heads, head_dim, block_size,
+                      max_blocks_per_seq, num_blocks, dtype, stream);
 }
 
 int pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,

@@ -60,6 +60,29 @@ int launch_decode_generic(const DecodeArgs& a, const DecodePlan& plan, hipStream
 // paths).
 int launch_partition_reduce(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 
+// Several query tokens per sequence, causal within each sequence's chunk: rows
+// query_start[b] .. query_start[b+1]-1 of q/out ([num_query_tokens, num_heads,
+// head_dim]) are the last tokens of sequence b's context.
+struct ChunkArgs {
+    void* out;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    const int32_t* query_start;
+    float scale;
+    int num_seqs, num_query_tokens, max_query_len;
+    int num_heads, num_kv_heads, head_dim, block_size, max_blocks, num_blocks, dtype;
+    int kv_fp8 = 0;
+    float k_scale = 1.f;
+    float v_scale = 1.f;
+};
+
+// Matrix-core chunk kernel (bfloat16/float16 queries, head_dim 128, block_size 16,
+// group <= 16).
+int launch_chunk_mfma(const ChunkArgs& a, hipStream_t stream);
+
 // Matrix-core kernels (bfloat16/float16, block_size 16).
 int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
                        hipStream_t stream);

@@ -26,6 +26,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("pkv_paged_attention_decode", "pkv_paged_attention_decode_append",
               "pkv_paged_attention_decode_fp8", "pkv_paged_attention_decode_append_fp8",
+              "pkv_paged_attention_chunk", "pkv_paged_attention_chunk_fp8",
               "pkv_reshape_and_cache", "pkv_reshape_and_cache_fp8", "pkv_copy_blocks",
               "pkv_paged_attention_workspace_size", "pkv_workspace_init", "pkv_version",
               "pkv_strerror"):
@@ -145,6 +146,42 @@ def test_fp8_decode_rejects_bad_arguments_on_the_host(fused):
     assert _decode_fp8(lib, fused, B=0, out=None, q=None, nk=None, nv=None) == E["OK"]
     if fused:
         assert _decode_fp8(lib, fused, nk=None) == E["NULL"]
+
+
+def _chunk(lib, fp8=False, **kw):
+    a = dict(out=1, q=1, k=1, v=1, ks=0.5, vs=0.5, tables=1, ctx=1, qs=1, scale=1.0, B=2, NQ=6,
+             MQ=4, Hq=8, Hkv=2, D=128, bs=16, MB=4, NB=16, dtype=BF16)
+    a.update(kw)
+    tail = (a["tables"], a["ctx"], a["qs"], a["scale"], a["B"], a["NQ"], a["MQ"], a["Hq"],
+            a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"], a["dtype"], None)
+    if fp8:
+        return lib.pkv_paged_attention_chunk_fp8(a["out"], a["q"], a["k"], a["v"], a["ks"],
+                                                 a["vs"], *tail)
+    return lib.pkv_paged_attention_chunk(a["out"], a["q"], a["k"], a["v"], *tail)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_chunk_rejects_bad_arguments_on_the_host(fp8):
+    lib = pkv.load()
+    assert _chunk(lib, fp8, dtype=F32) == E["UNSUPPORTED"]
+    assert _chunk(lib, fp8, D=64) == E["UNSUPPORTED"]
+    assert _chunk(lib, fp8, bs=8) == E["UNSUPPORTED"]
+    assert _chunk(lib, fp8, Hq=6, Hkv=4) == E["HEADS"]
+    assert _chunk(lib, fp8, Hq=64, Hkv=2) == E["HEADS"]           # group 32 > 16
+    assert _chunk(lib, fp8, B=-1) == E["SHAPE"]
+    assert _chunk(lib, fp8, NQ=-1) == E["SHAPE"]
+    assert _chunk(lib, fp8, MQ=-1) == E["SHAPE"]
+    assert _chunk(lib, fp8, qs=None) == E["NULL"]
+    assert _chunk(lib, fp8, q=None) == E["NULL"]
+    assert _chunk(lib, fp8, tables=None) == E["NULL"]
+    # nothing to attend: success without device work
+    assert _chunk(lib, fp8, B=0, out=None, q=None, qs=None) == E["OK"]
+    assert _chunk(lib, fp8, NQ=0, out=None, q=None) == E["OK"]
+    assert _chunk(lib, fp8, MQ=0, out=None) == E["OK"]
+    if fp8:
+        for bad in (0.0, -2.0, float("inf"), float("nan")):
+            assert _chunk(lib, fp8, ks=bad) == E["SHAPE"]
+            assert _chunk(lib, fp8, vs=bad) == E["SHAPE"]
 
 
 def test_fp8_append_rejects_bad_arguments_on_the_host():

@@ -58,6 +58,10 @@ class DecodeStep:
     partition_size: int = 0
     # 8-bit caches: k_cache/v_cache hold OCP FP8 E4M3 codes (uint8) with these scales
     kv_scales: Optional[Tuple[float, float]] = None
+    # several query tokens per sequence: q is [num_query_tokens, Hq, D] and sequence b
+    # owns rows query_start[b] .. query_start[b+1]-1 (its last context tokens)
+    query_start: Optional[torch.Tensor] = None    # int32 [B + 1]
+    max_query_len: int = 0
     extra: dict = field(default_factory=dict)
 
     @property
@@ -328,6 +332,26 @@ def with_fp8(step: DecodeStep, scales: Tuple[float, float] = FP8_SCALES) -> Deco
     step.v_cache = codes(step.v_cache, scales[1])
     step.kv_scales = (float(scales[0]), float(scales[1]))
     step.name = step.name + "_fp8"
+    return step
+
+
+def with_chunk(step: DecodeStep, query_lens: List[int], seed: int = 0) -> DecodeStep:
+    """Turn a batch into a multi-token query step: sequence b's last query_lens[b]
+    context tokens become its query rows (a prefill chunk or draft tokens to verify;
+    their K/V are the pool's values at those positions). q is redrawn as
+    [sum(query_lens), Hq, D] from N(0, 1), cast to the KV dtype (bf16/f16 for 8-bit
+    caches: the dtype of the batch)."""
+    if len(query_lens) != step.num_seqs:
+        raise ValueError("one query length per sequence")
+    dev = step.context_lens.device
+    qs = [0]
+    for n in query_lens:
+        qs.append(qs[-1] + int(n))
+    gen = torch.Generator(device=dev).manual_seed(seed + 15485863)
+    step.q = _normal((qs[-1], step.num_heads, step.head_dim), step.dtype, gen, dev)
+    step.query_start = torch.tensor(qs, dtype=torch.int32).to(dev)
+    step.max_query_len = max(query_lens) if query_lens else 0
+    step.name = step.name + "_chunk"
     return step
 
 
