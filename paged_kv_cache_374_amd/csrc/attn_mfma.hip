@@ -194,6 +194,9 @@ struct KvNative {
         uint4 v[4];
         uint4 q[4];
     };
+    // AUX: cache policy of the K/V loads (kStream when every byte is read once).
+    // WITH_Q false: the caller keeps the query in its own registers (r.q unused).
+    template <int AUX = kStream, bool WITH_Q = true>
     static __device__ __forceinline__ void issue(Regs& r, const T* k_cache, const T* v_cache,
                                                  const T* __restrict__ q, uint32_t tile,
                                                  int qrow, int qbytes, int qlane, int lane) {
@@ -211,11 +214,11 @@ struct KvNative {
         const int voff = (4 * grp * kD + 8 * c) * (int)sizeof(T);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            r.k[i] = buffer_load16<kStream>(rk, koff + i * 4 * kD * (int)sizeof(T));
+            r.k[i] = buffer_load16<AUX>(rk, koff + i * 4 * kD * (int)sizeof(T));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            r.v[i] = buffer_load16<kStream>(rv, voff + i * kD * (int)sizeof(T));
-        issue_query(r.q, q, qrow, ok ? qbytes : 0, qlane, lane);
+            r.v[i] = buffer_load16<AUX>(rv, voff + i * kD * (int)sizeof(T));
+        if constexpr (WITH_Q) issue_query(r.q, q, qrow, ok ? qbytes : 0, qlane, lane);
     }
     static __device__ __forceinline__ void stage_k(KTile& kt, const Regs& r, int lane) {
         const int c = lane & 15, grp = lane >> 4;
@@ -291,6 +294,7 @@ struct KvFp8 {
         uint2 v[4];
         uint4 q[4];
     };
+    template <int AUX = kStream, bool WITH_Q = true>
     static __device__ __forceinline__ void issue(Regs& r, const uint8_t* k_cache,
                                                  const uint8_t* v_cache,
                                                  const T* __restrict__ q, uint32_t tile,
@@ -307,10 +311,10 @@ struct KvFp8 {
         const int koff = (lane >> 3) * kD + 16 * (lane & 7);
         const int voff = 4 * (lane >> 4) * kD + 8 * (lane & 15);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) r.k[i] = buffer_load16<kStream>(rk, koff + i * 8 * kD);
+        for (int i = 0; i < 2; ++i) r.k[i] = buffer_load16<AUX>(rk, koff + i * 8 * kD);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r.v[i] = buffer_load8<kStream>(rv, voff + i * kD);
-        issue_query(r.q, q, qrow, ok ? qbytes : 0, qlane, lane);
+        for (int i = 0; i < 4; ++i) r.v[i] = buffer_load8<AUX>(rv, voff + i * kD);
+        if constexpr (WITH_Q) issue_query(r.q, q, qrow, ok ? qbytes : 0, qlane, lane);
     }
     static __device__ __forceinline__ void stage_k(KTile& kt, const Regs& r, int lane) {
         const int c2 = 2 * (lane & 7);   // the lane's first 8-dim chunk
@@ -362,29 +366,17 @@ __device__ __forceinline__ uint4 k_operand(const KTile& kt, int kk, int lane) {
     return kt.chunk[c][(4 * kk + grp) ^ (c & 7)];
 }
 
-// Fold one block into the wave's state. `valid` = tokens of the block inside the
-// context (0 masks the whole block); `lim` <= valid = tokens that count for the lane's
-// column (decode: lim = valid; query chunks: the column's causal limit). The running
-// max is updated every block (exact online softmax), so the loop carries no
-// conditionally updated state.
-template <typename T, typename KV>
-__device__ __forceinline__ void fold_block(WaveState& s, typename KV::Regs& r, KTile& kt,
-                                           int valid, int lim, float scale_log2, int lane) {
+// The query-dependent half of a fold: scores of one 16-column tile against the block's
+// K operand `ka` (k_operand order), masked to the first `lim` tokens for the lane's
+// column, the online-softmax update, and the PV product with the block's V rows `v`.
+template <typename T>
+__device__ __forceinline__ void fold_tile(WaveState& s, const uint4 (&ka)[4],
+                                          const uint4 (&qv)[4], const uint4 (&v)[4], int lim,
+                                          float scale_log2, int lane) {
     const int grp = lane >> 4;
-    KV::stage_k(kt, r, lane);
-    uint4 v[4];
-    KV::widen_v(r, v);
-    if (valid < kBS) {
-        // Slots past the context hold stale data (possibly NaN); a zero weight does not
-        // cancel a NaN inside the product, so their V rows are cleared. Their scores are
-        // replaced by -inf below (a select), so stale K never reaches the softmax.
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (4 * grp + e >= valid) v[e] = make_uint4(0, 0, 0, 0);
-    }
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc = Mma<T>::qk(k_operand(kt, i, lane), r.q[i], sc);
+    for (int i = 0; i < 4; ++i) sc = Mma<T>::qk(ka[i], qv[i], sc);
     float x[4];
     float mb = kNegInf;
 #pragma unroll
@@ -419,6 +411,40 @@ __device__ __forceinline__ void fold_block(WaveState& s, typename KV::Regs& r, K
     PKV_PV_STEP(0) PKV_PV_STEP(1) PKV_PV_STEP(2) PKV_PV_STEP(3)
     PKV_PV_STEP(4) PKV_PV_STEP(5) PKV_PV_STEP(6) PKV_PV_STEP(7)
 #undef PKV_PV_STEP
+}
+
+// The query-independent half: K through the wave's LDS tile into operand order (ka),
+// V widened to T with the rows past the context cleared. `valid` = tokens of the block
+// inside the context. Slots past the context hold stale data (possibly NaN); a zero
+// weight does not cancel a NaN inside the product, so their V rows are cleared, and
+// their scores are replaced by -inf in fold_tile (a select), so stale K never reaches
+// the softmax.
+template <typename T, typename KV>
+__device__ __forceinline__ void stage_block(const typename KV::Regs& r, KTile& kt, int valid,
+                                            int lane, uint4 (&ka)[4], uint4 (&v)[4]) {
+    const int grp = lane >> 4;
+    KV::stage_k(kt, r, lane);
+    KV::widen_v(r, v);
+    if (valid < kBS) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (4 * grp + e >= valid) v[e] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ka[i] = k_operand(kt, i, lane);
+}
+
+// Fold one block into the wave's state. `valid` = tokens of the block inside the
+// context (0 masks the whole block); `lim` <= valid = tokens that count for the lane's
+// column (decode: lim = valid; query chunks: the column's causal limit). The running
+// max is updated every block (exact online softmax), so the loop carries no
+// conditionally updated state.
+template <typename T, typename KV>
+__device__ __forceinline__ void fold_block(WaveState& s, typename KV::Regs& r, KTile& kt,
+                                           int valid, int lim, float scale_log2, int lane) {
+    uint4 ka[4], v[4];
+    stage_block<T, KV>(r, kt, valid, lane, ka, v);
+    fold_tile<T>(s, ka, r.q, v, lim, scale_log2, lane);
 }
 
 __device__ __forceinline__ float weight(float m, float M) {
@@ -1059,22 +1085,76 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
 // position n - T + j of an n-token context.
 //
 // The 16 MFMA columns of a wave hold TQ = 16 / G query tokens times the G heads of one
-// KV head: column c is token c / G, head c % G. One workgroup per (tile of TQ tokens,
-// KV head, sequence) streams the blocks its last row can see; its four waves take
-// every fourth block, and their pieces merge through LDS. Each lane masks the scores of
+// KV head: column c is token c / G, head c % G (a tile). Each lane masks the scores of
 // its own column: token t of a block that starts at position s counts for column c
-// when s + t <= (position of the tile's first row) + c / G. Tables are staged in
-// windows of kTabMax blocks, so the context length is not limited by LDS.
+// when s + t <= (position of the tile's first row) + c / G. Two kernels spread a
+// (sequence, KV head) over workgroups: chunk_split_kernel for short chunks (up to four
+// tiles, e.g. draft verification) and chunk_tiles_kernel for long ones (prefill).
+// Tables are staged in windows of kTabMax blocks, so the context length is not
+// limited by LDS.
 struct ChunkLds {
     uint32_t tile[kTabMax];
     uint8_t valid[kTabMax];
-    int8_t rel[kTabMax];   // first row's position minus the block's start, clipped
     KTile ktile[kWaves];
     float part[kWaves][Part<16>::kFloats];
 };
 
+// A wave's state -> normalised output rows for columns c < ncols, column c going to
+// row row0 + (c / group) * num_heads + c % group.
+template <typename T>
+__device__ __forceinline__ void wave_to_rows(T* out, int row0, const WaveState& s, int lane,
+                                             int ncols, int group, int num_heads,
+                                             float out_scale) {
+    const int c = lane & 15, grp = lane >> 4;
+    const float ls = head_lsum(s);
+    const float inv = ls > 0.f ? out_scale / ls : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int h = 4 * grp + e;
+        const float iv = __shfl(inv, h);
+        if (h < ncols) {
+            uint4 w;
+            w.x = Mma<T>::pack(s.o[0][e] * iv, s.o[1][e] * iv);
+            w.y = Mma<T>::pack(s.o[2][e] * iv, s.o[3][e] * iv);
+            w.z = Mma<T>::pack(s.o[4][e] * iv, s.o[5][e] * iv);
+            w.w = Mma<T>::pack(s.o[6][e] * iv, s.o[7][e] * iv);
+            const size_t row = (size_t)row0 + (h / group) * num_heads + h % group;
+            *reinterpret_cast<uint4*>(out + row * kD + 8 * c) = w;
+        }
+    }
+}
+
+// Rows of a workgroup whose rows all lie before the context: zero output. `row0` is
+// the query/output row of column 0 and `ntok` the workgroup's query tokens.
+template <typename T>
+__device__ __forceinline__ void zero_rows(T* out, int row0, int ntok, int group, int num_heads,
+                                          int tid) {
+    constexpr int kCols = kD / 4;
+    for (int i = tid; i < ntok * group * kCols; i += kThreads) {
+        const int h = i / kCols;
+        store4(out + ((size_t)row0 + (h / group) * num_heads + h % group) * kD + (i % kCols) * 4,
+               make_float4(0.f, 0.f, 0.f, 0.f));
+    }
+}
+
+// Table entries of blocks w0 .. w1-1 of sequence b into the workgroup's LDS window.
+__device__ __forceinline__ void stage_window(uint32_t* tile, uint8_t* valid,
+                                             const int32_t* __restrict__ tables, int b, int g,
+                                             int n, int w0, int w1, int max_blocks,
+                                             int num_blocks, int num_kv_heads, int tid) {
+    for (int j = w0 + tid; j < w1; j += kThreads) {
+        const int phys = tables[(size_t)b * max_blocks + j];
+        const bool ok = phys >= 0 && phys < num_blocks;
+        const int left = n - j * kBS;
+        tile[j - w0] = ok ? (uint32_t)phys * (uint32_t)num_kv_heads + (uint32_t)g : kNoTile;
+        valid[j - w0] = (uint8_t)(ok ? (left < kBS ? left : kBS) : 0);
+    }
+}
+
+// Short chunks: one tile per workgroup; its waves take every fourth block and their
+// pieces merge through LDS.
 template <typename T, typename KV>
-__global__ __launch_bounds__(kThreads) void chunk_mfma_kernel(
+__global__ __launch_bounds__(kThreads) void chunk_split_kernel(
     T* __restrict__ out, const T* __restrict__ q, const typename KV::Elem* k_cache,
     const typename KV::Elem* v_cache, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ query_start,
@@ -1089,22 +1169,16 @@ __global__ __launch_bounds__(kThreads) void chunk_mfma_kernel(
     const int T_b = r1 - r0;
     const int tok0 = blockIdx.x * tq;
     if (tok0 >= T_b) return;
-    const int ntok = min(tq, T_b - tok0);
     const int cap = max_blocks * kBS;
     int n = ctx_lens[b];
     n = n < 0 ? 0 : (n > cap ? cap : n);
-    const int first = n - T_b + tok0;              // position of the tile's first row
-    const int last = first + ntok - 1;             // position of its last row
-    const int nbv = last < 0 ? 0 : last / kBS + 1; // blocks the last row sees
+    const int ntok = min(tq, T_b - tok0);
+    const int first = n - T_b + tok0;                   // position of the tile's first row
+    const int nb = first + ntok - 1 < 0 ? 0 : (first + ntok - 1) / kBS + 1;
     const int ncols = ntok * group;
     const int row0 = (r0 + tok0) * num_heads + g * group;   // query/output row of column 0
-    constexpr int kCols = kD / 4;                  // float4 columns of a row
-    auto row_of = [&](int c) { return row0 + (c / group) * num_heads + c % group; };
-    if (nbv == 0) {
-        // every row of the tile lies before the context: zero output
-        for (int i = tid; i < ncols * kCols; i += kThreads)
-            store4(out + (size_t)row_of(i / kCols) * kD + (i % kCols) * 4,
-                   make_float4(0.f, 0.f, 0.f, 0.f));
+    if (nb == 0) {
+        zero_rows(out, row0, ntok, group, num_heads, tid);
         return;
     }
     // The lane's column: token ctok, head c % G. Columns past the tile (c >= ncols)
@@ -1112,23 +1186,15 @@ __global__ __launch_bounds__(kThreads) void chunk_mfma_kernel(
     const int c = lane & 15, ctok = c / group;
     const int qlane = (ctok * num_heads + c % group) * kD * (int)sizeof(T);
     const int qbytes = ((ntok - 1) * num_heads + group) * kD * (int)sizeof(T);
+    const int lim0 = first + ctok + 1;   // context tokens the lane's column sees
 
     WaveState st;
     reset(st);
-    for (int w0 = 0; w0 < nbv; w0 += kTabMax) {
-        const int w1 = min(nbv, w0 + kTabMax);
+    for (int w0 = 0; w0 < nb; w0 += kTabMax) {
+        const int w1 = min(nb, w0 + kTabMax);
         __syncthreads();   // the previous window's entries are no longer read
-        for (int j = w0 + tid; j < w1; j += kThreads) {
-            const int phys = tables[(size_t)b * max_blocks + j];
-            const bool ok = phys >= 0 && phys < num_blocks;
-            const int left = n - j * kBS;
-            int rel = first - j * kBS;
-            rel = rel < -kBS - 1 ? -kBS - 1 : (rel > kBS ? kBS : rel);
-            S.tile[j - w0] = ok ? (uint32_t)phys * (uint32_t)num_kv_heads + (uint32_t)g
-                                : kNoTile;
-            S.valid[j - w0] = (uint8_t)(ok ? (left < kBS ? left : kBS) : 0);
-            S.rel[j - w0] = (int8_t)rel;
-        }
+        stage_window(S.tile, S.valid, tables, b, g, n, w0, w1, max_blocks, num_blocks,
+                     num_kv_heads, tid);
         __syncthreads();
         // every step issues one block (a zero-record buffer past the window), so the
         // loads in flight never depend on the path taken
@@ -1144,7 +1210,7 @@ __global__ __launch_bounds__(kThreads) void chunk_mfma_kernel(
         if (j >= w1) break;                                                                  \
         {                                                                                    \
             const int vd = S.valid[j - w0];                                                  \
-            int lim = S.rel[j - w0] + ctok + 1;                                              \
+            int lim = lim0 - j * kBS;                                                        \
             lim = lim < 0 ? 0 : (lim > vd ? vd : lim);                                       \
             fold_block<T, KV>(st, R, S.ktile[wave], vd, lim, scale_log2, lane);              \
         }                                                                                    \
@@ -1160,15 +1226,133 @@ __global__ __launch_bounds__(kThreads) void chunk_mfma_kernel(
     __syncthreads();
     int P[kWaves];
     for (int v = 0; v < kWaves; ++v) P[v] = v;
+    constexpr int kCols = kD / 4;
     for (int i = tid; i < ncols * kCols; i += kThreads) {
         const int h = i / kCols, d0 = (i % kCols) * 4;
         float M, Ls;
         float4 o;
         merge_parts<16, kWaves, kWaves>(S.part, P, kWaves, h, d0, M, Ls, o);
         const float inv = Ls > 0.f ? out_scale / Ls : 0.f;
-        store4(out + (size_t)row_of(h) * kD + d0,
+        store4(out + ((size_t)row0 + (h / group) * num_heads + h % group) * kD + d0,
                make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv));
     }
+}
+
+// Register buffers per wave in chunk_tiles_kernel (its loads mostly hit L2).
+constexpr int kChunkRing = 2;
+
+// Long chunks: each wave owns NT consecutive tiles (NT * TQ tokens) and streams every
+// block its last row sees. A block is staged once (K through LDS into operand order, V
+// widened) and folded into all NT tiles; the queries stay in registers. The four waves
+// of a workgroup take consecutive spans and read the same lines close together in time
+// (cached loads: the lines are also reused by the sequence's other workgroups).
+struct ChunkTilesLds {
+    uint32_t tile[kTabMax];
+    uint8_t valid[kTabMax];
+    KTile ktile[kWaves];
+};
+
+template <typename T, typename KV, int NT>
+__global__ __launch_bounds__(kThreads) void chunk_tiles_kernel(
+    T* __restrict__ out, const T* __restrict__ q, const typename KV::Elem* k_cache,
+    const typename KV::Elem* v_cache, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ query_start,
+    float scale_log2, float out_scale, int num_query_tokens, int num_heads, int num_kv_heads,
+    int group, int tq, int max_blocks, int num_blocks) {
+    __shared__ ChunkTilesLds S;
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+    const int r0 = query_start[b], r1 = query_start[b + 1];
+    if (r0 < 0 || r1 < r0 || r1 > num_query_tokens) return;
+    const int T_b = r1 - r0;
+    const int span = NT * tq;                               // tokens per wave
+    const int tok_wg = blockIdx.x * kWaves * span;
+    if (tok_wg >= T_b) return;
+    const int cap = max_blocks * kBS;
+    int n = ctx_lens[b];
+    n = n < 0 ? 0 : (n > cap ? cap : n);
+    const int ntok_wg = min(kWaves * span, T_b - tok_wg);
+    const int last_wg = n - T_b + tok_wg + ntok_wg - 1;   // position of the last row
+    const int nb_wg = last_wg < 0 ? 0 : last_wg / kBS + 1;
+    if (nb_wg == 0) {
+        zero_rows(out, (r0 + tok_wg) * num_heads + g * group, ntok_wg, group, num_heads, tid);
+        return;
+    }
+    const int tok_w = tok_wg + wave * span;                 // this wave's first token
+    const int ntok_w = max(0, min(span, T_b - tok_w));
+    const int last_w = n - T_b + tok_w + ntok_w - 1;
+    const int nb_w = (ntok_w == 0 || last_w < 0) ? 0 : last_w / kBS + 1;
+    const int c = lane & 15, ctok = c / group;
+    const int qlane = (ctok * num_heads + c % group) * kD * (int)sizeof(T);
+    uint4 qv[NT][4];
+    WaveState st[NT];
+    int lim0[NT], row0[NT], ncols[NT], tlast[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int tok0 = tok_w + t * tq;
+        const int ntok = max(0, min(tq, T_b - tok0));
+        row0[t] = (r0 + tok0) * num_heads + g * group;
+        ncols[t] = ntok * group;
+        lim0[t] = n - T_b + tok0 + ctok + 1;
+        tlast[t] = ntok > 0 ? n - T_b + tok0 + ntok - 1 : -1;   // the tile's last position
+        issue_query(qv[t], q, ntok > 0 ? row0[t] : 0,
+                    ntok > 0 ? ((ntok - 1) * num_heads + group) * kD * (int)sizeof(T) : 0,
+                    qlane, lane);
+        reset(st[t]);
+    }
+    for (int w0 = 0; w0 < nb_wg; w0 += kTabMax) {
+        const int w1 = min(nb_wg, w0 + kTabMax);
+        __syncthreads();
+        stage_window(S.tile, S.valid, tables, b, g, n, w0, w1, max_blocks, num_blocks,
+                     num_kv_heads, tid);
+        __syncthreads();
+        const int jend = min(w1, nb_w);
+        auto issue = [&](typename KV::Regs& R, int ji) {
+            KV::template issue<0, false>(R, k_cache, v_cache, q,
+                                         ji < jend ? S.tile[ji - w0] : kNoTile, 0, 0, 0, lane);
+        };
+        // kChunkRing register buffers in fixed roles, the loop unrolled over them. The
+        // loop runs whole rounds: steps past the end fold an empty block (no valid
+        // tokens, zero-record loads: the state does not change). With no branch around
+        // a fold or an exit inside a round, the compiler keeps each buffer's loads where
+        // they are issued and waits for exactly the block being folded.
+        constexpr int kR = kChunkRing;
+        static_assert(kR >= 2 && kR <= 4, "2 to 4 buffers");
+        int j = w0;
+        typename KV::Regs B0, B1, B2, B3;
+        issue(B0, j);
+        issue(B1, j + 1);
+        if constexpr (kR > 2) issue(B2, j + 2);
+        if constexpr (kR > 3) issue(B3, j + 3);
+#define PKV_STEP(R)                                                                          \
+        {                                                                                    \
+            const int vd = j < jend ? (int)S.valid[j - w0] : 0;                              \
+            uint4 ka[4], v[4];                                                               \
+            stage_block<T, KV>(R, S.ktile[wave], vd, lane, ka, v);                           \
+            _Pragma("unroll")                                                                \
+            for (int t = 0; t < NT; ++t) {                                                   \
+                /* a tile that sees nothing of the block skips it (uniform) */               \
+                if (NT > 1 && j * kBS > tlast[t]) continue;                                  \
+                int lim = lim0[t] - j * kBS;                                                 \
+                lim = lim < 0 ? 0 : (lim > vd ? vd : lim);                                   \
+                fold_tile<T>(st[t], ka, qv[t], v, lim, scale_log2, lane);                    \
+            }                                                                                \
+        }                                                                                    \
+        issue(R, j + kR);                                                                    \
+        ++j;
+        if (jend > w0) {
+            do {
+                PKV_STEP(B0)
+                PKV_STEP(B1)
+                if constexpr (kR > 2) { PKV_STEP(B2) }
+                if constexpr (kR > 3) { PKV_STEP(B3) }
+            } while (j < jend);
+        }
+#undef PKV_STEP
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        wave_to_rows(out, row0[t], st[t], lane, ncols[t], group, num_heads, out_scale);
 }
 
 // Scale arguments of a launch: the key scale folds into the softmax scale, the value
@@ -1231,12 +1415,25 @@ int launch_chunk(const ChunkArgs& a, hipStream_t stream) {
     const bool fp8 = a.kv_fp8 != 0;
     const float scale_log2 = a.scale * (fp8 ? a.k_scale : 1.f) * kLog2e;
     const float out_scale = fp8 ? a.v_scale : 1.f;
-    hipLaunchKernelGGL((chunk_mfma_kernel<T, KV>), dim3(tiles, a.num_kv_heads, a.num_seqs),
-                       dim3(kThreads), 0, stream, (T*)a.out, (const T*)a.q,
-                       (const E*)a.k_cache, (const E*)a.v_cache, a.block_tables,
-                       a.context_lens, a.query_start, scale_log2, out_scale,
-                       a.num_query_tokens, a.num_heads, a.num_kv_heads, G, tq, a.max_blocks,
-                       a.num_blocks);
+    // Long chunks (more than four tiles): each wave folds NT tiles per staged
+    // block. Short ones: one tile per workgroup, its waves splitting the blocks.
+    constexpr int NT = 1;
+    if (tiles > kWaves)
+        hipLaunchKernelGGL((chunk_tiles_kernel<T, KV, NT>),
+                           dim3((tiles + kWaves * NT - 1) / (kWaves * NT), a.num_kv_heads,
+                                a.num_seqs),
+                           dim3(kThreads), 0, stream, (T*)a.out, (const T*)a.q,
+                           (const E*)a.k_cache, (const E*)a.v_cache, a.block_tables,
+                           a.context_lens, a.query_start, scale_log2, out_scale,
+                           a.num_query_tokens, a.num_heads, a.num_kv_heads, G, tq, a.max_blocks,
+                           a.num_blocks);
+    else
+        hipLaunchKernelGGL((chunk_split_kernel<T, KV>),
+                           dim3(tiles, a.num_kv_heads, a.num_seqs), dim3(kThreads), 0, stream,
+                           (T*)a.out, (const T*)a.q, (const E*)a.k_cache, (const E*)a.v_cache,
+                           a.block_tables, a.context_lens, a.query_start, scale_log2, out_scale,
+                           a.num_query_tokens, a.num_heads, a.num_kv_heads, G, tq, a.max_blocks,
+                           a.num_blocks);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

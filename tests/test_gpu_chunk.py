@@ -78,6 +78,24 @@ def test_chunk_matches_oracle(dt, group):
     assert torch.equal(out, _run(s)), "deterministic"
 
 
+@pytest.mark.parametrize("dt,group", CASES,
+                         ids=[f"{str(a).split('.')[-1]}-g{b}" for a, b in CASES])
+def test_short_chunks_match_oracle(dt, group):
+    """Chunks of at most four tiles (16 / G tokens each): the launch where a
+    workgroup's waves split the blocks of one tile, as for draft verification. The
+    long-chunk cases above run one tile per wave."""
+    tq = 16 // group
+    tl = [min(x, 4 * tq) for x in TLENS]
+    tl[LENS.index(40)] = min(4 * tq, 45)       # still rows before the context when tq > 10
+    seed = 2150 + group
+    _say(f"short chunks {dt} g={group} seed={seed} tlens={tl}")
+    s = _chunk(seed, LENS, tl, dt, group)
+    assert (s.max_query_len + tq - 1) // tq <= 4
+    out = _run(s)
+    assert _err(out, _want(s)) <= TOL[dt]
+    assert torch.equal(out, _run(s)), "deterministic"
+
+
 @pytest.mark.parametrize("dt,group", [(torch.bfloat16, 4), (torch.float16, 8)],
                          ids=["bf16-g4", "f16-g8"])
 def test_chunk_over_fp8_caches(dt, group):
@@ -86,11 +104,12 @@ def test_chunk_over_fp8_caches(dt, group):
     assert _err(_run(s), _want(s)) <= TOL[dt]
 
 
-def test_chunk_long_context_spans_table_windows():
+@pytest.mark.parametrize("tlens", [[3, 300], [3, 9]], ids=["long-chunks", "short-chunks"])
+def test_chunk_long_context_spans_table_windows(tlens):
     """A context of 2500 blocks (more than one staging window of tables) with a few
-    query tokens, and a whole-prompt chunk of 300 tokens on a shorter one."""
-    _say("chunk long context")
-    s = _chunk(2301, [40000, 700], [3, 300], torch.bfloat16, 4, nkv=1)
+    query tokens, next to a 700-token context, in both launch forms."""
+    _say(f"chunk long context {tlens}")
+    s = _chunk(2301, [40000, 700], tlens, torch.bfloat16, 4, nkv=1)
     assert _err(_run(s), _want(s)) <= TOL[torch.bfloat16]
 
 
