@@ -19,6 +19,12 @@ step does not find the previous step's KV in cache.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
+Workloads with several query tokens per sequence (llama3_8b_verify4: 4 draft tokens
+to verify; prefill_chunk512: 512-token prefill chunks) run reshape_and_cache of the
+chunk tokens, then paged_attention_chunk. A chunk workload whose arithmetic intensity
+exceeds the MI355X ridge point (2.5 PFLOP/s bf16 dense / 8 TB/s) is priced against
+the matrix-core peak instead of HBM.
+
 Prints one JSON line. ``roofline`` covers the decode kernel: algorithmic bytes
 per launch over its mean duration (HIP events on the launch stream) against the
 8 TB/s HBM peak. ``cpu_baseline`` times the CPU oracle on the host cores on the
@@ -38,6 +44,7 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention KV-read HBM GB/s (% of MI355X peak); seqs/s at 8B shape"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def log(msg):
@@ -48,6 +55,7 @@ def build_sets(name, rotate, dev):
     import workloads as W
     builder = W.WORKLOADS[name]
     base = {"tiny_fp32": 1001, "llama3_8b_decode": 1002, "llama3_8b_decode_fp8": 1002,
+            "llama3_8b_verify4": 1002, "prefill_chunk512": 1006,
             "llama_70b_decode": 1003, "long_context_decode": 1004,
             "shared_prefix_cow": 1005}[name]
     sets = []
@@ -59,6 +67,7 @@ def build_sets(name, rotate, dev):
         W.with_append(s, seed=base + 100 * i)
         s.out = torch.empty_like(s.q)
         s.kv = s.kv_bytes()          # computed once: no device sync inside the timed loop
+        s.flops = chunk_flops(s) if s.query_start is not None else 0
         # distinct physical blocks the decode reads (whole blocks), for batches that
         # share prefix blocks between sequences
         bs, tb = s.block_size, s.block_tables.cpu()
@@ -69,6 +78,19 @@ def build_sets(name, rotate, dev):
         sets.append(s)
         log(f"[bench] built {name} set {i}: batch {s.num_seqs}, kv bytes {s.kv_bytes()}")
     return sets
+
+
+def chunk_flops(s):
+    """Algorithmic FLOPs of one chunk attention call: every query row (token, head)
+    does 4 * D per context token it sees (QK and PV multiply-adds)."""
+    qs = s.query_start.cpu().tolist()
+    ctx = s.context_lens.cpu().tolist()
+    seen = 0
+    for b, n in enumerate(ctx):
+        T = qs[b + 1] - qs[b]
+        for j in range(T):
+            seen += max(0, n - T + j + 1)
+    return seen * s.num_heads * 4 * s.head_dim
 
 
 def older_tokens_to_setup(pkv, s):
@@ -112,6 +134,22 @@ def prepare(pkv, s, graphs, fused):
         # sits in a copied block, i.e. when the prefix ends on a block boundary.
         if s.extra.get("prefix_tokens", 0) % s.block_size != 0:
             copy = None
+    if s.query_start is not None:
+        # append the chunk tokens' K/V, then attend with every chunk token
+        s.fused = False
+        if s.kv_scales is not None:
+            def app(s=s):
+                pkv.reshape_and_cache_fp8(s.new_k, s.new_v, s.k_cache, s.v_cache,
+                                          s.slot_mapping, *s.kv_scales)
+        else:
+            app = pkv.PreparedReshapeAndCache(s.new_k, s.new_v, s.k_cache, s.v_cache,
+                                              s.slot_mapping)
+        ks, vs = s.kv_scales if s.kv_scales is not None else (None, None)
+        s.dec = pkv.PreparedChunk(s.out, s.q, s.k_cache, s.v_cache, s.block_tables,
+                                  s.context_lens, s.query_start, s.scale, s.max_query_len,
+                                  k_scale=ks, v_scale=vs)
+        finish_prepare(s, [app, s.dec], graphs)
+        return
     if s.new_k.shape[0] != s.num_seqs:
         older_tokens_to_setup(pkv, s)
     s.fused = fused
@@ -135,7 +173,11 @@ def prepare(pkv, s, graphs, fused):
         calls = [app, s.dec]
     if copy is not None:
         calls.insert(0, copy)
+    finish_prepare(s, calls, graphs)
 
+
+def finish_prepare(s, calls, graphs):
+    """Bind s.run to the step's calls, optionally captured in one HIP graph."""
     def run(calls=calls):
         for c in calls:
             c()
@@ -202,6 +244,41 @@ def cpu_baseline(s, seconds):
             "sample": f"{reps} whole batch(es) of pool set 0 ({s.num_seqs} sequences x "
                       f"{s.num_heads} heads, fp64 walk), {t_total:.1f} s",
             "seqs_per_s": s.num_seqs * reps / t_total}, err
+
+
+def cpu_baseline_chunk(s, seconds, mfma_bound):
+    """Time the fp64 chunk oracle on the host cores, one sequence of set 0 at a time
+    (a bounded sample of the batch), and check those rows against the GPU output."""
+    import numpy as np
+    import torch
+    import oracle
+    qs = s.query_start.cpu()
+    kc, vc = s.k_cache.cpu(), s.v_cache.cpu()
+    tables, ctx = s.block_tables.cpu(), s.context_lens.cpu()
+    got_all = s.out.detach().cpu().double().numpy()
+    t_total, flops, kv, err, done = 0.0, 0, 0, 0.0, 0
+    threads = oracle.max_threads()
+    elt = s.k_cache.element_size()
+    for b in range(s.num_seqs):
+        r0, r1 = int(qs[b]), int(qs[b + 1])
+        n, T = int(ctx[b]), r1 - r0
+        sub_qs = torch.tensor([0, T], dtype=torch.int32)
+        t0 = time.perf_counter()
+        want = oracle.paged_attention_chunk(s.q[r0:r1].cpu(), kc, vc, tables[b:b + 1],
+                                            ctx[b:b + 1], sub_qs, s.scale,
+                                            kv_scales=s.kv_scales, threads=threads)
+        t_total += time.perf_counter() - t0
+        err = max(err, float(np.max(np.abs(got_all[r0:r1] - want))) if T else 0.0)
+        flops += sum(max(0, n - T + j + 1) for j in range(T)) * s.num_heads * 4 * s.head_dim
+        kv += n * s.num_kv_heads * 2 * s.head_dim * elt
+        done += 1
+        if t_total >= seconds:
+            break
+    value = flops / t_total / 1e12 if mfma_bound else kv / t_total / 1e9
+    return {"value": value, "unit": "TFLOP/s" if mfma_bound else "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {s.num_seqs} sequences of pool set 0 (all their query "
+                      f"rows, fp64 walk), {t_total:.1f} s"}, err
 
 
 CALIB_PAIRS, CALIB_BLOCK_BYTES = 4096, 8 * 16 * 128 * 2
@@ -297,13 +374,21 @@ def main():
     dec_us = time_decode_kernel(sets, graphs=args.graphs)
     kv_per_launch = sum(s.kv for s in sets) / len(sets)
     achieved = kv_per_launch / (dec_us * 1e-6) / 1e9
+    chunk = s0.query_start is not None
+    flops_per_launch = sum(s.flops for s in sets) / len(sets)
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)   # FLOP per byte
+    mfma_bound = chunk and flops_per_launch / kv_per_launch > ridge
+    tflops = flops_per_launch / (dec_us * 1e-6) / 1e12 if chunk else None
 
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: oracle on the host cores")
         # the last step that used set 0 left its output in set 0's buffer
-        cpu, parity = cpu_baseline(s0, args.cpu_seconds)
+        if chunk:
+            cpu, parity = cpu_baseline_chunk(s0, args.cpu_seconds, mfma_bound)
+        else:
+            cpu, parity = cpu_baseline(s0, args.cpu_seconds)
 
     if args.calibrate:
         calibrate(pkv, dev)
@@ -342,22 +427,29 @@ def main():
             "kv_unique_block_bytes_per_step": int(sum(x.kv_unique for x in sets) / len(sets)),
             "partition_size": s0.partition_size,
             "pool_sets": len(sets),
-            "step": ("copy_blocks(K, V) + " if s0.copy_pairs is not None and
-                     s0.extra.get("prefix_tokens", 0) % s0.block_size == 0 else "") +
-                    ("paged_attention_decode_append (new token written at each context end, "
-                     "then attended; one kernel)" if s0.fused else
-                     "reshape_and_cache(new token) + paged_attention_decode"),
+            "step": ("reshape_and_cache(chunk tokens) + paged_attention_chunk "
+                     f"({s0.max_query_len} query tokens per sequence, causal)" if chunk else
+                     ("copy_blocks(K, V) + " if s0.copy_pairs is not None and
+                      s0.extra.get("prefix_tokens", 0) % s0.block_size == 0 else "") +
+                     ("paged_attention_decode_append (new token written at each context "
+                      "end, then attended; one kernel)" if s0.fused else
+                      "reshape_and_cache(new token) + paged_attention_decode")),
+            "query_tokens_per_step": int(s0.q.shape[0]),
+            "flops_per_step": int(flops_per_launch) if chunk else None,
+            "tflops": round(tflops, 2) if chunk else None,
             "launch": "one hip graph per step" if args.graphs else "direct (one call per step)",
             "wall_s_timed": round(wall, 4),
         },
         "roofline": {
-            "bound": "hbm",
-            "kernel": ("paged_attention_decode_append" if s0.fused
+            "bound": "mfma" if mfma_bound else "hbm",
+            "kernel": ("paged_attention_chunk" if chunk else
+                       "paged_attention_decode_append" if s0.fused
                        else "paged_attention_decode") + fp8,
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "achieved": round(tflops if mfma_bound else achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS if mfma_bound
+                          else achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_per_launch(s0.name),
             "launch_us_mean": round(dec_us, 3),
             "launch_timing": "back-to-back decode launches over the pool sets, HIP events",

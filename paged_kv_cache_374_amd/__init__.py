@@ -336,6 +336,36 @@ def paged_attention_chunk(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Ten
     return out
 
 
+class PreparedChunk:
+    """paged_attention_chunk validated once for a fixed set of tensors (serving loops,
+    HIP graph capture); calling it enqueues the kernel on ``stream`` or the current
+    stream of the tensors' device."""
+
+    def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                 scale, max_query_len: int, k_scale: Optional[float] = None,
+                 v_scale: Optional[float] = None):
+        fp8 = k_cache.dtype == torch.uint8
+        self._args = _chunk_args(out, q, k_cache, v_cache, block_tables, context_lens,
+                                 query_start, scale, max_query_len, fp8)
+        self._name = "pkv_paged_attention_chunk"
+        if fp8:
+            if k_scale is None or v_scale is None:
+                raise ValueError("8-bit caches need k_scale and v_scale")
+            self._args = _with_scales(self._args, 4, k_scale, v_scale)
+            self._name += "_fp8"
+        self._fn = getattr(load(), self._name)
+        self._device = q.device
+        self.out = out
+        self._keep = (out, q, k_cache, v_cache, block_tables, context_lens, query_start)
+
+    def __call__(self, stream: Optional[int] = None) -> torch.Tensor:
+        st = _stream(self._device) if stream is None else stream
+        rc = self._fn(*self._args, st)
+        if rc != 0:
+            raise PagedKVError(rc, self._name)
+        return self.out
+
+
 class PreparedDecode:
     """A decode call validated once for a fixed set of tensors, for loops that run
     it many times (serving steps, HIP graph capture). It owns a zero-initialised

@@ -167,3 +167,24 @@ def test_chunk_rejects_unsupported_shapes():
     with pytest.raises(ValueError):            # query_start of the wrong length
         pkv.paged_attention_chunk(torch.empty_like(s.q), s.q, s.k_cache, s.v_cache,
                                   s.block_tables, s.context_lens, s.query_start[:-1], s.scale)
+
+
+def test_prepared_chunk_in_graph_replays():
+    """The prepared chunk call captured in a HIP graph, replayed with new queries, matches
+    eager calls every time."""
+    _say("prepared chunk graph replays")
+    s = _chunk(2701, [300, 41, 1000, 17], [33, 41, 6, 2], torch.bfloat16, 4)
+    out = torch.empty_like(s.q)
+    step = pkv.PreparedChunk(out, s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens,
+                             s.query_start, s.scale, s.max_query_len)
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    gen = torch.Generator(device=DEV).manual_seed(4)
+    for r in range(3):
+        s.q.copy_(torch.randn(s.q.shape, generator=gen, device=DEV).to(s.q.dtype))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, _run(s)), f"replay {r}"

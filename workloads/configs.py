@@ -306,14 +306,6 @@ def llama3_8b_decode_fp8(seed: int = 1002, device="cpu", gen_device=None,
     return with_fp8(llama3_8b_decode(seed, device, gen_device, materialize))
 
 
-WORKLOADS = {
-    "tiny_fp32": tiny_fp32,
-    "llama3_8b_decode": llama3_8b_decode,
-    "llama3_8b_decode_fp8": llama3_8b_decode_fp8,
-    "llama_70b_decode": llama_70b_decode,
-    "long_context_decode": long_context_decode,
-    "shared_prefix_cow": shared_prefix_cow,
-}
 
 
 FP8_SCALES = (0.0137, 0.0211)
@@ -351,8 +343,47 @@ def with_chunk(step: DecodeStep, query_lens: List[int], seed: int = 0) -> Decode
     step.q = _normal((qs[-1], step.num_heads, step.head_dim), step.dtype, gen, dev)
     step.query_start = torch.tensor(qs, dtype=torch.int32).to(dev)
     step.max_query_len = max(query_lens) if query_lens else 0
+    # the chunk tokens' own K/V rows and slots (positions n - T .. n - 1), for a step
+    # that appends them before attending
+    tables = step.block_tables.to("cpu")
+    bs = step.block_size
+    slots = []
+    for b, (n, T) in enumerate(zip(step.context_lens.to("cpu").tolist(), query_lens)):
+        for pos in range(n - T, n):
+            slots.append(int(tables[b, pos // bs]) * bs + pos % bs if pos >= 0 else -1)
+    shape = (qs[-1], step.num_kv_heads, step.head_dim)
+    step.new_k = _normal(shape, step.dtype, gen, dev)
+    step.new_v = _normal(shape, step.dtype, gen, dev)
+    step.slot_mapping = torch.tensor(slots, dtype=torch.int64).to(dev)
     step.name = step.name + "_chunk"
     return step
+
+
+def llama3_8b_verify4(seed: int = 1002, device="cpu", gen_device=None,
+                      materialize: bool = True) -> DecodeStep:
+    """Draft verification on the Llama-3-8B-shaped batch: each sequence's last 4
+    context tokens are queries (speculative decoding checks 4 draft tokens at once)."""
+    s = llama3_8b_decode(seed, device, gen_device, materialize)
+    s = with_chunk(s, [4] * s.num_seqs, seed=seed)
+    s.name = "llama3_8b_verify4"
+    return s
+
+
+def prefill_chunk512(seed: int = 1006, device="cpu", gen_device=None,
+                     materialize: bool = True) -> DecodeStep:
+    """Chunked prefill: 8 sequences, 32/8 heads, D 128, bs 16, bf16; contexts
+    U[1024, 4096] whose last 512 tokens are the chunk being prefilled (each attends the
+    earlier tokens and the chunk up to itself). Pool = 1.1 x the blocks in use."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    ctx = torch.randint(1024, 4097, (8,), generator=g).tolist()
+    need = sum(blocks_needed(n, 16) for n in ctx)
+    nb = int(math.ceil(1.1 * need))
+    width = max(blocks_needed(n, 16) for n in ctx)
+    s = _scattered_batch("prefill_chunk512", seed, ctx, nb, 32, 8, 128, 16, width,
+                         torch.bfloat16, device, gen_device or device, materialize)
+    s = with_chunk(s, [512] * len(ctx), seed=seed)
+    s.name = "prefill_chunk512"
+    return s
 
 
 def with_append(step: DecodeStep, seed: int = 0) -> DecodeStep:
@@ -380,3 +411,15 @@ def with_append(step: DecodeStep, seed: int = 0) -> DecodeStep:
     step.new_v = _normal(shape, step.dtype, gen, dev)
     step.slot_mapping = torch.tensor(slots, dtype=torch.int64).to(dev)
     return step
+
+
+WORKLOADS = {
+    "tiny_fp32": tiny_fp32,
+    "llama3_8b_decode": llama3_8b_decode,
+    "llama3_8b_decode_fp8": llama3_8b_decode_fp8,
+    "llama3_8b_verify4": llama3_8b_verify4,
+    "prefill_chunk512": prefill_chunk512,
+    "llama_70b_decode": llama_70b_decode,
+    "long_context_decode": long_context_decode,
+    "shared_prefix_cow": shared_prefix_cow,
+}
