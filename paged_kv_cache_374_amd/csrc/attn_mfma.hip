@@ -1258,15 +1258,29 @@ __global__ __launch_bounds__(kThreads) void chunk_tiles_kernel(
     const typename KV::Elem* v_cache, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ query_start,
     float scale_log2, float out_scale, int num_query_tokens, int num_heads, int num_kv_heads,
-    int group, int tq, int max_blocks, int num_blocks) {
+    int group, int tq, int max_blocks, int num_blocks, int groups) {
     __shared__ ChunkTilesLds S;
-    const int g = blockIdx.y, b = blockIdx.z;
+    // One-dimensional grid over (sequence, KV head) pairs times span groups. The
+    // dispatcher deals workgroups round-robin over the 8 XCDs (workgroup i to XCD i % 8).
+    // Pair p goes to XCD p % 8 with all its span groups, so the workgroups that read the
+    // same lines share one L2, and every XCD gets a mix of sequences.
+    const int pairs = gridDim.x / groups;                   // num_seqs * Hkv
+    int pair, sg;
+    if (pairs % 8 == 0) {
+        const int x = blockIdx.x % 8, k = blockIdx.x / 8;
+        pair = x + 8 * (k / groups);
+        sg = k % groups;
+    } else {
+        pair = blockIdx.x / groups;
+        sg = blockIdx.x % groups;
+    }
+    const int g = pair % num_kv_heads, b = pair / num_kv_heads;
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int r0 = query_start[b], r1 = query_start[b + 1];
     if (r0 < 0 || r1 < r0 || r1 > num_query_tokens) return;
     const int T_b = r1 - r0;
     const int span = NT * tq;                               // tokens per wave
-    const int tok_wg = blockIdx.x * kWaves * span;
+    const int tok_wg = sg * kWaves * span;
     if (tok_wg >= T_b) return;
     const int cap = max_blocks * kBS;
     int n = ctx_lens[b];
@@ -1419,14 +1433,18 @@ int launch_chunk(const ChunkArgs& a, hipStream_t stream) {
     // block. Short ones: one tile per workgroup, its waves splitting the blocks.
     constexpr int NT = 1;
     if (tiles > kWaves)
-        hipLaunchKernelGGL((chunk_tiles_kernel<T, KV, NT>),
-                           dim3((tiles + kWaves * NT - 1) / (kWaves * NT), a.num_kv_heads,
-                                a.num_seqs),
+    {
+        // one-dimensional grid of (span group, KV head, sequence) items
+        const int groups = (tiles + kWaves * NT - 1) / (kWaves * NT);
+        const long long items = (long long)groups * a.num_kv_heads * a.num_seqs;
+        if (items > 0x7fffffffLL) return -1;
+        hipLaunchKernelGGL((chunk_tiles_kernel<T, KV, NT>), dim3((unsigned)items),
                            dim3(kThreads), 0, stream, (T*)a.out, (const T*)a.q,
                            (const E*)a.k_cache, (const E*)a.v_cache, a.block_tables,
                            a.context_lens, a.query_start, scale_log2, out_scale,
                            a.num_query_tokens, a.num_heads, a.num_kv_heads, G, tq, a.max_blocks,
-                           a.num_blocks);
+                           a.num_blocks, groups);
+    }
     else
         hipLaunchKernelGGL((chunk_split_kernel<T, KV>),
                            dim3(tiles, a.num_kv_heads, a.num_seqs), dim3(kThreads), 0, stream,
