@@ -74,6 +74,8 @@ def _bind(lib):
     lib.oracle_reshape_and_cache_fp8.restype = _I
     lib.oracle_reshape_and_cache_fp8.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                                  ctypes.c_float, ctypes.c_float]
+    lib.oracle_swap_blocks.restype = _I
+    lib.oracle_swap_blocks.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_long]
     lib.oracle_max_threads.restype = _I
     return lib
 
@@ -396,3 +398,23 @@ def copy_blocks(cache: torch.Tensor, pairs: torch.Tensor, lib=None) -> torch.Ten
     if rc != 0:
         raise ValueError(f"oracle_copy_blocks rejected its inputs ({rc})")
     return c
+
+
+def swap_blocks(dst_pool: torch.Tensor, src_pool: torch.Tensor, pairs: torch.Tensor,
+                lib=None) -> torch.Tensor:
+    """Expected destination pool after copying block src of src_pool over block dst of
+    dst_pool for each (src, dst) pair (a new CPU tensor). The pools share the block
+    layout [blocks, ...] and dtype; their block counts may differ."""
+    lib = lib or _load()
+    if dst_pool.dtype != src_pool.dtype or dst_pool.shape[1:] != src_pool.shape[1:]:
+        raise ValueError("pools must share dtype and block layout")
+    d = dst_pool.detach().to("cpu").clone().contiguous()
+    s = src_pool.detach().to("cpu").contiguous()
+    da, sa = _raw(d), _raw(s)
+    p = np.ascontiguousarray(pairs.to("cpu", torch.int32).numpy().reshape(-1, 2))
+    block_bytes = d[0].numel() * d.element_size() if d.shape[0] else 0
+    rc = lib.oracle_swap_blocks(_ptr(da), _ptr(sa), _ptr(p), p.shape[0], s.shape[0], d.shape[0],
+                                block_bytes)
+    if rc != 0:
+        raise ValueError(f"oracle_swap_blocks rejected its inputs ({rc})")
+    return d

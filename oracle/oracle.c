@@ -369,6 +369,24 @@ int oracle_copy_blocks(void* cache, const int32_t* pairs, int n, int num_blocks,
     return 0;
 }
 
+/*
+ * Swap between two pools of the same block layout (a GPU pool and a host pool): each
+ * (src, dst) pair copies block src of src_pool over block dst of dst_pool
+ * ([P2] "BlockAllocator 源码核心：vLLM 的显存管理心脏", CpuGpuBlockAllocator: when
+ * GPU blocks run short, cold blocks move to CPU memory and move back when they are
+ * needed again). Returns 0, or -2 for an index outside its pool.
+ */
+int oracle_swap_blocks(void* dst_pool, const void* src_pool, const int32_t* pairs, int n,
+                       int num_src_blocks, int num_dst_blocks, long block_bytes) {
+    for (int i = 0; i < n; ++i) {
+        const int from = pairs[2 * i], to = pairs[2 * i + 1];
+        if (from < 0 || from >= num_src_blocks || to < 0 || to >= num_dst_blocks) return -2;
+        memcpy((char*)dst_pool + (size_t)to * block_bytes,
+               (const char*)src_pool + (size_t)from * block_bytes, (size_t)block_bytes);
+    }
+    return 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

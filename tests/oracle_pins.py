@@ -642,10 +642,44 @@ def pin_chunk_last_row_is_decode(lib):
         _close(got[last.numpy()], want, 0.0, f"last rows {dt}")
 
 
+# ----------------------------------------------------------------------------- swap
+def pin_swap_roundtrip(lib):
+    """Swapping blocks out to a host pool and back in to other GPU blocks: the host pool
+    receives exactly torch's indexed copy of the source blocks, every other block of
+    both pools is unchanged, and the blocks swapped back in equal the originals (bf16
+    bit patterns, including NaN payloads, and 8-bit codes)."""
+    g = torch.Generator().manual_seed(91)
+    for dt, shape in ((torch.bfloat16, (20, 2, 4, 8)), (torch.uint8, (13, 3, 16, 16))):
+        if dt == torch.uint8:
+            gpu = torch.randint(0, 256, shape, generator=g, dtype=torch.uint8)
+        else:
+            gpu = torch.randn(shape, generator=g).to(dt)
+            gpu.view(torch.int16)[3, 0, 0, 0] = 0x7FC1      # a NaN payload travels as bits
+        host = torch.zeros((7,) + shape[1:], dtype=dt)
+        out_pairs = torch.tensor([[3, 0], [11, 4], [5, 6], [0, 2]], dtype=torch.int32)
+        host2 = oracle.swap_blocks(host, gpu, out_pairs, lib=lib)
+        want = host.clone()
+        want[out_pairs[:, 1].long()] = gpu[out_pairs[:, 0].long()]
+        assert torch.equal(host2.view(torch.uint8), want.view(torch.uint8)), f"swap out {dt}"
+        in_pairs = torch.tensor([[0, 9], [4, 1], [6, 12], [2, 7]], dtype=torch.int32)
+        gpu2 = oracle.swap_blocks(gpu, host2, in_pairs, lib=lib)
+        for (src, mid), (_, back) in zip(out_pairs.tolist(), in_pairs.tolist()):
+            assert torch.equal(gpu2[back].view(torch.uint8), gpu[src].view(torch.uint8))
+        keep = torch.ones(shape[0], dtype=torch.bool)
+        keep[in_pairs[:, 1].long()] = False
+        assert torch.equal(gpu2[keep].view(torch.uint8), gpu[keep].view(torch.uint8))
+    bad = torch.tensor([[0, 7]], dtype=torch.int32)                 # outside the host pool
+    try:
+        oracle.swap_blocks(torch.zeros(7, 4), torch.zeros(9, 4), bad, lib=lib)
+        raise AssertionError("an index outside the pool must be rejected")
+    except ValueError:
+        pass
+
+
 ALL_PINS = [pin_decoders, pin_sdpa_library, pin_dense_bruteforce, pin_worked_example,
             pin_two_token_closed_form, pin_context_one, pin_uniform_scores, pin_zero_context,
             pin_placement_permutation, pin_gqa_equals_repeated_mha, pin_stale_slots_unread,
             pin_linearity_in_values, pin_append_roundtrip, pin_copy_on_write,
             pin_decode_step_slots, pin_fp8_decode, pin_fp8_quantize, pin_fp8_attention,
             pin_fp8_append, pin_chunk_causal_sdpa, pin_chunk_dense, pin_chunk_causality,
-            pin_chunk_last_row_is_decode]
+            pin_chunk_last_row_is_decode, pin_swap_roundtrip]

@@ -49,6 +49,12 @@ MUTANTS = {
     "chunk_query_row_of_sequence": ("((size_t)r * Hq + h) * D", "((size_t)b * Hq + h) * D"),
     "chunk_row_owner_wrong": ("while (query_start[b + 1] <= r) ++b;",
                               "while (query_start[b + 1] < r) ++b;"),
+    "swap_pools_exchanged": ("memcpy((char*)dst_pool + (size_t)to * block_bytes,\n"
+                             "               (const char*)src_pool + (size_t)from * block_bytes,",
+                             "memcpy((char*)dst_pool + (size_t)from * block_bytes,\n"
+                             "               (const char*)src_pool + (size_t)to * block_bytes,"),
+    "swap_first_pair_skipped": ("for (int i = 0; i < n; ++i) {\n        const int from",
+                                "for (int i = 1; i < n; ++i) {\n        const int from"),
     "fp8_bias_wrong": ("expo - 10", "expo - 9"),
     "fp8_subnormal_step_wrong": ("ldexp((double)mant, -9)", "ldexp((double)mant, -10)"),
     "fp8_ties_away_from_zero": ("(int)nearbyint((2.0 * f - 1.0) * 8.0)",
