@@ -6,8 +6,10 @@
  *   pkv_reshape_and_cache       write each new token's K/V into its slot
  *   pkv_copy_blocks             copy whole blocks (copy-on-write)
  * plus pkv_paged_attention_decode_append (a decode step's append and attention in
- * one call), the same calls over 8-bit (FP8 E4M3) caches, workspace sizing and
- * initialisation, version and error strings.
+ * one call), the same calls over 8-bit (FP8 E4M3) caches, attention of several query
+ * tokens per sequence (pkv_paged_attention_chunk: prefill chunks, draft
+ * verification), block swaps between GPU and pinned host pools (pkv_swap_blocks),
+ * workspace sizing and initialisation, version and error strings.
  *
  * Pages cited (titles as published):
  *   [P1] "vLLM 源码解析：PagedAttention 如何让大模型推理提速 10 倍"
@@ -16,8 +18,9 @@
  *   [P3] "论文专题讲解：vLLM / PagedAttention：为什么 KV cache 需要分页管理"
  *
  * Common rules for every call:
- *  - All array pointers are DEVICE memory owned by the caller; the library never
- *    allocates, frees or retains them. Arrays are dense, row-major, contiguous.
+ *  - All array pointers are DEVICE memory owned by the caller (pkv_swap_blocks also
+ *    takes pinned host memory); the library never allocates, frees or retains them.
+ *    Arrays are dense, row-major, contiguous.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and the
  *    call returns before it completes. Nothing synchronises inside a call unless
  *    the environment variable PKV_VALIDATE=1 is set (see below).
@@ -315,6 +318,30 @@ int pkv_reshape_and_cache(const void* key, const void* value, void* k_cache, voi
  */
 int pkv_copy_blocks(void* cache, const int32_t* src_dst_pairs, int num_pairs, int num_blocks,
                     size_t block_bytes, pkv_stream_t stream);
+
+/*
+ * Whole-block copies between two pools of the same block layout, for swapping blocks
+ * between GPU memory and host memory ([P2] section "BlockAllocator 源码核心：vLLM 的
+ * 显存管理心脏": the CPU/GPU two-tier allocator moves cold blocks to CPU memory when GPU
+ * blocks run short and back when they are needed). Swap-out passes the GPU pool as
+ * src_pool and the host pool as dst_pool; swap-in the reverse. Two device pools work
+ * too.
+ *
+ * dst_pool, src_pool  num_dst_blocks / num_src_blocks blocks of block_bytes bytes. Each
+ *               is device memory or PINNED host memory (hipHostMalloc, or a torch tensor
+ *               made with pin_memory=True); the kernel reads and writes host memory
+ *               directly through its device mapping, one launch for all pairs. Any other
+ *               pointer (pageable host memory) returns PKV_E_UNSUPPORTED before anything
+ *               is enqueued. Pools must not overlap.
+ * src_dst_pairs int32 [num_pairs, 2] of (source block, destination block); device or
+ *               pinned host memory. Destinations must be distinct (caller contract;
+ *               checked under PKV_VALIDATE=1, like the ranges).
+ * block_bytes   a multiple of 4 (16 for the vectorised path); num_pairs may be 0.
+ * Bit-exact. Pairs with an index outside its pool are skipped.
+ */
+int pkv_swap_blocks(void* dst_pool, const void* src_pool, const int32_t* src_dst_pairs,
+                    int num_pairs, int num_src_blocks, int num_dst_blocks, size_t block_bytes,
+                    pkv_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -88,6 +88,8 @@ def load():
     lib.pkv_reshape_and_cache_fp8.argtypes = [_P] * 5 + [_F, _F] + [_I] * 6 + [_P]
     lib.pkv_reshape_and_cache.restype = _I
     lib.pkv_reshape_and_cache.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
+    lib.pkv_swap_blocks.restype = _I
+    lib.pkv_swap_blocks.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_size_t, _P]
     lib.pkv_copy_blocks.restype = _I
     lib.pkv_copy_blocks.argtypes = [_P, _P, _I, _I, ctypes.c_size_t, _P]
     _lib = lib
@@ -516,3 +518,53 @@ class PreparedCopyBlocks:
             rc = self._fn(*a, st)
             if rc != 0:
                 raise PagedKVError(rc, "pkv_copy_blocks")
+
+
+def _swap_args(dst_pool, src_pool, src_dst_pairs):
+    pools = (("dst_pool", dst_pool), ("src_pool", src_pool))
+    dev = [t.device for _, t in pools if t.is_cuda]
+    if not dev:
+        raise ValueError("at least one pool must be on the GPU")
+    for name, t in pools:
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if not t.is_cuda and not t.is_pinned():
+            raise ValueError(f"{name} is host memory that is not pinned (use pin_memory=True)")
+        if t.is_cuda and t.device != dev[0]:
+            raise ValueError("device pools must be on one device")
+    if dst_pool.dtype != src_pool.dtype or dst_pool.shape[1:] != src_pool.shape[1:]:
+        raise ValueError("pools must share dtype and block layout [blocks, ...]")
+    _gpu(src_dst_pairs, "src_dst_pairs", torch.int32)
+    if src_dst_pairs.device != dev[0]:
+        raise ValueError("src_dst_pairs must be on the pools' device")
+    p = src_dst_pairs.reshape(-1, 2)
+    bb = dst_pool[0].numel() * dst_pool.element_size() if dst_pool.shape[0] else \
+        int(torch.tensor(dst_pool.shape[1:]).prod()) * dst_pool.element_size()
+    return (dst_pool.data_ptr(), src_pool.data_ptr(), p.data_ptr(), p.shape[0],
+            src_pool.shape[0], dst_pool.shape[0], bb), dev[0]
+
+
+def swap_blocks(dst_pool: torch.Tensor, src_pool: torch.Tensor,
+                src_dst_pairs: torch.Tensor) -> None:
+    """Copy block src of src_pool over block dst of dst_pool for each (src, dst) pair
+    (int32 [n, 2] on the GPU). One pool is a GPU tensor, the other a GPU tensor or a
+    pinned CPU tensor (pin_memory=True) of the same dtype and block layout: swap-out
+    passes the host pool as dst_pool, swap-in as src_pool. Enqueued on the GPU's
+    current stream; host memory is complete once that stream is synchronised."""
+    args, dev = _swap_args(dst_pool, src_pool, src_dst_pairs)
+    _check(load().pkv_swap_blocks(*args, _stream(dev)), "pkv_swap_blocks")
+
+
+class PreparedSwapBlocks:
+    """swap_blocks validated once for a fixed set of tensors."""
+
+    def __init__(self, dst_pool, src_pool, src_dst_pairs):
+        self._args, self._device = _swap_args(dst_pool, src_pool, src_dst_pairs)
+        self._fn = load().pkv_swap_blocks
+        self._keep = (dst_pool, src_pool, src_dst_pairs)
+
+    def __call__(self, stream: Optional[int] = None) -> None:
+        st = _stream(self._device) if stream is None else stream
+        rc = self._fn(*self._args, st)
+        if rc != 0:
+            raise PagedKVError(rc, "pkv_swap_blocks")

@@ -133,6 +133,38 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(Chunk* __restrict__ ca
     }
 }
 
+// Whole-block copies from one pool to another of the same block layout: a device pool
+// and a pinned host pool mapped into the device's address space, in either direction,
+// or two device pools ([P2] section "BlockAllocator 源码核心：vLLM 的显存管理心脏": the
+// CPU/GPU two-tier allocator moves cold blocks to host memory and back). One block pair
+// per grid row. Each thread issues U loads before its U stores, so every wave keeps
+// U KiB in flight: reads of host memory cross the host link with microsecond latency.
+template <typename Chunk, int U>
+__global__ __launch_bounds__(256) void swap_blocks_kernel(Chunk* __restrict__ dst,
+                                                          const Chunk* __restrict__ src,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int num_pairs, int num_src,
+                                                          int num_dst, int64_t block_chunks) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int pi = blockIdx.y; pi < num_pairs; pi += gridDim.y) {
+        const int from = pairs[2 * pi];
+        const int to = pairs[2 * pi + 1];
+        if (from < 0 || from >= num_src || to < 0 || to >= num_dst) continue;
+        const Chunk* s = src + (int64_t)from * block_chunks;
+        Chunk* d = dst + (int64_t)to * block_chunks;
+        for (int64_t c0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c0 < block_chunks;
+             c0 += stride * U) {
+            Chunk v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (c0 + u * stride < block_chunks) v[u] = s[c0 + u * stride];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (c0 + u * stride < block_chunks) d[c0 + u * stride] = v[u];
+        }
+    }
+}
+
 int grid_for(int64_t items, int threads, int cap) {
     int64_t g = (items + threads - 1) / threads;
     if (g < 1) g = 1;
@@ -234,6 +266,26 @@ int launch_copy_blocks(void* cache, const int32_t* pairs, int num_pairs, int num
         hipLaunchKernelGGL(copy_blocks_kernel<uint32_t>, dim3(grid_for(chunks, 256, 64), gy),
                            dim3(256), 0, stream, (uint32_t*)cache, pairs, num_pairs, num_blocks,
                            chunks);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_swap_blocks(void* dst, const void* src, const int32_t* pairs, int num_pairs,
+                       int num_src_blocks, int num_dst_blocks, size_t block_bytes,
+                       hipStream_t stream) {
+    constexpr int U = 8;
+    const int gy = num_pairs > 65535 ? 65535 : num_pairs;
+    if (block_bytes % 16 == 0) {
+        const int64_t chunks = (int64_t)(block_bytes / 16);
+        hipLaunchKernelGGL((swap_blocks_kernel<uint4, U>), dim3(grid_for(chunks, 256 * U, 64), gy),
+                           dim3(256), 0, stream, (uint4*)dst, (const uint4*)src, pairs,
+                           num_pairs, num_src_blocks, num_dst_blocks, chunks);
+    } else {
+        const int64_t chunks = (int64_t)(block_bytes / 4);
+        hipLaunchKernelGGL((swap_blocks_kernel<uint32_t, U>),
+                           dim3(grid_for(chunks, 256 * U, 64), gy), dim3(256), 0, stream,
+                           (uint32_t*)dst, (const uint32_t*)src, pairs, num_pairs,
+                           num_src_blocks, num_dst_blocks, chunks);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

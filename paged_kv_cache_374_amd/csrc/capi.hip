@@ -42,6 +42,24 @@ bool fetch(std::vector<T>& host, const T* dev, size_t n, hipStream_t stream) {
     return hipStreamSynchronize(stream) == hipSuccess;
 }
 
+// The address at which the current device reaches `p`: p itself for device memory, the
+// device mapping for pinned host memory. nullptr for memory the device cannot reach
+// (pageable host memory, unknown pointers); the failed query's error is cleared so a
+// later launch check does not see it.
+const void* device_view(const void* p) {
+    hipPointerAttribute_t attr{};
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) return p;
+    if (attr.type == hipMemoryTypeHost && attr.devicePointer) {
+        if (!attr.hostPointer) return attr.devicePointer;
+        return (const char*)attr.devicePointer + ((const char*)p - (const char*)attr.hostPointer);
+    }
+    return nullptr;
+}
+
 // A cache scale must be a positive, finite binary32 value.
 bool scale_ok(float s) { return s > 0.f && s <= 3.4028235e38f; }
 
@@ -355,6 +373,36 @@ int pkv_copy_blocks(void* cache, const int32_t* src_dst_pairs, int num_pairs, in
     }
     return pkv::launch_copy_blocks(cache, src_dst_pairs, num_pairs, num_blocks, block_bytes,
                                    st) == 0
+               ? PKV_OK
+               : PKV_E_LAUNCH;
+}
+
+int pkv_swap_blocks(void* dst_pool, const void* src_pool, const int32_t* src_dst_pairs,
+                    int num_pairs, int num_src_blocks, int num_dst_blocks, size_t block_bytes,
+                    pkv_stream_t stream) {
+    if (num_pairs < 0 || num_src_blocks < 0 || num_dst_blocks < 0) return PKV_E_SHAPE;
+    if (block_bytes % 4 != 0) return PKV_E_UNSUPPORTED;
+    if (num_pairs == 0 || block_bytes == 0) return PKV_OK;
+    if (!dst_pool || !src_pool || !src_dst_pairs) return PKV_E_NULL;
+    // Both pools must be reachable from the device: device memory, or pinned host memory
+    // through its device mapping. Anything else is refused before any launch.
+    void* dst = const_cast<void*>(device_view(dst_pool));
+    const void* src = device_view(src_pool);
+    if (!dst || !src || !device_view(src_dst_pairs)) return PKV_E_UNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_enabled()) {
+        std::vector<int32_t> hp;
+        if (!fetch(hp, src_dst_pairs, (size_t)num_pairs * 2, st)) return PKV_E_LAUNCH;
+        std::vector<char> seen((size_t)num_dst_blocks, 0);
+        for (int i = 0; i < num_pairs; ++i) {
+            const int32_t a = hp[2 * i], b = hp[2 * i + 1];
+            if (a < 0 || a >= num_src_blocks || b < 0 || b >= num_dst_blocks || seen[b])
+                return PKV_E_INDEX;
+            seen[b] = 1;
+        }
+    }
+    return pkv::launch_swap_blocks(dst, src, src_dst_pairs, num_pairs, num_src_blocks,
+                                   num_dst_blocks, block_bytes, st) == 0
                ? PKV_OK
                : PKV_E_LAUNCH;
 }

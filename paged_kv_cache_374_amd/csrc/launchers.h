@@ -18,6 +18,12 @@ int launch_reshape_and_cache(const void* key, const void* value, void* k_cache, 
 int launch_copy_blocks(void* cache, const int32_t* pairs, int num_pairs, int num_blocks,
                        size_t block_bytes, hipStream_t stream);
 
+// Whole-block copies between two pools of one block layout; dst and src are addresses
+// the device can dereference (device memory, or pinned host memory's device mapping).
+int launch_swap_blocks(void* dst, const void* src, const int32_t* pairs, int num_pairs,
+                       int num_src_blocks, int num_dst_blocks, size_t block_bytes,
+                       hipStream_t stream);
+
 int launch_zero(void* p, size_t bytes, hipStream_t stream);
 
 struct DecodeArgs {

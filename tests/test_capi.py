@@ -28,6 +28,7 @@ def test_header_declares_the_entry_points():
               "pkv_paged_attention_decode_fp8", "pkv_paged_attention_decode_append_fp8",
               "pkv_paged_attention_chunk", "pkv_paged_attention_chunk_fp8",
               "pkv_reshape_and_cache", "pkv_reshape_and_cache_fp8", "pkv_copy_blocks",
+              "pkv_swap_blocks",
               "pkv_paged_attention_workspace_size", "pkv_workspace_init", "pkv_version",
               "pkv_strerror"):
         assert n in names
@@ -182,6 +183,19 @@ def test_chunk_rejects_bad_arguments_on_the_host(fp8):
         for bad in (0.0, -2.0, float("inf"), float("nan")):
             assert _chunk(lib, fp8, ks=bad) == E["SHAPE"]
             assert _chunk(lib, fp8, vs=bad) == E["SHAPE"]
+
+
+def test_swap_rejects_bad_arguments_on_the_host():
+    lib = pkv.load()
+    f = lib.pkv_swap_blocks
+    assert f(1, 1, 1, -1, 4, 4, 16, None) == E["SHAPE"]
+    assert f(1, 1, 1, 2, -4, 4, 16, None) == E["SHAPE"]
+    assert f(1, 1, 1, 2, 4, -4, 16, None) == E["SHAPE"]
+    assert f(1, 1, 1, 2, 4, 4, 18, None) == E["UNSUPPORTED"]
+    assert f(None, 1, 1, 2, 4, 4, 16, None) == E["NULL"]
+    assert f(1, None, 1, 2, 4, 4, 16, None) == E["NULL"]
+    assert f(1, 1, None, 2, 4, 4, 16, None) == E["NULL"]
+    assert f(None, None, None, 0, 4, 4, 16, None) == E["OK"]
 
 
 def test_fp8_append_rejects_bad_arguments_on_the_host():
