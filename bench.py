@@ -313,6 +313,89 @@ def traffic_per_launch(workload):
         return None
 
 
+HOST_LINK_PEAK_GBS = 63.0   # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130
+
+
+def bench_swap(args, pkv, dev):
+    """Swap step on the 8B batch's pool layout (8 KV heads x 16 x 128, bf16: 32 KiB per
+    block per pool): 512 blocks of the K and of the V pool out to a pinned host pool,
+    then 512 other blocks back in; four launches, whole-block copies."""
+    import numpy as np
+    import oracle
+    shape = (8, 16, 128)
+    n_gpu, n_host, n = 16384, 1024, 512
+    g = torch.Generator(device=dev).manual_seed(1007)
+    pools = [torch.randn((n_gpu,) + shape, generator=g, device=dev).to(torch.bfloat16)
+             for _ in range(2)]
+    hosts = [torch.zeros((n_host,) + shape, dtype=torch.bfloat16).pin_memory()
+             for _ in range(2)]
+    gc = torch.Generator().manual_seed(1008)
+    perm = torch.randperm(n_gpu, generator=gc)
+    out_pairs = torch.stack([perm[:n], torch.arange(n)], 1).to(torch.int32).to(dev)
+    in_pairs = torch.stack([torch.arange(n, 2 * n), perm[n:2 * n]], 1).to(torch.int32).to(dev)
+    calls = [pkv.PreparedSwapBlocks(h, p, out_pairs) for p, h in zip(pools, hosts)] + \
+            [pkv.PreparedSwapBlocks(p, h, in_pairs) for p, h in zip(pools, hosts)]
+    block = int(np.prod(shape)) * 2
+    step_bytes = 4 * n * block
+
+    def run():
+        for c in calls:
+            c()
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(args.steps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = a.elapsed_time(b)
+    value = step_bytes * args.steps / (ms * 1e-3) / 1e9
+    # one launch (the K pool's swap-out) on its own, back to back
+    a.record()
+    for _ in range(20):
+        calls[0]()
+    b.record()
+    torch.cuda.synchronize()
+    one_us = a.elapsed_time(b) * 1e3 / 20
+    achieved = n * block / (one_us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's block copy on the host: swap-out of the K pool's 512 blocks
+        src, host = pools[0].cpu(), hosts[0].clone()
+        pairs = out_pairs.cpu()
+        reps, tt = 0, 0.0
+        while tt < min(args.cpu_seconds, 5.0):
+            t1 = time.perf_counter()
+            oracle.swap_blocks(host, src, pairs)
+            tt += time.perf_counter() - t1
+            reps += 1
+        cpu = {"value": reps * n * block / tt / 1e9, "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{reps} swap-outs of {n} blocks (host memcpy), {tt:.1f} s"}
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "swap_blocks_8b", "block_bytes": block,
+                   "blocks_per_step": 4 * n, "bytes_per_step": step_bytes,
+                   "step": "swap_blocks: K and V pools, 512 blocks out to pinned host "
+                           "memory, 512 other blocks in",
+                   "launch": "direct (four calls per step)", "wall_s_timed": round(wall, 4)},
+        "roofline": {"bound": "host link", "kernel": "swap_blocks (swap-out)",
+                     "achieved": round(achieved, 2), "peak": HOST_LINK_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HOST_LINK_PEAK_GBS, 4),
+                     "traffic": None, "launch_us_mean": round(one_us, 3),
+                     "launch_timing": "20 back-to-back swap-outs, HIP events"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -345,6 +428,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     pkv.load()
+    if args.workload == "swap_blocks_8b":
+        bench_swap(args, pkv, dev)
+        return
     sets = build_sets(args.workload, max(1, args.rotate), dev)
     torch.cuda.synchronize()
     for s in sets:
