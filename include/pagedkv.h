@@ -64,7 +64,9 @@ enum {
     PKV_E_WORKSPACE = -5,    /* workspace NULL or smaller than pkv_paged_attention_workspace_size() */
     PKV_E_LAUNCH = -6,       /* the HIP runtime reported an error when enqueuing */
     PKV_E_INDEX = -7,        /* PKV_VALIDATE=1 only: an index array holds an out-of-range entry */
-    PKV_E_DEVICE = -8        /* no current HIP device could be queried */
+    PKV_E_DEVICE = -8,       /* no current HIP device could be queried */
+    PKV_E_NOSPACE = -9,      /* block manager: no free or evictable block for the request */
+    PKV_E_SEQUENCE = -10     /* block manager: unknown sequence id, or the id is taken */
 };
 
 /* A hipStream_t passed as an opaque pointer. */
@@ -342,6 +344,91 @@ int pkv_copy_blocks(void* cache, const int32_t* src_dst_pairs, int num_pairs, in
 int pkv_swap_blocks(void* dst_pool, const void* src_pool, const int32_t* src_dst_pairs,
                     int num_pairs, int num_src_blocks, int num_dst_blocks, size_t block_bytes,
                     pkv_stream_t stream);
+
+/*
+ * Host block manager (plain host code, no device work): decides which physical block
+ * and slot every token of every sequence uses, and produces the block tables, context
+ * lengths, slot mappings and copy-on-write pairs the device calls take.
+ *  - Token position p of a sequence lives in logical block p / bs at offset p % bs of
+ *    its table ([P2] section "Block Table 数据结构"); slot = physical * bs + offset.
+ *  - Free blocks form a stack: allocation pops, release pushes ([P2] section "内存分配
+ *    与回收流程"). A new manager hands out order[0], order[1], ... (order NULL: 0, 1, ...).
+ *  - Blocks are taken on demand: ceil(n / bs) for an n-token prompt, one more when a
+ *    decoded token finds the last block full ([P3] section "Block table：为什么它能减少
+ *    碎片"; [P1] section 六).
+ *  - Reference counts; appending into a block shared with another sequence first
+ *    copies it to a fresh block (copy-on-write) and reports the (src, dst) pair, which
+ *    the caller copies on the device (pkv_copy_blocks) before writing the token
+ *    ([P3] section "共享前缀和 copy-on-write"; [P1] section 五).
+ *  - Prefix caching ([P2] section "Copy-on-Write 与 Prefix Caching"): full blocks of
+ *    sequences added with token ids are cached under their whole token prefix (a
+ *    64-bit chained key, confirmed on a hit by the block's own tokens and its parent's
+ *    key); a prompt whose leading full blocks are cached references them.
+ *  - A cached block nobody references stays cold; with no free block, allocation
+ *    evicts the least recently released cold block ([P2] section "BlockAllocator
+ *    源码核心：vLLM 的显存管理心脏"). Sequences release their blocks last first.
+ *  - Each call checks that its blocks are available before changing anything and
+ *    returns PKV_E_NOSPACE otherwise.
+ * Not thread-safe; one manager per scheduler thread. Sequence ids are any int64.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* A manager over num_blocks blocks of block_size tokens; order (NULL or a permutation
+ * of 0..num_blocks-1) is the hand-out order of the initial free list. NULL on bad
+ * arguments or out of memory. */
+pkv_block_manager* pkv_bm_create(int num_blocks, int block_size, const int32_t* order);
+void pkv_bm_destroy(pkv_block_manager* bm);
+
+/* Free plus cold (evictable) blocks. */
+int pkv_bm_available(const pkv_block_manager* bm);
+
+/* 1 if a prompt of num_tokens tokens fits (ignoring prefix hits), else 0. */
+int pkv_bm_can_allocate(const pkv_block_manager* bm, int num_tokens);
+
+/* Place a new sequence's prompt of num_tokens tokens. token_ids (NULL: no prefix
+ * caching for this sequence) are host int32 [num_tokens]; *cached_tokens (may be NULL)
+ * receives the number of prompt tokens whose blocks were found in the cache (their
+ * K/V need not be computed again). */
+int pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id, int num_tokens,
+                        const int32_t* token_ids, int* cached_tokens);
+
+/* child_id shares every block of parent_id (parallel sampling, beam search). */
+int pkv_bm_fork(pkv_block_manager* bm, int64_t parent_id, int64_t child_id);
+
+/* Place the next token of seq_id: *slot receives its slot; *copy_src / *copy_dst the
+ * copy-on-write pair, or -1 / -1. token_id feeds the prefix cache of tracked
+ * sequences. */
+int pkv_bm_append_token(pkv_block_manager* bm, int64_t seq_id, int32_t token_id,
+                        int64_t* slot, int32_t* copy_src, int32_t* copy_dst);
+
+/* One decode step of a batch: pkv_bm_append_token for seq_ids[0..n-1] in order
+ * (token_ids may be NULL). slots int64 [n]; copy_pairs int32 [n, 2] (may be NULL),
+ * (-1, -1) where no copy is needed. Returns how many sequences were placed: n, or
+ * fewer when blocks ran out (the rest are untouched), or a negative error. */
+int pkv_bm_append_tokens(pkv_block_manager* bm, const int64_t* seq_ids,
+                         const int32_t* token_ids, int n, int64_t* slots,
+                         int32_t* copy_pairs);
+
+/* Release a finished sequence's blocks. */
+int pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id);
+
+/* Tokens placed for seq_id, or a negative error. */
+int64_t pkv_bm_num_tokens(const pkv_block_manager* bm, int64_t seq_id);
+
+/* The block table of seq_id: writes min(count, capacity) entries to out (may be NULL)
+ * and returns count, or a negative error. */
+int pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq_id, int32_t* out,
+                       int capacity);
+
+/* Reference count of a block (0 for free and cold blocks). */
+int pkv_bm_refcount(const pkv_block_manager* bm, int32_t block);
+
+/* Block tables of seq_ids as host int32 rows of `width` entries padded with -1, and
+ * their context lengths (host int32 [num_seqs]): the block_tables / context_lens
+ * arguments of the attention calls. PKV_E_SHAPE if a table is wider than width;
+ * nothing is written on error. */
+int pkv_bm_build_tables(const pkv_block_manager* bm, const int64_t* seq_ids, int num_seqs,
+                        int width, int32_t* tables, int32_t* context_lens);
 
 #ifdef __cplusplus
 }

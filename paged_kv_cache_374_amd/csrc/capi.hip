@@ -98,6 +98,8 @@ const char* pkv_strerror(int code) {
         case PKV_E_LAUNCH: return "the HIP runtime rejected a launch or copy";
         case PKV_E_INDEX: return "an index array holds an out-of-range entry (PKV_VALIDATE)";
         case PKV_E_DEVICE: return "no current HIP device";
+        case PKV_E_NOSPACE: return "no free or evictable block for the request";
+        case PKV_E_SEQUENCE: return "unknown sequence id, or the id is already in use";
         default: return "unknown pagedkv error";
     }
 }

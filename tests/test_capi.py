@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
               "pkv_paged_attention_decode_fp8", "pkv_paged_attention_decode_append_fp8",
               "pkv_paged_attention_chunk", "pkv_paged_attention_chunk_fp8",
               "pkv_reshape_and_cache", "pkv_reshape_and_cache_fp8", "pkv_copy_blocks",
-              "pkv_swap_blocks",
+              "pkv_swap_blocks", "pkv_bm_create", "pkv_bm_append_tokens",
+              "pkv_bm_build_tables",
               "pkv_paged_attention_workspace_size", "pkv_workspace_init", "pkv_version",
               "pkv_strerror"):
         assert n in names
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_error_strings():
     assert pkv.version().startswith("pagedkv")
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10):
         assert pkv.strerror(code) and pkv.strerror(code) != pkv.strerror(-99)
 
 
