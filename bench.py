@@ -396,6 +396,84 @@ def bench_swap(args, pkv, dev):
     print(json.dumps(line), flush=True)
 
 
+def bench_block_manager(args):
+    """Host block manager in a serving loop on the 8B pool (16384 blocks of 16 tokens):
+    32 prompts of 2040 tokens with token ids (prefix cache on), each forked into 8
+    samples (so the first decoded token of 7 samples copies the shared partial block),
+    then decode steps that append one token to all 256 sequences and rebuild the block
+    tables the attention call takes. Times the C++ manager; the CPU baseline runs the
+    same loop on the Python oracle for a few steps."""
+    import random
+    import numpy as np
+    import oracle.blockmgr as obm
+    from paged_kv_cache_374_amd.blocks import BlockManager
+
+    nb, bs, prompts, samples, plen = 16384, 16, 32, 8, 2040
+    steps = max(1, args.steps)
+    rng = random.Random(1009)
+    order = rng.sample(range(nb), nb)
+    toks = [[rng.randrange(32000) for _ in range(plen)] for _ in range(prompts)]
+
+    def setup(BM):
+        bm = BM(nb, bs, order)
+        sids = []
+        for p in range(prompts):
+            base = p * samples
+            bm.add_sequence(base, plen, toks[p])
+            sids.append(base)
+            for s in range(1, samples):
+                bm.fork(base, base + s)
+                sids.append(base + s)
+        return bm, sids
+
+    def run(bm, sids, n, batched):
+        width = (plen + n + bs - 1) // bs
+        appends = 0
+        sid_arr = np.asarray(sids, dtype=np.int64)
+        for i in range(n):
+            t = (i * 7 + np.arange(len(sids), dtype=np.int32)) % 32000
+            if batched:
+                placed, _, _ = bm.append_tokens(sid_arr, t)
+            else:
+                for sid, tok in zip(sids, t):
+                    bm.append_token(sid, tok)
+                placed = len(sids)
+            appends += placed
+            bm.build_tables(sid_arr, width)
+        return appends
+
+    bm, sids = setup(BlockManager)
+    run(bm, sids, 2, True)                         # warm-up on a throwaway manager
+    bm, sids = setup(BlockManager)
+    t0 = time.perf_counter()
+    appends = run(bm, sids, steps, True)
+    dt = time.perf_counter() - t0
+    value = appends / dt
+    cpu = None
+    if not args.no_cpu_baseline:
+        om, osids = setup(obm.BlockManager)
+        n_cpu = max(1, min(steps, 8))
+        t1 = time.perf_counter()
+        a_cpu = run(om, osids, n_cpu, False)
+        tc = time.perf_counter() - t1
+        cpu = {"value": a_cpu / tc, "unit": "appends/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n_cpu} decode steps of the same loop (Python oracle), {tc:.1f} s"}
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "appends/s", "n_gpus": 1,
+        "steps": steps, "warmup": 2, "ms_per_step": round(dt * 1e3 / steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": "block_manager_serving", "num_blocks": nb, "block_size": bs,
+                   "sequences": len(sids), "prompt_tokens": plen,
+                   "step": "append_tokens(256 sequences) + build_tables (host)",
+                   "wall_s_timed": round(dt, 4)},
+        "roofline": {"bound": "host", "achieved": round(value, 1), "peak": None,
+                     "unit": "appends/s", "frac": None, "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -423,6 +501,9 @@ def main():
     global torch
     import torch
     import paged_kv_cache_374_amd as pkv
+    if args.workload == "block_manager_serving":   # host code: no GPU needed
+        bench_block_manager(args)
+        return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)

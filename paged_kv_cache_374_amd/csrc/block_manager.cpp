@@ -353,17 +353,26 @@ int pkv_bm_build_tables(const pkv_block_manager* m, const int64_t* seq_ids, int 
     if (!m) return PKV_E_NULL;
     if (num_seqs < 0 || width < 0) return PKV_E_SHAPE;
     if (num_seqs > 0 && (!seq_ids || !tables || !context_lens)) return PKV_E_NULL;
-    for (int i = 0; i < num_seqs; ++i) {   // check everything before writing
+    // one lookup per sequence, everything checked before anything is written
+    std::vector<const Sequence*> found;
+    try {
+        found.resize(num_seqs);
+    } catch (...) {
+        return PKV_E_LAUNCH;
+    }
+    for (int i = 0; i < num_seqs; ++i) {
         const auto it = m->seqs.find(seq_ids[i]);
         if (it == m->seqs.end()) return PKV_E_SEQUENCE;
         if ((int)it->second.table.size() > width || it->second.len > 0x7fffffff)
             return PKV_E_SHAPE;
+        found[i] = &it->second;
     }
     for (int i = 0; i < num_seqs; ++i) {
-        const Sequence& s = m->seqs.find(seq_ids[i])->second;
+        const Sequence& s = *found[i];
         int32_t* row = tables + (size_t)i * width;
-        const int n = (int)s.table.size();
-        for (int j = 0; j < width; ++j) row[j] = j < n ? s.table[j] : -1;
+        const size_t n = s.table.size();
+        if (n) std::memcpy(row, s.table.data(), n * sizeof(int32_t));
+        for (size_t j = n; j < (size_t)width; ++j) row[j] = -1;
         context_lens[i] = (int32_t)s.len;
     }
     return PKV_OK;
