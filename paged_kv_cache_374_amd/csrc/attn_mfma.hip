@@ -1238,6 +1238,273 @@ __global__ __launch_bounds__(kThreads) void chunk_split_kernel(
     }
 }
 
+// ------------------------------------------------------------------ prefill chunks
+// Long chunks on 32x32 matrix-core tiles, flash-attention style. A workgroup takes
+// 4 x 32 query rows of one (sequence, KV head): each wave 32 rows, row r being query
+// token r / G and head r % G of the wave's tokens. Each step brings 32 context tokens
+// (two blocks) into LDS once for all four waves: K row-major with its 16-byte chunks
+// swizzled by token, V transposed (dims x tokens) so that the PV operand is one
+// 8-byte read. Per step and wave:
+//   S^T = K Q^T  (32 tokens x 32 rows, eight 32x32x16 products; Q stays in registers)
+//   online softmax per row: a lane's column is its row, so the max and the rescale of
+//   the accumulator stay in the lane (one exchange with the lane 32 apart)
+//   O^T += V^T P^T  (128 dims x 32 rows, sixteen 32x32x8 products; P^T is the score
+//   tile's own register layout)
+// The 32x32 layouts (checked on gfx950): A holds row l%32, k = K/2*(l/32) .. ; B holds
+// column l%32, the same k; D element v of lane l is row 8(v/4) + 4(l/32) + v%4, column
+// l%32. Slots past the context are cleared in V (a zero weight does not cancel a NaN)
+// and masked in S.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <typename T> struct Mma32;
+template <> struct Mma32<bf16_t> {
+    static __device__ __forceinline__ f32x16_t qk(const uint4& a, const uint4& b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                      __builtin_bit_cast(bf16x8_t, b), c, 0, 0,
+                                                      0);
+    }
+    static __device__ __forceinline__ f32x16_t pv(const uint2& a, const uint2& b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                       __builtin_bit_cast(i16x4_t, b), c, 0, 0,
+                                                       0);
+    }
+};
+template <> struct Mma32<f16_t> {
+    static __device__ __forceinline__ f32x16_t qk(const uint4& a, const uint4& b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                     __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x16_t pv(const uint2& a, const uint2& b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(f16x4_t, a),
+                                                   __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+    }
+};
+
+constexpr int kFaRows = 32;      // query rows per wave (the 32 columns of S^T)
+constexpr int kFaStep = 32;      // context tokens per step: two blocks of 16
+constexpr int kFaVtStride = 36;  // V^T row stride in elements: 32 tokens + 4 (8-byte reads
+                                 // of 32 consecutive rows hit 32 distinct bank pairs)
+
+struct FaLds {
+    uint32_t tile[kTabMax];
+    uint4 k[2][kFaStep][kD / 8];                 // [buffer][token][16-byte chunk ^ token%16]
+    uint16_t vt[2][kD][kFaVtStride];             // [buffer][dim][token]
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
+    T* __restrict__ out, const T* __restrict__ q, const T* __restrict__ k_cache,
+    const T* __restrict__ v_cache, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ query_start,
+    float scale_log2, int num_query_tokens, int num_heads, int num_kv_heads, int group,
+    int max_blocks, int num_blocks, int groups) {
+    __shared__ FaLds S;
+    // (sequence, KV head) pair p with all its row groups on XCD p % 8 (see
+    // chunk_tiles_kernel)
+    const int pairs = gridDim.x / groups;
+    int pair, sg;
+    if (pairs % 8 == 0) {
+        const int x = blockIdx.x % 8, k = blockIdx.x / 8;
+        pair = x + 8 * (k / groups);
+        sg = k % groups;
+    } else {
+        pair = blockIdx.x / groups;
+        sg = blockIdx.x % groups;
+    }
+    const int g = pair % num_kv_heads, b = pair / num_kv_heads;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+    const int r0 = query_start[b], r1 = query_start[b + 1];
+    if (r0 < 0 || r1 < r0 || r1 > num_query_tokens) return;
+    const int T_b = r1 - r0;
+    const int tqw = kFaRows / group;                 // query tokens per wave
+    const int tok_wg = sg * kWaves * tqw;
+    if (tok_wg >= T_b) return;
+    const int cap = max_blocks * kBS;
+    int n = ctx_lens[b];
+    n = n < 0 ? 0 : (n > cap ? cap : n);
+    const int ntok_wg = min(kWaves * tqw, T_b - tok_wg);
+    const int last_wg = n - T_b + tok_wg + ntok_wg - 1;   // position of the last row
+    if (last_wg < 0) {
+        zero_rows(out, (r0 + tok_wg) * num_heads + g * group, ntok_wg, group, num_heads, tid);
+        return;
+    }
+    const int steps = last_wg / kFaStep + 1;
+    const int nb_ctx = (n + kBS - 1) / kBS;
+    const int h = lane >> 5, r = lane & 31;
+    const int tok_w = tok_wg + wave * tqw;           // this wave's first query token
+    const int rtok = r / group, rhead = r % group;
+    const bool row_ok = r < tqw * group && tok_w + rtok < T_b;
+    const int pos = n - T_b + tok_w + rtok;          // the lane's row position
+    const int last_w = n - T_b + min(T_b, tok_w + tqw) - 1;   // the wave's last row
+
+    // the lane's query row, dims 16s + 8h .. +7 for k-step s (zeros past the chunk)
+    uint4 qv[kD / 16];
+    {
+        const int qbytes = (r1 - r0) * num_heads * kD * (int)sizeof(T);
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(q + (size_t)r0 * num_heads * kD), 0, qbytes, kRawBufferWord3);
+        const int qoff = row_ok
+            ? (((tok_w + rtok) * num_heads + g * group + rhead) * kD + 8 * h) * (int)sizeof(T)
+            : qbytes;
+#pragma unroll
+        for (int s = 0; s < kD / 16; ++s)
+            qv[s] = buffer_load16(rq, qoff + 16 * s * (int)sizeof(T));
+    }
+    f32x16_t acc[kD / 32];
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt) acc[dt] = f32x16_t{};
+    float m = kNegInf, lsum = 0.f;
+
+    // global -> registers. K: thread tid takes 16-byte chunk tid of both blocks of a
+    // step (token tid / 16 of the block, dims 8(tid % 16) .. +7). V: waves 0-1 take the
+    // first block and waves 2-3 the second; lane l of the wave takes tokens 2p, 2p + 1
+    // (p = l % 8) at chunk c = 8(wave % 2) + l / 8, so that the transposed store below
+    // writes one dword (two tokens of one dim) per row.
+    int w0 = 0, w1 = 0;
+    const int vblk = wave >> 1, vc = 8 * (wave & 1) + lane / 8, vp = lane % 8;
+    auto rsrc_of = [&](const T* cache, int jb) {
+        const uint32_t tl = uni(jb < w1 ? (int)S.tile[jb - w0] : (int)kNoTile);
+        const bool ok = tl != kNoTile;
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(cache + (size_t)(ok ? tl : 0u) * kTile), 0, ok ? kTile * (int)sizeof(T) : 0,
+            kRawBufferWord3);
+    };
+    auto load_step = [&](int st, uint4 (&kr)[2], uint4 (&vr)[2]) {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) kr[bi] = buffer_load16(rsrc_of(k_cache, 2 * st + bi), tid * 16);
+        const __amdgpu_buffer_rsrc_t rv = rsrc_of(v_cache, 2 * st + vblk);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            vr[e] = buffer_load16(rv, ((2 * vp + e) * kD + 8 * vc) * (int)sizeof(T));
+    };
+    // registers -> LDS buffer bf: K chunk swizzled by token; V transposed, two tokens of
+    // a dim per dword (V^T rows of kFaVtStride elements: 2-way bank conflicts on these
+    // writes, none on the PV reads), cleared past the context
+    auto store_step = [&](int st, int bf, const uint4 (&kr)[2], const uint4 (&vr)[2]) {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+            const int t = bi * kBS + tid / 16, c = tid % 16;
+            S.k[bf][t][c ^ (t & 15)] = kr[bi];
+        }
+        const int t0 = vblk * kBS + 2 * vp;                  // step-relative token
+        const uint4 za = st * kFaStep + t0 < n ? vr[0] : make_uint4(0, 0, 0, 0);
+        const uint4 zb = st * kFaStep + t0 + 1 < n ? vr[1] : make_uint4(0, 0, 0, 0);
+        uint32_t* vt = reinterpret_cast<uint32_t*>(&S.vt[bf][0][0]);
+        constexpr int kRow = kFaVtStride / 2;                // dwords per V^T row
+#define PKV_VT(X) vt[(8 * vc + (X)) * kRow + t0 / 2] = pick<X>(za, zb);
+        PKV_VT(0) PKV_VT(1) PKV_VT(2) PKV_VT(3) PKV_VT(4) PKV_VT(5) PKV_VT(6) PKV_VT(7)
+#undef PKV_VT
+    };
+    auto compute = [&](int st, int bf) {
+        const int tp0 = st * kFaStep;
+        if (tp0 > last_w) return;                    // none of the wave's rows sees it
+        f32x16_t sc = f32x16_t{};
+#pragma unroll
+        for (int s = 0; s < kD / 16; ++s)
+            sc = Mma32<T>::qk(S.k[bf][r][(2 * s + h) ^ (r & 15)], qv[s], sc);
+        // The VALU, not the matrix cores, bounds this loop (a wave64 VALU op takes four
+        // cycles): steps that every row of the wave sees whole skip the mask, the scale
+        // enters through one FMA before the exp (scale > 0, so the max of the raw scores
+        // gives the max of the scaled ones), and the accumulator is rescaled only when
+        // some row's max moved.
+        const bool whole = tp0 + kFaStep - 1 <= n - T_b + tok_w && tp0 + kFaStep <= n;
+        float mraw = kNegInf;
+        if (whole) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, sc[v]);
+        } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int tp = tp0 + 8 * (v / 4) + 4 * h + (v % 4);
+                sc[v] = (tp <= pos && tp < n) ? sc[v] : kNegInf;
+                mraw = fmaxf(mraw, sc[v]);
+            }
+        }
+        mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+        const float mn = fmaxf(m, mraw * scale_log2);
+        const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m - mn);
+        const float mu = (mn == kNegInf) ? 0.f : mn;
+        float ps = 0.f;
+        uint2 pb[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(sc[4 * s + e], scale_log2, -mu));
+            ps += (p[0] + p[1]) + (p[2] + p[3]);
+            pb[s] = make_uint2(Mma<T>::pack(p[0], p[1]), Mma<T>::pack(p[2], p[3]));
+        }
+        lsum = lsum * alpha + ps;
+        m = mn;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < kD / 32; ++dt) acc[dt] *= alpha;
+        }
+        // PV on 32x32x16 products over 16 tokens each. The k order inside a product is
+        // free as long as both operands use it: lane l supplies its own score registers
+        // (tokens 16s + 4h + 0..3 and 16s + 8 + 4h + 0..3), and V^T is read in the same
+        // order (two 8-byte pieces of its row).
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint4 pbk = make_uint4(pb[2 * s].x, pb[2 * s].y, pb[2 * s + 1].x, pb[2 * s + 1].y);
+#pragma unroll
+            for (int dt = 0; dt < kD / 32; ++dt) {
+                const uint16_t* row = &S.vt[bf][32 * dt + r][0];
+                const uint2 lo = *reinterpret_cast<const uint2*>(row + 16 * s + 4 * h);
+                const uint2 hi = *reinterpret_cast<const uint2*>(row + 16 * s + 8 + 4 * h);
+                acc[dt] = Mma32<T>::qk(make_uint4(lo.x, lo.y, hi.x, hi.y), pbk, acc[dt]);
+            }
+        }
+    };
+
+    const int nbl = 2 * steps;                       // blocks the steps cover
+    for (w0 = 0; w0 < nbl; w0 += kTabMax) {
+        w1 = min(nbl, w0 + kTabMax);
+        __syncthreads();                             // the previous window is done
+        for (int j = w0 + tid; j < w1; j += kThreads) {
+            int phys = j < nb_ctx ? tables[(size_t)b * max_blocks + j] : -1;
+            const bool ok = phys >= 0 && phys < num_blocks;
+            S.tile[j - w0] = ok ? (uint32_t)phys * (uint32_t)num_kv_heads + (uint32_t)g
+                                : kNoTile;
+        }
+        __syncthreads();
+        // Two register sets in ping-pong: the loads of step st + 2 go out while step st
+        // is computed, and step st + 1 (loaded a step earlier) goes to the other LDS
+        // buffer at the end of step st; one barrier per step.
+        const int s0 = w0 / 2, s1 = w1 / 2;
+        uint4 ka[2], va[2], kb[2], vb[2];
+        load_step(s0, ka, va);
+        if (s0 + 1 < s1) load_step(s0 + 1, kb, vb);
+        store_step(s0, 0, ka, va);
+        __syncthreads();
+        for (int st = s0; st < s1; st += 2) {
+            if (st + 2 < s1) load_step(st + 2, ka, va);
+            compute(st, 0);
+            if (st + 1 < s1) store_step(st + 1, 1, kb, vb);
+            __syncthreads();
+            if (st + 1 >= s1) break;
+            if (st + 3 < s1) load_step(st + 3, kb, vb);
+            compute(st + 1, 1);
+            if (st + 2 < s1) store_step(st + 2, 0, ka, va);
+            __syncthreads();
+        }
+    }
+    const float lt = lsum + __shfl_xor(lsum, 32);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (row_ok) {
+        T* orow = out + ((size_t)(r0 + tok_w + rtok) * num_heads + g * group + rhead) * kD;
+#pragma unroll
+        for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                uint2 w;
+                w.x = Mma<T>::pack(acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv);
+                w.y = Mma<T>::pack(acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
+                *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4 + 4 * h) = w;
+            }
+    }
+}
+
 // Register buffers per wave in chunk_tiles_kernel (its loads mostly hit L2).
 constexpr int kChunkRing = 2;
 
@@ -1432,7 +1699,18 @@ int launch_chunk(const ChunkArgs& a, hipStream_t stream) {
     // Long chunks (more than four tiles): each wave folds NT tiles per staged
     // block. Short ones: one tile per workgroup, its waves splitting the blocks.
     constexpr int NT = 1;
-    if (tiles > kWaves)
+    if (tiles > kWaves && !fp8 && a.scale > 0.f) {
+        // 16-bit caches: 32x32 tiles, K/V shared through LDS by the workgroup's waves
+        const int tqw = 32 / G;
+        const int groups = (a.max_query_len + kWaves * tqw - 1) / (kWaves * tqw);
+        const long long items = (long long)groups * a.num_kv_heads * a.num_seqs;
+        if (items > 0x7fffffffLL) return -1;
+        hipLaunchKernelGGL((chunk_fa_kernel<T>), dim3((unsigned)items), dim3(kThreads), 0, stream,
+                           (T*)a.out, (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache,
+                           a.block_tables, a.context_lens, a.query_start, scale_log2,
+                           a.num_query_tokens, a.num_heads, a.num_kv_heads, G, a.max_blocks,
+                           a.num_blocks, groups);
+    } else if (tiles > kWaves)
     {
         // one-dimensional grid of (span group, KV head, sequence) items
         const int groups = (tiles + kWaves * NT - 1) / (kWaves * NT);

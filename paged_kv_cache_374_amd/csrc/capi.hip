@@ -181,7 +181,8 @@ int chunk_call(void* out, const void* q, const void* k_cache, const void* v_cach
     if (kv_fp8 && !(scale_ok(k_scale) && scale_ok(v_scale))) return PKV_E_SHAPE;
     if (num_seqs > 65535 || num_kv_heads > 65535) return PKV_E_SHAPE;
     if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PKV_OK;
-    if ((long long)num_query_tokens * num_heads * head_dim > 0x7fffffffLL) return PKV_E_SHAPE;
+    // byte offsets into q and out are 32-bit in the kernels
+    if ((long long)num_query_tokens * num_heads * head_dim * 2 > 0x7fffffffLL) return PKV_E_SHAPE;
     if (!out || !q || !context_lens || !query_start) return PKV_E_NULL;
     if (max_blocks_per_seq > 0 && (!k_cache || !v_cache || !block_tables)) return PKV_E_NULL;
     hipStream_t st = (hipStream_t)stream;
