@@ -1243,12 +1243,12 @@ __global__ __launch_bounds__(kThreads) void chunk_split_kernel(
 // 4 x 32 query rows of one (sequence, KV head): each wave 32 rows, row r being query
 // token r / G and head r % G of the wave's tokens. Each step brings 32 context tokens
 // (two blocks) into LDS once for all four waves: K row-major with its 16-byte chunks
-// swizzled by token, V transposed (dims x tokens) so that the PV operand is one
-// 8-byte read. Per step and wave:
+// swizzled by token, V transposed (dims x tokens) so that a PV operand is two 8-byte
+// reads of one row. Per step and wave:
 //   S^T = K Q^T  (32 tokens x 32 rows, eight 32x32x16 products; Q stays in registers)
 //   online softmax per row: a lane's column is its row, so the max and the rescale of
 //   the accumulator stay in the lane (one exchange with the lane 32 apart)
-//   O^T += V^T P^T  (128 dims x 32 rows, sixteen 32x32x8 products; P^T is the score
+//   O^T += V^T P^T  (128 dims x 32 rows, eight 32x32x16 products; P^T is the score
 //   tile's own register layout)
 // The 32x32 layouts (checked on gfx950): A holds row l%32, k = K/2*(l/32) .. ; B holds
 // column l%32, the same k; D element v of lane l is row 8(v/4) + 4(l/32) + v%4, column
@@ -1258,30 +1258,24 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 template <typename T> struct Mma32;
 template <> struct Mma32<bf16_t> {
-    static __device__ __forceinline__ f32x16_t qk(const uint4& a, const uint4& b, f32x16_t c) {
+    static __device__ __forceinline__ f32x16_t mma(const uint4& a, const uint4& b, f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0,
                                                       0);
     }
-    static __device__ __forceinline__ f32x16_t pv(const uint2& a, const uint2& b, f32x16_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(i16x4_t, a),
-                                                       __builtin_bit_cast(i16x4_t, b), c, 0, 0,
-                                                       0);
-    }
 };
 template <> struct Mma32<f16_t> {
-    static __device__ __forceinline__ f32x16_t qk(const uint4& a, const uint4& b, f32x16_t c) {
+    static __device__ __forceinline__ f32x16_t mma(const uint4& a, const uint4& b, f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ f32x16_t pv(const uint2& a, const uint2& b, f32x16_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(f16x4_t, a),
-                                                   __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
     }
 };
 
 constexpr int kFaRows = 32;      // query rows per wave (the 32 columns of S^T)
 constexpr int kFaStep = 32;      // context tokens per step: two blocks of 16
+// A row's reference maximum moves only when a score passes it by more than this (log2
+// units): weights then stay below 2^8, and the final division cancels the reference.
+constexpr float kFaLazy = 8.f;
 constexpr int kFaVtStride = 36;  // V^T row stride in elements: 32 tokens + 4 (8-byte reads
                                  // of 32 consecutive rows hit 32 distinct bank pairs)
 
@@ -1401,12 +1395,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
         f32x16_t sc = f32x16_t{};
 #pragma unroll
         for (int s = 0; s < kD / 16; ++s)
-            sc = Mma32<T>::qk(S.k[bf][r][(2 * s + h) ^ (r & 15)], qv[s], sc);
+            sc = Mma32<T>::mma(S.k[bf][r][(2 * s + h) ^ (r & 15)], qv[s], sc);
         // The VALU, not the matrix cores, bounds this loop (a wave64 VALU op takes four
         // cycles): steps that every row of the wave sees whole skip the mask, the scale
         // enters through one FMA before the exp (scale > 0, so the max of the raw scores
-        // gives the max of the scaled ones), and the accumulator is rescaled only when
-        // some row's max moved.
+        // gives the max of the scaled ones), and a row's reference maximum moves (with a
+        // rescale of the accumulator) only when its scores pass it by more than kFaLazy.
         const bool whole = tp0 + kFaStep - 1 <= n - T_b + tok_w && tp0 + kFaStep <= n;
         float mraw = kNegInf;
         if (whole) {
@@ -1421,9 +1415,16 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
             }
         }
         mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
-        const float mn = fmaxf(m, mraw * scale_log2);
-        const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m - mn);
-        const float mu = (mn == kNegInf) ? 0.f : mn;
+        const float mc = mraw * scale_log2;
+        if (__any(mc > m + kFaLazy)) {
+            const float mn = fmaxf(m, mc);
+            const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m - mn);
+            lsum *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < kD / 32; ++dt) acc[dt] *= alpha;
+            m = mn;
+        }
+        const float mu = (m == kNegInf) ? 0.f : m;
         float ps = 0.f;
         uint2 pb[4];
 #pragma unroll
@@ -1434,12 +1435,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
             ps += (p[0] + p[1]) + (p[2] + p[3]);
             pb[s] = make_uint2(Mma<T>::pack(p[0], p[1]), Mma<T>::pack(p[2], p[3]));
         }
-        lsum = lsum * alpha + ps;
-        m = mn;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-            for (int dt = 0; dt < kD / 32; ++dt) acc[dt] *= alpha;
-        }
+        lsum += ps;
         // PV on 32x32x16 products over 16 tokens each. The k order inside a product is
         // free as long as both operands use it: lane l supplies its own score registers
         // (tokens 16s + 4h + 0..3 and 16s + 8 + 4h + 0..3), and V^T is read in the same
@@ -1452,7 +1448,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
                 const uint16_t* row = &S.vt[bf][32 * dt + r][0];
                 const uint2 lo = *reinterpret_cast<const uint2*>(row + 16 * s + 4 * h);
                 const uint2 hi = *reinterpret_cast<const uint2*>(row + 16 * s + 8 + 4 * h);
-                acc[dt] = Mma32<T>::qk(make_uint4(lo.x, lo.y, hi.x, hi.y), pbk, acc[dt]);
+                acc[dt] = Mma32<T>::mma(make_uint4(lo.x, lo.y, hi.x, hi.y), pbk, acc[dt]);
             }
         }
     };
