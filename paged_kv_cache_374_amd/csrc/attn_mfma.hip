@@ -1279,8 +1279,12 @@ constexpr float kFaLazy = 8.f;
 constexpr int kFaVtStride = 36;  // V^T row stride in elements: 32 tokens + 4 (8-byte reads
                                  // of 32 consecutive rows hit 32 distinct bank pairs)
 
+// Batches up to this many sequences run their heaviest work first (see chunk_fa_kernel).
+constexpr int kFaSortMax = 512;
+
 struct FaLds {
     uint32_t tile[kTabMax];
+    int seq;
     uint4 k[2][kFaStep][kD / 8];                 // [buffer][token][16-byte chunk ^ token%16]
     uint16_t vt[2][kD][kFaVtStride];             // [buffer][dim][token]
 };
@@ -1305,8 +1309,33 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
         pair = blockIdx.x / groups;
         sg = blockIdx.x % groups;
     }
-    const int g = pair % num_kv_heads, b = pair / num_kv_heads;
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+    // Heaviest work first, so that the longest workgroups do not start last: pair ranks
+    // go to the sequences in decreasing order of context length (ties by index), and a
+    // pair's row groups run from the last (which sees the most context) to the first.
+    // Every workgroup ranks the context lengths itself (staged in LDS).
+    const int nseq = pairs / num_kv_heads, g = pair % num_kv_heads;
+    int b = pair / num_kv_heads;
+    sg = groups - 1 - sg;
+    if (nseq <= kFaSortMax) {
+        const int cap0 = max_blocks * kBS;
+        for (int u = tid; u < nseq; u += kThreads) {
+            const int x = ctx_lens[u];
+            S.tile[u] = (uint32_t)(x < 0 ? 0 : (x > cap0 ? cap0 : x));
+        }
+        __syncthreads();
+        for (int u = tid; u < nseq; u += kThreads) {
+            const uint32_t key = S.tile[u];
+            int rank = 0;
+            for (int v = 0; v < nseq; ++v) {
+                const uint32_t kv = S.tile[v];
+                rank += (kv > key || (kv == key && v < u)) ? 1 : 0;
+            }
+            if (rank == b) S.seq = u;
+        }
+        __syncthreads();
+        b = S.seq;
+    }
     const int r0 = query_start[b], r1 = query_start[b + 1];
     if (r0 < 0 || r1 < r0 || r1 > num_query_tokens) return;
     const int T_b = r1 - r0;
