@@ -1242,9 +1242,9 @@ __global__ __launch_bounds__(kThreads) void chunk_split_kernel(
 // Long chunks on 32x32 matrix-core tiles, flash-attention style. A workgroup takes
 // 4 x 32 query rows of one (sequence, KV head): each wave 32 rows, row r being query
 // token r / G and head r % G of the wave's tokens. Each step brings 32 context tokens
-// (two blocks) into LDS once for all four waves: K row-major with its 16-byte chunks
-// swizzled by token, V transposed (dims x tokens) so that a PV operand is two 8-byte
-// reads of one row. Per step and wave:
+// (two blocks) into LDS once for all four waves, straight from HBM (buffer loads that
+// write LDS), K and V both row-major with their 16-byte chunks permuted per token; the
+// PV operand comes from transposing LDS reads. Per step and wave:
 //   S^T = K Q^T  (32 tokens x 32 rows, eight 32x32x16 products; Q stays in registers)
 //   online softmax per row: a lane's column is its row, so the max and the rescale of
 //   the accumulator stay in the lane (one exchange with the lane 32 apart)
@@ -1252,8 +1252,8 @@ __global__ __launch_bounds__(kThreads) void chunk_split_kernel(
 //   tile's own register layout)
 // The 32x32 layouts (checked on gfx950): A holds row l%32, k = K/2*(l/32) .. ; B holds
 // column l%32, the same k; D element v of lane l is row 8(v/4) + 4(l/32) + v%4, column
-// l%32. Slots past the context are cleared in V (a zero weight does not cancel a NaN)
-// and masked in S.
+// l%32. Slots past the context are loaded as zeros (a zero weight does not cancel a
+// NaN) and masked in S.
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 template <typename T> struct Mma32;
@@ -1273,21 +1273,65 @@ template <> struct Mma32<f16_t> {
 
 constexpr int kFaRows = 32;      // query rows per wave (the 32 columns of S^T)
 constexpr int kFaStep = 32;      // context tokens per step: two blocks of 16
+constexpr int kFaRing = 3;       // LDS slots: the step being multiplied and two in flight
+constexpr int kFaTab = 512;      // table entries staged per window (256 steps)
 // A row's reference maximum moves only when a score passes it by more than this (log2
 // units): weights then stay below 2^8, and the final division cancels the reference.
 constexpr float kFaLazy = 8.f;
-constexpr int kFaVtStride = 36;  // V^T row stride in elements: 32 tokens + 4 (8-byte reads
-                                 // of 32 consecutive rows hit 32 distinct bank pairs)
 
 // Batches up to this many sequences run their heaviest work first (see chunk_fa_kernel).
-constexpr int kFaSortMax = 512;
+constexpr int kFaSortMax = kFaTab;
 
+// K and V rows of a step in LDS, both [token][16-byte chunk] with the chunks of a row
+// permuted: K chunk c of token t sits at c ^ (t % 16) (the 16-byte score-operand reads
+// of 32 tokens hit distinct banks), V chunk c at c ^ 4 (t % 4) (the transposing 8-byte
+// reads of the PV operand, four tokens x 32 dims per half-wave, hit distinct banks).
 struct FaLds {
-    uint32_t tile[kTabMax];
+    uint32_t tile[kFaTab];
     int seq;
-    uint4 k[2][kFaStep][kD / 8];                 // [buffer][token][16-byte chunk ^ token%16]
-    uint16_t vt[2][kD][kFaVtStride];             // [buffer][dim][token]
+    uint4 k[kFaRing][kFaStep][kD / 8];
+    uint4 v[kFaRing][kFaStep][kD / 8];
 };
+
+// 16 bytes per lane from a raw buffer straight into LDS: lane l writes lds_addr + 16 l
+// (gfx950). Written as assembly so that the compiler's wait insertion does not treat
+// every later LDS read as dependent on it (that would drain all loads in flight); the
+// code orders it with explicit vector-memory counter waits and barriers instead. M0
+// holds the LDS address and needs one wait state before the load; the leading five
+// wait states cover descriptor words just written by v_readfirstlane (the compiler's
+// hazard checks do not look inside assembly).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void lds_load16(i32x4_t rsrc, uint32_t lds_addr, int voffset) {
+    asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+                 : "memory", "m0");
+}
+// A raw buffer descriptor (stride 0, num_records bytes) as four scalar words.
+__device__ __forceinline__ i32x4_t raw_rsrc_words(const void* base, int bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4_t w;
+    w.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    w.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
+    w.z = __builtin_amdgcn_readfirstlane(bytes);
+    w.w = kRawBufferWord3;
+    return w;
+}
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) void*)p);
+}
+// Workgroup barrier that orders memory operations in the compiler only; the waits that
+// the data needs are explicit before it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
@@ -1378,53 +1422,57 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
     for (int dt = 0; dt < kD / 32; ++dt) acc[dt] = f32x16_t{};
     float m = kNegInf, lsum = 0.f;
 
-    // global -> registers. K: thread tid takes 16-byte chunk tid of both blocks of a
-    // step (token tid / 16 of the block, dims 8(tid % 16) .. +7). V: waves 0-1 take the
-    // first block and waves 2-3 the second; lane l of the wave takes tokens 2p, 2p + 1
-    // (p = l % 8) at chunk c = 8(wave % 2) + l / 8, so that the transposed store below
-    // writes one dword (two tokens of one dim) per row.
+    // Global -> LDS without registers: buffer loads that write LDS directly, lane l of a
+    // wave to the wave's LDS base + 16 l. For block bi of a step, thread tid fills row
+    // bi * 16 + tid / 16, position tid % 16, so it fetches the chunk that the row's
+    // permutation puts there. A block's descriptor covers only its tokens inside the
+    // context (none for a missing block): loads past it write zeros, which keeps
+    // anything beyond the context out of the PV products (a zero weight does not cancel
+    // a NaN).
     int w0 = 0, w1 = 0;
-    const int vblk = wave >> 1, vc = 8 * (wave & 1) + lane / 8, vp = lane % 8;
-    auto rsrc_of = [&](const T* cache, int jb) {
-        const uint32_t tl = uni(jb < w1 ? (int)S.tile[jb - w0] : (int)kNoTile);
-        const bool ok = tl != kNoTile;
-        return __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(cache + (size_t)(ok ? tl : 0u) * kTile), 0, ok ? kTile * (int)sizeof(T) : 0,
-            kRawBufferWord3);
-    };
-    auto load_step = [&](int st, uint4 (&kr)[2], uint4 (&vr)[2]) {
-#pragma unroll
-        for (int bi = 0; bi < 2; ++bi) kr[bi] = buffer_load16(rsrc_of(k_cache, 2 * st + bi), tid * 16);
-        const __amdgpu_buffer_rsrc_t rv = rsrc_of(v_cache, 2 * st + vblk);
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-            vr[e] = buffer_load16(rv, ((2 * vp + e) * kD + 8 * vc) * (int)sizeof(T));
-    };
-    // registers -> LDS buffer bf: K chunk swizzled by token; V transposed, two tokens of
-    // a dim per dword (V^T rows of kFaVtStride elements: 2-way bank conflicts on these
-    // writes, none on the PV reads), cleared past the context
-    auto store_step = [&](int st, int bf, const uint4 (&kr)[2], const uint4 (&vr)[2]) {
+    const int tt = tid / 16, tc = tid % 16;
+    const int koff = (tt * (kD / 8) + (tc ^ tt)) * 16;
+    const int voff = (tt * (kD / 8) + (tc ^ (4 * (tt % 4)))) * 16;
+    auto issue = [&](int st, int sl) {
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi) {
-            const int t = bi * kBS + tid / 16, c = tid % 16;
-            S.k[bf][t][c ^ (t & 15)] = kr[bi];
+            const int jb = 2 * st + bi;
+            const uint32_t tl = uni(jb < w1 ? (int)S.tile[jb - w0] : (int)kNoTile);
+            const int nv = min(kBS, max(0, n - jb * kBS));
+            const bool ok = tl != kNoTile;
+            const size_t base = (size_t)(ok ? tl : 0u) * kTile;
+            const int bytes = ok ? nv * kD * (int)sizeof(T) : 0;
+            lds_load16(raw_rsrc_words(k_cache + base, bytes),
+                       uni(lds_address(&S.k[sl][bi * kBS + 4 * wave][0])), koff);
+            lds_load16(raw_rsrc_words(v_cache + base, bytes),
+                       uni(lds_address(&S.v[sl][bi * kBS + 4 * wave][0])), voff);
         }
-        const int t0 = vblk * kBS + 2 * vp;                  // step-relative token
-        const uint4 za = st * kFaStep + t0 < n ? vr[0] : make_uint4(0, 0, 0, 0);
-        const uint4 zb = st * kFaStep + t0 + 1 < n ? vr[1] : make_uint4(0, 0, 0, 0);
-        uint32_t* vt = reinterpret_cast<uint32_t*>(&S.vt[bf][0][0]);
-        constexpr int kRow = kFaVtStride / 2;                // dwords per V^T row
-#define PKV_VT(X) vt[(8 * vc + (X)) * kRow + t0 / 2] = pick<X>(za, zb);
-        PKV_VT(0) PKV_VT(1) PKV_VT(2) PKV_VT(3) PKV_VT(4) PKV_VT(5) PKV_VT(6) PKV_VT(7)
-#undef PKV_VT
     };
-    auto compute = [&](int st, int bf) {
+    // PV operand reads: ds_read_tr16_b64 gives lane m of each 16-lane group element j of
+    // source lane 4j + m / 4 at position m % 4. Source lane 4j + q of group G points at
+    // token 16s + 8e + 4h + j, dims 32dt + 16(G % 2) + 4q .. +3, so lane m receives dim
+    // 32dt + 16(G % 2) + m = 32dt + lane % 32 of tokens 16s + 8e + 4h + 0..3: the row and
+    // k order of the score registers that form the other operand.
+    const int tj = (lane % 16) / 4, tq = lane % 4, tg = (lane / 16) % 2;
+    auto v_operand = [&](int sl, int s, int dt) {
+        uint2 part[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int tok = 16 * s + 8 * e + 4 * h + tj;
+            const int chunk = (4 * dt + 2 * tg + tq / 2) ^ (4 * tj);
+            const char* p = reinterpret_cast<const char*>(&S.v[sl][tok][chunk]) + 8 * (tq % 2);
+            part[e] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t*)(p)));
+        }
+        return make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
+    };
+    auto compute = [&](int st, int sl) {
         const int tp0 = st * kFaStep;
         if (tp0 > last_w) return;                    // none of the wave's rows sees it
         f32x16_t sc = f32x16_t{};
 #pragma unroll
         for (int s = 0; s < kD / 16; ++s)
-            sc = Mma32<T>::mma(S.k[bf][r][(2 * s + h) ^ (r & 15)], qv[s], sc);
+            sc = Mma32<T>::mma(S.k[sl][r][(2 * s + h) ^ (r & 15)], qv[s], sc);
         // The VALU, not the matrix cores, bounds this loop (a wave64 VALU op takes four
         // cycles): steps that every row of the wave sees whole skip the mask, the scale
         // enters through one FMA before the exp (scale > 0, so the max of the raw scores
@@ -1467,24 +1515,25 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
         lsum += ps;
         // PV on 32x32x16 products over 16 tokens each. The k order inside a product is
         // free as long as both operands use it: lane l supplies its own score registers
-        // (tokens 16s + 4h + 0..3 and 16s + 8 + 4h + 0..3), and V^T is read in the same
-        // order (two 8-byte pieces of its row).
+        // (tokens 16s + 4h + 0..3 and 16s + 8 + 4h + 0..3), and the V operand is read in
+        // the same order.
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const uint4 pbk = make_uint4(pb[2 * s].x, pb[2 * s].y, pb[2 * s + 1].x, pb[2 * s + 1].y);
 #pragma unroll
-            for (int dt = 0; dt < kD / 32; ++dt) {
-                const uint16_t* row = &S.vt[bf][32 * dt + r][0];
-                const uint2 lo = *reinterpret_cast<const uint2*>(row + 16 * s + 4 * h);
-                const uint2 hi = *reinterpret_cast<const uint2*>(row + 16 * s + 8 + 4 * h);
-                acc[dt] = Mma32<T>::mma(make_uint4(lo.x, lo.y, hi.x, hi.y), pbk, acc[dt]);
-            }
+            for (int dt = 0; dt < kD / 32; ++dt)
+                acc[dt] = Mma32<T>::mma(v_operand(sl, s, dt), pbk, acc[dt]);
         }
     };
 
+    // Per table window: the loads of step st + kFaRing - 1 go out once every wave is past
+    // step st - 1 (whose slot they refill), so kFaRing - 1 steps are in flight while
+    // step st is computed; one barrier per step. The vector-memory counter wait before
+    // the barrier leaves the loads of later steps (four per thread and step) in flight.
     const int nbl = 2 * steps;                       // blocks the steps cover
-    for (w0 = 0; w0 < nbl; w0 += kTabMax) {
-        w1 = min(nbl, w0 + kTabMax);
+    static_assert(kFaRing == 3, "the waits below assume one later step in flight");
+    for (w0 = 0; w0 < nbl; w0 += kFaTab) {
+        w1 = min(nbl, w0 + kFaTab);
         __syncthreads();                             // the previous window is done
         for (int j = w0 + tid; j < w1; j += kThreads) {
             int phys = j < nb_ctx ? tables[(size_t)b * max_blocks + j] : -1;
@@ -1492,26 +1541,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
             S.tile[j - w0] = ok ? (uint32_t)phys * (uint32_t)num_kv_heads + (uint32_t)g
                                 : kNoTile;
         }
+        // no load of the compiler's own (the query row, the table) may be outstanding
+        // in the loop below, or its waits would also drain the LDS loads in flight
+        wait_vmem<0>();
         __syncthreads();
-        // Two register sets in ping-pong: the loads of step st + 2 go out while step st
-        // is computed, and step st + 1 (loaded a step earlier) goes to the other LDS
-        // buffer at the end of step st; one barrier per step.
-        const int s0 = w0 / 2, s1 = w1 / 2;
-        uint4 ka[2], va[2], kb[2], vb[2];
-        load_step(s0, ka, va);
-        if (s0 + 1 < s1) load_step(s0 + 1, kb, vb);
-        store_step(s0, 0, ka, va);
-        __syncthreads();
-        for (int st = s0; st < s1; st += 2) {
-            if (st + 2 < s1) load_step(st + 2, ka, va);
-            compute(st, 0);
-            if (st + 1 < s1) store_step(st + 1, 1, kb, vb);
-            __syncthreads();
-            if (st + 1 >= s1) break;
-            if (st + 3 < s1) load_step(st + 3, kb, vb);
-            compute(st + 1, 1);
-            if (st + 2 < s1) store_step(st + 2, 0, ka, va);
-            __syncthreads();
+        const int s0 = w0 / 2, ns = w1 / 2 - s0;
+        issue(s0, 0);
+        if (1 < ns) issue(s0 + 1, 1);
+        int sl = 0;
+        for (int i = 0; i < ns; ++i) {
+            if (i + 1 < ns) wait_vmem<4>(); else wait_vmem<0>();
+            barrier_only();
+            if (i + 2 < ns) issue(s0 + i + 2, sl == 0 ? 2 : sl - 1);
+            compute(s0 + i, sl);
+            sl = sl == 2 ? 0 : sl + 1;
         }
     }
     const float lt = lsum + __shfl_xor(lsum, 32);
