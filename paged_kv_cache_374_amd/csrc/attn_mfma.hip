@@ -233,22 +233,40 @@ struct KvNative {
         for (int e = 0; e < 4; ++e) v[e] = r.v[e];
     }
     // Append: chunk c (16 bytes) of the new K (kind 0) or V (kind 1) row of unit (b, g)
-    // goes to position n - 1 of the sequence (table row `table`), bit for bit. The source
-    // is loaded before the table entry is checked, so the two loads overlap.
+    // goes to position n - 1 of the sequence, bit for bit. It comes in two halves so a
+    // caller can issue the source loads early and store once the destination tile (the
+    // unit's last block, phys * Hkv + g, or kNoTile when its table entry is out of
+    // range) is known.
     static constexpr int kAppendChunks = kD * (int)sizeof(T) / 16;
+    struct AppendSrc {
+        uint4 val;
+    };
+    static __device__ __forceinline__ void append_load(AppendSrc& a, const T* __restrict__ new_k,
+                                                       const T* __restrict__ new_v, int b,
+                                                       int g, int Hkv, int kind, int c) {
+        const size_t src = ((size_t)b * Hkv + g) * kD;
+        a.val = reinterpret_cast<const uint4*>((kind ? new_v : new_k) + src)[c];
+    }
+    static __device__ __forceinline__ void append_store(const AppendSrc& a, T* k_cache,
+                                                        T* v_cache, uint32_t tile, int pos,
+                                                        int kind, int c, float, float) {
+        if (tile == kNoTile) return;
+        const size_t dst = ((size_t)tile * kBS + pos) * kD;
+        reinterpret_cast<uint4*>((kind ? v_cache : k_cache) + dst)[c] = a.val;
+    }
     static __device__ __forceinline__ void append(T* k_cache, T* v_cache,
                                                   const T* __restrict__ new_k,
                                                   const T* __restrict__ new_v,
                                                   const int32_t* __restrict__ table, int b,
                                                   int g, int Hkv, int n, int num_blocks,
-                                                  int kind, int c, float, float) {
+                                                  int kind, int c, float k_inv, float v_inv) {
+        AppendSrc a;
+        append_load(a, new_k, new_v, b, g, Hkv, kind, c);
         const int j = (n - 1) / kBS;
-        const size_t src = ((size_t)b * Hkv + g) * kD;
-        const uint4 val = reinterpret_cast<const uint4*>((kind ? new_v : new_k) + src)[c];
         const int phys = table[j];
-        if (phys < 0 || phys >= num_blocks) return;
-        const size_t dst = (((size_t)phys * Hkv + g) * kBS + (n - 1 - j * kBS)) * kD;
-        reinterpret_cast<uint4*>((kind ? v_cache : k_cache) + dst)[c] = val;
+        const bool ok = phys >= 0 && phys < num_blocks;
+        append_store(a, k_cache, v_cache, ok ? (uint32_t)phys * Hkv + g : kNoTile,
+                     n - 1 - j * kBS, kind, c, k_inv, v_inv);
     }
 };
 
@@ -331,20 +349,28 @@ struct KvFp8 {
     }
     // Append: chunk c (16 elements) of the new K or V row is quantised (binary32 product
     // with the reciprocal scale, then E4M3 nearest-even, saturating) into 16 codes at
-    // position n - 1 of the sequence.
+    // position n - 1 of the sequence. Split into source loads and the quantising store
+    // as for 16-bit caches.
     static constexpr int kAppendChunks = kD / 16;
-    static __device__ __forceinline__ void append(uint8_t* k_cache, uint8_t* v_cache,
-                                                  const T* __restrict__ new_k,
-                                                  const T* __restrict__ new_v,
-                                                  const int32_t* __restrict__ table, int b,
-                                                  int g, int Hkv, int n, int num_blocks,
-                                                  int kind, int c, float k_inv, float v_inv) {
-        const int j = (n - 1) / kBS;
+    struct AppendSrc {
+        uint4 lo, hi;
+    };
+    static __device__ __forceinline__ void append_load(AppendSrc& a, const T* __restrict__ new_k,
+                                                       const T* __restrict__ new_v, int b,
+                                                       int g, int Hkv, int kind, int c) {
         const uint4* src = reinterpret_cast<const uint4*>((kind ? new_v : new_k) +
                                                           ((size_t)b * Hkv + g) * kD + 16 * c);
+        a.lo = src[0];
+        a.hi = src[1];
+    }
+    static __device__ __forceinline__ void append_store(const AppendSrc& a, uint8_t* k_cache,
+                                                        uint8_t* v_cache, uint32_t tile, int pos,
+                                                        int kind, int c, float k_inv,
+                                                        float v_inv) {
+        if (tile == kNoTile) return;
         float f[16];
-        Vec16<T>::unpack(src[0], f);
-        Vec16<T>::unpack(src[1], f + 8);
+        Vec16<T>::unpack(a.lo, f);
+        Vec16<T>::unpack(a.hi, f + 8);
         const float inv = kind ? v_inv : k_inv;
         uint32_t w[4];
 #pragma unroll
@@ -352,11 +378,23 @@ struct KvFp8 {
             w[i] = fp8_e4m3_code(f[4 * i] * inv) | fp8_e4m3_code(f[4 * i + 1] * inv) << 8 |
                    fp8_e4m3_code(f[4 * i + 2] * inv) << 16 |
                    fp8_e4m3_code(f[4 * i + 3] * inv) << 24;
-        const int phys = table[j];
-        if (phys < 0 || phys >= num_blocks) return;
-        const size_t dst = (((size_t)phys * Hkv + g) * kBS + (n - 1 - j * kBS)) * kD + 16 * c;
+        const size_t dst = ((size_t)tile * kBS + pos) * kD + 16 * c;
         *reinterpret_cast<uint4*>((kind ? v_cache : k_cache) + dst) =
             make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    static __device__ __forceinline__ void append(uint8_t* k_cache, uint8_t* v_cache,
+                                                  const T* __restrict__ new_k,
+                                                  const T* __restrict__ new_v,
+                                                  const int32_t* __restrict__ table, int b,
+                                                  int g, int Hkv, int n, int num_blocks,
+                                                  int kind, int c, float k_inv, float v_inv) {
+        AppendSrc a;
+        append_load(a, new_k, new_v, b, g, Hkv, kind, c);
+        const int j = (n - 1) / kBS;
+        const int phys = table[j];
+        const bool ok = phys >= 0 && phys < num_blocks;
+        append_store(a, k_cache, v_cache, ok ? (uint32_t)phys * Hkv + g : kNoTile,
+                     n - 1 - j * kBS, kind, c, k_inv, v_inv);
     }
 };
 
@@ -583,15 +621,22 @@ __device__ __forceinline__ void merge_parts(const float (&rec)[NREC][Part<GMAX>:
 // so that branches on it are scalar and the compiler sees straight control flow.
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Largest sequence b with Hkv * pref[b] <= x (x below the total; pref in LDS). Such a
-// sequence is never empty: an empty one shares its prefix with the next.
+// Largest sequence b with Hkv * pref[b] <= x (x below the total, wave-uniform; pref in
+// LDS). Such a sequence is never empty: an empty one shares its prefix with the next.
+// Since pref is non-decreasing, b is a count: a ballot over every k-th entry
+// (k = ceil(num_seqs / 64)) finds the stretch of k sequences that holds b, a second
+// ballot counts inside it. One or two LDS round trips, where a binary search over 64
+// sequences takes six in a row.
 __device__ __forceinline__ int seq_of(const int* pref, int num_seqs, int Hkv, int x) {
-    int lo = 0, hi = num_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (Hkv * uni(pref[mid]) <= x) lo = mid; else hi = mid - 1;
-    }
-    return lo;
+    const int lane = __lane_id();
+    const int k = (num_seqs + 63) >> 6;
+    const int s = lane * k;
+    const bool le = s < num_seqs && Hkv * pref[s] <= x;
+    const int base = (__popcll(__ballot(le)) - 1) * k;
+    if (k == 1) return base;
+    const int s2 = base + 1 + lane;
+    const bool le2 = lane < k - 1 && s2 < num_seqs && Hkv * pref[s2] <= x;
+    return base + __popcll(__ballot(le2));
 }
 
 // The unit after (b, g): next KV head, else the first KV head of the next non-empty
@@ -728,11 +773,48 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
     const int x1 = shares.start(w + 1);
     if (x0 >= x1) return;
 
+    // ---- fused append, first half. The units whose last block lies in the share are
+    // consecutive: from the unit of the share's first block through the unit of its
+    // last block (that one only when it ends inside the share). Item `it` is unit
+    // au0 + it / (2 * chunks), its K (kind 0) or V row, chunk it % chunks. Each
+    // thread loads its first item's source now, so those loads overlap the table loads
+    // of the staging below; the destination comes from the staged table entry.
+    // The sequences of the share's first and last blocks bound every search below.
+    const int sb0 = seq_of(S.pref, num_seqs, Hkv, x0);
+    const int sb1 = seq_of(S.pref, num_seqs, Hkv, x1 - 1);
+    int au0 = 0, aitems = 0;
+    if (new_k != nullptr) {
+        const int p0 = uni(S.pref[sb0]), p1 = uni(S.pref[sb1]);
+        const int g0 = (x0 - Hkv * p0) / (uni(S.pref[sb0 + 1]) - p0);
+        const int g1 = (x1 - 1 - Hkv * p1) / (uni(S.pref[sb1 + 1]) - p1);
+        au0 = sb0 * Hkv + g0;
+        aitems = (sb1 * Hkv + g1 - au0 + 1) * 2 * KV::kAppendChunks;
+    }
+    // Item `it`: its unit (b, g), row kind and chunk c; returns the index in the share
+    // of the unit's last block, or -1 when that block lies past the share (or the
+    // sequence is empty).
+    auto item = [&](int it, int& b, int& g, int& kind, int& c) -> int {
+        const int u = au0 + it / (2 * KV::kAppendChunks);
+        b = u / Hkv;
+        g = u - b * Hkv;
+        kind = (it / KV::kAppendChunks) & 1;
+        c = it % KV::kAppendChunks;
+        const int nb = S.pref[b + 1] - S.pref[b];
+        const int last = Hkv * S.pref[b] + (g + 1) * nb - 1;
+        return (nb > 0 && last < x1) ? last - x0 : -1;
+    };
+    typename KV::AppendSrc a0;
+    int ai0 = -1, ab = 0, ag = 0, ak = 0, ac = 0;
+    if (tid < aitems) {
+        ai0 = item(tid, ab, ag, ak, ac);
+        KV::append_load(a0, new_k, new_v, ab, ag, Hkv, ak, ac);
+    }
+
     // ---- stage (tile, query row, valid tokens) of every block of the share. Each
     // thread finds its block's sequence by binary search over the prefix sums, so the
     // table loads of the whole share go out together.
     for (int xx = x0 + tid; xx < x1; xx += kThreads) {
-        int lo = 0, hi = num_seqs - 1;
+        int lo = sb0, hi = sb1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (Hkv * S.pref[mid] <= xx) lo = mid; else hi = mid - 1;
@@ -750,22 +832,21 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         S.qrow[xx - x0] = b * num_heads + g * group;
         S.valid[xx - x0] = (uint8_t)(ok ? (left < kBS ? left : kBS) : 0);
     }
-    // Fused append: the units whose last block lies in the share belong to the
-    // sequences from that of the share's first block to that of its last one.
-    if (new_k != nullptr) {
-        const int b0 = seq_of(S.pref, num_seqs, Hkv, x0);
-        const int b1 = seq_of(S.pref, num_seqs, Hkv, x1 - 1);
-        const int items = (b1 - b0 + 1) * Hkv * 2 * KV::kAppendChunks;
-        for (int it = tid; it < items; it += kThreads) {
-            const int u = it / (2 * KV::kAppendChunks);
-            const int b = b0 + u / Hkv, g = u - (u / Hkv) * Hkv;
-            const int nb = S.pref[b + 1] - S.pref[b];
-            const int last = Hkv * S.pref[b] + (g + 1) * nb - 1;
-            if (nb == 0 || last < x0 || last >= x1) continue;
-            KV::append(k_cache, v_cache, new_k, new_v, tables + (size_t)b * max_blocks, b, g,
-                       Hkv, S.ctx[b], num_blocks, (it / KV::kAppendChunks) & 1,
-                       it % KV::kAppendChunks, k_inv, v_inv);
-        }
+    __syncthreads();
+    // ---- fused append, second half: the stores, to the staged tile of each unit's last
+    // block (kNoTile for an out-of-range table entry: nothing is written). The workgroup
+    // barrier below orders them before the waves' loads of that block.
+    if (ai0 >= 0)
+        KV::append_store(a0, k_cache, v_cache, S.tile[ai0], (S.ctx[ab] - 1) % kBS, ak, ac,
+                         k_inv, v_inv);
+    for (int it = tid + kThreads; it < aitems; it += kThreads) {
+        int b, g, kind, c;
+        const int i = item(it, b, g, kind, c);
+        if (i < 0) continue;
+        typename KV::AppendSrc a;
+        KV::append_load(a, new_k, new_v, b, g, Hkv, kind, c);
+        KV::append_store(a, k_cache, v_cache, S.tile[i], (S.ctx[b] - 1) % kBS, kind, c, k_inv,
+                         v_inv);
     }
     __syncthreads();
 
