@@ -697,11 +697,74 @@ struct BalancedLds {
     uint8_t valid[kTabMax];           // tokens of the block inside the context
     KTile ktile[NW];
     float part[NW * 2][Part<GMAX>::kFloats];   // wave v: [2v] first, [2v+1] last unit piece
-    int4 ends[NW][2];                          // wave v's first and last unit (b, g, su, ue)
     MergePlan<NW> plan[NW + 1];                // candidate units of the end phase
     int nplan;                                 // how many of them have work
+    int4 cross[2];                             // units crossing the share's edges (b, g, su, ue)
+    int ncross;                                // how many
     int flag[2];
 };
+
+// End-phase plan of a share [x0, x1) cut into quarters of Cw blocks (run by one wave;
+// sb0..sb1 are the sequences the share touches). Candidate k is the first unit of
+// quarter k (k < nq) or the share's last unit (k = nq); lane k finds it. Units cut
+// between waves or between workgroups are all among the candidates, and at most two
+// of them (the share's first and last unit) cross its edges. For each candidate with
+// work, the plan names the LDS records of its pieces and where the merged result goes:
+// output rows for a unit inside the share, this workgroup's partial slot for a crossing
+// one (published for the count round).
+template <int GMAX, int NW>
+__device__ __forceinline__ void plan_end_phase(BalancedLds<GMAX, NW>& S, int sb0, int sb1,
+                                               int Hkv, int x0, int x1, int Cw, int w,
+                                               int num_heads, int group, int lane) {
+    const int nq = (x1 - x0 + Cw - 1) / Cw;   // non-empty quarters
+    const int k = lane;
+    int b = 0, g = 0, su = 0, ue = 0;
+    if (k <= nq) {
+        const int pos = k < nq ? x0 + k * Cw : x1 - 1;
+        int lo = sb0, hi = sb1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (Hkv * S.pref[mid] <= pos) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+        const int nb = S.pref[b + 1] - S.pref[b];
+        g = (pos - Hkv * S.pref[b]) / nb;
+        su = Hkv * S.pref[b] + g * nb;
+        ue = su + nb;
+    }
+    const int prev_su = __shfl(su, k > 0 ? k - 1 : 0);
+    // the crossing units: the first candidate if it starts before the share or ends
+    // after it, the last if it differs and ends after it
+    const int fb = __shfl(b, 0), fg = __shfl(g, 0), fs = __shfl(su, 0), fe = __shfl(ue, 0);
+    const int lb = __shfl(b, nq), lg = __shfl(g, nq), ls = __shfl(su, nq),
+              le = __shfl(ue, nq);
+    if (k == 0) {
+        int n = 0;
+        if (fs < x0 || fe > x1) S.cross[n++] = make_int4(fb, fg, fs, fe);
+        if (ls != fs && le > x1) S.cross[n++] = make_int4(lb, lg, ls, le);
+        S.ncross = n;
+    }
+    if (k <= nq) {
+        MergePlan<NW> pl;
+        const int lo = su > x0 ? su : x0, hi = ue < x1 ? ue : x1;
+        const int wlo = (lo - x0) / Cw, whi = (hi - 1 - x0) / Cw;
+        const bool crosses = su < x0 || ue > x1;
+        pl.cross = crosses;
+        // same unit as the previous candidate, or one wave saw all of it (written)
+        pl.n = ((k > 0 && prev_su == su) || (wlo == whi && !crosses)) ? 0 : whi - wlo + 1;
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            const int v = wlo + j < whi ? wlo + j : whi;
+            pl.rec[j] = 2 * v + (su <= x0 + v * Cw ? 0 : 1);
+        }
+        pl.row = b * num_heads + g * group;
+        pl.slot = (2 * w + (su <= x0 ? 0 : 1)) * Part<GMAX>::kFloats;
+        // keep only the candidates with work, packed to the front
+        const unsigned long long act = __ballot(pl.n > 0);
+        if (pl.n > 0) S.plan[__popcll(act & ((1ull << k) - 1))] = pl;
+        if (k == 0) S.nplan = __popcll(act);
+    }
+}
 
 // NW waves per workgroup, one workgroup per CU. 16-bit caches use one wave per SIMD:
 // with two waves on a SIMD the older one was measured to stream ~1.5x faster than the
@@ -860,7 +923,6 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         int g = (xa - Hkv * uni(S.pref[b])) / nb;
         int su = Hkv * uni(S.pref[b]) + g * nb;
         int ue = su + nb;
-        if (lane == 0) S.ends[wave][0] = make_int4(b, g, su, ue);
         int bn, gn;
         next_unit(S.pref, num_seqs, Hkv, b, g, bn, gn);
         // Every step issues one block (a zero-record buffer past the quarter's end), so
@@ -878,6 +940,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         typename KV::Regs R0, R1;
         issue(R0, xa);
         issue(R1, xa + 1);
+        // While the first blocks are in flight, wave 0 plans the end phase: it depends
+        // only on where the quarters and units begin and end, not on the data.
+        if (wave == 0) plan_end_phase(S, sb0, sb1, Hkv, x0, x1, Cw, w, num_heads, group, lane);
         WaveState st;
         reset(st);
         int x = xa;
@@ -921,65 +986,21 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         // The padding loads touch no memory, so this wait is short.
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         flush();
-        if (lane == 0) S.ends[wave][1] = make_int4(b, g, su, ue);
     }
     __syncthreads();
 
-    // ---- units cut between waves or between workgroups. Each such unit is the first
-    // unit of some non-empty quarter or the share's last unit. At most two of them (the
-    // share's first and last unit) cross its edges; all other pieces of those belong to
-    // other workgroups.
+    // ---- units cut between waves or between workgroups (planned by wave 0 before its
+    // loop: plan_end_phase). Pieces of a crossing unit outside the share belong to other
+    // workgroups.
     const __amdgpu_buffer_rsrc_t R = __builtin_amdgcn_make_buffer_rsrc(
         partials, 0, 2 * kMaxWorkers * Part<GMAX>::kFloats * (int)sizeof(float),
         kRawBufferWord3);
-    const int nq = (x1 - x0 + Cw - 1) / Cw;   // non-empty quarters
-    // candidate k: first unit of quarter k (k < nq), or the share's last unit (k = nq)
-    auto cand = [&](int k) { return k < nq ? S.ends[k][0] : S.ends[nq - 1][1]; };
-    // The crossing units: the first candidate if it starts before the share or ends
-    // after it, the last if it differs and ends after it.
-    int ncross = 0;
-    int cb0 = 0, cg0 = 0, cs0 = 0, ce0 = 0, cb1 = 0, cg1 = 0, cs1 = 0, ce1 = 0;
-    {
-        const int4 f = cand(0), l = cand(nq);
-        if (f.z < x0 || f.w > x1) {
-            cb0 = uni(f.x); cg0 = uni(f.y); cs0 = uni(f.z); ce0 = uni(f.w);
-            ncross = 1;
-        }
-        if (l.z != f.z && l.w > x1) {
-            if (ncross == 0) { cb0 = uni(l.x); cg0 = uni(l.y); cs0 = uni(l.z); ce0 = uni(l.w); }
-            else { cb1 = uni(l.x); cg1 = uni(l.y); cs1 = uni(l.z); ce1 = uni(l.w); }
-            ++ncross;
-        }
-    }
-    // Lane k of wave 0 writes the merge plan of candidate k; then every thread of the
-    // workgroup takes (candidate, dims) items, so the merges run on all waves at once.
-    // A unit inside the share is written out; a crossing unit's merged piece is
-    // published for the count round below.
-    if (tid <= nq) {
-        const int k = tid;
-        const int4 u = cand(k);
-        MergePlan<NW> pl;
-        const int su = u.z, ue = u.w;
-        const int lo = su > x0 ? su : x0, hi = ue < x1 ? ue : x1;
-        const int wlo = (lo - x0) / Cw, whi = (hi - 1 - x0) / Cw;
-        const bool crosses = su < x0 || ue > x1;
-        pl.cross = crosses;
-        // same unit as the previous candidate, or one wave saw all of it (written)
-        pl.n = ((k > 0 && cand(k - 1).z == su) || (wlo == whi && !crosses))
-                   ? 0 : whi - wlo + 1;
-#pragma unroll
-        for (int j = 0; j < NW; ++j) {
-            const int v = wlo + j < whi ? wlo + j : whi;
-            pl.rec[j] = 2 * v + (su <= x0 + v * Cw ? 0 : 1);
-        }
-        pl.row = u.x * num_heads + u.y * group;
-        pl.slot = (2 * w + (su <= x0 ? 0 : 1)) * Part<GMAX>::kFloats;
-        // keep only the candidates with work, packed to the front
-        const unsigned long long act = __ballot(pl.n > 0);
-        if (pl.n > 0) S.plan[__popcll(act & ((1ull << k) - 1))] = pl;
-        if (k == 0) S.nplan = __popcll(act);
-    }
-    __syncthreads();
+    // The crossing units and the merge plan were written before the loop (by wave 0).
+    const int ncross = uni(S.ncross);
+    const int cb0 = uni(S.cross[0].x), cg0 = uni(S.cross[0].y), cs0 = uni(S.cross[0].z),
+              ce0 = uni(S.cross[0].w);
+    const int cb1 = uni(S.cross[1].x), cg1 = uni(S.cross[1].y), cs1 = uni(S.cross[1].z),
+              ce1 = uni(S.cross[1].w);
     constexpr int kCols = kD / 4;   // float4 columns of a head's row
     for (int it = tid; it < S.nplan * group * kCols; it += kThreads) {
         const int k = it / (group * kCols), i = it - k * (group * kCols);
