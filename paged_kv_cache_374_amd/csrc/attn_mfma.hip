@@ -404,6 +404,11 @@ __device__ __forceinline__ uint4 k_operand(const KTile& kt, int kk, int lane) {
     return kt.chunk[c][(4 * kk + grp) ^ (c & 7)];
 }
 
+// How far (base 2) a block's scores may pass a column's reference maximum before the
+// reference moves: weights stay at most 2^8, far inside the range of binary32 sums and
+// of the bfloat16 / float16 operands of the PV product.
+constexpr float kLazyMax = 8.f;
+
 // The query-dependent half of a fold: scores of one 16-column tile against the block's
 // K operand `ka` (k_operand order), masked to the first `lim` tokens for the lane's
 // column, the online-softmax update, and the PV product with the block's V rows `v`.
@@ -424,9 +429,24 @@ __device__ __forceinline__ void fold_tile(WaveState& s, const uint4 (&ka)[4],
     }
     mb = fmaxf(mb, __shfl_xor(mb, 16));
     mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float mn = fmaxf(s.m, mb);
-    const float alpha = (s.m == kNegInf) ? 0.f : fast_exp2(s.m - mn);
-    const float mu = (mn == kNegInf) ? 0.f : mn;
+    // s.m is a reference maximum, moved only when a block's maximum passes it by more
+    // than kLazyMax (base-2 units), so weights stay below 2^kLazyMax. Most blocks leave
+    // it in place: their rescale factor would be exactly 1, and the wave skips the
+    // rescale of o (a wave-uniform branch). The result is the same ratio o / l.
+    if (__ballot(mb > s.m + kLazyMax) != 0) {
+        const float mn = mb > s.m + kLazyMax ? mb : s.m;
+        const float alpha = (s.m == kNegInf) ? 0.f : fast_exp2(s.m - mn);
+        s.lsum *= alpha;
+        s.m = mn;
+        // o[.][e] belongs to head 4(l/16)+e, whose factor lives in lane 4(l/16)+e.
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a = __shfl(alpha, 4 * grp + e);
+#pragma unroll
+            for (int n = 0; n < 8; ++n) s.o[n][e] *= a;
+        }
+    }
+    const float mu = (s.m == kNegInf) ? 0.f : s.m;
     float p[4];
     float ps = 0.f;
 #pragma unroll
@@ -434,15 +454,7 @@ __device__ __forceinline__ void fold_tile(WaveState& s, const uint4 (&ka)[4],
         p[e] = fast_exp2(x[e] - mu);
         ps += p[e];
     }
-    s.lsum = s.lsum * alpha + ps;
-    s.m = mn;
-    // o[.][e] belongs to head 4(l/16)+e, whose factor lives in lane 4(l/16)+e.
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float a = __shfl(alpha, 4 * grp + e);
-#pragma unroll
-        for (int n = 0; n < 8; ++n) s.o[n][e] *= a;
-    }
+    s.lsum += ps;
     const uint2 pa = make_uint2(Mma<T>::pack(p[0], p[1]), Mma<T>::pack(p[2], p[3]));
 #define PKV_PV_STEP(N)                                                                  \
     s.o[N] = Mma<T>::pv(pa, make_uint2(pick<N>(v[0], v[1]), pick<N>(v[2], v[3])), s.o[N]);
@@ -474,9 +486,7 @@ __device__ __forceinline__ void stage_block(const typename KV::Regs& r, KTile& k
 
 // Fold one block into the wave's state. `valid` = tokens of the block inside the
 // context (0 masks the whole block); `lim` <= valid = tokens that count for the lane's
-// column (decode: lim = valid; query chunks: the column's causal limit). The running
-// max is updated every block (exact online softmax), so the loop carries no
-// conditionally updated state.
+// column (decode: lim = valid; query chunks: the column's causal limit).
 template <typename T, typename KV>
 __device__ __forceinline__ void fold_block(WaveState& s, typename KV::Regs& r, KTile& kt,
                                            int valid, int lim, float scale_log2, int lane) {
