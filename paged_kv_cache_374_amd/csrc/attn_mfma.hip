@@ -13,7 +13,7 @@
 //   * QK^T of a block is one 16x16 tile: rows = the block's 16 tokens, columns = the
 //     query heads of the KV head (G <= 16, unused columns see a zero query). K arrives
 //     in whole 128-byte lines and passes through a per-wave LDS tile (chunk c of row t
-//     stored at slot c ^ (t & 7): conflict-free writes and operand reads) into the A
+//     stored at slot c ^ t: conflict-free writes and operand reads) into the A
 //     operand of v_mfma_f32_16x16x32; Q is the B operand with the same dim assignment.
 //   * The score tile comes out with lane l holding tokens 4(l/16)+r (r = 0..3) of
 //     head l%16, which is exactly the A-operand layout of v_mfma_f32_16x16x16 for
@@ -149,8 +149,11 @@ __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int offs
 }
 
 // Per-wave LDS tile that turns the line-coalesced K rows into MFMA operand order.
-// 16-byte chunk ch of token row t sits at slot ch ^ (t & 7) of the row, so both the
-// row-wise writes and the operand reads (16 rows, one chunk each) hit distinct banks.
+// 16-byte chunk ch of token row t (0..15) sits at slot ch ^ t of the row. Every row
+// starts on the same bank, so an operand read (one chunk from each of the 16 rows)
+// must find 16 different slots: with ch ^ (t & 7), rows t and t + 8 shared a slot,
+// and the LDS counters showed 19% (16-bit caches) and 39% (8-bit) of active LDS cycles
+// lost to bank conflicts. Row-wise writes stay a permutation of the row's slots.
 struct KTile {
     uint4 chunk[kBS][kD / 8];
 };
@@ -225,7 +228,7 @@ struct KvNative {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 4 * i + grp;
-            kt.chunk[t][c ^ (t & 7)] = r.k[i];
+            kt.chunk[t][c ^ (t & 15)] = r.k[i];
         }
     }
     static __device__ __forceinline__ void widen_v(const Regs& r, uint4 (&v)[4]) {
@@ -339,8 +342,8 @@ struct KvFp8 {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int t = 8 * i + (lane >> 3);
-            kt.chunk[t][c2 ^ (t & 7)] = widen8<T>(r.k[i].x, r.k[i].y);
-            kt.chunk[t][(c2 + 1) ^ (t & 7)] = widen8<T>(r.k[i].z, r.k[i].w);
+            kt.chunk[t][c2 ^ (t & 15)] = widen8<T>(r.k[i].x, r.k[i].y);
+            kt.chunk[t][(c2 + 1) ^ (t & 15)] = widen8<T>(r.k[i].z, r.k[i].w);
         }
     }
     static __device__ __forceinline__ void widen_v(const Regs& r, uint4 (&v)[4]) {
@@ -401,7 +404,7 @@ struct KvFp8 {
 // A operand of QK product kk for lane l: token l%16, dims 32kk + 8(l/16) .. +7.
 __device__ __forceinline__ uint4 k_operand(const KTile& kt, int kk, int lane) {
     const int c = lane & 15, grp = lane >> 4;
-    return kt.chunk[c][(4 * kk + grp) ^ (c & 7)];
+    return kt.chunk[c][(4 * kk + grp) ^ c];
 }
 
 // How far (base 2) a block's scores may pass a column's reference maximum before the

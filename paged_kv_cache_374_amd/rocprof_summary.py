@@ -7,6 +7,9 @@
 --trace: a `rocprofv3 --kernel-trace --stats --output-format csv` output directory
 (its *_kernel_stats.csv gives per-kernel call counts and durations).
 --fetch / --write: `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` directories.
+--pmc-extra (repeatable): further `--pmc` directories; every counter they hold for the
+kernel is listed, with LDS bank-conflict share and mean resident waves per CU derived
+where their counters are present.
 The counters are calibrated with the copy_blocks kernel profiled in the same run
 (`bench.py --calibrate` issues it on a known number of bytes): true bytes / counter
 reading of that kernel is the factor applied to the decode kernel's readings.
@@ -70,6 +73,43 @@ def counter_means(pmc_dir: str, counter: str):
     return path, {k: statistics.mean(v) for k, v in per.items()}
 
 
+def all_counter_means(pmc_dir: str, needle: str):
+    """Mean value per dispatch of every counter collected for the kernel matching
+    `needle`, plus the agent's CU and XCC counts and wave slots per CU."""
+    path = _one(os.path.join(pmc_dir, "**", "*counter_collection.csv"))
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if needle in r["Kernel_Name"]:
+                per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    agent = {}
+    with open(_one(os.path.join(pmc_dir, "**", "*agent_info.csv"))) as f:
+        for r in csv.DictReader(f):
+            if r.get("Cu_Count", "0") not in ("", "0"):
+                agent = {"cus": int(r["Cu_Count"]), "xcc": int(r["Num_Xcc"]),
+                         "slots": int(r["Max_Waves_Per_Cu"])}
+    return path, {k: statistics.mean(v) for k, v in per.items()}, agent
+
+
+def derived_rows(c, agent):
+    """Readings derived from the SQ/GRBM counters, where present. SQ_WAVE_CYCLES counts
+    in units of four cycles; GRBM_GUI_ACTIVE comes summed over the XCCs."""
+    out = []
+    if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_LDS_IDX_ACTIVE"):
+        out.append(("LDS bank-conflict cycles / LDS active cycles",
+                    f"{100 * c['SQ_LDS_BANK_CONFLICT'] / c['SQ_LDS_IDX_ACTIVE']:.1f}%"))
+    if "SQ_WAVE_CYCLES" in c and c.get("GRBM_GUI_ACTIVE") and agent:
+        gui = c["GRBM_GUI_ACTIVE"] / agent["xcc"]
+        waves = 4 * c["SQ_WAVE_CYCLES"] / gui / agent["cus"]
+        out.append(("mean resident waves per CU over the kernel",
+                    f"{waves:.2f} of {agent['slots']} ({100 * waves / agent['slots']:.1f}%)"))
+    if "SQ_INSTS_VALU" in c and c.get("SQ_WAVES"):
+        out.append(("VALU instructions per wave", f"{c['SQ_INSTS_VALU'] / c['SQ_WAVES']:.0f}"))
+    if "SQ_INSTS_MFMA" in c and c.get("SQ_WAVES"):
+        out.append(("MFMA instructions per wave", f"{c['SQ_INSTS_MFMA'] / c['SQ_WAVES']:.0f}"))
+    return out
+
+
 def pick(names, needle):
     hits = [n for n in names if needle in n]
     if not hits:
@@ -91,6 +131,9 @@ def main():
     ap.add_argument("--pmc-command", default="")
     ap.add_argument("--out", required=True)
     ap.add_argument("--traffic-json")
+    ap.add_argument("--pmc-extra", action="append", default=[],
+                    help="further `rocprofv3 --pmc` output directories (LDS, occupancy, ...)")
+    ap.add_argument("--pmc-extra-command", default="")
     args = ap.parse_args()
 
     tpath, rows = kernel_stats(args.trace)
@@ -133,6 +176,20 @@ def main():
                   f"{w_factor:.3f} | {write[kw]:.0f} | {wb:.0f} |", "",
                   f"HBM traffic per launch {traffic:.0f} B = "
                   f"{traffic / args.bytes_per_launch:.3f} x the algorithmic bytes."]
+    if args.pmc_extra:
+        lines += ["", f"Further counter passes: `{args.pmc_extra_command}`", "",
+                  "| counter | mean per dispatch of the kernel |", "|---|---|"]
+        merged, agent = {}, {}
+        for d_ in args.pmc_extra:
+            _, c, ag = all_counter_means(d_, args.kernel)
+            merged.update(c)
+            agent = agent or ag
+        for k in sorted(merged):
+            lines.append(f"| {k} | {merged[k]:.0f} |")
+        rows_d = derived_rows(merged, agent)
+        if rows_d:
+            lines += ["", "| derived | value |", "|---|---|"]
+            lines += [f"| {k} | {v} |" for k, v in rows_d]
     os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
