@@ -1090,6 +1090,41 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
     }
 }
 
+// ------------------------------------------------------------------ long with short
+// Kernels that give each (sequence, KV head) its own workgroup launch a grid of
+// (x, KV head, sequence) with two workgroups per CU, all resident at once. The
+// dispatcher hands every CU one workgroup of the grid's first half, then one of its
+// second half, so a CU that drew two long contexts would set the kernel's time. The
+// first half therefore takes the sequences in decreasing order of context length and
+// the second half in increasing order: long pairs with short. Every workgroup ranks
+// the clipped lengths itself, in `keys` (LDS, at least nseq entries; ties by index).
+// Batches above kPerUnitMaxSeqs keep their order. Has barriers: all threads must call
+// it.
+
+__device__ __forceinline__ int paired_sequence(const int32_t* __restrict__ ctx_lens, int nseq,
+                                               int b, int cap, uint32_t* keys, int& slot,
+                                               int tid, int nthreads) {
+    if (nseq <= 1 || nseq > kPerUnitMaxSeqs) return b;
+    const int half = (nseq + 1) / 2;
+    const int want = b < half ? b : nseq - 1 - (b - half);
+    for (int u = tid; u < nseq; u += nthreads) {
+        const int x = ctx_lens[u];
+        keys[u] = (uint32_t)(x < 0 ? 0 : (x > cap ? cap : x));
+    }
+    __syncthreads();
+    for (int u = tid; u < nseq; u += nthreads) {
+        const uint32_t key = keys[u];
+        int rank = 0;
+        for (int v = 0; v < nseq; ++v) {
+            const uint32_t kv = keys[v];
+            rank += (kv > key || (kv == key && v < u)) ? 1 : 0;
+        }
+        if (rank == want) slot = u;
+    }
+    __syncthreads();
+    return slot;
+}
+
 // ------------------------------------------------------------------ partitioned kernel
 template <int GMAX>
 struct PartLds {
@@ -1097,6 +1132,7 @@ struct PartLds {
     uint8_t valid[kTabMax];
     KTile ktile[kWaves];
     float part[kWaves][Part<GMAX>::kFloats];
+    int seq;
 };
 
 template <typename T, typename KV, int GMAX>
@@ -1108,9 +1144,15 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     int group, int max_blocks, int num_blocks, int part_blocks, int max_parts,
     float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
     __shared__ PartLds<GMAX> S;
-    const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int p = blockIdx.x, g = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int cap = max_blocks * kBS;
+    // one partition per context: one workgroup per (sequence, KV head), long paired
+    // with short on a CU
+    const int b = gridDim.x == 1
+                      ? paired_sequence(ctx_lens, gridDim.z, blockIdx.z, cap, S.tile, S.seq, tid,
+                                        kThreads)
+                      : blockIdx.z;
     int n = ctx_lens[b];
     n = n < 0 ? 0 : (n > cap ? cap : n);
     const int nb = (n + kBS - 1) / kBS;
@@ -1212,6 +1254,7 @@ struct ChunkLds {
     uint8_t valid[kTabMax];
     KTile ktile[kWaves];
     float part[kWaves][Part<16>::kFloats];
+    int seq;
 };
 
 // A wave's state -> normalised output rows for columns c < ncols, column c going to
@@ -1276,8 +1319,11 @@ __global__ __launch_bounds__(kThreads) void chunk_split_kernel(
     float scale_log2, float out_scale, int num_query_tokens, int num_heads, int num_kv_heads,
     int group, int tq, int max_blocks, int num_blocks) {
     __shared__ ChunkLds S;
-    const int g = blockIdx.y, b = blockIdx.z;
+    const int g = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+    // long contexts paired with short ones on a CU (paired_sequence)
+    const int b = paired_sequence(ctx_lens, gridDim.z, blockIdx.z, max_blocks * kBS, S.tile,
+                                  S.seq, tid, kThreads);
     const int r0 = query_start[b], r1 = query_start[b + 1];
     // rows outside the query array or a decreasing start: nothing is read or written
     if (r0 < 0 || r1 < r0 || r1 > num_query_tokens) return;

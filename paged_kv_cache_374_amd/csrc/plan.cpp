@@ -58,7 +58,19 @@ int plan_decode(const DecodeShape& s, DecodePlan* plan) {
     const bool fits = s.num_seqs <= kMaxSeqsBalanced &&
                       all_blocks <= (long long)kMaxWorkers * kShareMax &&
                       (size_t)s.num_seqs * s.num_kv_heads * sizeof(int32_t) <= kCounterBytes;
-    if (mfma && s.partition_size == 0 && fits) {
+    // Automatic choice on the matrix-core path: one workgroup per (sequence, KV head),
+    // long contexts paired with short ones on a CU, when there are enough units for two
+    // per CU and no context can be longer than kPerUnitMaxBlocks blocks (which bounds
+    // what one long unit can cost). It needs no workspace and no merges between
+    // workgroups. Otherwise the balanced split, which evens out any length mix.
+    const bool per_unit = mfma && s.partition_size == 0 && s.num_seqs <= kPerUnitMaxSeqs &&
+                          (long long)s.num_seqs * s.num_kv_heads >= kPerUnitMinUnits &&
+                          s.max_blocks <= kPerUnitMaxBlocks;
+    if (per_unit) {
+        p.path = Path::MfmaPartitioned;
+        p.partition_tokens = s.max_blocks * s.block_size;
+        p.max_partitions = 1;
+    } else if (mfma && s.partition_size == 0 && fits) {
         p.path = Path::MfmaBalanced;
         p.max_workers = kMaxWorkers;
         const size_t slot = (size_t)balanced_slot_floats(mfma_gmax(group)) * sizeof(float);

@@ -195,6 +195,45 @@ def test_llama3_8b_decode_full():
     assert _max_err(out, want) <= TOL[torch.bfloat16]
 
 
+def test_per_unit_path_ragged_lengths():
+    """512 (sequence, KV head) units whose table rows hold at most 128 blocks take one
+    workgroup per unit, long contexts paired with short ones on a CU (no workspace is
+    the sign of that path). Ragged lengths with empty contexts, one-token contexts and
+    block-edge tails: full output against the oracle, deterministic, and the fused step
+    bit-identical to the two-call form, caches byte for byte."""
+    lens = [0, 1, 15, 16, 17, 100, 513, 2048, 2047, 33, 1024, 7, 300, 1500, 64, 65] * 8
+    _say(f"per-unit path: {len(lens)} sequences x 4 KV heads")
+    s = W.batch_with_lengths(2900, lens, num_heads=16, num_kv_heads=4, head_dim=128,
+                             block_size=16, dtype=torch.bfloat16, device=DEV)
+    assert s.block_tables.shape[1] <= 128
+    # the per-unit path needs no workspace: the C call succeeds without one (the
+    # balanced path would return PKV_E_WORKSPACE)
+    lib = pkv.load()
+    out0 = torch.full_like(s.q, float("nan"))
+    rc = lib.pkv_paged_attention_decode(
+        out0.data_ptr(), s.q.data_ptr(), s.k_cache.data_ptr(), s.v_cache.data_ptr(),
+        s.block_tables.data_ptr(), s.context_lens.data_ptr(), float(s.scale), len(lens), 16,
+        4, 128, 16, s.block_tables.shape[1], s.k_cache.shape[0], 1, 0, None, 0,
+        torch.cuda.current_stream(DEV).cuda_stream)
+    assert rc == 0, pkv.strerror(rc)
+    out = decode(s)
+    assert torch.equal(out, out0)
+    assert _max_err(out, oracle_decode(s)) <= TOL[torch.bfloat16]
+    assert torch.equal(out, decode(s)), "deterministic"
+    W.with_append(s, seed=2900)
+    kc_a, vc_a = s.k_cache.clone(), s.v_cache.clone()
+    kc_b, vc_b = s.k_cache.clone(), s.v_cache.clone()
+    out_a, out_b = torch.empty_like(s.q), torch.empty_like(s.q)
+    pkv.paged_attention_decode_append(out_a, s.q, s.new_k, s.new_v, kc_a, vc_a, s.block_tables,
+                                      s.context_lens, s.scale)
+    pkv.reshape_and_cache(s.new_k, s.new_v, kc_b, vc_b, s.slot_mapping)
+    pkv.paged_attention_decode(out_b, s.q, kc_b, vc_b, s.block_tables, s.context_lens,
+                               s.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(kc_a, kc_b) and torch.equal(vc_a, vc_b), "fused append differs"
+    assert torch.equal(out_a, out_b), "fused step != two calls"
+
+
 def test_llama_70b_decode_sampled():
     _say("llama_70b_decode: 512 sampled rows vs oracle")
     s = W.llama_70b_decode(device=DEV, gen_device=DEV)
