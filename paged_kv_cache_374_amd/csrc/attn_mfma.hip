@@ -1092,12 +1092,14 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
 
 // ------------------------------------------------------------------ long with short
 // Kernels that give each (sequence, KV head) its own workgroup launch a grid of
-// (x, KV head, sequence) with two workgroups per CU, all resident at once. The
-// dispatcher hands every CU one workgroup of the grid's first half, then one of its
-// second half, so a CU that drew two long contexts would set the kernel's time. The
-// first half therefore takes the sequences in decreasing order of context length and
-// the second half in increasing order: long pairs with short. Every workgroup ranks
-// the clipped lengths itself, in `keys` (LDS, at least nseq entries; ties by index).
+// (x, KV head, sequence) with two workgroups per CU. When the grid is resident at once
+// (at most kPerUnitMinUnits workgroups), the dispatcher hands every CU one workgroup of
+// the grid's first half, then one of its second half, so a CU that drew two long
+// contexts would set the kernel's time. The first half therefore takes the sequences
+// in decreasing order of context length and the second half in increasing order: long
+// pairs with short. A larger grid runs in rounds and takes them longest first
+// throughout, so the longest start earliest. Every workgroup ranks the clipped lengths
+// itself, in `keys` (LDS, at least nseq entries; ties by index).
 // Batches above kPerUnitMaxSeqs keep their order. Has barriers: all threads must call
 // it.
 
@@ -1106,7 +1108,10 @@ __device__ __forceinline__ int paired_sequence(const int32_t* __restrict__ ctx_l
                                                int tid, int nthreads) {
     if (nseq <= 1 || nseq > kPerUnitMaxSeqs) return b;
     const int half = (nseq + 1) / 2;
-    const int want = b < half ? b : nseq - 1 - (b - half);
+    // more workgroups than two per CU: longest first throughout (the grid runs in
+    // rounds, and the longest should start earliest)
+    const bool rounds = (long long)nseq * gridDim.y * gridDim.x > kPerUnitMinUnits;
+    const int want = (rounds || b < half) ? b : nseq - 1 - (b - half);
     for (int u = tid; u < nseq; u += nthreads) {
         const int x = ctx_lens[u];
         keys[u] = (uint32_t)(x < 0 ? 0 : (x > cap ? cap : x));

@@ -52,12 +52,12 @@ constexpr int kMaxGroupGeneric = 8;
 // Sequences the balanced path scans in its prologue (LDS-resident prefix sums).
 constexpr int kMaxSeqsBalanced = 4096;
 // The automatic choice of one workgroup per (sequence, KV head) on the matrix-core
-// path: at least this many units (two per CU of a 256-CU MI355X, so long contexts can
-// pair with short ones), at most this many blocks per table row (2048 tokens at block
+// path: at least this many units (two per CU of a 256-CU MI355X, the grid that is
+// resident at once), at most this many blocks per table row (4096 tokens at block
 // size 16), and at most this many sequences (the batches whose lengths the kernel
 // ranks).
 constexpr int kPerUnitMinUnits = 512;
-constexpr int kPerUnitMaxBlocks = 128;
+constexpr int kPerUnitMaxBlocks = 256;
 constexpr int kPerUnitMaxSeqs = 512;
 
 // Validate sizes and choose a path. Returns 0 or a negative PKV_E_* code.

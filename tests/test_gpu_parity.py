@@ -195,17 +195,19 @@ def test_llama3_8b_decode_full():
     assert _max_err(out, want) <= TOL[torch.bfloat16]
 
 
-def test_per_unit_path_ragged_lengths():
-    """512 (sequence, KV head) units whose table rows hold at most 128 blocks take one
-    workgroup per unit, long contexts paired with short ones on a CU (no workspace is
-    the sign of that path). Ragged lengths with empty contexts, one-token contexts and
-    block-edge tails: full output against the oracle, deterministic, and the fused step
-    bit-identical to the two-call form, caches byte for byte."""
-    lens = [0, 1, 15, 16, 17, 100, 513, 2048, 2047, 33, 1024, 7, 300, 1500, 64, 65] * 8
+@pytest.mark.parametrize("reps", [8, 10], ids=["512-units-paired", "640-units-longest-first"])
+def test_per_unit_path_ragged_lengths(reps):
+    """At least 512 (sequence, KV head) units with table rows of at most 256 blocks take
+    one workgroup per unit (no workspace is the sign of that path): 512 units pair long
+    contexts with short ones on a CU, more run longest first. Ragged lengths with empty
+    contexts, one-token contexts and block-edge tails: full output against the oracle,
+    deterministic, and the fused step bit-identical to the two-call form, caches byte
+    for byte."""
+    lens = [0, 1, 15, 16, 17, 100, 513, 2048, 2047, 33, 1024, 7, 300, 1500, 64, 65] * reps
     _say(f"per-unit path: {len(lens)} sequences x 4 KV heads")
     s = W.batch_with_lengths(2900, lens, num_heads=16, num_kv_heads=4, head_dim=128,
                              block_size=16, dtype=torch.bfloat16, device=DEV)
-    assert s.block_tables.shape[1] <= 128
+    assert s.block_tables.shape[1] <= 256
     # the per-unit path needs no workspace: the C call succeeds without one (the
     # balanced path would return PKV_E_WORKSPACE)
     lib = pkv.load()
