@@ -54,11 +54,11 @@ constexpr int kMaxSeqsBalanced = 4096;
 // The automatic choice of one workgroup per (sequence, KV head) on the matrix-core
 // path: at least this many units (two per CU of a 256-CU MI355X, the grid that is
 // resident at once), at most this many blocks per table row (4096 tokens at block
-// size 16), and at most this many sequences (the batches whose lengths the kernel
-// ranks).
+// size 16), and at most this many sequences: every workgroup ranks the batch's lengths
+// in LDS at a cost of n * n / 256 steps per thread, about 2 us at 256 sequences.
 constexpr int kPerUnitMinUnits = 512;
 constexpr int kPerUnitMaxBlocks = 256;
-constexpr int kPerUnitMaxSeqs = 512;
+constexpr int kPerUnitMaxSeqs = 256;
 
 // Validate sizes and choose a path. Returns 0 or a negative PKV_E_* code.
 int plan_decode(const DecodeShape& s, DecodePlan* plan);
