@@ -337,13 +337,19 @@ struct KvFp8 {
         for (int i = 0; i < 4; ++i) r.v[i] = buffer_load8<AUX>(rv, voff + i * kD);
         if constexpr (WITH_Q) issue_query(r.q, q, qrow, ok ? qbytes : 0, qlane, lane);
     }
+    // Lane l holds chunks 2(l%8) and 2(l%8)+1 of its row. Lanes with l%8 >= 4 store
+    // their odd chunk first, so each eight-lane group of a store covers all eight
+    // 16-byte slots of a 128-byte bank period instead of only the even (or odd) ones.
     static __device__ __forceinline__ void stage_k(KTile& kt, const Regs& r, int lane) {
         const int c2 = 2 * (lane & 7);   // the lane's first 8-dim chunk
+        const int odd = (lane >> 2) & 1;  // 1: odd chunk first
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int t = 8 * i + (lane >> 3);
-            kt.chunk[t][c2 ^ (t & 15)] = widen8<T>(r.k[i].x, r.k[i].y);
-            kt.chunk[t][(c2 + 1) ^ (t & 15)] = widen8<T>(r.k[i].z, r.k[i].w);
+            const uint32_t a0 = odd ? r.k[i].z : r.k[i].x, a1 = odd ? r.k[i].w : r.k[i].y;
+            const uint32_t b0 = odd ? r.k[i].x : r.k[i].z, b1 = odd ? r.k[i].y : r.k[i].w;
+            kt.chunk[t][(c2 + odd) ^ (t & 15)] = widen8<T>(a0, a1);
+            kt.chunk[t][(c2 + 1 - odd) ^ (t & 15)] = widen8<T>(b0, b1);
         }
     }
     static __device__ __forceinline__ void widen_v(const Regs& r, uint4 (&v)[4]) {
