@@ -90,6 +90,35 @@ size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, int num_k
                                           int max_blocks_per_seq, int partition_size);
 
 /*
+ * Where a decode call with a partition size keeps its per-partition results in the
+ * workspace. A long context is cut into partitions; each partition's attention is
+ * reduced to a log-sum-exp record, and the reduction kernel merges the records of a
+ * row ([P1] section 四: per-block partial attention, merged at the end). The same
+ * records are what two devices holding different parts of one context would need to
+ * exchange.
+ *
+ * Arguments are those of the decode call (dtype included: it selects the kernel).
+ * Returns P, the partitions per (sequence, query head) row, and fills offsets[0..2]
+ * with the byte offsets in the workspace of three float32 arrays, record index
+ * r = (b * num_heads + h) * P + p:
+ *   m [r]             the partition's reference score, in base-2 units (score =
+ *                     scale * q.k * log2 e): at most the partition's largest score
+ *                     and less than 8 below it
+ *   l [r]             sum over the partition's tokens of 2^(score - m)
+ *   o [r, head_dim]   sum of 2^(score - m) * v over those tokens, divided by l
+ *                     (and multiplied by v_scale for 8-bit caches)
+ * Records exist after the call completes, for the sequences whose context spans more
+ * than one partition; partitions past a context's end are not written. Returns 0
+ * (offsets zero) when the call keeps no records (no partition size, or at most one
+ * partition per context); a negative PKV_E_* for sizes the decode call would refuse.
+ * Host only: no device access.
+ */
+int pkv_paged_attention_partials_layout(int num_seqs, int num_heads, int num_kv_heads,
+                                        int head_dim, int block_size, int max_blocks_per_seq,
+                                        int partition_size, pkv_dtype dtype,
+                                        size_t offsets[3]);
+
+/*
  * Zero-fill a workspace with a kernel on `stream` (no memset node, so the call can
  * sit inside a captured graph). A workspace must be zero-filled once before its
  * first use; every decode call leaves its bookkeeping zeroed again on completion,

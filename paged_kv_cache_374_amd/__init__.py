@@ -25,7 +25,8 @@ import torch
 __all__ = ["paged_attention_decode", "paged_attention_decode_append", "reshape_and_cache",
            "paged_attention_decode_fp8", "paged_attention_decode_append_fp8",
            "reshape_and_cache_fp8", "copy_blocks", "workspace_size",
-           "workspace_init", "version", "strerror", "PagedKVError", "library_path", "load",
+           "workspace_init", "partials_layout", "version", "strerror", "PagedKVError",
+           "library_path", "load",
            "PreparedDecode", "PreparedReshapeAndCache", "PreparedCopyBlocks"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -64,6 +65,8 @@ def load():
     lib.pkv_strerror.argtypes = [_I]
     lib.pkv_paged_attention_workspace_size.restype = ctypes.c_size_t
     lib.pkv_paged_attention_workspace_size.argtypes = [_I] * 7
+    lib.pkv_paged_attention_partials_layout.restype = _I
+    lib.pkv_paged_attention_partials_layout.argtypes = [_I] * 8 + [_P]
     lib.pkv_workspace_init.restype = _I
     lib.pkv_workspace_init.argtypes = [_P, ctypes.c_size_t, _P]
     lib.pkv_paged_attention_decode.restype = _I
@@ -129,6 +132,20 @@ def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: i
     return int(load().pkv_paged_attention_workspace_size(num_seqs, num_heads, num_kv_heads,
                                                           head_dim, block_size,
                                                           max_blocks_per_seq, partition_size))
+
+
+def partials_layout(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                    block_size: int, max_blocks_per_seq: int, partition_size: int,
+                    dtype: torch.dtype) -> Tuple[int, Tuple[int, int, int]]:
+    """(P, (offset of m, offset of l, offset of o)) of the per-partition records a
+    decode call with this partition size leaves in its workspace (P = 0: none)."""
+    offs = (ctypes.c_size_t * 3)()
+    rc = load().pkv_paged_attention_partials_layout(num_seqs, num_heads, num_kv_heads,
+                                                    head_dim, block_size, max_blocks_per_seq,
+                                                    partition_size, _DTYPES[dtype], offs)
+    if rc < 0:
+        raise PagedKVError(rc, "pkv_paged_attention_partials_layout")
+    return rc, (int(offs[0]), int(offs[1]), int(offs[2]))
 
 
 def workspace_init(workspace: torch.Tensor) -> None:
@@ -534,9 +551,13 @@ def _swap_args(dst_pool, src_pool, src_dst_pairs):
             raise ValueError("device pools must be on one device")
     if dst_pool.dtype != src_pool.dtype or dst_pool.shape[1:] != src_pool.shape[1:]:
         raise ValueError("pools must share dtype and block layout [blocks, ...]")
-    _gpu(src_dst_pairs, "src_dst_pairs", torch.int32)
-    if src_dst_pairs.device != dev[0]:
-        raise ValueError("src_dst_pairs must be on the pools' device")
+    if src_dst_pairs.dtype != torch.int32 or not src_dst_pairs.is_contiguous():
+        raise ValueError("src_dst_pairs must be a contiguous int32 tensor")
+    if src_dst_pairs.is_cuda:
+        if src_dst_pairs.device != dev[0]:
+            raise ValueError("src_dst_pairs must be on the pools' device")
+    elif not src_dst_pairs.is_pinned():
+        raise ValueError("src_dst_pairs must be on the GPU or in pinned host memory")
     p = src_dst_pairs.reshape(-1, 2)
     bb = dst_pool[0].numel() * dst_pool.element_size() if dst_pool.shape[0] else \
         int(torch.tensor(dst_pool.shape[1:]).prod()) * dst_pool.element_size()
@@ -547,7 +568,7 @@ def _swap_args(dst_pool, src_pool, src_dst_pairs):
 def swap_blocks(dst_pool: torch.Tensor, src_pool: torch.Tensor,
                 src_dst_pairs: torch.Tensor) -> None:
     """Copy block src of src_pool over block dst of dst_pool for each (src, dst) pair
-    (int32 [n, 2] on the GPU). One pool is a GPU tensor, the other a GPU tensor or a
+    (int32 [n, 2] on the GPU or in pinned host memory). One pool is a GPU tensor, the other a GPU tensor or a
     pinned CPU tensor (pin_memory=True) of the same dtype and block layout: swap-out
     passes the host pool as dst_pool, swap-in as src_pool. Enqueued on the GPU's
     current stream; host memory is complete once that stream is synchronised."""

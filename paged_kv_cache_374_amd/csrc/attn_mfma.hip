@@ -1471,13 +1471,24 @@ struct FaLds {
 // code orders it with explicit vector-memory counter waits and barriers instead. M0
 // holds the LDS address and needs one wait state before the load; the leading five
 // wait states cover descriptor words just written by v_readfirstlane (the compiler's
-// hazard checks do not look inside assembly).
+// hazard checks do not look inside assembly). M0 is a register the compiler reserves,
+// so the statement leaves it as it found it: the old value is kept in a scalar
+// temporary and put back after the load has issued (the load takes its LDS address at
+// issue), followed by one wait state for any M0 reader the compiler places next.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void lds_load16(i32x4_t rsrc, uint32_t lds_addr, int voffset) {
-    asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds_addr), "v"(voffset), "s"(rsrc)
-                 : "memory", "m0");
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_nop 4\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0"
+        : "=&s"(saved_m0)
+        : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+        : "memory");
 }
 // A raw buffer descriptor (stride 0, num_records bytes) as four scalar words.
 __device__ __forceinline__ i32x4_t raw_rsrc_words(const void* base, int bytes) {

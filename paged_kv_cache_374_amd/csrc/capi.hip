@@ -391,7 +391,8 @@ int pkv_swap_blocks(void* dst_pool, const void* src_pool, const int32_t* src_dst
     // through its device mapping. Anything else is refused before any launch.
     void* dst = const_cast<void*>(device_view(dst_pool));
     const void* src = device_view(src_pool);
-    if (!dst || !src || !device_view(src_dst_pairs)) return PKV_E_UNSUPPORTED;
+    const int32_t* pairs = static_cast<const int32_t*>(device_view(src_dst_pairs));
+    if (!dst || !src || !pairs) return PKV_E_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
     if (validate_enabled()) {
         std::vector<int32_t> hp;
@@ -404,7 +405,7 @@ int pkv_swap_blocks(void* dst_pool, const void* src_pool, const int32_t* src_dst
             seen[b] = 1;
         }
     }
-    return pkv::launch_swap_blocks(dst, src, src_dst_pairs, num_pairs, num_src_blocks,
+    return pkv::launch_swap_blocks(dst, src, pairs, num_pairs, num_src_blocks,
                                    num_dst_blocks, block_bytes, st) == 0
                ? PKV_OK
                : PKV_E_LAUNCH;

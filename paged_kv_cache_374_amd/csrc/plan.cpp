@@ -115,3 +115,24 @@ extern "C" size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads
     }
     return best;
 }
+
+extern "C" int pkv_paged_attention_partials_layout(int num_seqs, int num_heads,
+                                                   int num_kv_heads, int head_dim,
+                                                   int block_size, int max_blocks_per_seq,
+                                                   int partition_size, pkv_dtype dtype,
+                                                   size_t offsets[3]) {
+    if (!offsets) return PKV_E_NULL;
+    pkv::DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, 0, (int)dtype, partition_size};
+    pkv::DecodePlan p{};
+    const int rc = pkv::plan_decode(s, &p);
+    if (rc != PKV_OK) return rc;
+    offsets[0] = offsets[1] = offsets[2] = 0;
+    // only the fixed-partition paths keep per-partition records, and only when a
+    // context can span more than one partition
+    if (p.path == pkv::Path::MfmaBalanced || p.max_partitions <= 1 || p.bytes == 0) return 0;
+    offsets[0] = p.off_m;
+    offsets[1] = p.off_l;
+    offsets[2] = p.off_o;
+    return p.max_partitions;
+}

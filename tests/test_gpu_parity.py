@@ -180,11 +180,24 @@ def test_deterministic_across_runs():
 
 
 # ------------------------------------------------------------------ serving-shape workloads
-def _sample_rows(B, H, n, seed):
-    g = torch.Generator().manual_seed(seed)
-    bs = torch.randint(0, B, (n,), generator=g)
-    hs = torch.randint(0, H, (n,), generator=g)
-    return [(int(b), int(h)) for b, h in zip(bs, hs)]
+def _fused_full(s, part, label):
+    """The fused step (append at each context end, then attend) on a whole workload:
+    both pools byte for byte against the oracle's append, the whole output against
+    the oracle's decode over those pools."""
+    W.with_append(s, seed=int(s.extra["seed"]))
+    kc0, vc0 = s.k_cache, s.v_cache
+    want, ek, ev = oracle.decode_step(s.q, s.new_k, s.new_v, kc0, vc0, s.block_tables,
+                                      s.context_lens, s.scale)
+    kc, vc = kc0.clone(), vc0.clone()
+    out = torch.full_like(s.q, float("nan"))
+    pkv.paged_attention_decode_append(out, s.q, s.new_k, s.new_v, kc, vc, s.block_tables,
+                                      s.context_lens, s.scale, partition_size=part)
+    torch.cuda.synchronize()
+    assert torch.equal(kc.cpu(), ek), f"{label}: K pool differs from the oracle's append"
+    assert torch.equal(vc.cpu(), ev), f"{label}: V pool differs from the oracle's append"
+    err = _max_err(out, want)
+    _say(f"  {label} fused step partition {part}: max err {err:.3e}")
+    assert err <= TOL[torch.bfloat16], f"{label} fused partition {part}: max err {err}"
 
 
 def test_llama3_8b_decode_full():
@@ -236,28 +249,34 @@ def test_per_unit_path_ragged_lengths(reps):
     assert torch.equal(out_a, out_b), "fused step != two calls"
 
 
-def test_llama_70b_decode_sampled():
-    _say("llama_70b_decode: 512 sampled rows vs oracle")
+def test_llama_70b_decode_full():
+    """70B-shaped batch (256 sequences, 64/8 heads, log-normal contexts up to 4096):
+    every output row against the oracle on the library's own split (one workgroup per
+    unit, longest first) and on 512-token partitions plus the reduction; then the
+    fused step on the library's split."""
+    _say("llama_70b_decode: full output vs oracle")
     s = W.llama_70b_decode(device=DEV, gen_device=DEV)
-    out = decode(s)
-    rows = _sample_rows(256, 64, 512, 1)
-    # always include the longest and shortest contexts
-    ctx = s.context_lens.cpu()
-    rows += [(int(ctx.argmax()), 0), (int(ctx.argmin()), 63)]
-    want = oracle_decode(s, rows=rows)
-    got = torch.stack([out[b, h] for b, h in rows])
-    assert _max_err(got, want) <= TOL[torch.bfloat16]
+    want = oracle_decode(s)
+    for part in (0, 512):
+        err = _max_err(decode(s, partition_size=part), want)
+        _say(f"  partition {part}: max err {err:.3e}")
+        assert err <= TOL[torch.bfloat16], f"partition {part}: max err {err}"
+    _fused_full(s, 0, "llama_70b_decode")
 
 
-def test_long_context_split_k_sampled():
-    _say("long_context_decode: sampled rows vs oracle, partitions of 512")
+def test_long_context_split_k_full():
+    """Long contexts (8 sequences, 32K-128K tokens): every output row against the
+    oracle with 512-token partitions plus the reduction, and on the library's own
+    split (equal shares merged across workgroups); then the fused step with 512-token
+    partitions."""
+    _say("long_context_decode: full output vs oracle")
     s = W.long_context_decode(device=DEV, gen_device=DEV)
-    rows = _sample_rows(8, 32, 24, 2)
-    want = oracle_decode(s, rows=rows)
+    want = oracle_decode(s)
     for part in (512, 0):
-        out = decode(s, partition_size=part)
-        got = torch.stack([out[b, h] for b, h in rows])
-        assert _max_err(got, want) <= TOL[torch.bfloat16], part
+        err = _max_err(decode(s, partition_size=part), want)
+        _say(f"  partition {part}: max err {err:.3e}")
+        assert err <= TOL[torch.bfloat16], f"partition {part}: max err {err}"
+    _fused_full(s, 512, "long_context_decode")
 
 
 REDUCE = [(torch.float32, 64, 32), (torch.float32, 256, 32), (torch.bfloat16, 128, 16),
@@ -281,6 +300,10 @@ def test_reduce_many_partitions(dt, d, part):
 
 @pytest.mark.parametrize("prefix", [2048, 2040])
 def test_shared_prefix_cow_step(prefix):
+    """The shared-prefix batch in the pages' order: copy-on-write copies, every token
+    placed after the fork written, then the decode. Pools byte for byte; every output
+    row against the oracle on the library's split and on 512-token partitions. Then
+    the same step with the newest token appended by the fused call."""
     _say(f"shared_prefix_cow prefix={prefix}: copy_blocks, reshape_and_cache, decode")
     s = W.shared_prefix_cow(device=DEV, gen_device=DEV, prefix_tokens=prefix)
     kc, vc = s.k_cache.clone(), s.v_cache.clone()
@@ -294,11 +317,119 @@ def test_shared_prefix_cow_step(prefix):
     ev = oracle.copy_blocks(s.v_cache, s.copy_pairs)
     ek, ev = oracle.reshape_and_cache(s.new_k, s.new_v, ek, ev, s.slot_mapping)
     assert torch.equal(kc.cpu(), ek) and torch.equal(vc.cpu(), ev)
-    out = decode(s, kc=kc, vc=vc)
-    rows = _sample_rows(256, 32, 256, 3)
-    want = oracle_decode(s, rows=rows, kc=ek, vc=ev)
-    got = torch.stack([out[b, h] for b, h in rows])
-    assert _max_err(got, want) <= TOL[torch.bfloat16]
+    want = oracle_decode(s, kc=ek, vc=ev)
+    for part in (0, 512):
+        err = _max_err(decode(s, kc=kc, vc=vc, partition_size=part), want)
+        _say(f"  partition {part}: max err {err:.3e}")
+        assert err <= TOL[torch.bfloat16], f"partition {part}: max err {err}"
+    # fused form: each sequence's newest token is the last of its slots; write the
+    # others with reshape_and_cache, then append the newest and attend in one call
+    B = s.num_seqs
+    last = torch.cumsum(torch.tensor([d + 1 for d in s.extra["divergent"]]), 0) - 1
+    rest = torch.ones(s.slot_mapping.numel(), dtype=torch.bool)
+    rest[last] = False
+    kc2, vc2 = s.k_cache.clone(), s.v_cache.clone()
+    pkv.copy_blocks([kc2, vc2], s.copy_pairs)
+    pkv.reshape_and_cache(s.new_k[rest.to(DEV)].contiguous(), s.new_v[rest.to(DEV)].contiguous(),
+                          kc2, vc2, s.slot_mapping[rest.to(DEV)].contiguous())
+    out = torch.full_like(s.q, float("nan"))
+    lastd = last.to(DEV)
+    pkv.paged_attention_decode_append(out, s.q, s.new_k[lastd].contiguous(),
+                                      s.new_v[lastd].contiguous(), kc2, vc2, s.block_tables,
+                                      s.context_lens, s.scale)
+    torch.cuda.synchronize()
+    assert last.numel() == B
+    assert torch.equal(kc2.cpu(), ek) and torch.equal(vc2.cpu(), ev), "fused append differs"
+    err = _max_err(out, want)
+    _say(f"  fused step: max err {err:.3e}")
+    assert err <= TOL[torch.bfloat16], f"fused step: max err {err}"
+
+
+def _prompt_major_identical_q(s):
+    """q with every sample of a prompt given the first sample's query rows."""
+    P, S = s.extra["prompts"], s.extra["samples"]
+    q = s.q.view(P, S, s.num_heads, s.head_dim)
+    return q[:, :1].expand(P, S, s.num_heads, s.head_dim).contiguous().view_as(s.q)
+
+
+def test_shared_prefix_identical_contributions():
+    """Samples of one prompt point at the same physical prefix blocks. With identical
+    queries:
+      * attending only the shared prefix gives bit-identical output rows for the 8
+        samples, before and after copy-on-write (the copied block holds the same
+        bytes at another address), on the library's split and on 512-token
+        partitions, and the rows match the oracle;
+      * on the whole contexts with 512-token partitions, the records of the four
+        prefix partitions (tokens 0..2047) are bit-identical across the samples;
+      * with the suffix made identical too (same length, same bytes in each sample's
+        private blocks), the whole outputs are bit-identical."""
+    _say("shared prefix: identical prefix contributions (prefix 2048, 32 x 8 samples)")
+    s = W.shared_prefix_cow(device=DEV, gen_device=DEV, prefix_tokens=2048)
+    P, S, H, D = s.extra["prompts"], s.extra["samples"], s.num_heads, s.head_dim
+    q = _prompt_major_identical_q(s)
+    kc, vc = s.k_cache.clone(), s.v_cache.clone()
+    tables_before = s.block_tables.clone()
+    # before the copy: samples 1..7 still point at the root's block 127
+    for src, dst in s.copy_pairs.tolist():
+        tables_before[tables_before == dst] = src
+    pkv.copy_blocks([kc, vc], s.copy_pairs)
+    pkv.reshape_and_cache(s.new_k, s.new_v, kc, vc, s.slot_mapping)
+    torch.cuda.synchronize()
+    prefix_ctx = torch.full_like(s.context_lens, 2048)
+    want = oracle.paged_attention(q, kc, vc, s.block_tables, prefix_ctx, s.scale)
+    for tables, label in ((tables_before, "shared block 127"), (s.block_tables, "after CoW")):
+        for part in (0, 512):
+            out = torch.full_like(q, float("nan"))
+            pkv.paged_attention_decode(out, q, kc, vc, tables, prefix_ctx, s.scale,
+                                       partition_size=part)
+            torch.cuda.synchronize()
+            o = out.view(P, S, H, D)
+            assert torch.equal(o, o[:, :1].expand_as(o)), f"{label} partition {part}"
+            assert _max_err(out, want) <= TOL[torch.bfloat16], f"{label} partition {part}"
+    # prefix partition records on the whole contexts
+    B, MB = s.num_seqs, s.block_tables.shape[1]
+    npart, (om, ol, oo) = pkv.partials_layout(B, H, s.num_kv_heads, D, 16, MB, 512,
+                                              torch.bfloat16)
+    assert npart == (MB * 16 + 511) // 512 and npart >= 5
+    ws = torch.zeros(pkv.workspace_size(B, H, s.num_kv_heads, D, 16, MB, 512),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_decode(out, q, kc, vc, s.block_tables, s.context_lens, s.scale,
+                               partition_size=512, workspace=ws)
+    torch.cuda.synchronize()
+    rows = B * H * npart
+    m = ws[om:om + rows * 4].view(torch.float32).view(P, S, H, npart)[..., :4]
+    l = ws[ol:ol + rows * 4].view(torch.float32).view(P, S, H, npart)[..., :4]
+    o = ws[oo:oo + rows * D * 4].view(torch.float32).view(P, S, H, npart, D)[..., :4, :]
+    for name, x in (("m", m), ("l", l), ("o", o)):
+        assert torch.all(torch.isfinite(x)), name
+        assert torch.equal(x, x[:, :1].expand_as(x)), f"prefix partition records {name}"
+    assert torch.all(l >= 1.0), "every prefix partition holds its reference token"
+    # identical suffixes: every sample of a prompt attends the prompt's shortest
+    # context, and each sample's private blocks get the first sample's bytes
+    ctx = s.context_lens.view(P, S).min(dim=1, keepdim=True).values.expand(P, S)
+    ctx = ctx.contiguous().view(-1)
+    tb = s.block_tables.cpu().view(P, S, MB)
+    src_ids, dst_ids = [], []
+    for p_, n in enumerate(ctx.view(P, S)[:, 0].tolist()):
+        for j in range(128, (n + 15) // 16):
+            for s_ in range(1, S):
+                src_ids.append(int(tb[p_, 0, j]))
+                dst_ids.append(int(tb[p_, s_, j]))
+    assert min(src_ids + dst_ids) >= 0 and len(set(dst_ids)) == len(dst_ids)
+    src_t = torch.tensor(src_ids, device=DEV)
+    dst_t = torch.tensor(dst_ids, device=DEV)
+    kc[dst_t] = kc[src_t]
+    vc[dst_t] = vc[src_t]
+    for part in (0, 512):
+        out = torch.full_like(q, float("nan"))
+        pkv.paged_attention_decode(out, q, kc, vc, s.block_tables, ctx, s.scale,
+                                   partition_size=part)
+        torch.cuda.synchronize()
+        o = out.view(P, S, H, D)
+        assert torch.equal(o, o[:, :1].expand_as(o)), f"identical suffix partition {part}"
+    want = oracle.paged_attention(q, kc, vc, s.block_tables, ctx, s.scale)
+    assert _max_err(out, want) <= TOL[torch.bfloat16]
 
 
 # ------------------------------------------------------------------ matrix-core paths

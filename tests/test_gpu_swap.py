@@ -54,6 +54,24 @@ def test_swap_out_and_in_match_the_oracle(dt):
     assert torch.equal(gpu.cpu().view(torch.uint8), want_gpu.view(torch.uint8)), "swap in"
 
 
+def test_swap_pairs_in_pinned_host_memory():
+    """The pair list may itself live in pinned host memory: the kernel reads it through
+    the device mapping of that memory."""
+    _say("swap with pinned host pairs")
+    gpu = _pool(11, 40, torch.bfloat16)
+    host = _pool(12, 25, torch.bfloat16, pinned=True)
+    out_pairs = _pairs(13, 17, 40, 25).pin_memory()
+    want_host = oracle.swap_blocks(host, gpu, out_pairs)
+    pkv.swap_blocks(host, gpu, out_pairs)
+    torch.cuda.synchronize()
+    assert torch.equal(host.view(torch.uint8), want_host.view(torch.uint8)), "swap out"
+    in_pairs = _pairs(14, 11, 25, 40).pin_memory()
+    want_gpu = oracle.swap_blocks(gpu, host, in_pairs)
+    pkv.swap_blocks(gpu, host, in_pairs)
+    torch.cuda.synchronize()
+    assert torch.equal(gpu.cpu().view(torch.uint8), want_gpu.view(torch.uint8)), "swap in"
+
+
 def test_swap_between_two_gpu_pools_and_odd_block_bytes():
     """Two device pools; a block of 12 bytes (the 4-byte path)."""
     _say("swap gpu->gpu, 12-byte blocks")
