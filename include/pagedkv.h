@@ -66,7 +66,8 @@ enum {
     PKV_E_INDEX = -7,        /* PKV_VALIDATE=1 only: an index array holds an out-of-range entry */
     PKV_E_DEVICE = -8,       /* no current HIP device could be queried */
     PKV_E_NOSPACE = -9,      /* block manager: no free or evictable block for the request */
-    PKV_E_SEQUENCE = -10     /* block manager: unknown sequence id, or the id is taken */
+    PKV_E_SEQUENCE = -10,    /* block manager: unknown sequence id, or the id is taken */
+    PKV_E_SCRATCH = -11      /* the call needs more scratch than PKV_NOALLOC_SCRATCH_BYTES */
 };
 
 /* A hipStream_t passed as an opaque pointer. */
@@ -172,6 +173,38 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                int max_blocks_per_seq, int num_blocks, pkv_dtype dtype,
                                int partition_size, void* workspace, size_t workspace_bytes,
                                pkv_stream_t stream);
+
+/*
+ * pkv_paged_attention_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation. It runs the same kernels as
+ * pkv_paged_attention_decode (bit-identical results); their scratch (merge counters,
+ * partial results, per-partition records) is a fixed array of
+ * PKV_NOALLOC_SCRATCH_BYTES in device memory that the library holds on every GPU it
+ * runs on until the process ends. The call never allocates or frees device memory.
+ *
+ * Arguments, supported shapes, results and errors are those of
+ * pkv_paged_attention_decode, plus PKV_E_SCRATCH (nothing enqueued) when the call's
+ * scratch, pkv_paged_attention_workspace_size() for its shape and partition_size,
+ * exceeds PKV_NOALLOC_SCRATCH_BYTES. The library's own split (partition_size 0)
+ * fits at every supported size; fixed partitions fit while
+ * num_seqs * num_heads * partitions * (head_dim + 2) * 4 bytes stay below about
+ * 71 MiB (e.g. 8 sequences x 32 heads x 256 partitions of 512 tokens at head_dim 128).
+ *
+ * The first call on a device finds that device's copy of the array and clears its
+ * counter region on `stream`. Every call on one GPU shares that GPU's array, and
+ * each call leaves its counters zeroed for the next. Calls whose work may overlap on
+ * one GPU (different streams, or different host threads) race on the array and give
+ * undefined results: serialise them on one stream.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, float scale, int num_seqs,
+                                       int num_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int max_blocks_per_seq, int num_blocks,
+                                       pkv_dtype dtype, int partition_size,
+                                       pkv_stream_t stream);
 
 /*
  * One whole decode step in one call: append each sequence's newest token, then attend.

@@ -23,6 +23,7 @@ from typing import Dict, Iterable, Optional, Tuple, Union
 import torch
 
 __all__ = ["paged_attention_decode", "paged_attention_decode_append", "reshape_and_cache",
+           "paged_attention_decode_noalloc",
            "paged_attention_decode_fp8", "paged_attention_decode_append_fp8",
            "reshape_and_cache_fp8", "copy_blocks", "workspace_size",
            "workspace_init", "partials_layout", "version", "strerror", "PagedKVError",
@@ -72,6 +73,9 @@ def load():
     lib.pkv_paged_attention_decode.restype = _I
     lib.pkv_paged_attention_decode.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_float] + \
         [_I] * 9 + [_P, ctypes.c_size_t, _P]
+    lib.pkv_paged_attention_decode_noalloc.restype = _I
+    lib.pkv_paged_attention_decode_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_float] + \
+        [_I] * 9 + [_P]
     lib.pkv_paged_attention_decode_append.restype = _I
     lib.pkv_paged_attention_decode_append.argtypes = [_P] * 8 + [ctypes.c_float] + \
         [_I] * 9 + [_P, ctypes.c_size_t, _P]
@@ -175,10 +179,8 @@ def _workspace_for(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
     return ws
 
 
-def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, partition_size,
-                 workspace, own_workspace, kv_fp8=False):
-    """Validate one decode call; returns (ctypes argument tuple without the stream,
-    the workspace tensor in use). With kv_fp8 the caches are uint8 E4M3 codes."""
+def _decode_shape(out, q, k_cache, v_cache, block_tables, context_lens, kv_fp8=False):
+    """Validate the tensors of one decode call; returns (B, Hq, D, NB, Hkv, bs, MB)."""
     for name, t in (("out", out), ("q", q)):
         _gpu(t, name, q.dtype)
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
@@ -195,7 +197,15 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, pa
         raise ValueError("out must match q, and the caches' head_dim must match q")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
-    MB = block_tables.shape[1]
+    return B, Hq, D, NB, Hkv, bs, block_tables.shape[1]
+
+
+def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, partition_size,
+                 workspace, own_workspace, kv_fp8=False):
+    """Validate one decode call; returns (ctypes argument tuple without the stream,
+    the workspace tensor in use). With kv_fp8 the caches are uint8 E4M3 codes."""
+    B, Hq, D, NB, Hkv, bs, MB = _decode_shape(out, q, k_cache, v_cache, block_tables,
+                                              context_lens, kv_fp8)
     need = workspace_size(B, Hq, Hkv, D, bs, MB, partition_size)
     if workspace is None:
         if own_workspace and need > 0:
@@ -240,6 +250,23 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
                            partition_size, workspace, False)
     _check(load().pkv_paged_attention_decode(*args, _stream(q.device)),
            "pkv_paged_attention_decode")
+    return out
+
+
+def paged_attention_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                                   v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                   context_lens: torch.Tensor, scale: float,
+                                   partition_size: int = 0) -> torch.Tensor:
+    """paged_attention_decode with the library's fixed scratch array instead of a
+    workspace: allocates no device memory (graph capture, serving loops). Calls that
+    overlap on one GPU race on that array; run them on one stream."""
+    B, Hq, D, NB, Hkv, bs, MB = _decode_shape(out, q, k_cache, v_cache, block_tables,
+                                              context_lens)
+    _check(load().pkv_paged_attention_decode_noalloc(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), B, Hq, Hkv, D, bs, MB,
+        NB, _DTYPES[q.dtype], int(partition_size), _stream(q.device)),
+        "pkv_paged_attention_decode_noalloc")
     return out
 
 

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
+#include <mutex>
 #include <vector>
 
 #include "launchers.h"
@@ -81,6 +82,38 @@ int validate_tables(const pkv::DecodeShape& s, const int32_t* tables, const int3
     return PKV_OK;
 }
 
+// Scratch of pkv_paged_attention_decode_noalloc: one copy per device, zero at load.
+// Host code never names it directly (on the host the name is only a stand-in); it
+// uses the device address that hipGetSymbolAddress reports for the current device.
+static __device__ __align__(256) uint8_t scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's `scratch`, found once per device. On that
+// first call the counter region is cleared on `stream` with a fill kernel (the array
+// is zero at load already; every decode leaves its counters zeroed again).
+int noalloc_scratch(hipStream_t stream, void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return PKV_E_DEVICE;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return PKV_E_LAUNCH;
+        }
+        if (pkv::launch_zero(p, pkv::kCounterBytes, stream) != 0) return PKV_E_LAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -100,6 +133,7 @@ const char* pkv_strerror(int code) {
         case PKV_E_DEVICE: return "no current HIP device";
         case PKV_E_NOSPACE: return "no free or evictable block for the request";
         case PKV_E_SEQUENCE: return "unknown sequence id, or the id is already in use";
+        case PKV_E_SCRATCH: return "the call needs more scratch than the library's fixed array (PKV_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown pagedkv error";
     }
 }
@@ -221,6 +255,30 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                        context_lens, scale, num_seqs, num_heads, num_kv_heads, head_dim,
                        block_size, max_blocks_per_seq, num_blocks, dtype, partition_size,
                        workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, float scale, int num_seqs,
+                                       int num_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int max_blocks_per_seq, int num_blocks,
+                                       pkv_dtype dtype, int partition_size,
+                                       pkv_stream_t stream) {
+    pkv::DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, num_blocks, (int)dtype, partition_size};
+    pkv::DecodePlan plan{};
+    const int rc = pkv::plan_decode(s, &plan);
+    if (rc != PKV_OK) return rc;
+    if (plan.bytes > PKV_NOALLOC_SCRATCH_BYTES) return PKV_E_SCRATCH;
+    void* ws = nullptr;
+    if (plan.bytes > 0 && num_seqs > 0) {
+        const int sr = noalloc_scratch((hipStream_t)stream, &ws);
+        if (sr != PKV_OK) return sr;
+    }
+    return decode_call(out, q, nullptr, nullptr, k_cache, v_cache, 0, 1.f, 1.f, block_tables,
+                       context_lens, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                       block_size, max_blocks_per_seq, num_blocks, dtype, partition_size, ws,
+                       ws ? PKV_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 int pkv_paged_attention_decode_append(void* out, const void* q, const void* new_k,

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_error_strings():
     assert pkv.version().startswith("pagedkv")
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11):
         assert pkv.strerror(code) and pkv.strerror(code) != pkv.strerror(-99)
 
 
@@ -111,6 +111,29 @@ def test_decode_rejects_bad_arguments_on_the_host():
     assert _decode(lib, MB=64, part=16, ws=1, ws_bytes=16) == E["WORKSPACE"]
     # empty batch: nothing to do, success without any device work
     assert _decode(lib, B=0, out=None, q=None) == E["OK"]
+
+
+def test_noalloc_decode_rejects_bad_arguments_on_the_host():
+    """The decode without a workspace argument: the decode's own host errors, and
+    PKV_E_SCRATCH when the call needs more scratch than the library's fixed array.
+    None of these reach the device."""
+    lib = pkv.load()
+
+    def call(B=2, Hq=8, Hkv=2, D=64, bs=16, MB=4, NB=16, dtype=F32, part=0, out=1):
+        return lib.pkv_paged_attention_decode_noalloc(out, 1, 1, 1, 1, 1, 1.0, B, Hq, Hkv, D,
+                                                      bs, MB, NB, dtype, part, None)
+    assert call(Hq=6, Hkv=4) == E["HEADS"]
+    assert call(D=96) == E["UNSUPPORTED"]
+    assert call(B=-1) == E["SHAPE"]
+    assert call(part=24) == E["SHAPE"]
+    assert call(B=0, out=None) == E["OK"]
+    # 64 sequences x 32 heads x 256 partitions of 512 tokens: ~260 MiB of records
+    assert pkv.workspace_size(64, 32, 8, 128, 16, 8192, 512) > (72 << 20)
+    assert call(B=64, Hq=32, Hkv=8, D=128, MB=8192, NB=100000, dtype=BF16,
+                part=512) == -11
+    # the library's own split fits at every group size
+    for hq, hkv in ((32, 8), (64, 8), (16, 1)):
+        assert pkv.workspace_size(16, hq, hkv, 128, 16, 256, 0) <= (72 << 20)
 
 
 def _fused(lib, **kw):
