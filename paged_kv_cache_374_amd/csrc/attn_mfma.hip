@@ -131,6 +131,13 @@ __device__ __forceinline__ void reset(WaveState& s) {
     for (int n = 0; n < 8; ++n) s.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
+// Keeps the loads issued before it ahead of those issued after it. The ring loops wait
+// for a block with a vector-memory count that assumes the prologue issued the ring's
+// buffers in order; the count at the loop head must hold on the entry path and on the
+// back edge alike, and a prologue the scheduler had reordered made the compiler settle
+// on a count that waited for both buffers in every other step.
+__device__ __forceinline__ void issue_order() { asm volatile("" ::: "memory"); }
+
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-class parts.
 constexpr int kRawBufferWord3 = 0x00020000;
 
@@ -958,6 +965,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
         static_assert(kRing == 2, "the loop below is unrolled for two buffers");
         typename KV::Regs R0, R1;
         issue(R0, xa);
+        issue_order();
         issue(R1, xa + 1);
         // While the first blocks are in flight, wave 0 plans the end phase: it depends
         // only on where the quarters and units begin and end, not on the data.
@@ -1104,36 +1112,76 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_balanced_kernel(
 // contexts would set the kernel's time. The first half therefore takes the sequences
 // in decreasing order of context length and the second half in increasing order: long
 // pairs with short. A larger grid runs in rounds and takes them longest first
-// throughout, so the longest start earliest. Every workgroup ranks the clipped lengths
-// itself, in `keys` (LDS, at least nseq entries; ties by index).
-// Batches above kPerUnitMaxSeqs keep their order. Has barriers: all threads must call
-// it.
+// throughout, so the longest start earliest. Batches above kPerUnitMaxSeqs keep their
+// order.
+__device__ __forceinline__ bool ranks_lengths(int nseq) {
+    return nseq > 1 && nseq <= kPerUnitMaxSeqs;
+}
 
+// The sequence at position `want` when the clipped context lengths are ordered longest
+// first, equal lengths by index; its clipped length goes to `len`. Every wave finds it
+// on its own, with no LDS and no barrier: lane u holds the lengths of sequences u,
+// u + 64, u + 128 and u + 192, a binary search over the length value counts the longer
+// ones with ballots (the answer is the smallest x with at most `want` lengths above
+// it), and the position among the sequences of exactly that length picks one of them.
+// nseq <= kPerUnitMaxSeqs, want < nseq.
+__device__ __forceinline__ int select_by_length(const int32_t* __restrict__ ctx_lens, int nseq,
+                                                int want, int cap, int lane, int& len) {
+    static_assert(kPerUnitMaxSeqs <= 256, "four lengths per lane");
+    const int nr = (nseq + 63) >> 6;
+    int key[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int u = lane + 64 * r;
+        int x = -1;   // no sequence: never counted
+        if (r < nr && u < nseq) {
+            x = ctx_lens[u];
+            x = x < 0 ? 0 : (x > cap ? cap : x);
+        }
+        key[r] = x;
+    }
+    auto above = [&](int x) {
+        int c = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (r < nr) c += __popcll(__ballot(key[r] > x));
+        return c;
+    };
+    int lo = 0, hi = cap;   // above(hi) == 0 <= want, above(-1) == nseq > want
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (above(mid) <= want)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    len = lo;
+    int t = want - above(lo);   // position among the sequences of length lo
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (r >= nr) break;
+        unsigned long long m = __ballot(key[r] == lo);
+        const int c = __popcll(m);
+        if (t < c) {
+            for (int i = 0; i < t; ++i) m &= m - 1;
+            return 64 * r + __ffsll(m) - 1;
+        }
+        t -= c;
+    }
+    return 0;   // not reached for want < nseq
+}
+
+// The sequence workgroup (.., .., b) takes, and its clipped length in `len` when the
+// lengths were ranked (ranks_lengths(nseq); otherwise the caller reads it).
 __device__ __forceinline__ int paired_sequence(const int32_t* __restrict__ ctx_lens, int nseq,
-                                               int b, int cap, uint32_t* keys, int& slot,
-                                               int tid, int nthreads) {
-    if (nseq <= 1 || nseq > kPerUnitMaxSeqs) return b;
+                                               int b, int cap, int lane, int& len) {
+    if (!ranks_lengths(nseq)) return b;
     const int half = (nseq + 1) / 2;
     // more workgroups than two per CU: longest first throughout (the grid runs in
     // rounds, and the longest should start earliest)
     const bool rounds = (long long)nseq * gridDim.y * gridDim.x > kPerUnitMinUnits;
     const int want = (rounds || b < half) ? b : nseq - 1 - (b - half);
-    for (int u = tid; u < nseq; u += nthreads) {
-        const int x = ctx_lens[u];
-        keys[u] = (uint32_t)(x < 0 ? 0 : (x > cap ? cap : x));
-    }
-    __syncthreads();
-    for (int u = tid; u < nseq; u += nthreads) {
-        const uint32_t key = keys[u];
-        int rank = 0;
-        for (int v = 0; v < nseq; ++v) {
-            const uint32_t kv = keys[v];
-            rank += (kv > key || (kv == key && v < u)) ? 1 : 0;
-        }
-        if (rank == want) slot = u;
-    }
-    __syncthreads();
-    return slot;
+    return select_by_length(ctx_lens, nseq, want, cap, lane, len);
 }
 
 // ------------------------------------------------------------------ partitioned kernel
@@ -1143,7 +1191,6 @@ struct PartLds {
     uint8_t valid[kTabMax];
     KTile ktile[kWaves];
     float part[kWaves][Part<GMAX>::kFloats];
-    int seq;
 };
 
 template <typename T, typename KV, int GMAX>
@@ -1160,12 +1207,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     const int cap = max_blocks * kBS;
     // one partition per context: one workgroup per (sequence, KV head), long paired
     // with short on a CU
-    const int b = gridDim.x == 1
-                      ? paired_sequence(ctx_lens, gridDim.z, blockIdx.z, cap, S.tile, S.seq, tid,
-                                        kThreads)
-                      : blockIdx.z;
-    int n = ctx_lens[b];
-    n = n < 0 ? 0 : (n > cap ? cap : n);
+    const bool ranked = gridDim.x == 1 && ranks_lengths(gridDim.z);
+    int n = 0;
+    const int b = ranked ? paired_sequence(ctx_lens, gridDim.z, blockIdx.z, cap, lane, n)
+                         : blockIdx.z;
+    if (!ranked) {
+        n = ctx_lens[b];
+        n = n < 0 ? 0 : (n > cap ? cap : n);
+    }
     const int nb = (n + kBS - 1) / kBS;
     if (n == 0) {
         if (p == 0)
@@ -1207,6 +1256,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     };
     typename KV::Regs A, B;
     issue(A, j);
+    issue_order();
     issue(B, j + kWaves);
 #define PKV_STEP(R)                                                                          \
     if (j >= j1) break;                                                                      \
@@ -1265,7 +1315,6 @@ struct ChunkLds {
     uint8_t valid[kTabMax];
     KTile ktile[kWaves];
     float part[kWaves][Part<16>::kFloats];
-    int seq;
 };
 
 // A wave's state -> normalised output rows for columns c < ncols, column c going to
@@ -1333,8 +1382,9 @@ __global__ __launch_bounds__(kThreads) void chunk_split_kernel(
     const int g = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     // long contexts paired with short ones on a CU (paired_sequence)
-    const int b = paired_sequence(ctx_lens, gridDim.z, blockIdx.z, max_blocks * kBS, S.tile,
-                                  S.seq, tid, kThreads);
+    int ranked_len = 0;
+    const int b = paired_sequence(ctx_lens, gridDim.z, blockIdx.z, max_blocks * kBS, lane,
+                                  ranked_len);
     const int r0 = query_start[b], r1 = query_start[b + 1];
     // rows outside the query array or a decreasing start: nothing is read or written
     if (r0 < 0 || r1 < r0 || r1 > num_query_tokens) return;
@@ -1342,7 +1392,7 @@ __global__ __launch_bounds__(kThreads) void chunk_split_kernel(
     const int tok0 = blockIdx.x * tq;
     if (tok0 >= T_b) return;
     const int cap = max_blocks * kBS;
-    int n = ctx_lens[b];
+    int n = ranks_lengths(gridDim.z) ? ranked_len : ctx_lens[b];   // the ranking read it
     n = n < 0 ? 0 : (n > cap ? cap : n);
     const int ntok = min(tq, T_b - tok0);
     const int first = n - T_b + tok0;                   // position of the tile's first row
@@ -1377,6 +1427,7 @@ __global__ __launch_bounds__(kThreads) void chunk_split_kernel(
         int j = w0 + wave;
         typename KV::Regs A, B;
         issue(A, j);
+        issue_order();
         issue(B, j + kWaves);
 #define PKV_STEP(R)                                                                          \
         if (j >= w1) break;                                                                  \
@@ -1853,9 +1904,16 @@ __global__ __launch_bounds__(kThreads) void chunk_tiles_kernel(
         int j = w0;
         typename KV::Regs B0, B1, B2, B3;
         issue(B0, j);
+        issue_order();
         issue(B1, j + 1);
-        if constexpr (kR > 2) issue(B2, j + 2);
-        if constexpr (kR > 3) issue(B3, j + 3);
+        if constexpr (kR > 2) {
+            issue_order();
+            issue(B2, j + 2);
+        }
+        if constexpr (kR > 3) {
+            issue_order();
+            issue(B3, j + 3);
+        }
 #define PKV_STEP(R)                                                                          \
         {                                                                                    \
             const int vd = j < jend ? (int)S.valid[j - w0] : 0;                              \
