@@ -27,8 +27,15 @@ the matrix-core peak instead of HBM.
 
 Prints one JSON line. ``roofline`` covers the decode kernel: algorithmic bytes
 per launch over its mean duration (HIP events on the launch stream) against the
-8 TB/s HBM peak. ``cpu_baseline`` times the CPU oracle on the host cores on the
-first pool set (test infrastructure, never the product path).
+8 TB/s HBM peak; where sequences share blocks, the distinct bytes instead (the
+logical rate is kept beside it). ``roofline.gather_ceiling`` is the bandwidth probe
+(pkv_read_tiles) on exactly the tiles the decode reads, best of a sweep of launch
+shapes, and the decode's fraction of it. ``step_us`` is the p10/p50/p90 of single
+steps. ``cpu_baseline`` times the CPU oracle on the host cores on the first pool set
+(test infrastructure, never the product path), on all threads and, for the 8B and
+tiny cases, on one; it records the CPU model and socket count.
+
+    python bench.py --workload gather_ceiling   # the probe on its own
 """
 from __future__ import annotations
 
@@ -221,7 +228,7 @@ def time_decode_kernel(sets, graphs, per_set=4, reps=10):
     return a.elapsed_time(b) * 1e3 / (reps * len(order))
 
 
-def cpu_baseline(s, seconds):
+def cpu_baseline(s, seconds, one_thread_seconds=0.0):
     """Time the fp64 oracle on the host cores over whole batches of set 0."""
     import numpy as np
     import oracle
@@ -240,10 +247,44 @@ def cpu_baseline(s, seconds):
     kv = s.kv_bytes() * reps
     got = s.out.detach().cpu().double().numpy()
     err = float(np.max(np.abs(got - want)))
-    return {"value": kv / t_total / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} whole batch(es) of pool set 0 ({s.num_seqs} sequences x "
-                      f"{s.num_heads} heads, fp64 walk), {t_total:.1f} s",
-            "seqs_per_s": s.num_seqs * reps / t_total}, err
+    res = {"value": kv / t_total / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{reps} whole batch(es) of pool set 0 ({s.num_seqs} sequences x "
+                     f"{s.num_heads} heads, fp64 walk), {t_total:.1f} s",
+           "seqs_per_s": s.num_seqs * reps / t_total}
+    if one_thread_seconds > 0:
+        # the same walk on one host thread, whole batches for a bounded time
+        reps1, t1 = 0, 0.0
+        while t1 < one_thread_seconds and reps1 < 1000:
+            t0 = time.perf_counter()
+            prep(threads=1)
+            t1 += time.perf_counter() - t0
+            reps1 += 1
+        res["value_1thread"] = s.kv_bytes() * reps1 / t1 / 1e9
+        res["seqs_per_s_1thread"] = s.num_seqs * reps1 / t1
+        res["sample_1thread"] = f"{reps1} whole batch(es) of pool set 0 on 1 thread, {t1:.1f} s"
+    res.update(cpu_description())
+    return res, err
+
+
+def cpu_baseline_tiny():
+    """The oracle on the tiny float32 case (4 sequences, contexts 7..100, block size 4):
+    sequences per second on all host threads and on one."""
+    import oracle
+    import workloads as W
+    s = W.tiny_fp32(device="cpu", gen_device="cpu")
+    prep = oracle.PreparedAttention(s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens,
+                                    s.scale)
+    out = {}
+    for label, threads in (("all", oracle.max_threads()), ("1thread", 1)):
+        reps, tt = 0, 0.0
+        while tt < 0.5:
+            t0 = time.perf_counter()
+            prep(threads=threads)
+            tt += time.perf_counter() - t0
+            reps += 1
+        out[f"seqs_per_s_{label}"] = round(s.num_seqs * reps / tt, 1)
+    out["sample"] = f"tiny float32 batch (4 sequences, contexts 7/16/33/100), 0.5 s per setting"
+    return out
 
 
 def cpu_baseline_chunk(s, seconds, mfma_bound):
@@ -279,6 +320,89 @@ def cpu_baseline_chunk(s, seconds, mfma_bound):
             "kind": "oracle",
             "sample": f"{done} of {s.num_seqs} sequences of pool set 0 (all their query "
                       f"rows, fp64 walk), {t_total:.1f} s"}, err
+
+
+# Launch shapes the gather probe sweeps: workgroups of four waves, tiles in flight per wave.
+GATHER_SHAPES = [(wg, u) for wg in (256, 512, 1024, 2048) for u in (1, 2, 4)]
+
+
+def decode_tiles(s):
+    """Byte offsets, in a [2, num_blocks, Hkv, bs, D] K-then-V pool, of the tiles the
+    decode reads: for every (sequence, KV head), its K and V tile of each block, in
+    block order (the layout and the scattered physical placement of the workload)."""
+    NB, H, bs, D = s.k_cache.shape
+    tile = bs * D * s.k_cache.element_size()
+    tb, ctx = s.block_tables.cpu().to(torch.int64), s.context_lens.cpu().tolist()
+    parts = []
+    for b, n in enumerate(ctx):
+        nb = (n + bs - 1) // bs
+        if nb == 0:
+            continue
+        t = tb[b, :nb][None, :] * H + torch.arange(H)[:, None]        # [H, nb]
+        parts.append(torch.stack([t, t + NB * H], dim=-1).reshape(-1))  # K, V per block
+    return torch.cat(parts) * tile, tile
+
+
+def gather_ceiling(pkv, sets, reps=4):
+    """The bandwidth probe on exactly the tiles the decode reads (per pool set, K and V
+    copied into one pool of the same layout), swept over GATHER_SHAPES: returns the best
+    rate in GB/s, its shape and the whole sweep. Bytes are whole tiles, as the decode
+    fetches them."""
+    dev = sets[0].q.device
+    preps = []
+    for s in sets:
+        kv = torch.empty((2,) + tuple(s.k_cache.shape), dtype=s.k_cache.dtype, device=dev)
+        kv[0].copy_(s.k_cache)
+        kv[1].copy_(s.v_cache)
+        off, tile = decode_tiles(s)
+        preps.append((kv, off.to(dev), tile))
+    sink = torch.empty(max(w for w, _ in GATHER_SHAPES) * 256, dtype=torch.int32, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sweep = []
+    for wg, u in GATHER_SHAPES:
+        def run():
+            for kv, off, tile in preps:
+                pkv.read_tiles(kv, off, tile, wg, u, sink)
+        run()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (reps * len(preps))
+        nbytes = sum(off.numel() * tile for _, off, tile in preps) / len(preps)
+        sweep.append({"workgroups": wg, "tiles_in_flight": u, "us": round(us, 3),
+                      "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    del preps
+    best = max(sweep, key=lambda r: r["gbs"])
+    return best, sweep
+
+
+def cpu_description():
+    """CPU model and socket count of the host (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    model, sockets = None, None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            if k.strip() == "Model name":
+                model = v.strip()
+            elif k.strip() == "Socket(s)":
+                sockets = int(v.strip()) if v.strip().isdigit() else v.strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if model is None:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+    return {"cpu_model": model, "sockets": sockets, "logical_cpus": os.cpu_count()}
 
 
 CALIB_PAIRS, CALIB_BLOCK_BYTES = 4096, 8 * 16 * 128 * 2
@@ -396,6 +520,31 @@ def bench_swap(args, pkv, dev):
     print(json.dumps(line), flush=True)
 
 
+def bench_gather(args, pkv, dev):
+    """The gather ceiling on its own: the bandwidth probe on exactly the tiles the
+    8B-shaped decode reads (four pool sets), swept over launch shapes."""
+    sets = build_sets("llama3_8b_decode", max(1, args.rotate), dev)
+    torch.cuda.synchronize()
+    best, sweep = gather_ceiling(pkv, sets, reps=max(4, args.steps // len(sets)))
+    nbytes = sum(decode_tiles(s)[0].numel() * decode_tiles(s)[1] for s in sets) / len(sets)
+    line = {
+        "metric": METRIC, "value": best["gbs"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": 1, "ms_per_step": round(best["us"] / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gather_ceiling", "tiles_per_launch": int(nbytes // 4096),
+                   "bytes_per_launch": int(nbytes), "tile_bytes": 4096, "pool_sets": len(sets),
+                   "step": "pkv_read_tiles over the K and V tiles of the 8B-shaped decode "
+                           "batch (no arithmetic)"},
+        "roofline": {"bound": "hbm", "kernel": "read_tiles", "achieved": best["gbs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(best["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launch_us_mean": best["us"], "best_shape": best, "sweep": sweep},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def bench_block_manager(args):
     """Host block manager in a serving loop on the 8B pool (16384 blocks of 16 tokens):
     32 prompts of 2040 tokens with token ids (prefix cache on), each forked into 8
@@ -490,6 +639,8 @@ def main():
                          "adds a gap between steps)")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as two calls (reshape_and_cache, then decode)")
+    ap.add_argument("--no-gather", action="store_true",
+                    help="skip the gather-ceiling probe that runs after the decode timing")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run copy_blocks on a known byte count (counter calibration)")
     args = ap.parse_args()
@@ -511,6 +662,9 @@ def main():
     pkv.load()
     if args.workload == "swap_blocks_8b":
         bench_swap(args, pkv, dev)
+        return
+    if args.workload == "gather_ceiling":
+        bench_gather(args, pkv, dev)
         return
     sets = build_sets(args.workload, max(1, args.rotate), dev)
     torch.cuda.synchronize()
@@ -537,6 +691,20 @@ def main():
     value = kv_total / (ms * 1e-3) / 1e9
     s0 = sets[0]
     seqs_per_s = s0.num_seqs * args.steps / (ms * 1e-3)
+    # spread of single steps: the same steps again, an event between consecutive steps
+    n_spread = max(20, args.steps)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread + 1)]
+    evs[0].record()
+    for i in range(n_spread):
+        sets[i % len(sets)].run()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n_spread))
+    pct = lambda q: per_step[min(n_spread - 1, int(round(q * (n_spread - 1))))]
+    step_spread = {"p10": round(pct(0.1), 3), "p50": round(pct(0.5), 3),
+                   "p90": round(pct(0.9), 3), "samples": n_spread,
+                   "timing": "one HIP event between consecutive steps, a separate pass after "
+                             "the timed steps"}
     # the dominant kernel on its own, back to back over the same pool sets
     dec_us = time_decode_kernel(sets, graphs=args.graphs)
     kv_per_launch = sum(s.kv for s in sets) / len(sets)
@@ -547,6 +715,21 @@ def main():
     mfma_bound = chunk and flops_per_launch / kv_per_launch > ridge
     tflops = flops_per_launch / (dec_us * 1e-6) / 1e12 if chunk else None
 
+    # blocks shared by several sequences are read once from HBM: price the roofline on
+    # the distinct bytes (the logical figure stays in the line as well)
+    kv_unique = sum(x.kv_unique for x in sets) / len(sets)
+    shared = kv_unique < 0.98 * kv_per_launch
+    achieved_hbm = (kv_unique if shared else kv_per_launch) / (dec_us * 1e-6) / 1e9
+    gather = None
+    if not mfma_bound and not args.no_gather:
+        log("[bench] gather ceiling: the probe on the decode's tiles")
+        best, sweep = gather_ceiling(pkv, sets)
+        gather = {"gbs": best["gbs"], "shape": {k: best[k] for k in ("workgroups",
+                                                                       "tiles_in_flight")},
+                  "frac": round(achieved / best["gbs"], 4), "sweep": sweep,
+                  "what": "pkv_read_tiles on exactly the K and V tiles one decode launch "
+                          "reads (whole tiles, non-temporal), best launch shape"}
+
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
@@ -554,8 +737,12 @@ def main():
         # the last step that used set 0 left its output in set 0's buffer
         if chunk:
             cpu, parity = cpu_baseline_chunk(s0, args.cpu_seconds, mfma_bound)
+            cpu.update(cpu_description())
         else:
-            cpu, parity = cpu_baseline(s0, args.cpu_seconds)
+            one = args.cpu_seconds / 2 if s0.name in ("llama3_8b_decode", "tiny_fp32") else 0
+            cpu, parity = cpu_baseline(s0, args.cpu_seconds, one_thread_seconds=one)
+            if s0.name == "llama3_8b_decode":
+                cpu["tiny_fp32"] = cpu_baseline_tiny()
 
     if args.calibrate:
         calibrate(pkv, dev)
@@ -607,19 +794,24 @@ def main():
             "launch": "one hip graph per step" if args.graphs else "direct (one call per step)",
             "wall_s_timed": round(wall, 4),
         },
+        "step_us": step_spread,
         "roofline": {
             "bound": "mfma" if mfma_bound else "hbm",
             "kernel": ("paged_attention_chunk" if chunk else
                        "paged_attention_decode_append" if s0.fused
                        else "paged_attention_decode") + fp8,
-            "achieved": round(tflops if mfma_bound else achieved, 2),
+            "achieved": round(tflops if mfma_bound else achieved_hbm, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
             "unit": "TFLOP/s" if mfma_bound else "GB/s",
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS if mfma_bound
-                          else achieved / HBM_PEAK_GBS, 4),
+                          else achieved_hbm / HBM_PEAK_GBS, 4),
+            "bytes": ("distinct blocks read (shared blocks once)" if shared else
+                      "algorithmic KV bytes") if not mfma_bound else None,
+            "achieved_logical_gbs": round(achieved, 2) if shared else None,
             "traffic": traffic_per_launch(s0.name),
             "launch_us_mean": round(dec_us, 3),
             "launch_timing": "back-to-back decode launches over the pool sets, HIP events",
+            "gather_ceiling": gather,
         },
         "cpu_baseline": cpu,
     }

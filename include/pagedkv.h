@@ -492,6 +492,32 @@ int pkv_bm_refcount(const pkv_block_manager* bm, int32_t block);
 int pkv_bm_build_tables(const pkv_block_manager* bm, const int64_t* seq_ids, int num_seqs,
                         int width, int32_t* tables, int32_t* context_lens);
 
+/*
+ * Device-bandwidth probe (diagnostic; not part of the attention path). Reads num_tiles
+ * tiles of tile_bytes bytes, tile i starting at byte offsets[i] of base, each read once
+ * with the non-temporal hint the decode kernels use for K and V, and computes nothing
+ * from them. Timing it on the tiles a decode call reads gives the gather bandwidth the
+ * device reaches for the decode's access pattern (whole 2 or 4 KiB tiles at scattered
+ * addresses): [P3] section "它没有解决什么" notes that paging leaves attention bound by
+ * memory bandwidth, and this is that bound as measured, next to the HBM peak.
+ *
+ * base        device memory of base_bytes bytes; a tile that does not lie wholly inside
+ *             it, or whose offset is negative or not a multiple of 16, is skipped
+ * offsets     device int64 [num_tiles], byte offsets into base
+ * tile_bytes  2048 or 4096
+ * workgroups  1..65535 workgroups of four waves; wave w reads tiles w, w + W, ... (W the
+ *             number of waves)
+ * tiles_in_flight  1, 2 or 4 tiles whose loads one wave issues before using any
+ * sink        device uint32 [workgroups * 256]: written only in the (practically
+ *             impossible) case that a wave's XOR of its data equals a fixed word, which
+ *             keeps the loads from being optimised away
+ * Errors: PKV_E_SHAPE, PKV_E_UNSUPPORTED, PKV_E_NULL, PKV_E_LAUNCH; nothing is enqueued
+ * on error.
+ */
+int pkv_read_tiles(const void* base, size_t base_bytes, const int64_t* offsets, int num_tiles,
+                   int tile_bytes, int workgroups, int tiles_in_flight, uint32_t* sink,
+                   pkv_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ __all__ = ["paged_attention_decode", "paged_attention_decode_append", "reshape_a
            "paged_attention_decode_fp8", "paged_attention_decode_append_fp8",
            "reshape_and_cache_fp8", "copy_blocks", "workspace_size",
            "workspace_init", "partials_layout", "version", "strerror", "PagedKVError",
-           "library_path", "load",
+           "library_path", "load", "read_tiles",
            "PreparedDecode", "PreparedReshapeAndCache", "PreparedCopyBlocks"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +95,8 @@ def load():
     lib.pkv_reshape_and_cache_fp8.argtypes = [_P] * 5 + [_F, _F] + [_I] * 6 + [_P]
     lib.pkv_reshape_and_cache.restype = _I
     lib.pkv_reshape_and_cache.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
+    lib.pkv_read_tiles.restype = _I
+    lib.pkv_read_tiles.argtypes = [_P, ctypes.c_size_t, _P, _I, _I, _I, _I, _P, _P]
     lib.pkv_swap_blocks.restype = _I
     lib.pkv_swap_blocks.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_size_t, _P]
     lib.pkv_copy_blocks.restype = _I
@@ -616,3 +618,19 @@ class PreparedSwapBlocks:
         rc = self._fn(*self._args, st)
         if rc != 0:
             raise PagedKVError(rc, "pkv_swap_blocks")
+
+
+def read_tiles(base: torch.Tensor, offsets: torch.Tensor, tile_bytes: int, workgroups: int,
+               tiles_in_flight: int, sink: torch.Tensor) -> None:
+    """Bandwidth probe (diagnostic): read the tiles of tile_bytes bytes at byte offsets
+    ``offsets`` (int64, on the GPU) of the GPU tensor ``base``; ``sink`` is an int32 GPU
+    tensor of at least workgroups * 256 elements."""
+    _gpu(base, "base")
+    _gpu(offsets, "offsets", torch.int64)
+    _gpu(sink, "sink", torch.int32)
+    if sink.numel() < workgroups * 256:
+        raise ValueError("sink needs workgroups * 256 elements")
+    _check(load().pkv_read_tiles(base.data_ptr(), base.numel() * base.element_size(),
+                                 offsets.data_ptr(), offsets.numel(), tile_bytes, workgroups,
+                                 tiles_in_flight, sink.data_ptr(), _stream(base.device)),
+           "pkv_read_tiles")

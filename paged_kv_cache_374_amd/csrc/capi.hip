@@ -438,6 +438,21 @@ int pkv_copy_blocks(void* cache, const int32_t* src_dst_pairs, int num_pairs, in
                : PKV_E_LAUNCH;
 }
 
+int pkv_read_tiles(const void* base, size_t base_bytes, const int64_t* offsets, int num_tiles,
+                   int tile_bytes, int workgroups, int tiles_in_flight, uint32_t* sink,
+                   pkv_stream_t stream) {
+    if (num_tiles < 0 || workgroups < 1 || workgroups > 65535) return PKV_E_SHAPE;
+    if ((tile_bytes != 2048 && tile_bytes != 4096) ||
+        (tiles_in_flight != 1 && tiles_in_flight != 2 && tiles_in_flight != 4))
+        return PKV_E_UNSUPPORTED;
+    if (num_tiles == 0) return PKV_OK;
+    if (!base || !offsets || !sink) return PKV_E_NULL;
+    return pkv::launch_read_tiles(base, base_bytes, offsets, num_tiles, tile_bytes, workgroups,
+                                  tiles_in_flight, sink, (hipStream_t)stream) == 0
+               ? PKV_OK
+               : PKV_E_LAUNCH;
+}
+
 int pkv_swap_blocks(void* dst_pool, const void* src_pool, const int32_t* src_dst_pairs,
                     int num_pairs, int num_src_blocks, int num_dst_blocks, size_t block_bytes,
                     pkv_stream_t stream) {

@@ -26,6 +26,13 @@ int launch_swap_blocks(void* dst, const void* src, const int32_t* pairs, int num
 
 int launch_zero(void* p, size_t bytes, hipStream_t stream);
 
+// Gather-bandwidth probe: reads num_tiles tiles of tile_bytes (2048 or 4096) bytes at
+// base + offsets[i], with `workgroups` workgroups of four waves and `unroll` (1, 2, 4)
+// tiles in flight per wave; tiles outside [0, base_bytes) are skipped.
+int launch_read_tiles(const void* base, size_t base_bytes, const int64_t* offsets,
+                      int num_tiles, int tile_bytes, int workgroups, int unroll, uint32_t* sink,
+                      hipStream_t stream);
+
 struct DecodeArgs {
     void* out;
     const void* q;

@@ -29,7 +29,8 @@ import statistics
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/attn_mfma.hip", "csrc/attn_generic.hip", "csrc/cache_ops.hip",
-                  "csrc/plan.cpp", "csrc/plan.h", "csrc/capi.hip", "csrc/device_common.h")
+                  "csrc/plan.cpp", "csrc/plan.h", "csrc/capi.hip", "csrc/device_common.h",
+                  "csrc/read_probe.hip")
 CALIBRATION_KERNEL = "copy_blocks_kernel"
 
 
