@@ -39,6 +39,8 @@
 // shared reduction kernel, or writes the output when the context has one partition.
 //
 // Both kernels can also perform the append of a decode step (see "fused append").
+#include <type_traits>
+
 #include "device_common.h"
 #include "launchers.h"
 #include "pagedkv.h"
@@ -1614,14 +1616,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
         __syncthreads();
         b = S.seq;
     }
-    const int r0 = query_start[b], r1 = query_start[b + 1];
+    // b and everything derived from it are wave-uniform; saying so lets the compiler
+    // branch on them (the causal mask below is then skipped outright on whole steps)
+    b = uni(b);
+    const int r0 = uni(query_start[b]), r1 = uni(query_start[b + 1]);
     if (r0 < 0 || r1 < r0 || r1 > num_query_tokens) return;
     const int T_b = r1 - r0;
     const int tqw = kFaRows / group;                 // query tokens per wave
     const int tok_wg = sg * kWaves * tqw;
     if (tok_wg >= T_b) return;
     const int cap = max_blocks * kBS;
-    int n = ctx_lens[b];
+    int n = uni(ctx_lens[b]);
     n = n < 0 ? 0 : (n > cap ? cap : n);
     const int ntok_wg = min(kWaves * tqw, T_b - tok_wg);
     const int last_wg = n - T_b + tok_wg + ntok_wg - 1;   // position of the last row
@@ -1667,7 +1672,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
     const int tt = tid / 16, tc = tid % 16;
     const int koff = (tt * (kD / 8) + (tc ^ tt)) * 16;
     const int voff = (tt * (kD / 8) + (tc ^ (4 * (tt % 4)))) * 16;
-    auto issue = [&](int st, int sl) {
+    auto issue = [&](int st, auto slot) {
+        constexpr int sl = decltype(slot)::value;
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi) {
             const int jb = 2 * st + bi;
@@ -1688,7 +1694,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
     // 32dt + 16(G % 2) + m = 32dt + lane % 32 of tokens 16s + 8e + 4h + 0..3: the row and
     // k order of the score registers that form the other operand.
     const int tj = (lane % 16) / 4, tq = lane % 4, tg = (lane / 16) % 2;
-    auto v_operand = [&](int sl, int s, int dt) {
+    auto v_operand = [&](auto slot, int s, int dt) {
+        constexpr int sl = decltype(slot)::value;
         uint2 part[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -1700,7 +1707,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
         }
         return make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
     };
-    auto compute = [&](int st, int sl) {
+    auto compute = [&](int st, auto slot) {
+        constexpr int sl = decltype(slot)::value;
         const int tp0 = st * kFaStep;
         if (tp0 > last_w) return;                    // none of the wave's rows sees it
         f32x16_t sc = f32x16_t{};
@@ -1756,7 +1764,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
             const uint4 pbk = make_uint4(pb[2 * s].x, pb[2 * s].y, pb[2 * s + 1].x, pb[2 * s + 1].y);
 #pragma unroll
             for (int dt = 0; dt < kD / 32; ++dt)
-                acc[dt] = Mma32<T>::mma(v_operand(sl, s, dt), pbk, acc[dt]);
+                acc[dt] = Mma32<T>::mma(v_operand(slot, s, dt), pbk, acc[dt]);
         }
     };
 
@@ -1780,15 +1788,23 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
         wait_vmem<0>();
         __syncthreads();
         const int s0 = w0 / 2, ns = w1 / 2 - s0;
-        issue(s0, 0);
-        if (1 < ns) issue(s0 + 1, 1);
-        int sl = 0;
-        for (int i = 0; i < ns; ++i) {
+        using Slot0 = std::integral_constant<int, 0>;
+        using Slot1 = std::integral_constant<int, 1>;
+        using Slot2 = std::integral_constant<int, 2>;
+        issue(s0, Slot0{});
+        if (1 < ns) issue(s0 + 1, Slot1{});
+        // step i computes from slot i % 3 and refills slot (i + 2) % 3; the loop is
+        // unrolled over the three slots so that every LDS address is a constant offset
+        auto step = [&](int i, auto slot, auto refill) {
             if (i + 1 < ns) wait_vmem<4>(); else wait_vmem<0>();
             barrier_only();
-            if (i + 2 < ns) issue(s0 + i + 2, sl == 0 ? 2 : sl - 1);
-            compute(s0 + i, sl);
-            sl = sl == 2 ? 0 : sl + 1;
+            if (i + 2 < ns) issue(s0 + i + 2, refill);
+            compute(s0 + i, slot);
+        };
+        for (int i = 0; i < ns; i += 3) {
+            step(i, Slot0{}, Slot2{});
+            if (i + 1 < ns) step(i + 1, Slot1{}, Slot0{});
+            if (i + 2 < ns) step(i + 2, Slot2{}, Slot1{});
         }
     }
     const float lt = lsum + __shfl_xor(lsum, 32);
