@@ -62,8 +62,11 @@ def kernel_stats(trace_dir: str):
     return path, rows
 
 
-def counter_means(pmc_dir: str, counter: str):
-    """Mean counter value (KiB as rocprofv3 reports it) per kernel name."""
+def counter_means(pmc_dir: str, counter: str, calibration: str = CALIBRATION_KERNEL):
+    """Mean counter value (KiB as rocprofv3 reports it) per kernel name. For the
+    calibration kernel only the dispatches within half of its largest reading count:
+    a workload may run the same kernel on far fewer bytes (copy-on-write copies), and
+    the calibration call is the one of known size."""
     path = _one(os.path.join(pmc_dir, "**", "*counter_collection.csv"))
     per = {}
     with open(path) as f:
@@ -71,7 +74,12 @@ def counter_means(pmc_dir: str, counter: str):
             if r["Counter_Name"] != counter:
                 continue
             per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-    return path, {k: statistics.mean(v) for k, v in per.items()}
+    out = {}
+    for k, v in per.items():
+        if calibration in k:
+            v = [x for x in v if x >= 0.5 * max(v)]
+        out[k] = statistics.mean(v)
+    return path, out
 
 
 def all_counter_means(pmc_dir: str, needle: str):
