@@ -64,7 +64,7 @@ def build_sets(name, rotate, dev):
     base = {"tiny_fp32": 1001, "llama3_8b_decode": 1002, "llama3_8b_decode_fp8": 1002,
             "llama3_8b_verify4": 1002, "prefill_chunk512": 1006,
             "llama_70b_decode": 1003, "long_context_decode": 1004,
-            "shared_prefix_cow": 1005}[name]
+            "shared_prefix_cow": 1005, "skewed_decode": 1007}[name]
     sets = []
     for i in range(rotate):
         kw = {"device": dev}

@@ -145,8 +145,12 @@ constexpr int kRawBufferWord3 = 0x00020000;
 
 // Cache policy of the K/V loads: non-temporal. Every KV byte is read once per call,
 // and keeping it out of L2 and the Infinity Cache measured ~8% more gather bandwidth
-// (6.3 vs 5.8 TB/s for 285 MB of 4 KiB tiles).
+// (6.3 vs 5.8 TB/s for 285 MB of 4 KiB tiles) and 12-14% shorter decode kernels.
+// Blocks that several sequences of the batch reference are the exception: the
+// per-unit kernel reads those sequences with kShared, the default policy, so that the
+// neighbours that read the same blocks find them in L2.
 constexpr int kStream = 2;
+constexpr int kShared = 0;
 
 template <int AUX = 0>
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int offset) {
@@ -1120,33 +1124,67 @@ __device__ __forceinline__ bool ranks_lengths(int nseq) {
     return nseq > 1 && nseq <= kPerUnitMaxSeqs;
 }
 
-// The sequence at position `want` when the clipped context lengths are ordered longest
-// first, equal lengths by index; its clipped length goes to `len`. Every wave finds it
-// on its own, with no LDS and no barrier: lane u holds the lengths of sequences u,
-// u + 64, u + 128 and u + 192, a binary search over the length value counts the longer
-// ones with ballots (the answer is the smallest x with at most `want` lengths above
-// it), and the position among the sequences of exactly that length picks one of them.
-// nseq <= kPerUnitMaxSeqs, want < nseq.
-__device__ __forceinline__ int select_by_length(const int32_t* __restrict__ ctx_lens, int nseq,
-                                                int want, int cap, int lane, int& len) {
-    static_assert(kPerUnitMaxSeqs <= 256, "four lengths per lane");
-    const int nr = (nseq + 63) >> 6;
+// Lane u holds the clipped lengths of sequences u, u + 64, u + 128 and u + 192 (-1 past
+// the batch). nseq <= kPerUnitMaxSeqs.
+struct LengthKeys {
     int key[4];
+};
+
+__device__ __forceinline__ LengthKeys load_lengths(const int32_t* __restrict__ ctx_lens,
+                                                   int nseq, int cap, int lane) {
+    static_assert(kPerUnitMaxSeqs <= 256, "four lengths per lane");
+    LengthKeys k;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int u = lane + 64 * r;
         int x = -1;   // no sequence: never counted
-        if (r < nr && u < nseq) {
+        if (u < nseq) {
             x = ctx_lens[u];
             x = x < 0 ? 0 : (x > cap ? cap : x);
         }
-        key[r] = x;
+        k.key[r] = x;
     }
+    return k;
+}
+
+// Wave-wide maximum of x (every lane's value), with row-local DPP steps (lanes ^1, ^2,
+// then rotations by 4 and 8 within each row of 16) and one read of each row.
+__device__ __forceinline__ int wave_max(int x) {
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));    // quad [1,0,3,2]
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));    // quad [2,3,0,1]
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false));   // row_ror:4
+    x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));   // row_ror:8
+    return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+               max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+// True when every length lies within an eighth of the longest.
+__device__ __forceinline__ bool narrow_lengths(const LengthKeys& k, int cap) {
+    int hi = -1, neg_lo = -cap;   // minimum through the maximum of negated lengths
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        hi = max(hi, k.key[r]);
+        if (k.key[r] >= 0) neg_lo = max(neg_lo, -k.key[r]);
+    }
+    hi = wave_max(hi);
+    const int lo = -wave_max(neg_lo);
+    return 8 * (hi - lo) <= hi;
+}
+
+// The sequence at position `want` when the lengths are ordered longest first, equal
+// lengths by index; its length goes to `len`. Every wave finds it on its own, with no
+// LDS and no barrier: a binary search over the length value counts the longer ones
+// with ballots (the answer is the smallest x with at most `want` lengths above it), and
+// the position among the sequences of exactly that length picks one of them.
+// want < nseq.
+__device__ __forceinline__ int select_by_length(const LengthKeys& k, int nseq, int want,
+                                                int cap, int& len) {
+    const int nr = (nseq + 63) >> 6;
     auto above = [&](int x) {
         int c = 0;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            if (r < nr) c += __popcll(__ballot(key[r] > x));
+            if (r < nr) c += __popcll(__ballot(k.key[r] > x));
         return c;
     };
     int lo = 0, hi = cap;   // above(hi) == 0 <= want, above(-1) == nseq > want
@@ -1162,7 +1200,7 @@ __device__ __forceinline__ int select_by_length(const int32_t* __restrict__ ctx_
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         if (r >= nr) break;
-        unsigned long long m = __ballot(key[r] == lo);
+        unsigned long long m = __ballot(k.key[r] == lo);
         const int c = __popcll(m);
         if (t < c) {
             for (int i = 0; i < t; ++i) m &= m - 1;
@@ -1173,17 +1211,39 @@ __device__ __forceinline__ int select_by_length(const int32_t* __restrict__ ctx_
     return 0;   // not reached for want < nseq
 }
 
-// The sequence workgroup (.., .., b) takes, and its clipped length in `len` when the
-// lengths were ranked (ranks_lengths(nseq); otherwise the caller reads it).
+// The sequence workgroup (.., .., b) takes, and its clipped length in `len`. Lengths
+// that all lie within an eighth of the longest keep the caller's order: pairing or
+// ranking them would even out the CUs' shares by at most that eighth, while the
+// caller's order keeps neighbours together, which is where sequences that share prefix
+// blocks sit (the samples of one prompt), so that one XCD reads a shared block for
+// several of them while it is still in its L2.
 __device__ __forceinline__ int paired_sequence(const int32_t* __restrict__ ctx_lens, int nseq,
                                                int b, int cap, int lane, int& len) {
-    if (!ranks_lengths(nseq)) return b;
+    auto own = [&] {
+        const int x = ctx_lens[b];
+        len = x < 0 ? 0 : (x > cap ? cap : x);
+        return b;
+    };
+    if (!ranks_lengths(nseq)) return own();
+    const LengthKeys k = load_lengths(ctx_lens, nseq, cap, lane);
+    if (narrow_lengths(k, cap)) return own();
     const int half = (nseq + 1) / 2;
     // more workgroups than two per CU: longest first throughout (the grid runs in
     // rounds, and the longest should start earliest)
     const bool rounds = (long long)nseq * gridDim.y * gridDim.x > kPerUnitMinUnits;
     const int want = (rounds || b < half) ? b : nseq - 1 - (b - half);
-    return select_by_length(ctx_lens, nseq, want, cap, lane, len);
+    return select_by_length(k, nseq, want, cap, len);
+}
+
+// True when sequence b's first block is also the first block of sequence b - 1 or
+// b + 1 (the samples of one prompt, forked from it, sit next to each other and
+// reference its blocks).
+__device__ __forceinline__ bool shares_first_block(const int32_t* __restrict__ tables, int b,
+                                                   int nseq, int max_blocks) {
+    const int first = tables[(size_t)b * max_blocks];
+    const int prev = b > 0 ? tables[(size_t)(b - 1) * max_blocks] : -1;
+    const int next = b + 1 < nseq ? tables[(size_t)(b + 1) * max_blocks] : -1;
+    return first >= 0 && (first == prev || first == next);
 }
 
 // ------------------------------------------------------------------ partitioned kernel
@@ -1191,6 +1251,7 @@ template <int GMAX>
 struct PartLds {
     uint32_t tile[kTabMax];
     uint8_t valid[kTabMax];
+    int shared;   // shares_first_block for the workgroup's sequence
     KTile ktile[kWaves];
     float part[kWaves][Part<GMAX>::kFloats];
 };
@@ -1209,11 +1270,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     const int cap = max_blocks * kBS;
     // one partition per context: one workgroup per (sequence, KV head), long paired
     // with short on a CU
-    const bool ranked = gridDim.x == 1 && ranks_lengths(gridDim.z);
     int n = 0;
-    const int b = ranked ? paired_sequence(ctx_lens, gridDim.z, blockIdx.z, cap, lane, n)
-                         : blockIdx.z;
-    if (!ranked) {
+    const int b = uni(gridDim.x == 1
+                          ? paired_sequence(ctx_lens, gridDim.z, blockIdx.z, cap, lane, n)
+                          : blockIdx.z);
+    if (gridDim.x != 1) {
         n = ctx_lens[b];
         n = n < 0 ? 0 : (n > cap ? cap : n);
     }
@@ -1236,6 +1297,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
         S.tile[j - j0] = ok ? (uint32_t)phys * (uint32_t)num_kv_heads + (uint32_t)g : kNoTile;
         S.valid[j - j0] = (uint8_t)(ok ? (left < kBS ? left : kBS) : 0);
     }
+    // the cache policy's test reads beside the table (its latency hides behind it)
+    if (tid == kThreads - 1) S.shared = shares_first_block(tables, b, gridDim.z, max_blocks);
     // fused append: the partition holding the newest token writes its K and V rows
     // (the barrier below orders the stores before this workgroup's loads)
     if (new_k != nullptr && (n - 1) / kBS >= j0 && (n - 1) / kBS < j1 &&
@@ -1244,33 +1307,42 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
                    num_kv_heads, n, num_blocks, tid / KV::kAppendChunks,
                    tid % KV::kAppendChunks, k_inv, v_inv);
     __syncthreads();
+    const bool shared = uni(S.shared) != 0;
     WaveState st;
     reset(st);
     // waves take every fourth block; two register buffers in fixed roles
     const int qrow = b * num_heads + g * group;
-    int j = j0 + wave;
     // every step issues one block (a zero-record buffer past the end): the loads in
     // flight never depend on the path taken
     const int qbytes = group * kD * (int)sizeof(T), qlane = (lane & 15) * kD * (int)sizeof(T);
-    auto issue = [&](typename KV::Regs& R, int ji) {
-        KV::issue(R, k_cache, v_cache, q, ji < j1 ? S.tile[ji - j0] : kNoTile, qrow, qbytes,
-                  qlane, lane);
-    };
-    typename KV::Regs A, B;
-    issue(A, j);
-    issue_order();
-    issue(B, j + kWaves);
+    auto stream_blocks = [&](auto policy) {
+        constexpr int AUX = decltype(policy)::value;
+        auto issue = [&](typename KV::Regs& R, int ji) {
+            KV::template issue<AUX>(R, k_cache, v_cache, q,
+                                    ji < j1 ? S.tile[ji - j0] : kNoTile, qrow, qbytes, qlane,
+                                    lane);
+        };
+        int j = j0 + wave;
+        typename KV::Regs A, B;
+        issue(A, j);
+        issue_order();
+        issue(B, j + kWaves);
 #define PKV_STEP(R)                                                                          \
     if (j >= j1) break;                                                                      \
     fold_block<T, KV>(st, R, S.ktile[wave], S.valid[j - j0], S.valid[j - j0], scale_log2,    \
                       lane);                                                                 \
     issue(R, j + 2 * kWaves);                                                                \
     j += kWaves;
-    while (true) {
-        PKV_STEP(A)
-        PKV_STEP(B)
-    }
+        while (true) {
+            PKV_STEP(A)
+            PKV_STEP(B)
+        }
 #undef PKV_STEP
+    };
+    if (shared)
+        stream_blocks(std::integral_constant<int, kShared>{});
+    else
+        stream_blocks(std::integral_constant<int, kStream>{});
 
     wave_to_part<GMAX>(S.part[wave], st, lane, group);
     __syncthreads();
@@ -1384,18 +1456,15 @@ __global__ __launch_bounds__(kThreads) void chunk_split_kernel(
     const int g = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     // long contexts paired with short ones on a CU (paired_sequence)
-    int ranked_len = 0;
-    const int b = paired_sequence(ctx_lens, gridDim.z, blockIdx.z, max_blocks * kBS, lane,
-                                  ranked_len);
+    const int cap = max_blocks * kBS;
+    int n = 0;
+    const int b = paired_sequence(ctx_lens, gridDim.z, blockIdx.z, cap, lane, n);
     const int r0 = query_start[b], r1 = query_start[b + 1];
     // rows outside the query array or a decreasing start: nothing is read or written
     if (r0 < 0 || r1 < r0 || r1 > num_query_tokens) return;
     const int T_b = r1 - r0;
     const int tok0 = blockIdx.x * tq;
     if (tok0 >= T_b) return;
-    const int cap = max_blocks * kBS;
-    int n = ranks_lengths(gridDim.z) ? ranked_len : ctx_lens[b];   // the ranking read it
-    n = n < 0 ? 0 : (n > cap ? cap : n);
     const int ntok = min(tq, T_b - tok0);
     const int first = n - T_b + tok0;                   // position of the tile's first row
     const int nb = first + ntok - 1 < 0 ? 0 : (first + ntok - 1) / kBS + 1;

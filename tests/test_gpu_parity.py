@@ -264,6 +264,20 @@ def test_llama_70b_decode_full():
     _fused_full(s, 0, "llama_70b_decode")
 
 
+def test_skewed_decode_full():
+    """One 4096-token context among 63 of 128-512 tokens: every output row against the
+    oracle on the library's own split and on 512-token partitions plus the reduction;
+    then the fused step on the library's split."""
+    _say("skewed_decode: full output vs oracle")
+    s = W.skewed_decode(device=DEV, gen_device=DEV)
+    want = oracle_decode(s)
+    for part in (0, 512):
+        err = _max_err(decode(s, partition_size=part), want)
+        _say(f"  partition {part}: max err {err:.3e}")
+        assert err <= TOL[torch.bfloat16], f"partition {part}: max err {err}"
+    _fused_full(s, 0, "skewed_decode")
+
+
 def test_long_context_split_k_full():
     """Long contexts (8 sequences, 32K-128K tokens): every output row against the
     oracle with 512-token partitions plus the reduction, and on the library's own
@@ -298,12 +312,16 @@ def test_reduce_many_partitions(dt, d, part):
     assert _max_err(out, want) <= TOL[dt]
 
 
-@pytest.mark.parametrize("prefix", [2048, 2040])
+@pytest.mark.parametrize("prefix", [2048, 2040, 40])
 def test_shared_prefix_cow_step(prefix):
     """The shared-prefix batch in the pages' order: copy-on-write copies, every token
     placed after the fork written, then the decode. Pools byte for byte; every output
     row against the oracle on the library's split and on 512-token partitions. Then
-    the same step with the newest token appended by the fused call."""
+    the same step with the newest token appended by the fused call.
+
+    With 2048 and 2040 prefix tokens the lengths lie within an eighth of the longest
+    (the kernel keeps the batch order); with 40 they span 42..297 (it ranks them):
+    both orders read the shared blocks with the cache policy for shared blocks."""
     _say(f"shared_prefix_cow prefix={prefix}: copy_blocks, reshape_and_cache, decode")
     s = W.shared_prefix_cow(device=DEV, gen_device=DEV, prefix_tokens=prefix)
     kc, vc = s.k_cache.clone(), s.v_cache.clone()

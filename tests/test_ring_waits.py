@@ -48,8 +48,10 @@ def _kernel(lines, pattern):
     return lines[start:end]
 
 
-def _streaming_loop(body):
-    """Lines of the loop (label .. back branch) that holds the most non-temporal loads."""
+def _streaming_loop(body, nt=True):
+    """Lines of the loop (label .. back branch) that holds the most buffer loads with
+    (nt=True) or without (nt=False) the non-temporal bit; of loops with equally many,
+    the first to close (an inner loop before the loop around it)."""
     labels = {m.group(1): i for i, l in enumerate(body) if (m := re.match(r"^(\.LBB\d+_\d+):", l))}
     best = None
     for i, l in enumerate(body):
@@ -57,11 +59,17 @@ def _streaming_loop(body):
         if not m or labels.get(m.group(1), i) >= i:
             continue
         h = labels[m.group(1)]
-        nt = sum(1 for x in body[h:i] if "buffer_load" in x and " nt" in x)
-        if best is None or nt > best[2]:
-            best = (h, i, nt)
+        count = sum(1 for x in body[h:i] if "buffer_load" in x and (" nt" in x) == nt)
+        if best is None or count > best[2]:
+            best = (h, i, count)
     assert best and best[2] > 0, "no streaming loop found"
     return body[best[0]:best[1] + 1]
+
+
+def _waits(loop):
+    # every wait from the loop head to its back branch, the back edge included (a
+    # compiler that copies the ring's registers there must first wait for them)
+    return [int(m.group(1)) for l in loop if (m := re.search(r"s_waitcnt vmcnt\((\d+)\)", l))]
 
 
 # (kernel name pattern, lowest wait a fold may use)
@@ -74,9 +82,15 @@ CASES = [(f"decode_mfma_partition_kernelINS_{t}ENS0_{kv}IS2_EELi{g}E", floor)
 
 @pytest.mark.parametrize("pattern,floor", CASES, ids=[c[0][:60] for c in CASES])
 def test_every_fold_leaves_the_other_buffer_in_flight(assembly, pattern, floor):
-    loop = _streaming_loop(_kernel(assembly, pattern))
-    # every wait from the loop head to its back branch, the back edge included (a
-    # compiler that copies the ring's registers there must first wait for them)
-    waits = [int(m.group(1)) for l in loop if (m := re.search(r"s_waitcnt vmcnt\((\d+)\)", l))]
-    assert waits, "no waits in the loop"
-    assert min(waits) >= floor, f"a fold waits with vmcnt({min(waits)}): {waits}"
+    body = _kernel(assembly, pattern)
+    # the per-unit kernel streams with either cache policy: non-temporal, and the
+    # default for sequences that share blocks with a neighbour (a loop of its own)
+    policies = (True, False) if "partition" in pattern else (True,)
+    for nt in policies:
+        loop = _streaming_loop(body, nt)
+        if not nt:
+            assert sum(1 for l in loop if "buffer_load" in l and " nt" not in l) >= 12, \
+                "no loop streams with the default cache policy"
+        waits = _waits(loop)
+        assert waits, "no waits in the loop"
+        assert min(waits) >= floor, f"a fold waits with vmcnt({min(waits)}): {waits}"

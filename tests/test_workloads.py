@@ -103,6 +103,16 @@ def test_llama3_8b_shape():
     assert len(flat) == len(set(flat))          # no sharing in this workload
 
 
+def test_skewed_shape():
+    s = W.skewed_decode(materialize=False)
+    used = _check_step(s, 32, 8, 128, 16)
+    ctx = s.context_lens.tolist()
+    assert s.block_tables.shape == (64, 256) and s.num_blocks == 16384
+    assert sorted(ctx)[-1] == 4096 and sorted(ctx)[-2] <= 512 and min(ctx) >= 128
+    flat = [x for r in used for x in r]
+    assert len(flat) == len(set(flat))
+
+
 def test_llama_70b_shape():
     s = W.llama_70b_decode(materialize=False)
     used = _check_step(s, 64, 8, 128, 16)

@@ -188,6 +188,21 @@ def llama_70b_decode(seed: int = 1003, device="cpu", gen_device=None,
                             16, 256, torch.bfloat16, device, gen_device, materialize)
 
 
+def skewed_decode(seed: int = 1007, device="cpu", gen_device=None,
+                  materialize: bool = True) -> DecodeStep:
+    """Llama-3-8B-shaped batch with one long context among short ones: 64 sequences,
+    one of 4096 tokens at a seeded position and 63 uniform in [128, 512], 32 query /
+    8 KV heads, head_dim 128, block_size 16, blocks drawn from a shuffled pool of
+    16384, bfloat16. The long sequence holds about a fifth of the batch's KV bytes,
+    which a split of one workgroup per (sequence, KV head) cannot spread."""
+    gen_device = device if gen_device is None else gen_device
+    g = torch.Generator(device="cpu").manual_seed(seed + 7919)
+    ctx = torch.randint(128, 513, (64,), generator=g).tolist()
+    ctx[int(torch.randint(0, 64, (1,), generator=g))] = 4096
+    return _scattered_batch("skewed_decode", seed, ctx, 16384, 32, 8, 128, 16, 256,
+                            torch.bfloat16, device, gen_device, materialize)
+
+
 def long_context_decode(seed: int = 1004, device="cpu", gen_device=None,
                         materialize: bool = True) -> DecodeStep:
     """Long-context decode for the split-K path: 8 sequences, 32 query / 8 KV heads,
@@ -422,4 +437,5 @@ WORKLOADS = {
     "llama_70b_decode": llama_70b_decode,
     "long_context_decode": long_context_decode,
     "shared_prefix_cow": shared_prefix_cow,
+    "skewed_decode": skewed_decode,
 }
