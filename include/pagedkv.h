@@ -154,7 +154,9 @@ int pkv_workspace_init(void* workspace, size_t workspace_bytes, pkv_stream_t str
  * scale         multiplier of q.k (typically 1/sqrt(head_dim))
  * dtype         element type of out, q and the caches; accumulation is float32,
  *               the output is rounded to nearest-even
- * partition_size  0: the library chooses how to split the work (recommended);
+ * partition_size  0: the library chooses how to split the work (recommended;
+ *               a context far longer than the batch's average is cut across
+ *               several workgroups, their results merged through the workspace);
  *               >0: split every context into partitions of this many tokens
  *               (a multiple of block_size), one partial result per partition,
  *               merged by a separate reduction kernel

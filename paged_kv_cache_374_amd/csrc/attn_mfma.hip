@@ -1158,18 +1158,30 @@ __device__ __forceinline__ int wave_max(int x) {
                max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
-// True when every length lies within an eighth of the longest.
-__device__ __forceinline__ bool narrow_lengths(const LengthKeys& k, int cap) {
-    int hi = -1, neg_lo = -cap;   // minimum through the maximum of negated lengths
+// Wave-wide sum of x, with the same steps as wave_max.
+__device__ __forceinline__ int wave_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);
+    return (__builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16)) +
+           (__builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48));
+}
+
+// Longest and shortest of the lengths (wave-uniform).
+__device__ __forceinline__ void length_range(const LengthKeys& k, int cap, int& hi, int& lo) {
+    int h = -1, neg_lo = -cap;   // minimum through the maximum of negated lengths
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        hi = max(hi, k.key[r]);
+        h = max(h, k.key[r]);
         if (k.key[r] >= 0) neg_lo = max(neg_lo, -k.key[r]);
     }
-    hi = wave_max(hi);
-    const int lo = -wave_max(neg_lo);
-    return 8 * (hi - lo) <= hi;
+    hi = wave_max(h);
+    lo = -wave_max(neg_lo);
 }
+
+// True when every length lies within an eighth of the longest.
+__device__ __forceinline__ bool narrow_range(int hi, int lo) { return 8 * (hi - lo) <= hi; }
 
 // The sequence at position `want` when the lengths are ordered longest first, equal
 // lengths by index; its length goes to `len`. Every wave finds it on its own, with no
@@ -1211,6 +1223,15 @@ __device__ __forceinline__ int select_by_length(const LengthKeys& k, int nseq, i
     return 0;   // not reached for want < nseq
 }
 
+// Position in the longest-first order of the sequence that workgroup (.., .., b) takes.
+// More workgroups than two per CU: longest first throughout (the grid runs in rounds,
+// and the longest should start earliest); else the second half runs shortest first.
+__device__ __forceinline__ int pairing_position(int nseq, int b) {
+    const int half = (nseq + 1) / 2;
+    const bool rounds = (long long)nseq * gridDim.y * gridDim.x > kPerUnitMinUnits;
+    return (rounds || b < half) ? b : nseq - 1 - (b - half);
+}
+
 // The sequence workgroup (.., .., b) takes, and its clipped length in `len`. Lengths
 // that all lie within an eighth of the longest keep the caller's order: pairing or
 // ranking them would even out the CUs' shares by at most that eighth, while the
@@ -1226,13 +1247,122 @@ __device__ __forceinline__ int paired_sequence(const int32_t* __restrict__ ctx_l
     };
     if (!ranks_lengths(nseq)) return own();
     const LengthKeys k = load_lengths(ctx_lens, nseq, cap, lane);
-    if (narrow_lengths(k, cap)) return own();
-    const int half = (nseq + 1) / 2;
-    // more workgroups than two per CU: longest first throughout (the grid runs in
-    // rounds, and the longest should start earliest)
-    const bool rounds = (long long)nseq * gridDim.y * gridDim.x > kPerUnitMinUnits;
-    const int want = (rounds || b < half) ? b : nseq - 1 - (b - half);
-    return select_by_length(k, nseq, want, cap, len);
+    int hi, lo;
+    length_range(k, cap, hi, lo);
+    if (narrow_range(hi, lo)) return own();
+    return select_by_length(k, nseq, pairing_position(nseq, b), cap, len);
+}
+
+// ------------------------------------------------------------------ long units
+// One workgroup per (sequence, KV head) cannot finish before its longest unit does.
+// With S the blocks of all units over the workgroup slots (two per CU), a unit of more
+// than 2S blocks outlasts any pairing of it with a short one, so it is cut into pieces
+// of P >= S blocks: its own workgroup folds the first piece, and helper workgroups,
+// launched after the batch's (grid z >= num_seqs), fold the others, each long unit's
+// pieces in turn, in sequence order. Every piece's partial result goes to a workspace
+// record; the last piece to finish (a device-scope counter per unit) merges them all
+// in piece order. P grows when the pieces would outnumber the helpers.
+struct UnitWork {
+    int b = 0, n = 0;     // sequence and its clipped length
+    int j0 = 0, j1 = 0;   // blocks this workgroup folds
+    int pieces = 1;       // workgroups that share the unit
+    int piece = 0;        // this workgroup's piece
+    int rec = 0;          // record of the unit's first piece (per KV head)
+};
+
+// The work of workgroup z of a per-unit grid of nseq + helpers workgroups per KV head;
+// false when it has none (a helper with no piece to fold).
+__device__ __forceinline__ bool unit_work(const int32_t* __restrict__ ctx_lens, int nseq, int z,
+                                          int cap, int lane, int slots, int helpers, int hkv,
+                                          UnitWork& w) {
+    auto own = [&](int b) {
+        const int x = ctx_lens[b];
+        w.b = b;
+        w.n = x < 0 ? 0 : (x > cap ? cap : x);
+        w.j1 = (w.n + kBS - 1) / kBS;
+        return true;
+    };
+    if (!ranks_lengths(nseq)) return z < nseq && own(z);
+    const LengthKeys k = load_lengths(ctx_lens, nseq, cap, lane);
+    int nbk[4], sum = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        nbk[r] = k.key[r] > 0 ? (k.key[r] + kBS - 1) / kBS : 0;
+        sum += nbk[r];
+    }
+    int hi, lo;
+    length_range(k, cap, hi, lo);
+    int S = 0, P = 0;   // P = 0: no unit is cut
+    if (helpers > 0) {
+        // at most kPerUnitMaxBlocks blocks per unit, and helpers come with at most one
+        // merge counter per unit (2^18 units): 32-bit safe
+        S = (wave_sum(sum) * hkv + slots - 1) / slots;
+        if (S < 1) S = 1;
+        if ((hi + kBS - 1) / kBS > 2 * S) {
+            int bl = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bl += nbk[r] > 2 * S ? nbk[r] : 0;
+            bl = wave_sum(bl);
+            P = max(S, (bl + helpers - 1) / helpers);
+        }
+    }
+    // Long units in sequence order: visit(u, blocks, pieces, first record) returns true
+    // to stop. Lanes past the batch hold 0 blocks, so they are never long.
+    auto walk = [&](auto visit) {
+        int c = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            unsigned long long m = __ballot(nbk[r] > 2 * S);
+            while (m) {
+                const int l = __ffsll(m) - 1;
+                m &= m - 1;
+                const int nb = __builtin_amdgcn_readlane(nbk[r], l);
+                const int kk = (nb + P - 1) / P;
+                if (visit(64 * r + l, nb, kk, c)) return;
+                c += kk;
+            }
+        }
+    };
+    if (z >= nseq) {
+        if (P == 0) return false;
+        int h = z - nseq;   // extra piece h of the whole batch
+        bool found = false;
+        walk([&](int u, int nb, int kk, int c) {
+            if (h >= kk - 1) {
+                h -= kk - 1;
+                return false;
+            }
+            own(u);
+            w.pieces = kk;
+            w.piece = h + 1;
+            w.j0 = w.piece * P;
+            w.j1 = min(nb, w.j0 + P);
+            w.rec = c;
+            found = true;
+            return true;
+        });
+        return found;
+    }
+    if (narrow_range(hi, lo)) {
+        own(z);
+    } else {
+        int len;
+        const int b = select_by_length(k, nseq, pairing_position(nseq, z), cap, len);
+        w.b = b;
+        w.n = len;
+        w.j1 = (len + kBS - 1) / kBS;
+    }
+    if (P > 0 && w.j1 > 2 * S && w.j1 > P) {
+        const int b = w.b;
+        walk([&](int u, int nb, int kk, int c) {
+            if (u != b) return false;
+            w.pieces = kk;
+            w.j1 = P;
+            w.rec = c;
+            return true;
+        });
+    }
+    return true;
 }
 
 // True when sequence b's first block is also the first block of sequence b - 1 or
@@ -1252,6 +1382,7 @@ struct PartLds {
     uint32_t tile[kTabMax];
     uint8_t valid[kTabMax];
     int shared;   // shares_first_block for the workgroup's sequence
+    int last;     // this workgroup merges the pieces of its unit
     KTile ktile[kWaves];
     float part[kWaves][Part<GMAX>::kFloats];
 };
@@ -1263,21 +1394,28 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     const int32_t* __restrict__ tables, const int32_t* __restrict__ ctx_lens, float scale_log2,
     float out_scale, float k_inv, float v_inv, int num_heads, int num_kv_heads,
     int group, int max_blocks, int num_blocks, int part_blocks, int max_parts,
-    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
+    float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, int num_seqs,
+    int slots, int32_t* __restrict__ counters, float* __restrict__ records, int rec_per_head) {
     __shared__ PartLds<GMAX> S;
     const int p = blockIdx.x, g = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int cap = max_blocks * kBS;
     // one partition per context: one workgroup per (sequence, KV head), long paired
-    // with short on a CU
-    int n = 0;
-    const int b = uni(gridDim.x == 1
-                          ? paired_sequence(ctx_lens, gridDim.z, blockIdx.z, cap, lane, n)
-                          : blockIdx.z);
-    if (gridDim.x != 1) {
-        n = ctx_lens[b];
-        n = n < 0 ? 0 : (n > cap ? cap : n);
+    // with short on a CU, long units cut into pieces (unit_work)
+    UnitWork w;
+    if (gridDim.x == 1) {
+        if (!unit_work(ctx_lens, num_seqs, blockIdx.z, cap, lane, slots,
+                       (int)gridDim.z - num_seqs, num_kv_heads, w))
+            return;
+    } else {
+        w.b = blockIdx.z;
+        const int x = ctx_lens[w.b];
+        w.n = x < 0 ? 0 : (x > cap ? cap : x);
+        const int nbw = (w.n + kBS - 1) / kBS;
+        w.j0 = p * part_blocks;
+        w.j1 = min(nbw, w.j0 + part_blocks);
     }
+    const int b = uni(w.b), n = uni(w.n), pieces = uni(w.pieces);
     const int nb = (n + kBS - 1) / kBS;
     if (n == 0) {
         if (p == 0)
@@ -1286,9 +1424,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
                        make_float4(0.f, 0.f, 0.f, 0.f));
         return;
     }
-    const int j0 = p * part_blocks;
+    const int j0 = uni(w.j0);
     if (j0 >= nb) return;
-    const int j1 = min(nb, j0 + part_blocks);
+    const int j1 = uni(w.j1);
     const int nparts = (nb + part_blocks - 1) / part_blocks;
     for (int j = j0 + tid; j < j1; j += kThreads) {
         const int phys = tables[(size_t)b * max_blocks + j];
@@ -1298,7 +1436,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
         S.valid[j - j0] = (uint8_t)(ok ? (left < kBS ? left : kBS) : 0);
     }
     // the cache policy's test reads beside the table (its latency hides behind it)
-    if (tid == kThreads - 1) S.shared = shares_first_block(tables, b, gridDim.z, max_blocks);
+    if (tid == kThreads - 1) S.shared = shares_first_block(tables, b, num_seqs, max_blocks);
     // fused append: the partition holding the newest token writes its K and V rows
     // (the barrier below orders the stores before this workgroup's loads)
     if (new_k != nullptr && (n - 1) / kBS >= j0 && (n - 1) / kBS < j1 &&
@@ -1348,11 +1486,27 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     __syncthreads();
     int P[kWaves];
     for (int v = 0; v < kWaves; ++v) P[v] = v;
-    for (int i = tid; i < group * (kD / 4); i += kThreads) {
-        const int h = i / (kD / 4), d0 = (i % (kD / 4)) * 4;
+    constexpr int kCols = kD / 4;   // float4 columns of a head's row
+    // pieces of a long unit: records of kFloats floats, rec_per_head per KV head
+    const __amdgpu_buffer_rsrc_t R = __builtin_amdgcn_make_buffer_rsrc(
+        records, 0, pieces > 1 ? num_kv_heads * rec_per_head * Part<GMAX>::kFloats * 4 : 0,
+        kRawBufferWord3);
+    const int rec0 = (g * rec_per_head + uni(w.rec)) * Part<GMAX>::kFloats;
+    for (int i = tid; i < group * kCols; i += kThreads) {
+        const int h = i / kCols, d0 = (i % kCols) * 4;
         float M, Ls;
         float4 o;
         merge_parts<GMAX, kWaves, kWaves>(S.part, P, kWaves, h, d0, M, Ls, o);
+        if (pieces > 1) {
+            // this piece, with write-through stores (see kCoherent)
+            const int sl = rec0 + uni(w.piece) * Part<GMAX>::kFloats;
+            publish4(R, 4 * (sl + h * kD + d0), o);
+            if (d0 == 0) {
+                publish1(R, 4 * (sl + Part<GMAX>::kM + h), M);
+                publish1(R, 4 * (sl + Part<GMAX>::kL + h), Ls);
+            }
+            continue;
+        }
         const float inv = Ls > 0.f ? out_scale / Ls : 0.f;
         o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
         const size_t hrow = (size_t)b * num_heads + g * group + h;
@@ -1367,6 +1521,45 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
             }
         }
     }
+    if (pieces == 1) return;
+    // The wait and barrier complete every published store before the counter moves;
+    // the last piece to arrive reads all of them back (coherent loads) and merges them
+    // in piece order, then leaves the counter at zero for the next call.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const int done = __hip_atomic_fetch_add(&counters[b * num_kv_heads + g], 1,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        S.last = done == pieces - 1;
+    }
+    __syncthreads();
+    if (!uni(S.last)) return;
+    T* rows = out + ((size_t)b * num_heads + (size_t)g * group) * kD;
+    for (int i = tid; i < group * kCols; i += kThreads) {
+        const int h = i / kCols, d0 = (i % kCols) * 4;
+        float M = kNegInf, Ls = 0.f;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+        for (int v = 0; v < pieces; ++v) {
+            const int sl = rec0 + v * Part<GMAX>::kFloats;
+            const float m = fetch1(R, 4 * (sl + Part<GMAX>::kM + h));
+            const float l = fetch1(R, 4 * (sl + Part<GMAX>::kL + h));
+            const float4 pv = fetch4(R, 4 * (sl + h * kD + d0));
+            const float Mn = fmaxf(M, m);
+            const float a = weight(M, Mn), c = weight(m, Mn);
+            Ls = Ls * a + l * c;
+            o.x = o.x * a + pv.x * c;
+            o.y = o.y * a + pv.y * c;
+            o.z = o.z * a + pv.z * c;
+            o.w = o.w * a + pv.w * c;
+            M = Mn;
+        }
+        const float inv = Ls > 0.f ? out_scale / Ls : 0.f;
+        store4(rows + h * kD + d0, make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv));
+    }
+    if (tid == 0)
+        __hip_atomic_store(&counters[b * num_kv_heads + g], 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ query chunks
@@ -2060,22 +2253,30 @@ int launch_balanced(const DecodeArgs& a, const DecodePlan& plan, int workers,
 }
 
 template <typename T, typename KV, int GMAX>
-int launch_partitioned(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
+int launch_partitioned(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
+                       hipStream_t stream) {
     const DecodeShape& s = a.shape;
     char* ws = (char*)a.workspace;
     const bool split = plan.max_partitions > 1;
+    // helpers only on the per-unit grid (one partition per context): one per workgroup
+    // slot (two per CU), spread over the KV heads
+    int helpers = split ? 0 : max(1, 2 * num_cus / s.num_kv_heads);
+    if (helpers > plan.helpers) helpers = plan.helpers;
     using E = typename KV::Elem;
     const Scales sc = scales_of(a);
     hipLaunchKernelGGL((decode_mfma_partition_kernel<T, KV, GMAX>),
-                       dim3(plan.max_partitions, s.num_kv_heads, s.num_seqs), dim3(kThreads), 0,
-                       stream, (T*)a.out, (const T*)a.q, (E*)a.k_cache, (E*)a.v_cache,
-                       (const T*)a.new_k, (const T*)a.new_v, a.block_tables, a.context_lens,
-                       sc.scale_log2, sc.out_scale, sc.k_inv, sc.v_inv,
+                       dim3(plan.max_partitions, s.num_kv_heads, s.num_seqs + helpers),
+                       dim3(kThreads), 0, stream, (T*)a.out, (const T*)a.q, (E*)a.k_cache,
+                       (E*)a.v_cache, (const T*)a.new_k, (const T*)a.new_v, a.block_tables,
+                       a.context_lens, sc.scale_log2, sc.out_scale, sc.k_inv, sc.v_inv,
                        s.num_heads, s.num_kv_heads, plan.group, s.max_blocks, s.num_blocks,
                        plan.partition_tokens / kBS, plan.max_partitions,
                        split ? (float*)(ws + plan.off_m) : nullptr,
                        split ? (float*)(ws + plan.off_l) : nullptr,
-                       split ? (float*)(ws + plan.off_o) : nullptr);
+                       split ? (float*)(ws + plan.off_o) : nullptr, s.num_seqs, 2 * num_cus,
+                       helpers ? (int32_t*)(ws + plan.off_counters) : nullptr,
+                       helpers ? (float*)(ws + plan.off_partials) : nullptr,
+                       plan.rec_per_head);
     if (hipGetLastError() != hipSuccess) return -1;
     return split ? launch_partition_reduce(a, plan, stream) : 0;
 }
@@ -2142,9 +2343,9 @@ int launch_format(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
         if (G <= 8) return launch_balanced<T, KV, 8, NW>(a, plan, workers, stream);
         return launch_balanced<T, KV, 16, 4>(a, plan, workers, stream);
     }
-    if (G <= 4) return launch_partitioned<T, KV, 4>(a, plan, stream);
-    if (G <= 8) return launch_partitioned<T, KV, 8>(a, plan, stream);
-    return launch_partitioned<T, KV, 16>(a, plan, stream);
+    if (G <= 4) return launch_partitioned<T, KV, 4>(a, plan, num_cus, stream);
+    if (G <= 8) return launch_partitioned<T, KV, 8>(a, plan, num_cus, stream);
+    return launch_partitioned<T, KV, 16>(a, plan, num_cus, stream);
 }
 
 template <typename T>

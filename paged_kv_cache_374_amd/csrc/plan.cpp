@@ -70,6 +70,19 @@ int plan_decode(const DecodeShape& s, DecodePlan* plan) {
         p.path = Path::MfmaPartitioned;
         p.partition_tokens = s.max_blocks * s.block_size;
         p.max_partitions = 1;
+        // pieces of long units: a counter per unit, records for every piece (at most
+        // one per helper plus one per long unit), byte offsets within 32 bits
+        const size_t rec = (size_t)balanced_slot_floats(mfma_gmax(group)) * sizeof(float);
+        const size_t per_head = (size_t)kPerUnitMaxHelpers + (size_t)s.num_seqs;
+        const size_t rec_bytes = (size_t)s.num_kv_heads * per_head * rec;
+        if ((size_t)s.num_seqs * s.num_kv_heads * sizeof(int32_t) <= kCounterBytes &&
+            rec_bytes <= 0x7fffffffULL) {
+            p.helpers = kPerUnitMaxHelpers;
+            p.rec_per_head = (int)per_head;
+            p.off_counters = 0;
+            p.off_partials = kCounterBytes;
+            p.bytes = kCounterBytes + rec_bytes;
+        }
     } else if (mfma && s.partition_size == 0 && fits) {
         p.path = Path::MfmaBalanced;
         p.max_workers = kMaxWorkers;

@@ -28,7 +28,9 @@ struct DecodePlan {
     int max_partitions;     // fixed-partition paths: ceil(max_blocks*block_size / partition)
     int max_workers;        // balanced path: upper bound on workers (partial slots = 2 per worker)
     size_t off_m, off_l, off_o;          // fixed-partition partial results
-    size_t off_counters, off_partials;   // balanced path
+    size_t off_counters, off_partials;   // balanced path; per-unit path's long units
+    int helpers;            // per-unit path: most helper workgroups per KV head (0: none)
+    int rec_per_head;       // per-unit path: piece records per KV head
     size_t bytes;                        // total workspace bytes
 };
 
@@ -54,11 +56,16 @@ constexpr int kMaxSeqsBalanced = 4096;
 // The automatic choice of one workgroup per (sequence, KV head) on the matrix-core
 // path: at least this many units (two per CU of a 256-CU MI355X, the grid that is
 // resident at once), at most this many blocks per table row (4096 tokens at block
-// size 16), and at most this many sequences: every workgroup ranks the batch's lengths
-// in LDS at a cost of n * n / 256 steps per thread, about 2 us at 256 sequences.
+// size 16), and at most this many sequences (every workgroup ranks the batch's
+// lengths, four per lane of a wave).
 constexpr int kPerUnitMinUnits = 512;
 constexpr int kPerUnitMaxBlocks = 256;
 constexpr int kPerUnitMaxSeqs = 256;
+// Most helper workgroups per KV head that the per-unit grid adds for the pieces of
+// units too long for one workgroup (the launch takes one per workgroup slot of the
+// device, two per CU, spread over the KV heads); they return at once when the batch
+// has none.
+constexpr int kPerUnitMaxHelpers = 64;
 
 // Validate sizes and choose a path. Returns 0 or a negative PKV_E_* code.
 int plan_decode(const DecodeShape& s, DecodePlan* plan);

@@ -211,7 +211,9 @@ def test_llama3_8b_decode_full():
 @pytest.mark.parametrize("reps", [8, 10], ids=["512-units-paired", "640-units-longest-first"])
 def test_per_unit_path_ragged_lengths(reps):
     """At least 512 (sequence, KV head) units with table rows of at most 256 blocks take
-    one workgroup per unit (no workspace is the sign of that path): 512 units pair long
+    one workgroup per unit (a workspace of the counters plus piece records for 64
+    helpers and one per sequence per KV head suffices on that path, and is far too
+    small for the balanced path's): 512 units pair long
     contexts with short ones on a CU, more run longest first. Ragged lengths with empty
     contexts, one-token contexts and block-edge tails: full output against the oracle,
     deterministic, and the fused step bit-identical to the two-call form, caches byte
@@ -220,15 +222,19 @@ def test_per_unit_path_ragged_lengths(reps):
     _say(f"per-unit path: {len(lens)} sequences x 4 KV heads")
     s = W.batch_with_lengths(2900, lens, num_heads=16, num_kv_heads=4, head_dim=128,
                              block_size=16, dtype=torch.bfloat16, device=DEV)
-    assert s.block_tables.shape[1] <= 256
-    # the per-unit path needs no workspace: the C call succeeds without one (the
-    # balanced path would return PKV_E_WORKSPACE)
+    width = s.block_tables.shape[1]
+    assert width <= 256
+    record = (4 * 128 + 2 * 4 + 63) // 64 * 64 * 4
+    need = (1 << 20) + 4 * (64 + len(lens)) * record
+    assert pkv.workspace_size(len(lens), 16, 4, 128, 16, width, 0) >= need
+    # through the C call with a workspace of exactly that size
     lib = pkv.load()
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     out0 = torch.full_like(s.q, float("nan"))
     rc = lib.pkv_paged_attention_decode(
         out0.data_ptr(), s.q.data_ptr(), s.k_cache.data_ptr(), s.v_cache.data_ptr(),
         s.block_tables.data_ptr(), s.context_lens.data_ptr(), float(s.scale), len(lens), 16,
-        4, 128, 16, s.block_tables.shape[1], s.k_cache.shape[0], 1, 0, None, 0,
+        4, 128, 16, width, s.k_cache.shape[0], 1, 0, ws.data_ptr(), need,
         torch.cuda.current_stream(DEV).cuda_stream)
     assert rc == 0, pkv.strerror(rc)
     out = decode(s)

@@ -50,18 +50,25 @@ def _kernel(lines, pattern):
 
 def _streaming_loop(body, nt=True):
     """Lines of the loop (label .. back branch) that holds the most buffer loads with
-    (nt=True) or without (nt=False) the non-temporal bit; of loops with equally many,
-    the first to close (an inner loop before the loop around it)."""
+    (nt=True) or without (nt=False) the non-temporal bit, among the spans that hold no
+    smaller span with six or more such loads (a loop around the streaming loop, or a
+    back branch that the compiler placed at the end of the kernel, spans it); of spans
+    with equally many, the first to close."""
     labels = {m.group(1): i for i, l in enumerate(body) if (m := re.match(r"^(\.LBB\d+_\d+):", l))}
-    best = None
+    spans = []
     for i, l in enumerate(body):
         m = re.search(r"s_(?:cbranch_\w+|branch)\s+(\.LBB\d+_\d+)", l)
         if not m or labels.get(m.group(1), i) >= i:
             continue
         h = labels[m.group(1)]
         count = sum(1 for x in body[h:i] if "buffer_load" in x and (" nt" in x) == nt)
-        if best is None or count > best[2]:
-            best = (h, i, count)
+        spans.append((h, i, count))
+    inner = [a for a in spans
+             if not any(b != a and b[2] >= 6 and a[0] <= b[0] and b[1] <= a[1] for b in spans)]
+    best = None
+    for sp in inner:
+        if best is None or sp[2] > best[2]:
+            best = sp
     assert best and best[2] > 0, "no streaming loop found"
     return body[best[0]:best[1] + 1]
 
