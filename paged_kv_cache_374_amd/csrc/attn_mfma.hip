@@ -1257,11 +1257,13 @@ __device__ __forceinline__ int paired_sequence(const int32_t* __restrict__ ctx_l
 // One workgroup per (sequence, KV head) cannot finish before its longest unit does.
 // With S the blocks of all units over the workgroup slots (two per CU), a unit of more
 // than 2S blocks outlasts any pairing of it with a short one, so it is cut into pieces
-// of P >= S blocks: its own workgroup folds the first piece, and helper workgroups,
-// launched after the batch's (grid z >= num_seqs), fold the others, each long unit's
-// pieces in turn, in sequence order. Every piece's partial result goes to a workspace
-// record; the last piece to finish (a device-scope counter per unit) merges them all
-// in piece order. P grows when the pieces would outnumber the helpers.
+// of P >= S/2 blocks (helpers start only when a slot frees, so their pieces are half
+// a slot's share; S/3 measured slower, S slower still): its own workgroup folds the
+// first piece, and helper workgroups, launched after the batch's (grid z >=
+// num_seqs), fold the others, each long unit's pieces in turn, in sequence order.
+// Every piece's partial result goes to a workspace record; the last piece to finish
+// (a device-scope counter per unit) merges them all in piece order. P grows when the
+// pieces would outnumber the helpers.
 struct UnitWork {
     int b = 0, n = 0;     // sequence and its clipped length
     int j0 = 0, j1 = 0;   // blocks this workgroup folds
@@ -1303,7 +1305,7 @@ __device__ __forceinline__ bool unit_work(const int32_t* __restrict__ ctx_lens, 
 #pragma unroll
             for (int r = 0; r < 4; ++r) bl += nbk[r] > 2 * S ? nbk[r] : 0;
             bl = wave_sum(bl);
-            P = max(S, (bl + helpers - 1) / helpers);
+            P = max((S + 1) / 2, (bl + helpers - 1) / helpers);
         }
     }
     // Long units in sequence order: visit(u, blocks, pieces, first record) returns true

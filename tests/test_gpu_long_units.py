@@ -2,9 +2,9 @@
 
 The per-unit grid (one workgroup per (sequence, KV head)) cuts a unit of more than 2S
 blocks, S being the blocks of all units over the device's workgroup slots (two per
-CU), into pieces of P = max(S, ceil(long blocks / helpers)) blocks: the unit's own
-workgroup folds the first, helper workgroups the others, and the last piece to finish
-merges them. Every case compares the whole output with the oracle (bfloat16 bound
+CU), into pieces of P = max(ceil(S / 2), ceil(long blocks / helpers)) blocks: the
+unit's own workgroup folds the first, helper workgroups the others, and the last
+piece to finish merges them. Every case compares the whole output with the oracle (bfloat16 bound
 2e-2, float16 5e-3, as in the other parity tests), checks that a second call gives the
 same bits (the merge counters are left at zero), and reads the workspace to check that
 the pieces were really cut where the rule above puts them.
@@ -51,7 +51,7 @@ def _expected_pieces(lens, hkv):
     if max(nbs) <= 2 * S:
         return [], helpers
     long_blocks = sum(nb for nb in nbs if nb > 2 * S)
-    P = max(S, -(-long_blocks // helpers))
+    P = max((S + 1) // 2, -(-long_blocks // helpers))
     cut, c = [], 0
     for b, nb in enumerate(nbs):
         if nb > 2 * S:
