@@ -193,7 +193,7 @@ def skewed_decode(seed: int = 1007, device="cpu", gen_device=None,
     """Llama-3-8B-shaped batch with one long context among short ones: 64 sequences,
     one of 4096 tokens at a seeded position and 63 uniform in [128, 512], 32 query /
     8 KV heads, head_dim 128, block_size 16, blocks drawn from a shuffled pool of
-    16384, bfloat16. The long sequence holds about a fifth of the batch's KV bytes,
+    16384, bfloat16. The long sequence holds about a sixth of the batch's KV bytes,
     which a split of one workgroup per (sequence, KV head) cannot spread."""
     gen_device = device if gen_device is None else gen_device
     g = torch.Generator(device="cpu").manual_seed(seed + 7919)
