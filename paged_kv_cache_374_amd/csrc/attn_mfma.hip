@@ -369,40 +369,34 @@ struct KvFp8 {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = widen8<T>(r.v[e].x, r.v[e].y);
     }
-    // Append: chunk c (16 elements) of the new K or V row is quantised (binary32 product
-    // with the reciprocal scale, then E4M3 nearest-even, saturating) into 16 codes at
+    // Append: chunk c (4 elements) of the new K or V row is quantised (binary32 product
+    // with the reciprocal scale, then E4M3 nearest-even, saturating) into 4 codes at
     // position n - 1 of the sequence. Split into source loads and the quantising store
-    // as for 16-bit caches.
-    static constexpr int kAppendChunks = kD / 16;
+    // as for 16-bit caches. Four elements per thread spread a row pair over a whole wave:
+    // the quantiser is about 20 VALU instructions per element, and with 16 elements per
+    // thread it held up the workgroup's first loads by ~0.7 us.
+    static constexpr int kAppendChunks = kD / 4;
     struct AppendSrc {
-        uint4 lo, hi;
+        uint2 v;
     };
     static __device__ __forceinline__ void append_load(AppendSrc& a, const T* __restrict__ new_k,
                                                        const T* __restrict__ new_v, int b,
                                                        int g, int Hkv, int kind, int c) {
-        const uint4* src = reinterpret_cast<const uint4*>((kind ? new_v : new_k) +
-                                                          ((size_t)b * Hkv + g) * kD + 16 * c);
-        a.lo = src[0];
-        a.hi = src[1];
+        a.v = *reinterpret_cast<const uint2*>((kind ? new_v : new_k) +
+                                              ((size_t)b * Hkv + g) * kD + 4 * c);
     }
     static __device__ __forceinline__ void append_store(const AppendSrc& a, uint8_t* k_cache,
                                                         uint8_t* v_cache, uint32_t tile, int pos,
                                                         int kind, int c, float k_inv,
                                                         float v_inv) {
         if (tile == kNoTile) return;
-        float f[16];
-        Vec16<T>::unpack(a.lo, f);
-        Vec16<T>::unpack(a.hi, f + 8);
+        float f[8];
+        Vec16<T>::unpack(make_uint4(a.v.x, a.v.y, 0u, 0u), f);
         const float inv = kind ? v_inv : k_inv;
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w[i] = fp8_e4m3_code(f[4 * i] * inv) | fp8_e4m3_code(f[4 * i + 1] * inv) << 8 |
-                   fp8_e4m3_code(f[4 * i + 2] * inv) << 16 |
-                   fp8_e4m3_code(f[4 * i + 3] * inv) << 24;
-        const size_t dst = ((size_t)tile * kBS + pos) * kD + 16 * c;
-        *reinterpret_cast<uint4*>((kind ? v_cache : k_cache) + dst) =
-            make_uint4(w[0], w[1], w[2], w[3]);
+        const uint32_t w = fp8_e4m3_code(f[0] * inv) | fp8_e4m3_code(f[1] * inv) << 8 |
+                           fp8_e4m3_code(f[2] * inv) << 16 | fp8_e4m3_code(f[3] * inv) << 24;
+        const size_t dst = ((size_t)tile * kBS + pos) * kD + 4 * c;
+        *reinterpret_cast<uint32_t*>((kind ? v_cache : k_cache) + dst) = w;
     }
     static __device__ __forceinline__ void append(uint8_t* k_cache, uint8_t* v_cache,
                                                   const T* __restrict__ new_k,
