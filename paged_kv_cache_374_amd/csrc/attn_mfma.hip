@@ -1118,10 +1118,11 @@ __device__ __forceinline__ bool ranks_lengths(int nseq) {
     return nseq > 1 && nseq <= kPerUnitMaxSeqs;
 }
 
-// Lane u holds the clipped lengths of sequences u, u + 64, u + 128 and u + 192 (-1 past
-// the batch). nseq <= kPerUnitMaxSeqs.
+// Lane u holds the clipped lengths of sequences u, u + 64, u + 128 and u + 192 and
+// their block counts (-1 past the batch). nseq <= kPerUnitMaxSeqs.
 struct LengthKeys {
-    int key[4];
+    int len[4];
+    int key[4];   // blocks: the work a sequence's unit holds
 };
 
 __device__ __forceinline__ LengthKeys load_lengths(const int32_t* __restrict__ ctx_lens,
@@ -1136,9 +1137,18 @@ __device__ __forceinline__ LengthKeys load_lengths(const int32_t* __restrict__ c
             x = ctx_lens[u];
             x = x < 0 ? 0 : (x > cap ? cap : x);
         }
-        k.key[r] = x;
+        k.len[r] = x;
+        k.key[r] = x < 0 ? -1 : (x + kBS - 1) / kBS;
     }
     return k;
+}
+
+// The clipped length of sequence u (wave-uniform u < nseq).
+__device__ __forceinline__ int length_of(const LengthKeys& k, int u) {
+    const int l = u & 63, r = u >> 6;
+    const int v0 = __builtin_amdgcn_readlane(k.len[0], l), v1 = __builtin_amdgcn_readlane(k.len[1], l);
+    const int v2 = __builtin_amdgcn_readlane(k.len[2], l), v3 = __builtin_amdgcn_readlane(k.len[3], l);
+    return r == 0 ? v0 : r == 1 ? v1 : r == 2 ? v2 : v3;
 }
 
 // Wave-wide maximum of x (every lane's value), with row-local DPP steps (lanes ^1, ^2,
@@ -1167,8 +1177,8 @@ __device__ __forceinline__ void length_range(const LengthKeys& k, int cap, int& 
     int h = -1, neg_lo = -cap;   // minimum through the maximum of negated lengths
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        h = max(h, k.key[r]);
-        if (k.key[r] >= 0) neg_lo = max(neg_lo, -k.key[r]);
+        h = max(h, k.len[r]);
+        if (k.len[r] >= 0) neg_lo = max(neg_lo, -k.len[r]);
     }
     hi = wave_max(h);
     lo = -wave_max(neg_lo);
@@ -1177,14 +1187,15 @@ __device__ __forceinline__ void length_range(const LengthKeys& k, int cap, int& 
 // True when every length lies within an eighth of the longest.
 __device__ __forceinline__ bool narrow_range(int hi, int lo) { return 8 * (hi - lo) <= hi; }
 
-// The sequence at position `want` when the lengths are ordered longest first, equal
-// lengths by index; its length goes to `len`. Every wave finds it on its own, with no
-// LDS and no barrier: a binary search over the length value counts the longer ones
-// with ballots (the answer is the smallest x with at most `want` lengths above it), and
-// the position among the sequences of exactly that length picks one of them.
-// want < nseq.
+// The sequence at position `want` when the units are ordered by block count, most
+// first, equal counts by index; its length goes to `len`. Blocks are the work a unit
+// holds, and counting them rather than tokens shortens the search: `lo` and `hi` bound
+// the counts (the batch's shortest and longest). Every wave finds it on its own, with
+// no LDS and no barrier: a binary search over the count counts the larger ones with
+// ballots (the answer is the smallest x with at most `want` counts above it), and the
+// position among the units of exactly that count picks one of them. want < nseq.
 __device__ __forceinline__ int select_by_length(const LengthKeys& k, int nseq, int want,
-                                                int cap, int& len) {
+                                                int lo, int hi, int& len) {
     const int nr = (nseq + 63) >> 6;
     auto above = [&](int x) {
         int c = 0;
@@ -1193,7 +1204,7 @@ __device__ __forceinline__ int select_by_length(const LengthKeys& k, int nseq, i
             if (r < nr) c += __popcll(__ballot(k.key[r] > x));
         return c;
     };
-    int lo = 0, hi = cap;   // above(hi) == 0 <= want, above(-1) == nseq > want
+    // above(hi) == 0 <= want, above(lo - 1) == nseq > want
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
         if (above(mid) <= want)
@@ -1201,8 +1212,7 @@ __device__ __forceinline__ int select_by_length(const LengthKeys& k, int nseq, i
         else
             lo = mid + 1;
     }
-    len = lo;
-    int t = want - above(lo);   // position among the sequences of length lo
+    int t = want - above(lo);   // position among the units of lo blocks
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         if (r >= nr) break;
@@ -1210,10 +1220,13 @@ __device__ __forceinline__ int select_by_length(const LengthKeys& k, int nseq, i
         const int c = __popcll(m);
         if (t < c) {
             for (int i = 0; i < t; ++i) m &= m - 1;
-            return 64 * r + __ffsll(m) - 1;
+            const int u = 64 * r + __ffsll(m) - 1;
+            len = length_of(k, u);
+            return u;
         }
         t -= c;
     }
+    len = 0;
     return 0;   // not reached for want < nseq
 }
 
@@ -1244,14 +1257,15 @@ __device__ __forceinline__ int paired_sequence(const int32_t* __restrict__ ctx_l
     int hi, lo;
     length_range(k, cap, hi, lo);
     if (narrow_range(hi, lo)) return own();
-    return select_by_length(k, nseq, pairing_position(nseq, b), cap, len);
+    return select_by_length(k, nseq, pairing_position(nseq, b), (lo + kBS - 1) / kBS,
+                            (hi + kBS - 1) / kBS, len);
 }
 
 // ------------------------------------------------------------------ long units
 // One workgroup per (sequence, KV head) cannot finish before its longest unit does.
 // With S the blocks of all units over the workgroup slots (two per CU), a unit of more
 // than 2S blocks outlasts any pairing of it with a short one, so it is cut into pieces
-// of P >= S/2 blocks (helpers start only when a slot frees, so their pieces are half
+// of P >= S/2 blocks (S rounded up) (helpers start only when a slot frees, so their pieces are half
 // a slot's share; S/3 measured slower, S slower still): its own workgroup folds the
 // first piece, and helper workgroups, launched after the batch's (grid z >=
 // num_seqs), fold the others, each long unit's pieces in turn, in sequence order.
@@ -1271,36 +1285,43 @@ struct UnitWork {
 __device__ __forceinline__ bool unit_work(const int32_t* __restrict__ ctx_lens, int nseq, int z,
                                           int cap, int lane, int slots, int helpers, int hkv,
                                           UnitWork& w) {
-    auto own = [&](int b) {
-        const int x = ctx_lens[b];
-        w.b = b;
+    if (!ranks_lengths(nseq)) {
+        if (z >= nseq) return false;
+        const int x = ctx_lens[z];
+        w.b = z;
         w.n = x < 0 ? 0 : (x > cap ? cap : x);
         w.j1 = (w.n + kBS - 1) / kBS;
         return true;
-    };
-    if (!ranks_lengths(nseq)) return z < nseq && own(z);
+    }
     const LengthKeys k = load_lengths(ctx_lens, nseq, cap, lane);
+    auto own = [&](int b) {
+        w.b = b;
+        w.n = length_of(k, b);
+        w.j1 = (w.n + kBS - 1) / kBS;
+    };
     int nbk[4], sum = 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        nbk[r] = k.key[r] > 0 ? (k.key[r] + kBS - 1) / kBS : 0;
+        nbk[r] = k.key[r] > 0 ? k.key[r] : 0;
         sum += nbk[r];
     }
     int hi, lo;
     length_range(k, cap, hi, lo);
-    int S = 0, P = 0;   // P = 0: no unit is cut
-    if (helpers > 0) {
-        // at most kPerUnitMaxBlocks blocks per unit, and helpers come with at most one
-        // merge counter per unit (2^18 units): 32-bit safe
-        S = (wave_sum(sum) * hkv + slots - 1) / slots;
+    // A unit is long when it holds more than twice the blocks of an average slot:
+    // blocks * slots > 2 * (blocks of all units). At most kPerUnitMaxBlocks blocks per
+    // unit, and helpers come with at most one merge counter per unit (2^18 units):
+    // 32-bit safe.
+    const int all = helpers > 0 ? wave_sum(sum) * hkv : 0;
+    auto is_long = [&](int nb) { return nb * slots > 2 * all; };
+    int P = 0;   // piece length; 0: no unit is cut
+    if (helpers > 0 && is_long((hi + kBS - 1) / kBS)) {
+        int S = (all + slots - 1) / slots;   // blocks of an average slot
         if (S < 1) S = 1;
-        if ((hi + kBS - 1) / kBS > 2 * S) {
-            int bl = 0;
+        int bl = 0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) bl += nbk[r] > 2 * S ? nbk[r] : 0;
-            bl = wave_sum(bl);
-            P = max((S + 1) / 2, (bl + helpers - 1) / helpers);
-        }
+        for (int r = 0; r < 4; ++r) bl += is_long(nbk[r]) ? nbk[r] : 0;
+        bl = wave_sum(bl);
+        P = max((S + 1) / 2, (bl + helpers - 1) / helpers);
     }
     // Long units in sequence order: visit(u, blocks, pieces, first record) returns true
     // to stop. Lanes past the batch hold 0 blocks, so they are never long.
@@ -1308,7 +1329,7 @@ __device__ __forceinline__ bool unit_work(const int32_t* __restrict__ ctx_lens, 
         int c = 0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            unsigned long long m = __ballot(nbk[r] > 2 * S);
+            unsigned long long m = __ballot(is_long(nbk[r]));
             while (m) {
                 const int l = __ffsll(m) - 1;
                 m &= m - 1;
@@ -1343,12 +1364,13 @@ __device__ __forceinline__ bool unit_work(const int32_t* __restrict__ ctx_lens, 
         own(z);
     } else {
         int len;
-        const int b = select_by_length(k, nseq, pairing_position(nseq, z), cap, len);
+        const int b = select_by_length(k, nseq, pairing_position(nseq, z),
+                                       (lo + kBS - 1) / kBS, (hi + kBS - 1) / kBS, len);
         w.b = b;
         w.n = len;
         w.j1 = (len + kBS - 1) / kBS;
     }
-    if (P > 0 && w.j1 > 2 * S && w.j1 > P) {
+    if (P > 0 && is_long(w.j1) && w.j1 > P) {
         const int b = w.b;
         walk([&](int u, int nb, int kk, int c) {
             if (u != b) return false;

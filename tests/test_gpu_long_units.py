@@ -1,10 +1,11 @@
 """GPU parity of the per-unit decode when some units are too long for one workgroup.
 
-The per-unit grid (one workgroup per (sequence, KV head)) cuts a unit of more than 2S
-blocks, S being the blocks of all units over the device's workgroup slots (two per
-CU), into pieces of P = max(ceil(S / 2), ceil(long blocks / helpers)) blocks: the
-unit's own workgroup folds the first, helper workgroups the others, and the last
-piece to finish merges them. Every case compares the whole output with the oracle (bfloat16 bound
+The per-unit grid (one workgroup per (sequence, KV head)) cuts a unit of more than
+twice the blocks of an average workgroup slot (blocks x slots > 2 x the blocks of all
+units; two slots per CU) into pieces of P = max(ceil(S / 2), ceil(long blocks /
+helpers)) blocks, S = ceil(blocks of all units / slots): the unit's own workgroup
+folds the first, helper workgroups the others, and the last piece to finish merges
+them. Every case compares the whole output with the oracle (bfloat16 bound
 2e-2, float16 5e-3, as in the other parity tests), checks that a second call gives the
 same bits (the merge counters are left at zero), and reads the workspace to check that
 the pieces were really cut where the rule above puts them.
@@ -47,14 +48,19 @@ def _expected_pieces(lens, hkv):
     slots = 2 * torch.cuda.get_device_properties(DEV).multi_processor_count
     helpers = min(MAX_HELPERS, max(1, slots // hkv))
     nbs = [(max(n, 0) + 15) // 16 for n in lens]
-    S = max(1, -(-sum(nbs) * hkv // slots))
-    if max(nbs) <= 2 * S:
+    total = sum(nbs) * hkv
+
+    def is_long(nb):
+        return nb * slots > 2 * total
+
+    if not is_long(max(nbs)):
         return [], helpers
-    long_blocks = sum(nb for nb in nbs if nb > 2 * S)
+    S = max(1, -(-total // slots))
+    long_blocks = sum(nb for nb in nbs if is_long(nb))
     P = max((S + 1) // 2, -(-long_blocks // helpers))
     cut, c = [], 0
     for b, nb in enumerate(nbs):
-        if nb > 2 * S:
+        if is_long(nb):
             kk = -(-nb // P)
             if kk > 1:
                 cut.append((b, kk, c))
