@@ -8,8 +8,9 @@
  * plus pkv_paged_attention_decode_append (a decode step's append and attention in
  * one call), the same calls over 8-bit (FP8 E4M3) caches, attention of several query
  * tokens per sequence (pkv_paged_attention_chunk: prefill chunks, draft
- * verification), block swaps between GPU and pinned host pools (pkv_swap_blocks),
- * workspace sizing and initialisation, version and error strings.
+ * verification), a decode that reads prefix blocks shared by several sequences once
+ * (pkv_paged_attention_decode_grouped), block swaps between GPU and pinned host pools
+ * (pkv_swap_blocks), workspace sizing and initialisation, version and error strings.
  *
  * Pages cited (titles as published):
  *   [P1] "vLLM 源码解析：PagedAttention 如何让大模型推理提速 10 倍"
@@ -293,6 +294,99 @@ int pkv_paged_attention_decode_append_fp8(void* out, const void* q, const void* 
                                           int num_blocks, pkv_dtype dtype, int partition_size,
                                           void* workspace, size_t workspace_bytes,
                                           pkv_stream_t stream);
+
+/*
+ * Decode of a batch whose sequences share prefix blocks, reading each shared block
+ * once per group instead of once per sequence. [P1] section 五 and [P3] section
+ * "共享前缀和 copy-on-write" describe the sharing: the samples of one prompt (parallel
+ * sampling, beam search, requests under one system prompt) point their block tables at
+ * the same physical blocks of the prompt, and only the block that one of them writes
+ * is copied. The result is that of pkv_paged_attention_decode (new_k == NULL) or
+ * pkv_paged_attention_decode_append (new_k != NULL) on the same arguments; only the
+ * order in which partial results are merged differs, so results agree with those calls
+ * within rounding, not bit for bit.
+ *
+ * Groups: group i is the consecutive sequences group_start[i] .. group_start[i+1]-1,
+ * whose block tables hold the same physical blocks in entries 0 .. group_prefix[i]-1.
+ * The groups cover the batch in order: group_start[0] = 0, non-decreasing,
+ * group_start[num_groups] = num_seqs (a sequence that shares nothing is a group of one
+ * with prefix 0). pkv_prefix_groups derives such groups from the tables on the host.
+ *
+ * How it runs: one kernel attends every group's prefix blocks with the members of the
+ * group as the columns of the matrix-core tiles (a tile of 16 columns is 16 / G
+ * members' G query heads), in parts of 64 blocks, and writes one log-sum-exp record per
+ * (member, query head, part) to the workspace; the decode kernel then attends each
+ * member's other blocks and merges the records into its output. A member attends the
+ * prefix blocks before its own context end; with new_k != NULL the block of its
+ * newest token is always attended by the decode kernel (which writes the token first),
+ * even when the group's prefix covers it.
+ *
+ * group_start   int32 [num_groups + 1], device
+ * group_prefix  int32 [num_groups], device; each in [0, max_prefix_blocks]
+ * num_groups    >= 1 when num_seqs > 0
+ * max_group_size  the largest group_start[i+1] - group_start[i] (at least 1)
+ * max_prefix_blocks  an upper bound of group_prefix (<= max_blocks_per_seq); sizes
+ *               the workspace and the prefix kernel's grid
+ * new_k, new_v  NULL (plain decode) or [num_seqs, num_kv_heads, head_dim] rows appended
+ *               at position context_lens[b] - 1 before the attention, as in
+ *               pkv_paged_attention_decode_append; both NULL or both non-NULL
+ *               (PKV_E_NULL otherwise)
+ * workspace     device scratch of at least pkv_paged_attention_grouped_workspace_size()
+ *               bytes (no initialisation needed; its first MiB is left untouched, so the
+ *               workspace of pkv_paged_attention_decode can serve when large enough)
+ * All other arguments as in pkv_paged_attention_decode (no partition_size).
+ * Supported: dtype bfloat16/float16, head_dim 128, block_size 16, num_heads /
+ * num_kv_heads <= 16, max_blocks_per_seq <= 2048 (PKV_E_UNSUPPORTED / PKV_E_HEADS /
+ * PKV_E_SHAPE otherwise). Errors: PKV_E_WORKSPACE for a missing or small workspace;
+ * the common rules otherwise. With PKV_VALIDATE=1 the groups are also checked (cover
+ * the batch in order, sizes and prefixes within their bounds, members' table entries
+ * equal over the prefix): PKV_E_INDEX. Groups that break these rules without
+ * PKV_VALIDATE give unspecified results but no access outside the arrays.
+ * Caller contract: that of pkv_paged_attention_decode_append when appending.
+ * Deterministic: the same inputs give bit-identical outputs.
+ */
+size_t pkv_paged_attention_grouped_workspace_size(int num_seqs, int num_heads,
+                                                  int max_prefix_blocks);
+int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* new_k,
+                                       const void* new_v, void* k_cache, void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       const int32_t* group_start, const int32_t* group_prefix,
+                                       int num_groups, int max_group_size,
+                                       int max_prefix_blocks, float scale, int num_seqs,
+                                       int num_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int max_blocks_per_seq, int num_blocks,
+                                       pkv_dtype dtype, void* workspace,
+                                       size_t workspace_bytes, pkv_stream_t stream);
+
+/* pkv_paged_attention_decode_grouped over 8-bit caches (scales and quantised append as
+ * in pkv_paged_attention_decode_append_fp8). */
+int pkv_paged_attention_decode_grouped_fp8(
+    void* out, const void* q, const void* new_k, const void* new_v, void* k_cache,
+    void* v_cache, float k_scale, float v_scale, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* group_start, const int32_t* group_prefix,
+    int num_groups, int max_group_size, int max_prefix_blocks, float scale, int num_seqs,
+    int num_heads, int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+    int num_blocks, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+    pkv_stream_t stream);
+
+/*
+ * Host helper for the grouped decode: groups of consecutive sequences that share prefix
+ * blocks, read from HOST copies of the block tables and context lengths (no device
+ * work). A group is a maximal run of sequences whose first table entry is the same
+ * non-negative block and that each hold at least one full block; its prefix is the
+ * number of leading entries on which all members agree and that are full blocks
+ * (context_lens / block_size, rounded down) of every member. Every other sequence is a
+ * group of one with prefix 0.
+ * block_tables [num_seqs, max_blocks_per_seq], context_lens [num_seqs]: host, read.
+ * group_start  host, written: num_groups + 1 entries (room for num_seqs + 1).
+ * group_prefix host, written: num_groups entries (room for num_seqs).
+ * num_groups, max_group_size, max_prefix_blocks: written (0 for an empty batch).
+ * Errors: PKV_E_SHAPE (negative sizes, block_size <= 0), PKV_E_NULL.
+ */
+int pkv_prefix_groups(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                      int max_blocks_per_seq, int block_size, int32_t* group_start,
+                      int32_t* group_prefix, int* num_groups, int* max_group_size,
+                      int* max_prefix_blocks);
 
 /* pkv_reshape_and_cache into 8-bit caches: key/value ([num_tokens, num_kv_heads,
  * head_dim] of dtype float32, bfloat16 or float16) are quantised as described above.

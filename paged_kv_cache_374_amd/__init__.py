@@ -13,6 +13,10 @@ the call raises.
     ..._fp8 variants of the three: caches are uint8 tensors of OCP FP8 E4M3 codes with
     one scale each (key = code value * k_scale, value = code value * v_scale)
     copy_blocks(caches, src_dst_pairs)
+    paged_attention_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens,
+                                   scale, prefix_groups(block_tables, context_lens, bs))
+        the decode of a batch whose sequences share prefix blocks, each shared block
+        read once per group
 """
 from __future__ import annotations
 
@@ -28,7 +32,9 @@ __all__ = ["paged_attention_decode", "paged_attention_decode_append", "reshape_a
            "reshape_and_cache_fp8", "copy_blocks", "workspace_size",
            "workspace_init", "partials_layout", "version", "strerror", "PagedKVError",
            "library_path", "load", "read_tiles",
-           "PreparedDecode", "PreparedReshapeAndCache", "PreparedCopyBlocks"]
+           "PreparedDecode", "PreparedReshapeAndCache", "PreparedCopyBlocks",
+           "PrefixGroups", "prefix_groups", "grouped_workspace_size",
+           "paged_attention_decode_grouped", "PreparedGroupedDecode"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
@@ -101,6 +107,16 @@ def load():
     lib.pkv_swap_blocks.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_size_t, _P]
     lib.pkv_copy_blocks.restype = _I
     lib.pkv_copy_blocks.argtypes = [_P, _P, _I, _I, ctypes.c_size_t, _P]
+    lib.pkv_paged_attention_grouped_workspace_size.restype = ctypes.c_size_t
+    lib.pkv_paged_attention_grouped_workspace_size.argtypes = [_I] * 3
+    lib.pkv_paged_attention_decode_grouped.restype = _I
+    lib.pkv_paged_attention_decode_grouped.argtypes = [_P] * 10 + [_I] * 3 + [_F] + \
+        [_I] * 8 + [_P, ctypes.c_size_t, _P]
+    lib.pkv_paged_attention_decode_grouped_fp8.restype = _I
+    lib.pkv_paged_attention_decode_grouped_fp8.argtypes = [_P] * 6 + [_F, _F] + [_P] * 4 + \
+        [_I] * 3 + [_F] + [_I] * 8 + [_P, ctypes.c_size_t, _P]
+    lib.pkv_prefix_groups.restype = _I
+    lib.pkv_prefix_groups.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _P, _P]
     _lib = lib
     return lib
 
@@ -455,6 +471,118 @@ class PreparedDecode:
         if rc != 0:
             raise PagedKVError(rc, self._name)
         return self.out
+
+
+class PrefixGroups:
+    """Groups of consecutive sequences sharing prefix blocks (see prefix_groups):
+    group_start [num_groups + 1] and group_prefix [num_groups] as int32 tensors on the
+    batch's device, and the bounds the grouped decode is sized by."""
+
+    def __init__(self, group_start: torch.Tensor, group_prefix: torch.Tensor,
+                 max_group_size: int, max_prefix_blocks: int):
+        self.group_start = group_start
+        self.group_prefix = group_prefix
+        self.num_groups = int(group_prefix.shape[0])
+        self.max_group_size = int(max_group_size)
+        self.max_prefix_blocks = int(max_prefix_blocks)
+
+
+def prefix_groups(block_tables: torch.Tensor, context_lens: torch.Tensor,
+                  block_size: int, device: Optional[torch.device] = None) -> PrefixGroups:
+    """Host derivation of the groups (pkv_prefix_groups): maximal runs of sequences
+    whose first table entry is the same block, with the leading entries they share as
+    full blocks. Reads host copies of the tables (a device sync when they are on the
+    GPU); the groups are placed on ``device`` (default: the tables' device)."""
+    if block_tables.dim() != 2 or context_lens.dim() != 1 or \
+            context_lens.shape[0] != block_tables.shape[0]:
+        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    dev = block_tables.device if device is None else torch.device(device)
+    t = block_tables.detach().to("cpu", torch.int32).contiguous()
+    c = context_lens.detach().to("cpu", torch.int32).contiguous()
+    B, MB = t.shape
+    start = torch.empty(B + 1, dtype=torch.int32)
+    pfx = torch.empty(max(B, 1), dtype=torch.int32)
+    ng, gmax, pmax = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(load().pkv_prefix_groups(t.data_ptr(), c.data_ptr(), B, MB, int(block_size),
+                                    start.data_ptr(), pfx.data_ptr(), ctypes.byref(ng),
+                                    ctypes.byref(gmax), ctypes.byref(pmax)),
+           "pkv_prefix_groups")
+    n = ng.value
+    return PrefixGroups(start[:n + 1].to(dev), pfx[:n].to(dev), gmax.value, pmax.value)
+
+
+def grouped_workspace_size(num_seqs: int, num_heads: int, max_prefix_blocks: int) -> int:
+    return int(load().pkv_paged_attention_grouped_workspace_size(num_seqs, num_heads,
+                                                                  max_prefix_blocks))
+
+
+class PreparedGroupedDecode:
+    """The grouped decode (pkv_paged_attention_decode_grouped) validated once for a
+    fixed set of tensors: prefix blocks shared by a group's sequences are read once for
+    the group. With ``new_k``/``new_v`` it is the fused step (append, then attend);
+    uint8 caches (E4M3 codes) need k_scale and v_scale. It owns a workspace unless one
+    is passed."""
+
+    def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                 groups: PrefixGroups, new_k: Optional[torch.Tensor] = None,
+                 new_v: Optional[torch.Tensor] = None, k_scale: Optional[float] = None,
+                 v_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+        fp8 = k_cache.dtype == torch.uint8
+        if fp8 and (k_scale is None or v_scale is None):
+            raise ValueError("8-bit caches need k_scale and v_scale")
+        B, Hq, D, NB, Hkv, bs, MB = _decode_shape(out, q, k_cache, v_cache, block_tables,
+                                                  context_lens, fp8)
+        _gpu(groups.group_start, "group_start", torch.int32)
+        _gpu(groups.group_prefix, "group_prefix", torch.int32)
+        if groups.group_start.shape != (groups.num_groups + 1,):
+            raise ValueError("group_start must hold num_groups + 1 entries")
+        if (new_k is None) != (new_v is None):
+            raise ValueError("pass both new_k and new_v, or neither")
+        rows = _new_rows(new_k, new_v, q, k_cache) if new_k is not None else (None, None)
+        need = grouped_workspace_size(B, Hq, groups.max_prefix_blocks)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        else:
+            _gpu(workspace, "workspace")
+        self.workspace = workspace
+        head = (out.data_ptr(), q.data_ptr()) + rows + (k_cache.data_ptr(),
+                                                        v_cache.data_ptr())
+        tail = (block_tables.data_ptr(), context_lens.data_ptr(),
+                groups.group_start.data_ptr(), groups.group_prefix.data_ptr(),
+                groups.num_groups, groups.max_group_size, groups.max_prefix_blocks,
+                float(scale), B, Hq, Hkv, D, bs, MB, NB, _DTYPES[q.dtype],
+                workspace.data_ptr(), workspace.numel())
+        self._name = "pkv_paged_attention_decode_grouped"
+        if fp8:
+            if not (float(k_scale) > 0 and float(v_scale) > 0):
+                raise ValueError("cache scales must be positive")
+            self._args = head + (float(k_scale), float(v_scale)) + tail
+            self._name += "_fp8"
+        else:
+            self._args = head + tail
+        self._fn = getattr(load(), self._name)
+        self._device = q.device
+        self.out = out
+        self._keep = (out, q, k_cache, v_cache, block_tables, context_lens, new_k, new_v,
+                      groups.group_start, groups.group_prefix)
+
+    def __call__(self, stream: Optional[int] = None) -> torch.Tensor:
+        st = _stream(self._device) if stream is None else stream
+        rc = self._fn(*self._args, st)
+        if rc != 0:
+            raise PagedKVError(rc, self._name)
+        return self.out
+
+
+def paged_attention_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens,
+                                   scale, groups: PrefixGroups, new_k=None, new_v=None,
+                                   k_scale=None, v_scale=None,
+                                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """paged_attention_decode (or, with new_k/new_v, paged_attention_decode_append) for
+    a batch whose groups of sequences share prefix blocks: each shared block is read
+    once per group. ``groups`` comes from prefix_groups or is built by the caller."""
+    return PreparedGroupedDecode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                 groups, new_k, new_v, k_scale, v_scale, workspace)()
 
 
 def _append_args(key, value, k_cache, v_cache, slot_mapping):

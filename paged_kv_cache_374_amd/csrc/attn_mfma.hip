@@ -58,6 +58,9 @@ constexpr int kTabMax = kShareMax;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr uint32_t kNoTile = 0xffffffffu;
+// Blocks of a shared prefix that one workgroup of group_prefix_kernel attends (one
+// record per part).
+constexpr int kGroupPart = kGroupPartBlocks;
 // Register buffers per wave in the balanced kernel: while one block is folded, the
 // next one is in flight. Measured on the Llama-3-8B-shaped batch (four waves per CU):
 // 2 buffers 53.6 us, 3 buffers 55.7, 4 buffers 56.4, 6 buffers 58. The memory
@@ -1394,6 +1397,16 @@ __device__ __forceinline__ bool shares_first_block(const int32_t* __restrict__ t
     return first >= 0 && (first == prev || first == next);
 }
 
+// A grouped decode (see "shared prefixes") attends the first prefix_blocks() blocks of a
+// member in group_prefix_kernel: the group's prefix, but never the block of the
+// member's newest token when the step appends it (that token is written by the decode
+// kernel, which reads it after the write), and never past its context.
+__device__ __forceinline__ int prefix_blocks(int pfx, int n, int appending) {
+    if (n <= 0) return 0;
+    const int own = appending ? (n - 1) / kBS : (n + kBS - 1) / kBS;
+    return pfx < own ? pfx : own;
+}
+
 // ------------------------------------------------------------------ partitioned kernel
 template <int GMAX>
 struct PartLds {
@@ -1413,7 +1426,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     float out_scale, float k_inv, float v_inv, int num_heads, int num_kv_heads,
     int group, int max_blocks, int num_blocks, int part_blocks, int max_parts,
     float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, int num_seqs,
-    int slots, int32_t* __restrict__ counters, float* __restrict__ records, int rec_per_head) {
+    int slots, int32_t* __restrict__ counters, float* __restrict__ records, int rec_per_head,
+    const int32_t* __restrict__ seq_prefix, const float* __restrict__ pre_m,
+    const float* __restrict__ pre_l, const float* __restrict__ pre_o, int pre_parts) {
     __shared__ PartLds<GMAX> S;
     const int p = blockIdx.x, g = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
@@ -1442,8 +1457,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
                        make_float4(0.f, 0.f, 0.f, 0.f));
         return;
     }
-    const int j0 = uni(w.j0);
-    if (j0 >= nb) return;
+    // Grouped decode: the group's shared prefix blocks were attended by
+    // group_prefix_kernel; this workgroup attends the rest and merges the prefix's
+    // records (kGroupPart blocks each) into its output.
+    int pfx = seq_prefix != nullptr ? uni(seq_prefix[b]) : 0;
+    pfx = pfx < 0 ? 0 : (pfx > pre_parts * kGroupPart ? pre_parts * kGroupPart : pfx);
+    const int pre_n = (pfx + kGroupPart - 1) / kGroupPart;
+    const int j0 = pfx > 0 ? prefix_blocks(pfx, n, new_k != nullptr) : uni(w.j0);
+    if (j0 >= nb && pre_n == 0) return;
     const int j1 = uni(w.j1);
     const int nparts = (nb + part_blocks - 1) / part_blocks;
     for (int j = j0 + tid; j < j1; j += kThreads) {
@@ -1454,7 +1475,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
         S.valid[j - j0] = (uint8_t)(ok ? (left < kBS ? left : kBS) : 0);
     }
     // the cache policy's test reads beside the table (its latency hides behind it)
-    if (tid == kThreads - 1) S.shared = shares_first_block(tables, b, num_seqs, max_blocks);
+    // (a grouped decode's members read only their own blocks here)
+    if (tid == kThreads - 1)
+        S.shared = pfx == 0 && shares_first_block(tables, b, num_seqs, max_blocks);
     // fused append: the partition holding the newest token writes its K and V rows
     // (the barrier below orders the stores before this workgroup's loads)
     if (new_k != nullptr && (n - 1) / kBS >= j0 && (n - 1) / kBS < j1 &&
@@ -1515,6 +1538,19 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
         float M, Ls;
         float4 o;
         merge_parts<GMAX, kWaves, kWaves>(S.part, P, kWaves, h, d0, M, Ls, o);
+        for (int pp = 0; pp < pre_n; ++pp) {
+            const size_t r = ((size_t)b * num_heads + g * group + h) * pre_parts + pp;
+            const float mp = pre_m[r], lp = pre_l[r];
+            const float4 op = *reinterpret_cast<const float4*>(pre_o + r * kD + d0);
+            const float Mn = fmaxf(M, mp);
+            const float a = weight(M, Mn), cw = weight(mp, Mn);
+            Ls = Ls * a + lp * cw;
+            o.x = o.x * a + op.x * cw;
+            o.y = o.y * a + op.y * cw;
+            o.z = o.z * a + op.z * cw;
+            o.w = o.w * a + op.w * cw;
+            M = Mn;
+        }
         if (pieces > 1) {
             // this piece, with write-through stores (see kCoherent)
             const int sl = rec0 + uni(w.piece) * Part<GMAX>::kFloats;
@@ -1740,6 +1776,134 @@ __global__ __launch_bounds__(kThreads) void chunk_split_kernel(
         const float inv = Ls > 0.f ? out_scale / Ls : 0.f;
         store4(out + ((size_t)row0 + (h / group) * num_heads + h % group) * kD + d0,
                make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv));
+    }
+}
+
+// ------------------------------------------------------------------ shared prefixes
+// Sequences that share their leading blocks (the samples of one prompt, forked from it:
+// [P1] section 五, [P3] section "共享前缀和 copy-on-write") can be decoded as groups:
+// consecutive sequences group_start[i] .. group_start[i+1]-1 whose first
+// group_prefix[i] table entries are the same physical blocks. group_prefix_kernel
+// attends those blocks once for all members of a group. The members are the columns
+// of the matrix-core tiles (column c: member c / G, head c % G, laid out as the query
+// chunks lay out their tokens), each column masked to its own context, so a tile of 16
+// columns reads a block once instead of once per member. The prefix is cut into parts
+// of kGroupPart blocks, one workgroup each, and each part leaves a log-sum-exp record
+// (m, l, unnormalised o) per (member, query head). The per-unit decode kernel then
+// attends each member's remaining blocks and merges the records into its output. A
+// member's share of the prefix is prefix_blocks() (above).
+struct GroupLds {
+    uint32_t tile[kGroupPart];
+    uint8_t valid[kGroupPart];
+    KTile ktile[kWaves];
+    float part[kWaves][Part<16>::kFloats];
+};
+
+// One-dimensional grid over (tile, unit), a unit being (part, KV head, group): unit u =
+// part + parts * (g + Hkv * group index), units padded to a multiple of 8. Workgroup
+// L takes tile (L / 8) % tiles of unit (L / 8 / tiles) * 8 + L % 8, so the tiles of one
+// unit sit 8 workgroups apart in dispatch order, which places them on one XCD
+// (workgroups go to the XCDs in turn): all but the first read the part's blocks from
+// that XCD's L2.
+template <typename T, typename KV>
+__global__ __launch_bounds__(kThreads) void group_prefix_kernel(
+    const T* __restrict__ q, const typename KV::Elem* k_cache,
+    const typename KV::Elem* v_cache, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ group_start,
+    const int32_t* __restrict__ group_prefix, float scale_log2, int num_seqs, int num_heads,
+    int num_kv_heads, int group, int tiles, int units, int max_blocks, int num_blocks,
+    int max_prefix, int pre_parts, int appending, int32_t* __restrict__ seq_prefix,
+    float* __restrict__ rec_m, float* __restrict__ rec_l, float* __restrict__ rec_o) {
+    __shared__ GroupLds S;
+    const int L = blockIdx.x, hi = L >> 3;
+    const int tile = hi % tiles, u = (hi / tiles) * 8 + (L & 7);
+    if (u >= units) return;
+    const int part = u % pre_parts, g = (u / pre_parts) % num_kv_heads;
+    const int gi = u / pre_parts / num_kv_heads;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+    const int s0 = uni(group_start[gi]), s1 = uni(group_start[gi + 1]);
+    // a group outside the batch or with a decreasing start: nothing is read or written
+    if (s0 < 0 || s1 < s0 || s1 > num_seqs) return;
+    const int k = s1 - s0;
+    int pfx = uni(group_prefix[gi]);
+    pfx = pfx < 0 ? 0 : (pfx > max_prefix ? max_prefix : pfx);
+    // every member learns its group's prefix (where the decode kernel starts)
+    if (part == 0 && g == 0 && tile == 0)
+        for (int m = tid; m < k; m += kThreads) seq_prefix[s0 + m] = pfx;
+    // parts the decode kernel reads (j0 < pfx) each leave a record for every column
+    const int j0 = part * kGroupPart;
+    const int ncols = min(16, k * group - tile * 16);
+    if (j0 >= pfx || ncols <= 0) return;
+    // the lane's column: member m, head c % G, and the prefix tokens it attends
+    const int c = tile * 16 + (lane & 15);
+    const int m = c / group;
+    const int cap = max_blocks * kBS;
+    int lim0 = 0;
+    if (m < k) {
+        int n = ctx_lens[s0 + m];
+        n = n < 0 ? 0 : (n > cap ? cap : n);
+        lim0 = min(n, prefix_blocks(pfx, n, appending) * kBS);
+    }
+    // Columns past the group (m >= k) point past its query rows and read zeros; they
+    // are never written.
+    const int row0 = s0 * num_heads + g * group;   // query row of member 0, head 0
+    const int qlane = (m * num_heads + c % group) * kD * (int)sizeof(T);
+    const int qbytes = ((k - 1) * num_heads + group) * kD * (int)sizeof(T);
+    // Blocks and slots that some column of the tile attends: slots past all of them
+    // are cleared like the slots past a context (they may never have been written);
+    // a part past them folds nothing and leaves empty records.
+    const int nmax = wave_max(lim0);
+    const int j1 = min(min(pfx, j0 + kGroupPart), (nmax + kBS - 1) / kBS);
+    // the first member's table entries
+    stage_window(S.tile, S.valid, tables, s0, g, nmax, j0, j1, max_blocks, num_blocks,
+                 num_kv_heads, tid);
+    __syncthreads();
+    WaveState st;
+    reset(st);
+    // every step issues one block (a zero-record buffer past the part)
+    auto issue = [&](typename KV::Regs& R, int ji) {
+        KV::issue(R, k_cache, v_cache, q, ji < j1 ? S.tile[ji - j0] : kNoTile, row0, qbytes,
+                  qlane, lane);
+    };
+    int j = j0 + wave;
+    typename KV::Regs A, B;
+    issue(A, j);
+    issue_order();
+    issue(B, j + kWaves);
+#define PKV_STEP(R)                                                                          \
+    if (j >= j1) break;                                                                      \
+    {                                                                                        \
+        const int vd = S.valid[j - j0];                                                      \
+        int lim = lim0 - j * kBS;                                                            \
+        lim = lim < 0 ? 0 : (lim > vd ? vd : lim);                                           \
+        fold_block<T, KV>(st, R, S.ktile[wave], vd, lim, scale_log2, lane);                  \
+    }                                                                                        \
+    issue(R, j + 2 * kWaves);                                                                \
+    j += kWaves;
+    while (true) {
+        PKV_STEP(A)
+        PKV_STEP(B)
+    }
+#undef PKV_STEP
+    wave_to_part<16>(S.part[wave], st, lane, ncols);
+    __syncthreads();
+    int P[kWaves];
+    for (int v = 0; v < kWaves; ++v) P[v] = v;
+    constexpr int kCols = kD / 4;
+    for (int i = tid; i < ncols * kCols; i += kThreads) {
+        const int h = i / kCols, d0 = (i % kCols) * 4;
+        float M, Ls;
+        float4 o;
+        merge_parts<16, kWaves, kWaves>(S.part, P, kWaves, h, d0, M, Ls, o);
+        const int cc = tile * 16 + h;   // the record's member cc / G and head cc % G
+        const size_t r =
+            ((size_t)(s0 + cc / group) * num_heads + g * group + cc % group) * pre_parts +
+            part;
+        *reinterpret_cast<float4*>(rec_o + r * kD + d0) = o;
+        if (d0 == 0) {
+            rec_m[r] = M;
+            rec_l[r] = Ls;
+        }
     }
 }
 
@@ -2294,9 +2458,61 @@ int launch_partitioned(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
                        split ? (float*)(ws + plan.off_o) : nullptr, s.num_seqs, 2 * num_cus,
                        helpers ? (int32_t*)(ws + plan.off_counters) : nullptr,
                        helpers ? (float*)(ws + plan.off_partials) : nullptr,
-                       plan.rec_per_head);
+                       plan.rec_per_head, (const int32_t*)nullptr, (const float*)nullptr,
+                       (const float*)nullptr, (const float*)nullptr, 0);
     if (hipGetLastError() != hipSuccess) return -1;
     return split ? launch_partition_reduce(a, plan, stream) : 0;
+}
+
+// Grouped decode: the prefix kernel over every group's shared blocks, then the per-unit
+// decode kernel over each member's remaining blocks (no helpers: a member's unit is
+// never cut), merging the prefix records.
+template <typename T, typename KV, int GMAX>
+int launch_grouped_t(const DecodeArgs& a, const GroupArgs& ga, const GroupPlan& gp,
+                     int num_cus, hipStream_t stream) {
+    const DecodeShape& s = a.shape;
+    char* ws = (char*)a.workspace;
+    using E = typename KV::Elem;
+    const Scales sc = scales_of(a);
+    const int G = s.num_heads / s.num_kv_heads;
+    const long long units = (long long)gp.pre_parts * s.num_kv_heads * ga.num_groups;
+    const long long units8 = (units + 7) / 8 * 8;
+    if (units8 * gp.tiles > 0x7fffffffLL) return -1;
+    int32_t* seq_prefix = nullptr;
+    float *rm = nullptr, *rl = nullptr, *ro = nullptr;
+    if (units > 0) {
+        seq_prefix = (int32_t*)(ws + gp.off_prefix);
+        rm = (float*)(ws + gp.off_m);
+        rl = (float*)(ws + gp.off_l);
+        ro = (float*)(ws + gp.off_o);
+        hipLaunchKernelGGL((group_prefix_kernel<T, KV>), dim3((unsigned)(units8 * gp.tiles)),
+                           dim3(kThreads), 0, stream, (const T*)a.q, (const E*)a.k_cache,
+                           (const E*)a.v_cache, a.block_tables, a.context_lens,
+                           ga.group_start, ga.group_prefix, sc.scale_log2, s.num_seqs,
+                           s.num_heads, s.num_kv_heads, G, gp.tiles, (int)units, s.max_blocks,
+                           s.num_blocks, ga.max_prefix, gp.pre_parts, a.new_k != nullptr ? 1 : 0,
+                           seq_prefix, rm, rl, ro);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
+    hipLaunchKernelGGL((decode_mfma_partition_kernel<T, KV, GMAX>),
+                       dim3(1, s.num_kv_heads, s.num_seqs), dim3(kThreads), 0, stream,
+                       (T*)a.out, (const T*)a.q, (E*)a.k_cache, (E*)a.v_cache,
+                       (const T*)a.new_k, (const T*)a.new_v, a.block_tables, a.context_lens,
+                       sc.scale_log2, sc.out_scale, sc.k_inv, sc.v_inv, s.num_heads,
+                       s.num_kv_heads, G, s.max_blocks, s.num_blocks, s.max_blocks, 1,
+                       (float*)nullptr, (float*)nullptr, (float*)nullptr, s.num_seqs,
+                       2 * num_cus, (int32_t*)nullptr, (float*)nullptr, 0, seq_prefix, rm, rl,
+                       ro, units > 0 ? gp.pre_parts : 0);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <typename T, typename KV>
+int launch_grouped_kv(const DecodeArgs& a, const GroupArgs& ga, const GroupPlan& gp,
+                      int num_cus, hipStream_t stream) {
+    const int G = a.shape.num_heads / a.shape.num_kv_heads;
+    if (G <= 4) return launch_grouped_t<T, KV, 4>(a, ga, gp, num_cus, stream);
+    if (G <= 8) return launch_grouped_t<T, KV, 8>(a, ga, gp, num_cus, stream);
+    return launch_grouped_t<T, KV, 16>(a, ga, gp, num_cus, stream);
 }
 
 template <typename T, typename KV>
@@ -2382,6 +2598,22 @@ int launch_chunk_mfma(const ChunkArgs& a, hipStream_t stream) {
         return a.kv_fp8 ? launch_chunk<f16_t, KvFp8<f16_t>>(a, stream)
                         : launch_chunk<f16_t, KvNative<f16_t>>(a, stream);
     return -1;
+}
+
+int launch_decode_grouped(const DecodeArgs& a, const GroupArgs& ga, const GroupPlan& gp,
+                          int num_cus, hipStream_t stream) {
+    if (a.shape.num_kv_heads <= 0 || a.shape.num_heads % a.shape.num_kv_heads != 0) return -1;
+    switch (a.shape.dtype) {
+        case PKV_BFLOAT16:
+            return a.kv_fp8 ? launch_grouped_kv<bf16_t, KvFp8<bf16_t>>(a, ga, gp, num_cus, stream)
+                            : launch_grouped_kv<bf16_t, KvNative<bf16_t>>(a, ga, gp, num_cus,
+                                                                          stream);
+        case PKV_FLOAT16:
+            return a.kv_fp8 ? launch_grouped_kv<f16_t, KvFp8<f16_t>>(a, ga, gp, num_cus, stream)
+                            : launch_grouped_kv<f16_t, KvNative<f16_t>>(a, ga, gp, num_cus,
+                                                                        stream);
+        default: return -1;
+    }
 }
 
 int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& plan, int num_cus,

@@ -196,6 +196,70 @@ int decode_call(void* out, const void* q, const void* new_k, const void* new_v,
     return lr == 0 ? PKV_OK : PKV_E_LAUNCH;
 }
 
+// Host check of a grouped decode's groups (PKV_VALIDATE=1): they cover the batch in
+// order, no group exceeds max_group_size, every prefix lies in [0, max_prefix], and
+// the members of a group hold the same table entries over its prefix.
+int validate_groups(const pkv::DecodeShape& s, const int32_t* tables, const int32_t* start,
+                    const int32_t* prefix, int num_groups, int max_group_size, int max_prefix,
+                    hipStream_t stream) {
+    std::vector<int32_t> hs, hp, ht;
+    if (!fetch(hs, start, (size_t)num_groups + 1, stream) ||
+        !fetch(hp, prefix, (size_t)num_groups, stream) ||
+        !fetch(ht, tables, (size_t)s.num_seqs * s.max_blocks, stream))
+        return PKV_E_LAUNCH;
+    if (hs[0] != 0 || hs[num_groups] != s.num_seqs) return PKV_E_INDEX;
+    for (int i = 0; i < num_groups; ++i) {
+        const int a = hs[i], b = hs[i + 1], p = hp[i];
+        if (b < a || b - a > max_group_size || p < 0 || p > max_prefix) return PKV_E_INDEX;
+        for (int m = a + 1; m < b; ++m)
+            for (int j = 0; j < p; ++j)
+                if (ht[(size_t)m * s.max_blocks + j] != ht[(size_t)a * s.max_blocks + j])
+                    return PKV_E_INDEX;
+    }
+    return PKV_OK;
+}
+
+// Shared by the 16-bit and 8-bit grouped decode entry points.
+int grouped_call(void* out, const void* q, const void* new_k, const void* new_v,
+                 const void* k_cache, const void* v_cache, int kv_fp8, float k_scale,
+                 float v_scale, const int32_t* block_tables, const int32_t* context_lens,
+                 const int32_t* group_start, const int32_t* group_prefix, int num_groups,
+                 int max_group_size, int max_prefix_blocks, float scale, int num_seqs,
+                 int num_heads, int num_kv_heads, int head_dim, int block_size,
+                 int max_blocks_per_seq, int num_blocks, pkv_dtype dtype, void* workspace,
+                 size_t workspace_bytes, pkv_stream_t stream) {
+    pkv::DecodeShape s{num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, num_blocks, (int)dtype, 0};
+    pkv::GroupPlan gp{};
+    const int rc = pkv::plan_grouped(s, num_groups, max_group_size, max_prefix_blocks, &gp);
+    if (rc != PKV_OK) return rc;
+    if (kv_fp8 && !(scale_ok(k_scale) && scale_ok(v_scale))) return PKV_E_SHAPE;
+    if ((new_k == nullptr) != (new_v == nullptr)) return PKV_E_NULL;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !context_lens || !group_start || !group_prefix) return PKV_E_NULL;
+    if (max_blocks_per_seq > 0 && (!k_cache || !v_cache || !block_tables)) return PKV_E_NULL;
+    if (!workspace || workspace_bytes < gp.bytes) return PKV_E_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    if (validate_enabled()) {
+        int v = validate_tables(s, block_tables, context_lens, st);
+        if (v == PKV_OK)
+            v = validate_groups(s, block_tables, group_start, group_prefix, num_groups,
+                                max_group_size, max_prefix_blocks, st);
+        if (v != PKV_OK) return v;
+    }
+    pkv::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, scale, s, workspace};
+    a.new_k = new_k;
+    a.new_v = new_v;
+    a.kv_fp8 = kv_fp8;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    const pkv::GroupArgs ga{group_start, group_prefix, num_groups, max_group_size,
+                            max_prefix_blocks};
+    const int cus = current_device_cus();
+    if (cus <= 0) return PKV_E_DEVICE;
+    return pkv::launch_decode_grouped(a, ga, gp, cus, st) == 0 ? PKV_OK : PKV_E_LAUNCH;
+}
+
 // Shared by the 16-bit and 8-bit chunk entry points.
 int chunk_call(void* out, const void* q, const void* k_cache, const void* v_cache, int kv_fp8,
                float k_scale, float v_scale, const int32_t* block_tables,
@@ -325,6 +389,38 @@ int pkv_paged_attention_decode_append_fp8(void* out, const void* q, const void* 
                        block_tables, context_lens, scale, num_seqs, num_heads, num_kv_heads,
                        head_dim, block_size, max_blocks_per_seq, num_blocks, dtype,
                        partition_size, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attention_decode_grouped(void* out, const void* q, const void* new_k,
+                                       const void* new_v, void* k_cache, void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       const int32_t* group_start, const int32_t* group_prefix,
+                                       int num_groups, int max_group_size,
+                                       int max_prefix_blocks, float scale, int num_seqs,
+                                       int num_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int max_blocks_per_seq, int num_blocks,
+                                       pkv_dtype dtype, void* workspace,
+                                       size_t workspace_bytes, pkv_stream_t stream) {
+    return grouped_call(out, q, new_k, new_v, k_cache, v_cache, 0, 1.f, 1.f, block_tables,
+                        context_lens, group_start, group_prefix, num_groups, max_group_size,
+                        max_prefix_blocks, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                        block_size, max_blocks_per_seq, num_blocks, dtype, workspace,
+                        workspace_bytes, stream);
+}
+
+int pkv_paged_attention_decode_grouped_fp8(
+    void* out, const void* q, const void* new_k, const void* new_v, void* k_cache,
+    void* v_cache, float k_scale, float v_scale, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* group_start, const int32_t* group_prefix,
+    int num_groups, int max_group_size, int max_prefix_blocks, float scale, int num_seqs,
+    int num_heads, int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+    int num_blocks, pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+    pkv_stream_t stream) {
+    return grouped_call(out, q, new_k, new_v, k_cache, v_cache, 1, k_scale, v_scale,
+                        block_tables, context_lens, group_start, group_prefix, num_groups,
+                        max_group_size, max_prefix_blocks, scale, num_seqs, num_heads,
+                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                        dtype, workspace, workspace_bytes, stream);
 }
 
 int pkv_paged_attention_chunk(void* out, const void* q, const void* k_cache,

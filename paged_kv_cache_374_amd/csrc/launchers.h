@@ -96,6 +96,19 @@ struct ChunkArgs {
 // group <= 16).
 int launch_chunk_mfma(const ChunkArgs& a, hipStream_t stream);
 
+// Grouped decode: sequences group_start[i] .. group_start[i+1]-1 share their first
+// group_prefix[i] (<= max_prefix) table entries; groups cover the batch in order.
+struct GroupArgs {
+    const int32_t* group_start;    // [num_groups + 1], device
+    const int32_t* group_prefix;   // [num_groups], device
+    int num_groups, max_group_size, max_prefix;
+};
+
+// Matrix-core grouped decode (shared prefixes attended once per group, then the rest of
+// each sequence); the workspace is laid out by plan_grouped.
+int launch_decode_grouped(const DecodeArgs& a, const GroupArgs& ga, const GroupPlan& gp,
+                          int num_cus, hipStream_t stream);
+
 // Matrix-core kernels (bfloat16/float16, block_size 16).
 int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
                        hipStream_t stream);

@@ -111,7 +111,108 @@ int plan_decode(const DecodeShape& s, DecodePlan* plan) {
     return PKV_OK;
 }
 
+int plan_grouped(const DecodeShape& s, int num_groups, int max_group_size, int max_prefix,
+                 GroupPlan* plan) {
+    if (s.num_seqs < 0 || s.num_heads <= 0 || s.num_kv_heads <= 0 || s.max_blocks < 0 ||
+        s.num_blocks < 0 || num_groups < 0 || max_group_size < 0 || max_prefix < 0)
+        return PKV_E_SHAPE;
+    if (s.num_heads % s.num_kv_heads != 0) return PKV_E_HEADS;
+    const int group = s.num_heads / s.num_kv_heads;
+    if (group > kMaxGroup) return PKV_E_HEADS;
+    if (!mfma_eligible(s.dtype, s.head_dim, s.block_size, group)) return PKV_E_UNSUPPORTED;
+    // the decode kernel stages a sequence's table row in LDS; grid y/z limits
+    if (s.max_blocks > kShareMax || max_prefix > s.max_blocks) return PKV_E_SHAPE;
+    if (s.num_seqs > 65535 || num_groups > 65535 || s.num_kv_heads > 65535) return PKV_E_SHAPE;
+    // every sequence belongs to a group
+    if (s.num_seqs > 0 && (num_groups == 0 || max_group_size == 0)) return PKV_E_SHAPE;
+    if (max_group_size > s.num_seqs) return PKV_E_SHAPE;
+    // query byte offsets within a group (and up to a tile past it) are 32-bit in the
+    // prefix kernel
+    if ((long long)(max_group_size + 16) * s.num_heads * s.head_dim * 2 > 0x7fffffffLL)
+        return PKV_E_SHAPE;
+    GroupPlan p{};
+    p.pre_parts = (max_prefix + kGroupPartBlocks - 1) / kGroupPartBlocks;
+    p.tiles = (int)(((long long)max_group_size * group + 15) / 16);
+    p.parts8 = (p.pre_parts + 7) / 8 * 8;
+    if ((long long)p.tiles * (p.parts8 > 0 ? p.parts8 : 8) > 0x7fffffffLL) return PKV_E_SHAPE;
+    if (s.num_seqs > 0) {
+        const size_t recs = (size_t)s.num_seqs * s.num_heads * p.pre_parts;
+        p.off_prefix = kCounterBytes;
+        p.off_m = p.off_prefix + align_up((size_t)s.num_seqs * sizeof(int32_t), 256);
+        p.off_l = p.off_m + align_up(recs * sizeof(float), 256);
+        p.off_o = p.off_l + align_up(recs * sizeof(float), 256);
+        p.bytes = p.off_o + recs * s.head_dim * sizeof(float);
+    }
+    *plan = p;
+    return PKV_OK;
+}
+
 }  // namespace pkv
+
+extern "C" size_t pkv_paged_attention_grouped_workspace_size(int num_seqs, int num_heads,
+                                                             int max_prefix_blocks) {
+    if (num_seqs <= 0 || num_heads <= 0 || max_prefix_blocks < 0) return 0;
+    const size_t parts =
+        ((size_t)max_prefix_blocks + pkv::kGroupPartBlocks - 1) / pkv::kGroupPartBlocks;
+    const size_t recs = (size_t)num_seqs * num_heads * parts;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    return pkv::kCounterBytes + up((size_t)num_seqs * sizeof(int32_t)) +
+           2 * up(recs * sizeof(float)) + recs * pkv::kMfmaHeadDim * sizeof(float);
+}
+
+extern "C" int pkv_prefix_groups(const int32_t* block_tables, const int32_t* context_lens,
+                                 int num_seqs, int max_blocks_per_seq, int block_size,
+                                 int32_t* group_start, int32_t* group_prefix, int* num_groups,
+                                 int* max_group_size, int* max_prefix_blocks) {
+    if (num_seqs < 0 || max_blocks_per_seq < 0 || block_size <= 0) return PKV_E_SHAPE;
+    if (!num_groups || !max_group_size || !max_prefix_blocks) return PKV_E_NULL;
+    if (num_seqs > 0 && (!context_lens || !group_start || !group_prefix)) return PKV_E_NULL;
+    if (num_seqs > 0 && max_blocks_per_seq > 0 && !block_tables) return PKV_E_NULL;
+    const size_t W = (size_t)max_blocks_per_seq;
+    // blocks of sequence b that are full (shared blocks are only ever full ones)
+    auto full = [&](int b) {
+        const long long n = context_lens[b];
+        const long long f = n <= 0 ? 0 : n / block_size;
+        return (int)(f < max_blocks_per_seq ? f : max_blocks_per_seq);
+    };
+    int ng = 0, gmax = 0, pmax = 0;
+    int b = 0;
+    while (b < num_seqs) {
+        // a run of sequences whose first full block is the same physical block
+        int e = b + 1;
+        int pfx = full(b);
+        if (pfx > 0 && block_tables[(size_t)b * W] >= 0) {
+            while (e < num_seqs && full(e) > 0 &&
+                   block_tables[(size_t)e * W] == block_tables[(size_t)b * W])
+                ++e;
+        }
+        if (e - b < 2) {
+            pfx = 0;
+        } else {
+            // leading entries that every member holds in full and all agree on
+            for (int m = b + 1; m < e; ++m) {
+                const int f = full(m);
+                if (f < pfx) pfx = f;
+                int j = 0;
+                while (j < pfx &&
+                       block_tables[(size_t)m * W + j] == block_tables[(size_t)b * W + j])
+                    ++j;
+                pfx = j;
+            }
+        }
+        group_start[ng] = b;
+        group_prefix[ng] = pfx;
+        ++ng;
+        if (e - b > gmax) gmax = e - b;
+        if (pfx > pmax) pmax = pfx;
+        b = e;
+    }
+    if (num_seqs > 0) group_start[ng] = num_seqs;
+    *num_groups = ng;
+    *max_group_size = gmax;
+    *max_prefix_blocks = pmax;
+    return PKV_OK;
+}
 
 extern "C" size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads,
                                                      int num_kv_heads, int head_dim,

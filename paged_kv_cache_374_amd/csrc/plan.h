@@ -70,6 +70,25 @@ constexpr int kPerUnitMaxHelpers = 64;
 // Validate sizes and choose a path. Returns 0 or a negative PKV_E_* code.
 int plan_decode(const DecodeShape& s, DecodePlan* plan);
 
+// Grouped decode (sequences sharing prefix blocks): blocks of a shared prefix per
+// workgroup of the prefix kernel, each leaving one record per (sequence, query head).
+constexpr int kGroupPartBlocks = 64;
+
+// Grouped decode launch sizes and workspace layout (byte offsets; everything lies above
+// the kCounterBytes of merge counters that start every workspace).
+struct GroupPlan {
+    int pre_parts;   // records per (sequence, query head): ceil(max_prefix / kGroupPartBlocks)
+    int tiles;       // 16-column tiles of the largest group (members x group)
+    int parts8;      // pre_parts rounded up to a multiple of 8
+    size_t off_prefix, off_m, off_l, off_o;
+    size_t bytes;    // total workspace bytes (0 for an empty batch)
+};
+
+// Validate the grouped decode's sizes (matrix-core shapes only) and lay out its
+// workspace. Returns 0 or a negative PKV_E_* code.
+int plan_grouped(const DecodeShape& s, int num_groups, int max_group_size, int max_prefix,
+                 GroupPlan* plan);
+
 // True when the matrix-core kernel supports this dtype / head_dim / block_size / group.
 bool mfma_eligible(int dtype, int head_dim, int block_size, int group);
 

@@ -32,7 +32,9 @@ def test_header_declares_the_entry_points():
               "pkv_swap_blocks", "pkv_bm_create", "pkv_bm_append_tokens",
               "pkv_bm_build_tables",
               "pkv_paged_attention_workspace_size", "pkv_workspace_init", "pkv_version",
-              "pkv_strerror"):
+              "pkv_strerror", "pkv_paged_attention_decode_grouped",
+              "pkv_paged_attention_decode_grouped_fp8",
+              "pkv_paged_attention_grouped_workspace_size", "pkv_prefix_groups"):
         assert n in names
 
 
@@ -193,6 +195,132 @@ def test_fp8_decode_rejects_bad_arguments_on_the_host(fused):
     assert _decode_fp8(lib, fused, B=0, out=None, q=None, nk=None, nv=None) == E["OK"]
     if fused:
         assert _decode_fp8(lib, fused, nk=None) == E["NULL"]
+
+
+def _grouped(lib, fp8=False, **kw):
+    a = dict(out=1, q=1, nk=None, nv=None, k=1, v=1, ks=0.5, vs=0.5, tables=1, ctx=1, gs=1,
+             gp=1, NG=2, GMAX=4, PMAX=10, scale=1.0, B=8, Hq=32, Hkv=8, D=128, bs=16, MB=64,
+             NB=600, dtype=BF16, ws=1, ws_bytes=1 << 30)
+    a.update(kw)
+    tail = (a["tables"], a["ctx"], a["gs"], a["gp"], a["NG"], a["GMAX"], a["PMAX"],
+            a["scale"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"],
+            a["dtype"], a["ws"], a["ws_bytes"], None)
+    if fp8:
+        return lib.pkv_paged_attention_decode_grouped_fp8(a["out"], a["q"], a["nk"], a["nv"],
+                                                          a["k"], a["v"], a["ks"], a["vs"],
+                                                          *tail)
+    return lib.pkv_paged_attention_decode_grouped(a["out"], a["q"], a["nk"], a["nv"], a["k"],
+                                                  a["v"], *tail)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_grouped_decode_rejects_bad_arguments_on_the_host(fp8):
+    lib = pkv.load()
+    # matrix-core shapes only
+    assert _grouped(lib, fp8, dtype=F32) == E["UNSUPPORTED"]
+    assert _grouped(lib, fp8, D=64) == E["UNSUPPORTED"]
+    assert _grouped(lib, fp8, bs=8) == E["UNSUPPORTED"]
+    assert _grouped(lib, fp8, Hq=6, Hkv=4) == E["HEADS"]
+    assert _grouped(lib, fp8, Hq=64, Hkv=2) == E["HEADS"]
+    # groups: at least one covering a non-empty batch, none larger than the batch, the
+    # prefix bound within the table rows, table rows within the staged window
+    assert _grouped(lib, fp8, NG=0) == E["SHAPE"]
+    assert _grouped(lib, fp8, GMAX=0) == E["SHAPE"]
+    assert _grouped(lib, fp8, GMAX=9) == E["SHAPE"]
+    assert _grouped(lib, fp8, PMAX=65) == E["SHAPE"]
+    assert _grouped(lib, fp8, PMAX=-1) == E["SHAPE"]
+    assert _grouped(lib, fp8, MB=2049, PMAX=10) == E["SHAPE"]
+    assert _grouped(lib, fp8, B=-1) == E["SHAPE"]
+    # pointers: both appended rows or neither; the group arrays; the workspace
+    assert _grouped(lib, fp8, nk=1) == E["NULL"]
+    assert _grouped(lib, fp8, nv=1) == E["NULL"]
+    assert _grouped(lib, fp8, gs=None) == E["NULL"]
+    assert _grouped(lib, fp8, gp=None) == E["NULL"]
+    assert _grouped(lib, fp8, q=None) == E["NULL"]
+    assert _grouped(lib, fp8, ws=None) == E["WORKSPACE"]
+    need = pkv.grouped_workspace_size(8, 32, 10)
+    assert _grouped(lib, fp8, ws_bytes=need - 1) == E["WORKSPACE"]
+    if fp8:
+        for bad in (0.0, -1.0, float("inf"), float("nan")):
+            assert _grouped(lib, fp8, ks=bad) == E["SHAPE"]
+            assert _grouped(lib, fp8, vs=bad) == E["SHAPE"]
+    # empty batch: nothing to do
+    assert _grouped(lib, fp8, B=0, NG=0, GMAX=0, out=None, q=None, gs=None, gp=None,
+                    ws=None, ws_bytes=0) == E["OK"]
+
+
+def test_grouped_workspace_arithmetic():
+    # counters' MiB, the per-sequence prefixes, then m, l (256-byte aligned) and o of
+    # one record per (sequence, query head, 64-block part)
+    B, H, P = 256, 32, 2   # 127 prefix blocks -> two parts
+    align = lambda x: (x + 255) // 256 * 256
+    recs = B * H * P
+    expect = (1 << 20) + align(B * 4) + 2 * align(recs * 4) + recs * 128 * 4
+    assert pkv.grouped_workspace_size(B, H, 127) == expect
+    assert pkv.grouped_workspace_size(B, H, 128) == expect
+    assert pkv.grouped_workspace_size(B, H, 129) > expect
+    assert pkv.grouped_workspace_size(B, H, 0) == (1 << 20) + align(B * 4)
+    assert pkv.grouped_workspace_size(0, H, 127) == 0
+
+
+def _groups_by_reading(tables, ctx, bs):
+    """The rule of pkv_prefix_groups read literally: maximal runs of sequences whose
+    first entry is the same non-negative block and that hold a full block; prefix =
+    leading entries equal across the run within every member's full blocks."""
+    B = len(ctx)
+    full = [max(0, n) // bs if n > 0 else 0 for n in ctx]
+    full = [min(f, len(tables[0]) if tables else 0) for f in full]
+    out, b = [], 0
+    while b < B:
+        e = b + 1
+        if full[b] > 0 and tables[b][0] >= 0:
+            while e < B and full[e] > 0 and tables[e][0] == tables[b][0]:
+                e += 1
+        if e - b == 1:
+            out.append((b, 0))
+        else:
+            lim = min(full[b:e])
+            p = 0
+            while p < lim and all(tables[m][p] == tables[b][p] for m in range(b, e)):
+                p += 1
+            out.append((b, p))
+        b = e
+    return out
+
+
+def test_prefix_groups_host_helper():
+    g = torch.Generator().manual_seed(77)
+    for trial in range(40):
+        B = int(torch.randint(1, 40, (1,), generator=g))
+        MB = int(torch.randint(1, 12, (1,), generator=g))
+        bs = [1, 4, 16][trial % 3]
+        tables = torch.randint(-1, 30, (B, MB), generator=g, dtype=torch.int32)
+        ctx = torch.randint(-3, MB * bs + 1, (B,), generator=g, dtype=torch.int32)
+        # runs of sequences copying a leader's leading entries
+        b = 0
+        while b < B:
+            k = int(torch.randint(1, 6, (1,), generator=g))
+            p = int(torch.randint(0, MB + 1, (1,), generator=g))
+            tables[b + 1:b + k, :p] = tables[b, :p]
+            b += k
+        got = pkv.prefix_groups(tables, ctx, bs)
+        want = _groups_by_reading(tables.tolist(), ctx.tolist(), bs)
+        assert got.group_start.tolist() == [a for a, _ in want] + [B]
+        assert got.group_prefix.tolist() == [p for _, p in want]
+        sizes = [y - x for x, y in zip(got.group_start.tolist(), got.group_start.tolist()[1:])]
+        assert got.max_group_size == max(sizes)
+        assert got.max_prefix_blocks == max(p for _, p in want)
+    # the shared-prefix batch: 32 prompts x 8 samples share 127 blocks (the copy-on-write
+    # copied the last prompt block for samples 1..7)
+    import workloads as W
+    s = W.shared_prefix_cow(materialize=False)
+    got = pkv.prefix_groups(s.block_tables, s.context_lens, 16)
+    assert got.group_start.tolist() == list(range(0, 257, 8))
+    assert got.group_prefix.tolist() == [127] * 32
+    # empty batch
+    e = pkv.prefix_groups(torch.zeros(0, 4, dtype=torch.int32),
+                          torch.zeros(0, dtype=torch.int32), 16)
+    assert e.num_groups == 0 and e.max_group_size == 0 and e.max_prefix_blocks == 0
 
 
 def _chunk(lib, fp8=False, **kw):

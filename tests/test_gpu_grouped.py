@@ -1,0 +1,284 @@
+"""GPU parity of the grouped decode: sequences that share prefix blocks, the shared
+blocks attended once per group (pkv_paged_attention_decode_grouped).
+
+Every case compares the whole output with the oracle (bfloat16 bound 2e-2, float16
+5e-3, as in the other parity tests) and, for the fused step, the pools byte for byte
+with the oracle's decode step; a second call must give the same bits. The groups come
+from the host helper (pkv_prefix_groups) on the shared-prefix batch, and are set by
+hand elsewhere: ragged tiles (group x heads not a multiple of 16), prefixes of one, two
+and three 64-block parts, members shorter than their group's prefix, empty contexts,
+groups of one, and the grouped-query factors 1, 4, 8 and 16.
+"""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_374_amd as pkv
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: 2e-2, torch.float16: 5e-3}
+DEV = torch.device("cuda:0")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _err(got, want):
+    g = got.detach().cpu().to(torch.float64).numpy()
+    assert np.all(np.isfinite(g)), "non-finite output"
+    return float(np.max(np.abs(g - want)))
+
+
+def _groups(s):
+    st = torch.tensor(s.extra["group_start"], dtype=torch.int32, device=DEV)
+    pf = torch.tensor(s.extra["group_prefix"], dtype=torch.int32, device=DEV)
+    sizes = [b - a for a, b in zip(s.extra["group_start"], s.extra["group_start"][1:])]
+    return pkv.PrefixGroups(st, pf, max(sizes), max(s.extra["group_prefix"]))
+
+
+def _grouped(s, groups, kc=None, vc=None, new=False, fp8=False):
+    out = torch.full_like(s.q, float("nan"))
+    ks, vs = s.kv_scales if fp8 else (None, None)
+    call = pkv.PreparedGroupedDecode(out, s.q, s.k_cache if kc is None else kc,
+                                     s.v_cache if vc is None else vc, s.block_tables,
+                                     s.context_lens, s.scale, groups,
+                                     new_k=s.new_k if new else None,
+                                     new_v=s.new_v if new else None, k_scale=ks, v_scale=vs)
+    call()
+    torch.cuda.synchronize()
+    return out, call
+
+
+# (label, seed, lengths, group sizes, prefixes, query heads, KV heads, dtype)
+def _lens(seed, n, lo, hi):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(lo, hi + 1, (n,), generator=g).tolist()
+
+
+CASES = [
+    # group 4: 8-member groups fill two tiles; prefixes of one to three parts
+    ("group 4, mixed groups", 3101, _lens(3101, 40, 2100, 2400),
+     [8, 8, 1, 3, 5, 8, 2, 1, 4], [127, 64, 0, 65, 129, 1, 130, 0, 40], 32, 8, torch.bfloat16),
+    # group 8: 9 members = 72 columns (a ragged fifth tile); members shorter than the
+    # prefix (their own length bounds what they attend)
+    ("group 8, ragged tile, short members", 3102,
+     [3000, 2900, 1500, 3100, 700, 2990, 3001, 16, 2050, 3000, 2222, 1999],
+     [9, 3], [150, 100], 64, 8, torch.float16),
+    # group 16: one member per tile
+    ("group 16", 3103, _lens(3103, 12, 1100, 1300), [4, 4, 4], [60, 68, 1], 128, 8,
+     torch.bfloat16),
+    # group 1: 16 members per tile, a group of 20 members
+    ("group 1, 20 members", 3104, _lens(3104, 24, 900, 1400), [20, 4], [55, 30], 4, 4,
+     torch.bfloat16),
+]
+
+
+def _case_batch(case):
+    label, seed, lens, sizes, pfx, hq, hkv, dt = case
+    s = W.batch_with_lengths(seed, lens, num_heads=hq, num_kv_heads=hkv, head_dim=128,
+                             block_size=16, dtype=dt, device=DEV)
+    # the first member of each group holds the whole prefix
+    a = 0
+    for k, p in zip(sizes, pfx):
+        assert (lens[a] + 15) // 16 >= p, (label, a)
+        a += k
+    return W.with_shared_prefixes(s, sizes, pfx)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_grouped_decode(case):
+    s = _case_batch(case)
+    _say(f"grouped decode: {case[0]} seed={case[1]}")
+    groups = _groups(s)
+    want = oracle.paged_attention(s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens,
+                                  s.scale)
+    out, call = _grouped(s, groups)
+    err = _err(out, want)
+    _say(f"  max err {err:.3e}")
+    assert err <= TOL[case[7]], err
+    again = call().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out, again), "second call differs"
+
+
+def test_grouped_empty_member_and_singletons():
+    """A group holding an empty context (zero output row) and a member whose context
+    ends inside the first prefix block; groups of one around it."""
+    lens = [1800, 0, 5, 1700, 1024, 33]
+    s = W.batch_with_lengths(3105, lens, num_heads=32, num_kv_heads=8, head_dim=128,
+                             block_size=16, dtype=torch.bfloat16, device=DEV)
+    s = W.with_shared_prefixes(s, [4, 1, 1], [100, 0, 0])
+    _say("grouped decode: empty member, short member, singletons")
+    want = oracle.paged_attention(s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens,
+                                  s.scale)
+    out, _ = _grouped(s, _groups(s))
+    assert torch.all(out[1] == 0), "empty context must give a zero row"
+    err = _err(out, want)
+    _say(f"  max err {err:.3e}")
+    assert err <= TOL[torch.bfloat16], err
+
+
+def test_grouped_fused_append():
+    """The fused step on hand-made groups: every member's newest token lies past its
+    group's prefix, as copy-on-write guarantees."""
+    lens = _lens(3106, 24, 1000, 1600)
+    s = W.batch_with_lengths(3106, lens, num_heads=32, num_kv_heads=8, head_dim=128,
+                             block_size=16, dtype=torch.bfloat16, device=DEV)
+    s = W.with_shared_prefixes(s, [8, 8, 5, 3], [62, 40, 61, 3])
+    W.with_append(s, seed=3106)
+    _say("grouped decode: fused append")
+    want, ek, ev = oracle.decode_step(s.q, s.new_k, s.new_v, s.k_cache, s.v_cache,
+                                      s.block_tables, s.context_lens, s.scale)
+    kc, vc = s.k_cache.clone(), s.v_cache.clone()
+    out, _ = _grouped(s, _groups(s), kc, vc, new=True)
+    assert torch.equal(kc.cpu(), ek) and torch.equal(vc.cpu(), ev), "pools differ"
+    err = _err(out, want)
+    _say(f"  max err {err:.3e}")
+    assert err <= TOL[torch.bfloat16], err
+
+
+def _cow_step_inputs(prefix):
+    """The shared-prefix batch after its copy-on-write copies and every token before
+    each sequence's newest written (as earlier steps would have), plus the newest
+    rows to append."""
+    s = W.shared_prefix_cow(device=DEV, gen_device=DEV, prefix_tokens=prefix)
+    last = torch.cumsum(torch.tensor([d + 1 for d in s.extra["divergent"]]), 0) - 1
+    rest = torch.ones(s.slot_mapping.numel(), dtype=torch.bool)
+    rest[last] = False
+    ek = oracle.copy_blocks(s.k_cache, s.copy_pairs)
+    ev = oracle.copy_blocks(s.v_cache, s.copy_pairs)
+    ek, ev = oracle.reshape_and_cache(s.new_k, s.new_v, ek, ev, s.slot_mapping)
+    pkv.copy_blocks([s.k_cache, s.v_cache], s.copy_pairs)
+    r = rest.to(DEV)
+    pkv.reshape_and_cache(s.new_k[r].contiguous(), s.new_v[r].contiguous(), s.k_cache,
+                          s.v_cache, s.slot_mapping[r].contiguous())
+    torch.cuda.synchronize()
+    ld = last.to(DEV)
+    s.new_k, s.new_v = s.new_k[ld].contiguous(), s.new_v[ld].contiguous()
+    return s, ek, ev
+
+
+@pytest.mark.parametrize("prefix", [2048, 2040])
+def test_grouped_shared_prefix_cow(prefix):
+    """The shared-prefix batch (32 prompts x 8 samples): groups from the host helper
+    (127 shared blocks: the copy-on-write copies the last prompt block for samples
+    1..7), the fused step against the oracle's step, then the plain decode of the
+    result against the oracle and against the per-sequence decode."""
+    s, ek, ev = _cow_step_inputs(prefix)
+    groups = pkv.prefix_groups(s.block_tables, s.context_lens, 16)
+    _say(f"grouped decode: shared_prefix_cow prefix={prefix}, {groups.num_groups} groups, "
+         f"prefix {groups.max_prefix_blocks} blocks")
+    assert groups.num_groups == 32 and groups.max_group_size == 8
+    assert groups.max_prefix_blocks == 127
+    assert groups.group_prefix.cpu().tolist() == [127] * 32
+    want = oracle.paged_attention(s.q, ek, ev, s.block_tables, s.context_lens, s.scale)
+    kc, vc = s.k_cache.clone(), s.v_cache.clone()
+    out, _ = _grouped(s, groups, kc, vc, new=True)
+    assert torch.equal(kc.cpu(), ek) and torch.equal(vc.cpu(), ev), "fused append differs"
+    err = _err(out, want)
+    _say(f"  fused step: max err {err:.3e}")
+    assert err <= TOL[torch.bfloat16], err
+    out2, _ = _grouped(s, groups, kc, vc)
+    err2 = _err(out2, want)
+    ref = torch.full_like(s.q, float("nan"))
+    pkv.paged_attention_decode(ref, s.q, kc, vc, s.block_tables, s.context_lens, s.scale)
+    torch.cuda.synchronize()
+    diff = float((out2.float() - ref.float()).abs().max())
+    _say(f"  plain decode: max err {err2:.3e}; vs the per-sequence decode {diff:.3e}")
+    assert err2 <= TOL[torch.bfloat16], err2
+    assert diff <= TOL[torch.bfloat16], diff
+
+
+def test_grouped_fp8():
+    """8-bit caches: the shared-prefix batch's fused step."""
+    s, ek, ev = _cow_step_inputs(2048)
+    s.k_cache, s.v_cache = ek.to(DEV), ev.to(DEV)
+    W.with_fp8(s)
+    ks, vs = s.kv_scales
+    groups = pkv.prefix_groups(s.block_tables, s.context_lens, 16)
+    _say("grouped decode: fp8 caches, shared_prefix_cow fused step")
+    want, wk, wv = oracle.decode_step_fp8(s.q, s.new_k, s.new_v, s.k_cache, s.v_cache, ks,
+                                          vs, s.block_tables, s.context_lens, s.scale)
+    kc, vc = s.k_cache.clone(), s.v_cache.clone()
+    out, _ = _grouped(s, groups, kc, vc, new=True, fp8=True)
+    assert torch.equal(kc.cpu(), wk) and torch.equal(vc.cpu(), wv), "pools differ"
+    err = _err(out, want)
+    _say(f"  max err {err:.3e}")
+    assert err <= TOL[torch.bfloat16], err
+
+
+def test_grouped_shared_workspace():
+    """One workspace serves a grouped call after a per-sequence decode that cut long
+    units (its merge counters in the first MiB are left untouched and zero)."""
+    lens = [4096] + _lens(3107, 63, 64, 512)
+    s = W.batch_with_lengths(3107, lens, num_heads=32, num_kv_heads=8, head_dim=128,
+                             block_size=16, dtype=torch.bfloat16, device=DEV)
+    s = W.with_shared_prefixes(s, [1, 9, 54], [0, 4, 3])
+    _say("grouped decode: workspace shared with the per-sequence decode")
+    groups = _groups(s)
+    MB = s.block_tables.shape[1]
+    need = max(pkv.workspace_size(64, 32, 8, 128, 16, MB),
+               pkv.grouped_workspace_size(64, 32, groups.max_prefix_blocks))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    want = oracle.paged_attention(s.q, s.k_cache, s.v_cache, s.block_tables, s.context_lens,
+                                  s.scale)
+    for _ in range(2):
+        a = torch.full_like(s.q, float("nan"))
+        pkv.paged_attention_decode(a, s.q, s.k_cache, s.v_cache, s.block_tables,
+                                   s.context_lens, s.scale, workspace=ws)
+        b = torch.full_like(s.q, float("nan"))
+        pkv.paged_attention_decode_grouped(b, s.q, s.k_cache, s.v_cache, s.block_tables,
+                                           s.context_lens, s.scale, groups, workspace=ws)
+        torch.cuda.synchronize()
+        assert _err(a, want) <= TOL[torch.bfloat16]
+        assert _err(b, want) <= TOL[torch.bfloat16]
+    assert not torch.any(ws[:1 << 20]), "merge counters left non-zero"
+
+
+_VALIDATE_SCRIPT = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+import paged_kv_cache_374_amd as pkv, workloads as W
+dev = torch.device("cuda:0")
+s = W.batch_with_lengths(3108, [300, 310, 320, 330], num_heads=32, num_kv_heads=8,
+                         head_dim=128, block_size=16, dtype=torch.bfloat16, device=dev)
+s = W.with_shared_prefixes(s, [2, 2], [10, 5])
+out = torch.empty_like(s.q)
+def call(start, prefix, gmax, pmax):
+    g = pkv.PrefixGroups(torch.tensor(start, dtype=torch.int32, device=dev),
+                         torch.tensor(prefix, dtype=torch.int32, device=dev), gmax, pmax)
+    try:
+        pkv.paged_attention_decode_grouped(out, s.q, s.k_cache, s.v_cache, s.block_tables,
+                                           s.context_lens, s.scale, g)
+        torch.cuda.synchronize()
+        return 0
+    except pkv.PagedKVError as e:
+        return e.code
+print("ok", call([0, 2, 4], [10, 5], 2, 10), flush=True)
+print("gap", call([0, 2, 3], [10, 5], 2, 10), flush=True)
+print("unequal", call([0, 2, 4], [10, 6], 2, 10), flush=True)
+print("big", call([0, 1, 4], [10, 5], 2, 10), flush=True)
+"""
+
+
+def test_grouped_validation():
+    """PKV_VALIDATE=1 (its own process: the setting is read once): groups that leave a
+    sequence out, members that disagree over the prefix, and a group larger than
+    max_group_size are refused with PKV_E_INDEX before any launch."""
+    _say("grouped decode: PKV_VALIDATE=1 in a child process")
+    env = dict(os.environ, PKV_VALIDATE="1")
+    r = subprocess.run([sys.executable, "-c", _VALIDATE_SCRIPT, ROOT], env=env,
+                       capture_output=True, text=True, timeout=300)
+    _say(r.stdout + r.stderr[-2000:])
+    assert r.returncode == 0
+    got = dict(line.split() for line in r.stdout.strip().splitlines())
+    assert got == {"ok": "0", "gap": "-7", "unequal": "-7", "big": "-7"}, got

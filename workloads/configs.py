@@ -401,6 +401,33 @@ def prefill_chunk512(seed: int = 1006, device="cpu", gen_device=None,
     return s
 
 
+def with_shared_prefixes(step: DecodeStep, sizes: List[int],
+                         prefixes: List[int]) -> DecodeStep:
+    """Make groups of consecutive sequences share prefix blocks: group i holds the next
+    sizes[i] sequences, and its members' first prefixes[i] table entries are set to its
+    first member's entries (the samples of one prompt pointing at the prompt's blocks).
+    The members' own blocks at those positions are simply no longer referenced. A
+    member shorter than the prefix keeps only its own length. The groups are stored as
+    step.extra["group_start"] / ["group_prefix"] (lists)."""
+    if sum(sizes) != step.num_seqs or len(prefixes) != len(sizes):
+        raise ValueError("group sizes must cover the batch, one prefix per group")
+    tables = step.block_tables.to("cpu").clone()
+    width = tables.shape[1]
+    start = [0]
+    for k, p in zip(sizes, prefixes):
+        a = start[-1]
+        if p > width:
+            raise ValueError("prefix longer than the table rows")
+        if p > 0 and int(tables[a, p - 1]) < 0:
+            raise ValueError("a group's first member must hold the whole prefix")
+        tables[a + 1:a + k, :p] = tables[a, :p]
+        start.append(a + k)
+    step.block_tables = tables.to(step.block_tables.device)
+    step.extra["group_start"] = start
+    step.extra["group_prefix"] = list(prefixes)
+    return step
+
+
 def with_append(step: DecodeStep, seed: int = 0) -> DecodeStep:
     """Turn a decode batch into a full decode step: the last token of every context
     is the newly generated one, so its K/V are written into its slot first
