@@ -127,12 +127,13 @@ def older_tokens_to_setup(pkv, s):
     torch.cuda.synchronize()
 
 
-def prepare(pkv, s, graphs, fused):
+def prepare(pkv, s, graphs, fused, grouped=True):
     """Bind the step once: by default the fused call (append at each context end, then
     decode: one kernel on the matrix-core paths); with ``fused`` false the two calls
-    reshape_and_cache + paged_attention_decode. ``s.dec`` is the call that carries the
-    decode kernel. With ``graphs`` the step is captured into one HIP graph, so a step
-    is one graph launch."""
+    reshape_and_cache + paged_attention_decode. A batch whose sequences share prefix
+    blocks uses the grouped decode unless ``grouped`` is false. ``s.dec`` is the call
+    that carries the decode kernels. With ``graphs`` the step is captured into one HIP
+    graph, so a step is one graph launch."""
     copy = None
     if s.copy_pairs is not None and s.copy_pairs.numel() > 0:
         copy = pkv.PreparedCopyBlocks([s.k_cache, s.v_cache], s.copy_pairs)
@@ -161,7 +162,28 @@ def prepare(pkv, s, graphs, fused):
         older_tokens_to_setup(pkv, s)
     s.fused = fused
     ks, vs = s.kv_scales if s.kv_scales is not None else (None, None)
-    if s.fused:
+    if grouped and s.kv_unique < 0.98 * s.kv:
+        # sequences share prefix blocks: the grouped decode reads each shared block once
+        # per group (two kernels: the groups' prefixes, then each sequence's own
+        # blocks). The groups come from the block tables, derived once on the host
+        # before any timing, as a scheduler would when it forks the samples.
+        s.groups = pkv.prefix_groups(s.block_tables, s.context_lens, s.block_size)
+        s.dec = pkv.PreparedGroupedDecode(s.out, s.q, s.k_cache, s.v_cache, s.block_tables,
+                                          s.context_lens, s.scale, s.groups,
+                                          new_k=s.new_k if s.fused else None,
+                                          new_v=s.new_v if s.fused else None,
+                                          k_scale=ks, v_scale=vs)
+        calls = [s.dec]
+        if not s.fused:
+            if s.kv_scales is not None:
+                def app(s=s):
+                    pkv.reshape_and_cache_fp8(s.new_k, s.new_v, s.k_cache, s.v_cache,
+                                              s.slot_mapping, *s.kv_scales)
+            else:
+                app = pkv.PreparedReshapeAndCache(s.new_k, s.new_v, s.k_cache, s.v_cache,
+                                                  s.slot_mapping)
+            calls = [app, s.dec]
+    elif s.fused:
         s.dec = pkv.PreparedDecode(s.out, s.q, s.k_cache, s.v_cache, s.block_tables,
                                    s.context_lens, s.scale, partition_size=s.partition_size,
                                    new_k=s.new_k, new_v=s.new_v, k_scale=ks, v_scale=vs)
@@ -639,6 +661,10 @@ def main():
                          "adds a gap between steps)")
     ap.add_argument("--unfused", action="store_true",
                     help="run the step as two calls (reshape_and_cache, then decode)")
+    ap.add_argument("--no-groups", action="store_true",
+                    help="decode a batch whose sequences share prefix blocks one sequence at "
+                         "a time (default: the grouped decode, shared blocks read once per "
+                         "group)")
     ap.add_argument("--no-gather", action="store_true",
                     help="skip the gather-ceiling probe that runs after the decode timing")
     ap.add_argument("--calibrate", action="store_true",
@@ -669,7 +695,8 @@ def main():
     sets = build_sets(args.workload, max(1, args.rotate), dev)
     torch.cuda.synchronize()
     for s in sets:
-        prepare(pkv, s, graphs=args.graphs, fused=not args.unfused)
+        prepare(pkv, s, graphs=args.graphs, fused=not args.unfused,
+                grouped=not args.no_groups)
 
     for i in range(args.warmup):
         sets[i % len(sets)].run()
@@ -747,6 +774,7 @@ def main():
     if args.calibrate:
         calibrate(pkv, dev)
 
+    grouped_dec = getattr(s0, "groups", None) is not None
     elt = s0.k_cache.element_size()
     dname = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[s0.dtype]
     kv_dname = "fp8_e4m3" if s0.kv_scales is not None else dname
@@ -785,9 +813,19 @@ def main():
                      f"({s0.max_query_len} query tokens per sequence, causal)" if chunk else
                      ("copy_blocks(K, V) + " if s0.copy_pairs is not None and
                       s0.extra.get("prefix_tokens", 0) % s0.block_size == 0 else "") +
-                     ("paged_attention_decode_append (new token written at each context "
+                     (("paged_attention_decode_grouped with the new tokens (the groups' "
+                       "shared prefix blocks attended once per group, then each sequence's "
+                       "own blocks, its new token written first, and the merge; two "
+                       "kernels)" if s0.fused else
+                       "reshape_and_cache(new token) + paged_attention_decode_grouped")
+                      if grouped_dec else
+                      "paged_attention_decode_append (new token written at each context "
                       "end, then attended; one kernel)" if s0.fused else
                       "reshape_and_cache(new token) + paged_attention_decode")),
+            "groups": ({"num_groups": s0.groups.num_groups,
+                        "max_group_size": s0.groups.max_group_size,
+                        "max_prefix_blocks": s0.groups.max_prefix_blocks}
+                       if grouped_dec else None),
             "query_tokens_per_step": int(s0.q.shape[0]),
             "flops_per_step": int(flops_per_launch) if chunk else None,
             "tflops": round(tflops, 2) if chunk else None,
@@ -798,6 +836,7 @@ def main():
         "roofline": {
             "bound": "mfma" if mfma_bound else "hbm",
             "kernel": ("paged_attention_chunk" if chunk else
+                       "paged_attention_decode_grouped (both kernels)" if grouped_dec else
                        "paged_attention_decode_append" if s0.fused
                        else "paged_attention_decode") + fp8,
             "achieved": round(tflops if mfma_bound else achieved_hbm, 2),

@@ -312,32 +312,33 @@ int pkv_paged_attention_decode_append_fp8(void* out, const void* q, const void* 
  * group_start[num_groups] = num_seqs (a sequence that shares nothing is a group of one
  * with prefix 0). pkv_prefix_groups derives such groups from the tables on the host.
  *
- * How it runs: one kernel attends every group's prefix blocks with the members of the
- * group as the columns of the matrix-core tiles (a tile of 16 columns is 16 / G
- * members' G query heads), in parts of 64 blocks, and writes one log-sum-exp record per
- * (member, query head, part) to the workspace; the decode kernel then attends each
- * member's other blocks and merges the records into its output. A member attends the
- * prefix blocks before its own context end; with new_k != NULL the block of its
- * newest token is always attended by the decode kernel (which writes the token first),
- * even when the group's prefix covers it.
+ * How it runs: the members of a group are the columns of the matrix-core tiles (a
+ * tile of 16 columns holds 16 / G whole members, G = num_heads / num_kv_heads). One
+ * workgroup per (group, KV head, tile) reads each prefix block once for all of its
+ * members, then each member's own blocks, and writes the members' output rows. A
+ * prefix longer than 128 blocks is cut into parts of 128 blocks, one workgroup each,
+ * whose log-sum-exp records go to the workspace and are merged by a second kernel. A
+ * member attends the prefix blocks before its own context end; with new_k != NULL the
+ * block of its newest token is always read as one of its own blocks, after the
+ * workgroup has written the token, even when the group's prefix covers it.
  *
  * group_start   int32 [num_groups + 1], device
  * group_prefix  int32 [num_groups], device; each in [0, max_prefix_blocks]
  * num_groups    >= 1 when num_seqs > 0
  * max_group_size  the largest group_start[i+1] - group_start[i] (at least 1)
  * max_prefix_blocks  an upper bound of group_prefix (<= max_blocks_per_seq); sizes
- *               the workspace and the prefix kernel's grid
+ *               the workspace and the grid
  * new_k, new_v  NULL (plain decode) or [num_seqs, num_kv_heads, head_dim] rows appended
  *               at position context_lens[b] - 1 before the attention, as in
  *               pkv_paged_attention_decode_append; both NULL or both non-NULL
  *               (PKV_E_NULL otherwise)
  * workspace     device scratch of at least pkv_paged_attention_grouped_workspace_size()
- *               bytes (no initialisation needed; its first MiB is left untouched, so the
- *               workspace of pkv_paged_attention_decode can serve when large enough)
+ *               bytes, which is 0 (NULL allowed) when max_prefix_blocks <= 128; no
+ *               initialisation needed; its first MiB is left untouched, so the
+ *               workspace of pkv_paged_attention_decode can serve when large enough
  * All other arguments as in pkv_paged_attention_decode (no partition_size).
  * Supported: dtype bfloat16/float16, head_dim 128, block_size 16, num_heads /
- * num_kv_heads <= 16, max_blocks_per_seq <= 2048 (PKV_E_UNSUPPORTED / PKV_E_HEADS /
- * PKV_E_SHAPE otherwise). Errors: PKV_E_WORKSPACE for a missing or small workspace;
+ * num_kv_heads <= 16 (PKV_E_UNSUPPORTED / PKV_E_HEADS otherwise). Errors: PKV_E_WORKSPACE for a missing or small workspace;
  * the common rules otherwise. With PKV_VALIDATE=1 the groups are also checked (cover
  * the batch in order, sizes and prefixes within their bounds, members' table entries
  * equal over the prefix): PKV_E_INDEX. Groups that break these rules without

@@ -519,9 +519,10 @@ def grouped_workspace_size(num_seqs: int, num_heads: int, max_prefix_blocks: int
 class PreparedGroupedDecode:
     """The grouped decode (pkv_paged_attention_decode_grouped) validated once for a
     fixed set of tensors: prefix blocks shared by a group's sequences are read once for
-    the group. With ``new_k``/``new_v`` it is the fused step (append, then attend);
-    uint8 caches (E4M3 codes) need k_scale and v_scale. It owns a workspace unless one
-    is passed."""
+    the group's tile of members. With ``new_k``/``new_v`` it is the fused step (append,
+    then attend); uint8 caches (E4M3 codes) need k_scale and v_scale. It owns a
+    workspace (needed only for prefixes of more than 128 blocks) unless one is
+    passed."""
 
     def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, scale,
                  groups: PrefixGroups, new_k: Optional[torch.Tensor] = None,
@@ -540,18 +541,19 @@ class PreparedGroupedDecode:
             raise ValueError("pass both new_k and new_v, or neither")
         rows = _new_rows(new_k, new_v, q, k_cache) if new_k is not None else (None, None)
         need = grouped_workspace_size(B, Hq, groups.max_prefix_blocks)
-        if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-        else:
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        elif workspace is not None:
             _gpu(workspace, "workspace")
         self.workspace = workspace
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() if workspace is not None else 0
         head = (out.data_ptr(), q.data_ptr()) + rows + (k_cache.data_ptr(),
                                                         v_cache.data_ptr())
         tail = (block_tables.data_ptr(), context_lens.data_ptr(),
                 groups.group_start.data_ptr(), groups.group_prefix.data_ptr(),
                 groups.num_groups, groups.max_group_size, groups.max_prefix_blocks,
-                float(scale), B, Hq, Hkv, D, bs, MB, NB, _DTYPES[q.dtype],
-                workspace.data_ptr(), workspace.numel())
+                float(scale), B, Hq, Hkv, D, bs, MB, NB, _DTYPES[q.dtype], ws_ptr, ws_bytes)
         self._name = "pkv_paged_attention_decode_grouped"
         if fp8:
             if not (float(k_scale) > 0 and float(v_scale) > 0):

@@ -58,8 +58,7 @@ constexpr int kTabMax = kShareMax;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr uint32_t kNoTile = 0xffffffffu;
-// Blocks of a shared prefix that one workgroup of group_prefix_kernel attends (one
-// record per part).
+// Blocks of a shared prefix that one workgroup of the grouped decode attends.
 constexpr int kGroupPart = kGroupPartBlocks;
 // Register buffers per wave in the balanced kernel: while one block is folded, the
 // next one is in flight. Measured on the Llama-3-8B-shaped batch (four waves per CU):
@@ -1397,16 +1396,6 @@ __device__ __forceinline__ bool shares_first_block(const int32_t* __restrict__ t
     return first >= 0 && (first == prev || first == next);
 }
 
-// A grouped decode (see "shared prefixes") attends the first prefix_blocks() blocks of a
-// member in group_prefix_kernel: the group's prefix, but never the block of the
-// member's newest token when the step appends it (that token is written by the decode
-// kernel, which reads it after the write), and never past its context.
-__device__ __forceinline__ int prefix_blocks(int pfx, int n, int appending) {
-    if (n <= 0) return 0;
-    const int own = appending ? (n - 1) / kBS : (n + kBS - 1) / kBS;
-    return pfx < own ? pfx : own;
-}
-
 // ------------------------------------------------------------------ partitioned kernel
 template <int GMAX>
 struct PartLds {
@@ -1426,9 +1415,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     float out_scale, float k_inv, float v_inv, int num_heads, int num_kv_heads,
     int group, int max_blocks, int num_blocks, int part_blocks, int max_parts,
     float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, int num_seqs,
-    int slots, int32_t* __restrict__ counters, float* __restrict__ records, int rec_per_head,
-    const int32_t* __restrict__ seq_prefix, const float* __restrict__ pre_m,
-    const float* __restrict__ pre_l, const float* __restrict__ pre_o, int pre_parts) {
+    int slots, int32_t* __restrict__ counters, float* __restrict__ records, int rec_per_head) {
     __shared__ PartLds<GMAX> S;
     const int p = blockIdx.x, g = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
@@ -1457,14 +1444,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
                        make_float4(0.f, 0.f, 0.f, 0.f));
         return;
     }
-    // Grouped decode: the group's shared prefix blocks were attended by
-    // group_prefix_kernel; this workgroup attends the rest and merges the prefix's
-    // records (kGroupPart blocks each) into its output.
-    int pfx = seq_prefix != nullptr ? uni(seq_prefix[b]) : 0;
-    pfx = pfx < 0 ? 0 : (pfx > pre_parts * kGroupPart ? pre_parts * kGroupPart : pfx);
-    const int pre_n = (pfx + kGroupPart - 1) / kGroupPart;
-    const int j0 = pfx > 0 ? prefix_blocks(pfx, n, new_k != nullptr) : uni(w.j0);
-    if (j0 >= nb && pre_n == 0) return;
+    const int j0 = uni(w.j0);
+    if (j0 >= nb) return;
     const int j1 = uni(w.j1);
     const int nparts = (nb + part_blocks - 1) / part_blocks;
     for (int j = j0 + tid; j < j1; j += kThreads) {
@@ -1475,9 +1456,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
         S.valid[j - j0] = (uint8_t)(ok ? (left < kBS ? left : kBS) : 0);
     }
     // the cache policy's test reads beside the table (its latency hides behind it)
-    // (a grouped decode's members read only their own blocks here)
-    if (tid == kThreads - 1)
-        S.shared = pfx == 0 && shares_first_block(tables, b, num_seqs, max_blocks);
+    if (tid == kThreads - 1) S.shared = shares_first_block(tables, b, num_seqs, max_blocks);
     // fused append: the partition holding the newest token writes its K and V rows
     // (the barrier below orders the stores before this workgroup's loads)
     if (new_k != nullptr && (n - 1) / kBS >= j0 && (n - 1) / kBS < j1 &&
@@ -1538,19 +1517,6 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
         float M, Ls;
         float4 o;
         merge_parts<GMAX, kWaves, kWaves>(S.part, P, kWaves, h, d0, M, Ls, o);
-        for (int pp = 0; pp < pre_n; ++pp) {
-            const size_t r = ((size_t)b * num_heads + g * group + h) * pre_parts + pp;
-            const float mp = pre_m[r], lp = pre_l[r];
-            const float4 op = *reinterpret_cast<const float4*>(pre_o + r * kD + d0);
-            const float Mn = fmaxf(M, mp);
-            const float a = weight(M, Mn), cw = weight(mp, Mn);
-            Ls = Ls * a + lp * cw;
-            o.x = o.x * a + op.x * cw;
-            o.y = o.y * a + op.y * cw;
-            o.z = o.z * a + op.z * cw;
-            o.w = o.w * a + op.w * cw;
-            M = Mn;
-        }
         if (pieces > 1) {
             // this piece, with write-through stores (see kCoherent)
             const int sl = rec0 + uni(w.piece) * Part<GMAX>::kFloats;
@@ -1783,43 +1749,73 @@ __global__ __launch_bounds__(kThreads) void chunk_split_kernel(
 // Sequences that share their leading blocks (the samples of one prompt, forked from it:
 // [P1] section 五, [P3] section "共享前缀和 copy-on-write") can be decoded as groups:
 // consecutive sequences group_start[i] .. group_start[i+1]-1 whose first
-// group_prefix[i] table entries are the same physical blocks. group_prefix_kernel
-// attends those blocks once for all members of a group. The members are the columns
-// of the matrix-core tiles (column c: member c / G, head c % G, laid out as the query
-// chunks lay out their tokens), each column masked to its own context, so a tile of 16
-// columns reads a block once instead of once per member. The prefix is cut into parts
-// of kGroupPart blocks, one workgroup each, and each part leaves a log-sum-exp record
-// (m, l, unnormalised o) per (member, query head). The per-unit decode kernel then
-// attends each member's remaining blocks and merges the records into its output. A
-// member's share of the prefix is prefix_blocks() (above).
+// group_prefix[i] table entries are the same physical blocks. The members of a group are
+// the columns of the matrix-core tiles: a tile holds mpt = 16 / G members (column c:
+// member c / G of the tile, head c % G, as the query chunks lay out their tokens), and
+// each column is masked to its own context. A tile's workgroup reads each prefix block
+// once for all of its members, then each member's own blocks (columns of other members
+// masked), so a block shared by the group is read once per tile instead of once per
+// member. A prefix longer than kGroupPart blocks is cut into parts, one workgroup each;
+// the last part also takes the members' own blocks. A group of one part writes its
+// output directly; otherwise each part leaves a log-sum-exp record (m, l, unnormalised
+// o) per (member, query head) and group_merge_kernel combines them.
+//
+// A member's share of the prefix is prefix_blocks(): the group's prefix, but never the
+// block of its newest token when the step appends it (the workgroup writes that token
+// first, so it must read the block after the write), and never past its context.
+__device__ __forceinline__ int prefix_blocks(int pfx, int n, int appending) {
+    if (n <= 0) return 0;
+    const int own = appending ? (n - 1) / kBS : (n + kBS - 1) / kBS;
+    return pfx < own ? pfx : own;
+}
+
+// Table entries a tile's workgroup stages at a time: its list of blocks (the part's
+// prefix blocks, then each member's own blocks) goes through LDS in windows.
+constexpr int kGroupWindow = 1024;
+// Tiles (of 16 columns) a workgroup folds every prefix block into, and its waves.
+constexpr int kGroupTiles = kGroupTilesPerWorkgroup;
+constexpr int kGroupWaves = 4;
+// Most members of one workgroup (16 columns per tile, at least one column per member).
+constexpr int kGroupMembers = 16 * kGroupTiles;
+static_assert(kGroupMembers <= 64, "members of a workgroup are the lanes of one wave");
+
+template <int NW>
 struct GroupLds {
-    uint32_t tile[kGroupPart];
-    uint8_t valid[kGroupPart];
-    KTile ktile[kWaves];
-    float part[kWaves][Part<16>::kFloats];
+    uint32_t tile[kGroupWindow];
+    uint8_t valid[kGroupWindow];
+    int8_t owner[kGroupWindow];   // -1: a prefix block; else the member (in the workgroup) it belongs to
+    int priv[kGroupMembers + 1];  // members' own blocks, exclusive prefix sums
+    int mn[kGroupMembers];        // members' context lengths
+    int me[kGroupMembers];        // and prefix shares
+    KTile ktile[NW];
+    float part[NW][Part<16>::kFloats];
 };
 
-// One-dimensional grid over (tile, unit), a unit being (part, KV head, group): unit u =
-// part + parts * (g + Hkv * group index), units padded to a multiple of 8. Workgroup
-// L takes tile (L / 8) % tiles of unit (L / 8 / tiles) * 8 + L % 8, so the tiles of one
-// unit sit 8 workgroups apart in dispatch order, which places them on one XCD
-// (workgroups go to the XCDs in turn): all but the first read the part's blocks from
-// that XCD's L2.
-template <typename T, typename KV>
-__global__ __launch_bounds__(kThreads) void group_prefix_kernel(
-    const T* __restrict__ q, const typename KV::Elem* k_cache,
-    const typename KV::Elem* v_cache, const int32_t* __restrict__ tables,
-    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ group_start,
-    const int32_t* __restrict__ group_prefix, float scale_log2, int num_seqs, int num_heads,
-    int num_kv_heads, int group, int tiles, int units, int max_blocks, int num_blocks,
-    int max_prefix, int pre_parts, int appending, int32_t* __restrict__ seq_prefix,
+// One-dimensional grid over (tile set, unit), a unit being (part, KV head, group): unit
+// u = part + parts * (g + Hkv * group index), units padded to a multiple of 8. Each
+// workgroup takes NT tiles of a group (NT * mpt members): its waves fold every staged
+// prefix block into all NT tiles (the K and V registers shared) and each member's own
+// block into that member's tile. Workgroup L takes tile set (L / 8) % sets of unit
+// (L / 8 / sets) * 8 + L % 8, so the tile sets of one unit sit 8 workgroups apart in
+// dispatch order, which places them on one XCD (workgroups go to the XCDs in turn):
+// all but the first read the prefix blocks from that XCD's L2.
+template <typename T, typename KV, int NT, int NW>
+__global__ __launch_bounds__(64 * NW) void group_tile_kernel(
+    T* __restrict__ out, const T* __restrict__ q, typename KV::Elem* k_cache,
+    typename KV::Elem* v_cache, const T* __restrict__ new_k, const T* __restrict__ new_v,
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ ctx_lens,
+    const int32_t* __restrict__ group_start, const int32_t* __restrict__ group_prefix,
+    float scale_log2, float out_scale, float k_inv, float v_inv, int num_seqs, int num_heads,
+    int num_kv_heads, int group, int mpt, int sets, int units, int max_blocks,
+    int num_blocks, int max_prefix, int parts_max, int32_t* __restrict__ seq_prefix,
     float* __restrict__ rec_m, float* __restrict__ rec_l, float* __restrict__ rec_o) {
-    __shared__ GroupLds S;
+    __shared__ GroupLds<NW> S;
+    constexpr int kT = 64 * NW;
     const int L = blockIdx.x, hi = L >> 3;
-    const int tile = hi % tiles, u = (hi / tiles) * 8 + (L & 7);
+    const int set = hi % sets, u = (hi / sets) * 8 + (L & 7);
     if (u >= units) return;
-    const int part = u % pre_parts, g = (u / pre_parts) % num_kv_heads;
-    const int gi = u / pre_parts / num_kv_heads;
+    const int part = u % parts_max, g = (u / parts_max) % num_kv_heads;
+    const int gi = u / parts_max / num_kv_heads;
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int s0 = uni(group_start[gi]), s1 = uni(group_start[gi + 1]);
     // a group outside the batch or with a decreasing start: nothing is read or written
@@ -1827,84 +1823,209 @@ __global__ __launch_bounds__(kThreads) void group_prefix_kernel(
     const int k = s1 - s0;
     int pfx = uni(group_prefix[gi]);
     pfx = pfx < 0 ? 0 : (pfx > max_prefix ? max_prefix : pfx);
-    // every member learns its group's prefix (where the decode kernel starts)
-    if (part == 0 && g == 0 && tile == 0)
-        for (int m = tid; m < k; m += kThreads) seq_prefix[s0 + m] = pfx;
-    // parts the decode kernel reads (j0 < pfx) each leave a record for every column
-    const int j0 = part * kGroupPart;
-    const int ncols = min(16, k * group - tile * 16);
-    if (j0 >= pfx || ncols <= 0) return;
-    // the lane's column: member m, head c % G, and the prefix tokens it attends
-    const int c = tile * 16 + (lane & 15);
-    const int m = c / group;
+    const int parts = pfx > 0 ? (pfx + kGroupPart - 1) / kGroupPart : 1;
+    // the merge kernel learns each member's prefix
+    if (seq_prefix != nullptr && part == 0 && g == 0 && set == 0)
+        for (int m = tid; m < k; m += kT) seq_prefix[s0 + m] = pfx;
+    const int m0 = set * NT * mpt;   // the workgroup's first member
+    if (part >= parts || m0 >= k) return;
+    const int nm = min(NT * mpt, k - m0);    // members of this workgroup
+    const int nt = (nm + mpt - 1) / mpt;     // tiles holding them
+    const bool last = part == parts - 1;
+    const int appending = new_k != nullptr;
     const int cap = max_blocks * kBS;
-    int lim0 = 0;
-    if (m < k) {
-        int n = ctx_lens[s0 + m];
-        n = n < 0 ? 0 : (n > cap ? cap : n);
-        lim0 = min(n, prefix_blocks(pfx, n, appending) * kBS);
+    // members' lengths, prefix shares and (last part) own block counts
+    if (wave == 0) {
+        int n = 0, e = 0, own = 0;
+        if (lane < nm) {
+            n = ctx_lens[s0 + m0 + lane];
+            n = n < 0 ? 0 : (n > cap ? cap : n);
+            e = prefix_blocks(pfx, n, appending);
+            own = last ? (n + kBS - 1) / kBS - e : 0;
+        }
+        int incl = own;   // inclusive prefix sum over the lanes
+#pragma unroll
+        for (int d = 1; d < kGroupMembers; d <<= 1) {
+            const int y = __shfl_up(incl, d);
+            if (lane >= d) incl += y;
+        }
+        if (lane < kGroupMembers) {
+            S.mn[lane] = n;
+            S.me[lane] = e;
+            S.priv[lane + 1] = incl;
+        }
+        if (lane == 0) S.priv[0] = 0;
     }
-    // Columns past the group (m >= k) point past its query rows and read zeros; they
-    // are never written.
-    const int row0 = s0 * num_heads + g * group;   // query row of member 0, head 0
-    const int qlane = (m * num_heads + c % group) * kD * (int)sizeof(T);
-    const int qbytes = ((k - 1) * num_heads + group) * kD * (int)sizeof(T);
-    // Blocks and slots that some column of the tile attends: slots past all of them
-    // are cleared like the slots past a context (they may never have been written);
-    // a part past them folds nothing and leaves empty records.
-    const int nmax = wave_max(lim0);
-    const int j1 = min(min(pfx, j0 + kGroupPart), (nmax + kBS - 1) / kBS);
-    // the first member's table entries
-    stage_window(S.tile, S.valid, tables, s0, g, nmax, j0, j1, max_blocks, num_blocks,
-                 num_kv_heads, tid);
+    // fused append (last part): each member's newest row, before any block is read
+    if (appending && last)
+        for (int i = tid; i < nm * 2 * KV::kAppendChunks; i += kT) {
+            const int mi = i / (2 * KV::kAppendChunks), r = i % (2 * KV::kAppendChunks);
+            const int b = s0 + m0 + mi;
+            int n = ctx_lens[b];
+            n = n < 0 ? 0 : (n > cap ? cap : n);
+            if (n > 0)
+                KV::append(k_cache, v_cache, new_k, new_v, tables + (size_t)b * max_blocks, b, g,
+                           num_kv_heads, n, num_blocks, r / KV::kAppendChunks,
+                           r % KV::kAppendChunks, k_inv, v_inv);
+        }
     __syncthreads();
-    WaveState st;
-    reset(st);
-    // every step issues one block (a zero-record buffer past the part)
-    auto issue = [&](typename KV::Regs& R, int ji) {
-        KV::issue(R, k_cache, v_cache, q, ji < j1 ? S.tile[ji - j0] : kNoTile, row0, qbytes,
-                  qlane, lane);
-    };
-    int j = j0 + wave;
-    typename KV::Regs A, B;
-    issue(A, j);
-    issue_order();
-    issue(B, j + kWaves);
+    // The lane's column in tile t: member t * mpt + c / G of the workgroup, head c % G.
+    // Columns past the members point past their query rows and read zeros; they are
+    // never written.
+    const int c = lane & 15, cm = c / group;
+    const int row0 = (s0 + m0) * num_heads + g * group;   // query row of member 0, head 0
+    int lim0[NT];     // prefix tokens the lane's column of tile t attends
+    uint4 qv[NT][4];  // its query, loaded once
+    int pmax = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int mi = t * mpt + cm;
+        const bool live = c < mpt * group && mi < nm;
+        lim0[t] = live ? min(S.mn[mi], S.me[mi] * kBS) : 0;
+        pmax = max(pmax, lim0[t]);
+        const int tm = min(mpt, max(0, nm - t * mpt));   // members of tile t
+        const int qrow = row0 + t * mpt * num_heads;
+        const int qbytes = tm > 0 ? ((tm - 1) * num_heads + group) * kD * (int)sizeof(T) : 0;
+        issue_query(qv[t], q, qrow, qbytes, (cm * num_heads + c % group) * kD * (int)sizeof(T),
+                    lane);
+    }
+    // prefix blocks of this part that some column attends; slots past all of them are
+    // cleared like the slots past a context (they may never have been written)
+    const int nmax = wave_max(pmax);
+    const int j0 = part * kGroupPart;
+    const int np = max(0, min(min(pfx, j0 + kGroupPart), (nmax + kBS - 1) / kBS) - j0);
+    const int total = np + uni(S.priv[nm]);
+    WaveState st[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) reset(st[t]);
+    for (int w0 = 0; w0 < total; w0 += kGroupWindow) {
+        const int w1 = min(total, w0 + kGroupWindow);
+        __syncthreads();   // the previous window's entries are no longer read
+        for (int x = w0 + tid; x < w1; x += kT) {
+            int b, j, n, own = -1;
+            if (x < np) {   // a prefix block, from the first member's table
+                b = s0;
+                j = j0 + x;
+                n = nmax;
+            } else {        // member own's block
+                const int y = x - np;
+                own = 0;
+                while (own < nm - 1 && S.priv[own + 1] <= y) ++own;
+                b = s0 + m0 + own;
+                j = S.me[own] + (y - S.priv[own]);
+                n = S.mn[own];
+            }
+            const int phys = tables[(size_t)b * max_blocks + j];
+            const bool ok = phys >= 0 && phys < num_blocks;
+            const int left = n - j * kBS;
+            S.tile[x - w0] = ok ? (uint32_t)phys * (uint32_t)num_kv_heads + (uint32_t)g : kNoTile;
+            S.valid[x - w0] = (uint8_t)(ok ? (left < kBS ? left : kBS) : 0);
+            S.owner[x - w0] = (int8_t)own;
+        }
+        __syncthreads();
+        // every step issues one block (a zero-record buffer past the window)
+        auto issue = [&](typename KV::Regs& R, int xi) {
+            KV::template issue<kStream, false>(R, k_cache, v_cache, q,
+                                               xi < w1 ? S.tile[xi - w0] : kNoTile, 0, 0, 0,
+                                               lane);
+        };
+        int x = w0 + wave;
+        typename KV::Regs A, B;
+        issue(A, x);
+        issue_order();
+        issue(B, x + NW);
 #define PKV_STEP(R)                                                                          \
-    if (j >= j1) break;                                                                      \
-    {                                                                                        \
-        const int vd = S.valid[j - j0];                                                      \
-        int lim = lim0 - j * kBS;                                                            \
-        lim = lim < 0 ? 0 : (lim > vd ? vd : lim);                                           \
-        fold_block<T, KV>(st, R, S.ktile[wave], vd, lim, scale_log2, lane);                  \
-    }                                                                                        \
-    issue(R, j + 2 * kWaves);                                                                \
-    j += kWaves;
-    while (true) {
-        PKV_STEP(A)
-        PKV_STEP(B)
-    }
+        if (x >= w1) break;                                                                  \
+        {                                                                                    \
+            const int vd = S.valid[x - w0], ow = uni(S.owner[x - w0]);                       \
+            uint4 ka[4], v[4];                                                               \
+            stage_block<T, KV>(R, S.ktile[wave], vd, lane, ka, v);                           \
+            _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                 \
+                if (t >= nt) break;                                                          \
+                int lim;                                                                     \
+                if (ow < 0) {                                                                \
+                    lim = lim0[t] - (j0 + x) * kBS;                                          \
+                    lim = lim < 0 ? 0 : (lim > vd ? vd : lim);                               \
+                } else {                                                                     \
+                    if (ow / mpt != t) continue;                                             \
+                    lim = (c < mpt * group && t * mpt + cm == ow) ? vd : 0;                  \
+                }                                                                            \
+                fold_tile<T>(st[t], ka, qv[t], v, lim, scale_log2, lane);                    \
+            }                                                                                \
+        }                                                                                    \
+        issue(R, x + 2 * NW);                                                            \
+        x += NW;
+        while (true) {
+            PKV_STEP(A)
+            PKV_STEP(B)
+        }
 #undef PKV_STEP
-    wave_to_part<16>(S.part[wave], st, lane, ncols);
-    __syncthreads();
-    int P[kWaves];
-    for (int v = 0; v < kWaves; ++v) P[v] = v;
+    }
+    int P[NW];
+    for (int v = 0; v < NW; ++v) P[v] = v;
     constexpr int kCols = kD / 4;
-    for (int i = tid; i < ncols * kCols; i += kThreads) {
-        const int h = i / kCols, d0 = (i % kCols) * 4;
-        float M, Ls;
-        float4 o;
-        merge_parts<16, kWaves, kWaves>(S.part, P, kWaves, h, d0, M, Ls, o);
-        const int cc = tile * 16 + h;   // the record's member cc / G and head cc % G
-        const size_t r =
-            ((size_t)(s0 + cc / group) * num_heads + g * group + cc % group) * pre_parts +
-            part;
-        *reinterpret_cast<float4*>(rec_o + r * kD + d0) = o;
-        if (d0 == 0) {
-            rec_m[r] = M;
-            rec_l[r] = Ls;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if (t >= nt) break;
+        const int ncols = min(mpt, nm - t * mpt) * group;
+        if (t > 0) __syncthreads();   // the previous tile's records are no longer read
+        wave_to_part<16>(S.part[wave], st[t], lane, ncols);
+        __syncthreads();
+        for (int i = tid; i < ncols * kCols; i += kT) {
+            const int h = i / kCols, d0 = (i % kCols) * 4;
+            float M, Ls;
+            float4 o;
+            merge_parts<16, NW, NW>(S.part, P, NW, h, d0, M, Ls, o);
+            const size_t row =
+                (size_t)row0 + (t * mpt + h / group) * num_heads + h % group;
+            if (parts == 1) {
+                const float inv = Ls > 0.f ? out_scale / Ls : 0.f;
+                store4(out + row * kD + d0,
+                       make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv));
+            } else {
+                const size_t r = row * parts_max + part;
+                *reinterpret_cast<float4*>(rec_o + r * kD + d0) = o;
+                if (d0 == 0) {
+                    rec_m[r] = M;
+                    rec_l[r] = Ls;
+                }
+            }
         }
     }
+}
+
+// Output rows of the members of groups with several prefix parts: the parts' records
+// merged in part order, normalised. One thread per (query row, four dims).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void group_merge_kernel(
+    T* __restrict__ out, const int32_t* __restrict__ seq_prefix, const float* __restrict__ rec_m,
+    const float* __restrict__ rec_l, const float* __restrict__ rec_o, float out_scale,
+    int num_rows, int num_heads, int max_prefix, int parts_max) {
+    constexpr int kCols = kD / 4;
+    const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= (long long)num_rows * kCols) return;
+    const int row = (int)(i / kCols), d0 = (int)(i % kCols) * 4;
+    int pfx = seq_prefix[row / num_heads];
+    pfx = pfx < 0 ? 0 : (pfx > max_prefix ? max_prefix : pfx);
+    const int parts = (pfx + kGroupPart - 1) / kGroupPart;
+    if (parts <= 1) return;   // written by the tile kernel
+    float M = kNegInf, Ls = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p = 0; p < parts; ++p) {
+        const size_t r = (size_t)row * parts_max + p;
+        const float m = rec_m[r], l = rec_l[r];
+        const float4 v = *reinterpret_cast<const float4*>(rec_o + r * kD + d0);
+        const float Mn = fmaxf(M, m);
+        const float a = weight(M, Mn), cw = weight(m, Mn);
+        Ls = Ls * a + l * cw;
+        o.x = o.x * a + v.x * cw;
+        o.y = o.y * a + v.y * cw;
+        o.z = o.z * a + v.z * cw;
+        o.w = o.w * a + v.w * cw;
+        M = Mn;
+    }
+    const float inv = Ls > 0.f ? out_scale / Ls : 0.f;
+    store4(out + (size_t)row * kD + d0, make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv));
 }
 
 // ------------------------------------------------------------------ prefill chunks
@@ -2458,61 +2579,49 @@ int launch_partitioned(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
                        split ? (float*)(ws + plan.off_o) : nullptr, s.num_seqs, 2 * num_cus,
                        helpers ? (int32_t*)(ws + plan.off_counters) : nullptr,
                        helpers ? (float*)(ws + plan.off_partials) : nullptr,
-                       plan.rec_per_head, (const int32_t*)nullptr, (const float*)nullptr,
-                       (const float*)nullptr, (const float*)nullptr, 0);
+                       plan.rec_per_head);
     if (hipGetLastError() != hipSuccess) return -1;
     return split ? launch_partition_reduce(a, plan, stream) : 0;
 }
 
-// Grouped decode: the prefix kernel over every group's shared blocks, then the per-unit
-// decode kernel over each member's remaining blocks (no helpers: a member's unit is
-// never cut), merging the prefix records.
-template <typename T, typename KV, int GMAX>
+// Grouped decode: the tile kernel over every group (its prefix parts and its members'
+// own blocks), then, when some prefix has several parts, the merge kernel.
+template <typename T, typename KV>
 int launch_grouped_t(const DecodeArgs& a, const GroupArgs& ga, const GroupPlan& gp,
-                     int num_cus, hipStream_t stream) {
+                     hipStream_t stream) {
     const DecodeShape& s = a.shape;
     char* ws = (char*)a.workspace;
     using E = typename KV::Elem;
     const Scales sc = scales_of(a);
     const int G = s.num_heads / s.num_kv_heads;
-    const long long units = (long long)gp.pre_parts * s.num_kv_heads * ga.num_groups;
+    const long long units = (long long)gp.parts * s.num_kv_heads * ga.num_groups;
     const long long units8 = (units + 7) / 8 * 8;
+    if (units == 0) return 0;
     if (units8 * gp.tiles > 0x7fffffffLL) return -1;
-    int32_t* seq_prefix = nullptr;
-    float *rm = nullptr, *rl = nullptr, *ro = nullptr;
-    if (units > 0) {
-        seq_prefix = (int32_t*)(ws + gp.off_prefix);
-        rm = (float*)(ws + gp.off_m);
-        rl = (float*)(ws + gp.off_l);
-        ro = (float*)(ws + gp.off_o);
-        hipLaunchKernelGGL((group_prefix_kernel<T, KV>), dim3((unsigned)(units8 * gp.tiles)),
-                           dim3(kThreads), 0, stream, (const T*)a.q, (const E*)a.k_cache,
-                           (const E*)a.v_cache, a.block_tables, a.context_lens,
-                           ga.group_start, ga.group_prefix, sc.scale_log2, s.num_seqs,
-                           s.num_heads, s.num_kv_heads, G, gp.tiles, (int)units, s.max_blocks,
-                           s.num_blocks, ga.max_prefix, gp.pre_parts, a.new_k != nullptr ? 1 : 0,
-                           seq_prefix, rm, rl, ro);
+    const bool merge = gp.parts > 1;
+    int32_t* seq_prefix = merge ? (int32_t*)(ws + gp.off_prefix) : nullptr;
+    float* rm = merge ? (float*)(ws + gp.off_m) : nullptr;
+    float* rl = merge ? (float*)(ws + gp.off_l) : nullptr;
+    float* ro = merge ? (float*)(ws + gp.off_o) : nullptr;
+    hipLaunchKernelGGL((group_tile_kernel<T, KV, kGroupTiles, kGroupWaves>),
+                       dim3((unsigned)(units8 * gp.tiles)), dim3(64 * kGroupWaves), 0, stream, (T*)a.out, (const T*)a.q, (E*)a.k_cache,
+                       (E*)a.v_cache, (const T*)a.new_k, (const T*)a.new_v, a.block_tables,
+                       a.context_lens, ga.group_start, ga.group_prefix, sc.scale_log2,
+                       sc.out_scale, sc.k_inv, sc.v_inv, s.num_seqs, s.num_heads,
+                       s.num_kv_heads, G, gp.members_per_tile, gp.tiles, (int)units,
+                       s.max_blocks, s.num_blocks, ga.max_prefix, gp.parts, seq_prefix, rm, rl,
+                       ro);
+    if (hipGetLastError() != hipSuccess) return -1;
+    if (merge) {
+        const long long threads = (long long)s.num_seqs * s.num_heads * (kD / 4);
+        hipLaunchKernelGGL((group_merge_kernel<T>),
+                           dim3((unsigned)((threads + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, stream, (T*)a.out, seq_prefix, rm, rl, ro,
+                           sc.out_scale, s.num_seqs * s.num_heads, s.num_heads, ga.max_prefix,
+                           gp.parts);
         if (hipGetLastError() != hipSuccess) return -1;
     }
-    hipLaunchKernelGGL((decode_mfma_partition_kernel<T, KV, GMAX>),
-                       dim3(1, s.num_kv_heads, s.num_seqs), dim3(kThreads), 0, stream,
-                       (T*)a.out, (const T*)a.q, (E*)a.k_cache, (E*)a.v_cache,
-                       (const T*)a.new_k, (const T*)a.new_v, a.block_tables, a.context_lens,
-                       sc.scale_log2, sc.out_scale, sc.k_inv, sc.v_inv, s.num_heads,
-                       s.num_kv_heads, G, s.max_blocks, s.num_blocks, s.max_blocks, 1,
-                       (float*)nullptr, (float*)nullptr, (float*)nullptr, s.num_seqs,
-                       2 * num_cus, (int32_t*)nullptr, (float*)nullptr, 0, seq_prefix, rm, rl,
-                       ro, units > 0 ? gp.pre_parts : 0);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-template <typename T, typename KV>
-int launch_grouped_kv(const DecodeArgs& a, const GroupArgs& ga, const GroupPlan& gp,
-                      int num_cus, hipStream_t stream) {
-    const int G = a.shape.num_heads / a.shape.num_kv_heads;
-    if (G <= 4) return launch_grouped_t<T, KV, 4>(a, ga, gp, num_cus, stream);
-    if (G <= 8) return launch_grouped_t<T, KV, 8>(a, ga, gp, num_cus, stream);
-    return launch_grouped_t<T, KV, 16>(a, ga, gp, num_cus, stream);
+    return 0;
 }
 
 template <typename T, typename KV>
@@ -2601,17 +2710,15 @@ int launch_chunk_mfma(const ChunkArgs& a, hipStream_t stream) {
 }
 
 int launch_decode_grouped(const DecodeArgs& a, const GroupArgs& ga, const GroupPlan& gp,
-                          int num_cus, hipStream_t stream) {
+                          hipStream_t stream) {
     if (a.shape.num_kv_heads <= 0 || a.shape.num_heads % a.shape.num_kv_heads != 0) return -1;
     switch (a.shape.dtype) {
         case PKV_BFLOAT16:
-            return a.kv_fp8 ? launch_grouped_kv<bf16_t, KvFp8<bf16_t>>(a, ga, gp, num_cus, stream)
-                            : launch_grouped_kv<bf16_t, KvNative<bf16_t>>(a, ga, gp, num_cus,
-                                                                          stream);
+            return a.kv_fp8 ? launch_grouped_t<bf16_t, KvFp8<bf16_t>>(a, ga, gp, stream)
+                            : launch_grouped_t<bf16_t, KvNative<bf16_t>>(a, ga, gp, stream);
         case PKV_FLOAT16:
-            return a.kv_fp8 ? launch_grouped_kv<f16_t, KvFp8<f16_t>>(a, ga, gp, num_cus, stream)
-                            : launch_grouped_kv<f16_t, KvNative<f16_t>>(a, ga, gp, num_cus,
-                                                                        stream);
+            return a.kv_fp8 ? launch_grouped_t<f16_t, KvFp8<f16_t>>(a, ga, gp, stream)
+                            : launch_grouped_t<f16_t, KvNative<f16_t>>(a, ga, gp, stream);
         default: return -1;
     }
 }

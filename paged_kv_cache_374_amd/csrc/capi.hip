@@ -238,7 +238,7 @@ int grouped_call(void* out, const void* q, const void* new_k, const void* new_v,
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !context_lens || !group_start || !group_prefix) return PKV_E_NULL;
     if (max_blocks_per_seq > 0 && (!k_cache || !v_cache || !block_tables)) return PKV_E_NULL;
-    if (!workspace || workspace_bytes < gp.bytes) return PKV_E_WORKSPACE;
+    if (gp.bytes > 0 && (!workspace || workspace_bytes < gp.bytes)) return PKV_E_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     if (validate_enabled()) {
         int v = validate_tables(s, block_tables, context_lens, st);
@@ -255,9 +255,7 @@ int grouped_call(void* out, const void* q, const void* new_k, const void* new_v,
     a.v_scale = v_scale;
     const pkv::GroupArgs ga{group_start, group_prefix, num_groups, max_group_size,
                             max_prefix_blocks};
-    const int cus = current_device_cus();
-    if (cus <= 0) return PKV_E_DEVICE;
-    return pkv::launch_decode_grouped(a, ga, gp, cus, st) == 0 ? PKV_OK : PKV_E_LAUNCH;
+    return pkv::launch_decode_grouped(a, ga, gp, st) == 0 ? PKV_OK : PKV_E_LAUNCH;
 }
 
 // Shared by the 16-bit and 8-bit chunk entry points.

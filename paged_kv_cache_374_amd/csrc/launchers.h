@@ -104,10 +104,10 @@ struct GroupArgs {
     int num_groups, max_group_size, max_prefix;
 };
 
-// Matrix-core grouped decode (shared prefixes attended once per group, then the rest of
-// each sequence); the workspace is laid out by plan_grouped.
+// Matrix-core grouped decode (each shared prefix block read once per tile of a group's
+// members, then the members' own blocks); the workspace is laid out by plan_grouped.
 int launch_decode_grouped(const DecodeArgs& a, const GroupArgs& ga, const GroupPlan& gp,
-                          int num_cus, hipStream_t stream);
+                          hipStream_t stream);
 
 // Matrix-core kernels (bfloat16/float16, block_size 16).
 int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& plan, int num_cus,

@@ -120,23 +120,26 @@ int plan_grouped(const DecodeShape& s, int num_groups, int max_group_size, int m
     const int group = s.num_heads / s.num_kv_heads;
     if (group > kMaxGroup) return PKV_E_HEADS;
     if (!mfma_eligible(s.dtype, s.head_dim, s.block_size, group)) return PKV_E_UNSUPPORTED;
-    // the decode kernel stages a sequence's table row in LDS; grid y/z limits
-    if (s.max_blocks > kShareMax || max_prefix > s.max_blocks) return PKV_E_SHAPE;
+    if ((long long)s.max_blocks * s.block_size > (1LL << 30) || max_prefix > s.max_blocks)
+        return PKV_E_SHAPE;
     if (s.num_seqs > 65535 || num_groups > 65535 || s.num_kv_heads > 65535) return PKV_E_SHAPE;
     // every sequence belongs to a group
     if (s.num_seqs > 0 && (num_groups == 0 || max_group_size == 0)) return PKV_E_SHAPE;
     if (max_group_size > s.num_seqs) return PKV_E_SHAPE;
     // query byte offsets within a group (and up to a tile past it) are 32-bit in the
-    // prefix kernel
+    // tile kernel
     if ((long long)(max_group_size + 16) * s.num_heads * s.head_dim * 2 > 0x7fffffffLL)
         return PKV_E_SHAPE;
     GroupPlan p{};
-    p.pre_parts = (max_prefix + kGroupPartBlocks - 1) / kGroupPartBlocks;
-    p.tiles = (int)(((long long)max_group_size * group + 15) / 16);
-    p.parts8 = (p.pre_parts + 7) / 8 * 8;
-    if ((long long)p.tiles * (p.parts8 > 0 ? p.parts8 : 8) > 0x7fffffffLL) return PKV_E_SHAPE;
-    if (s.num_seqs > 0) {
-        const size_t recs = (size_t)s.num_seqs * s.num_heads * p.pre_parts;
+    p.parts = max_prefix > kGroupPartBlocks
+                  ? (max_prefix + kGroupPartBlocks - 1) / kGroupPartBlocks : 1;
+    p.members_per_tile = 16 / group;
+    const int per_set = p.members_per_tile * kGroupTilesPerWorkgroup;
+    p.tiles = (max_group_size + per_set - 1) / per_set;
+    const long long units8 = ((long long)p.parts * s.num_kv_heads * num_groups + 7) / 8 * 8;
+    if (units8 * p.tiles > 0x7fffffffLL) return PKV_E_SHAPE;
+    if (s.num_seqs > 0 && p.parts > 1) {
+        const size_t recs = (size_t)s.num_seqs * s.num_heads * p.parts;
         p.off_prefix = kCounterBytes;
         p.off_m = p.off_prefix + align_up((size_t)s.num_seqs * sizeof(int32_t), 256);
         p.off_l = p.off_m + align_up(recs * sizeof(float), 256);
@@ -151,7 +154,9 @@ int plan_grouped(const DecodeShape& s, int num_groups, int max_group_size, int m
 
 extern "C" size_t pkv_paged_attention_grouped_workspace_size(int num_seqs, int num_heads,
                                                              int max_prefix_blocks) {
-    if (num_seqs <= 0 || num_heads <= 0 || max_prefix_blocks < 0) return 0;
+    // records only when a prefix needs several parts
+    if (num_seqs <= 0 || num_heads <= 0 || max_prefix_blocks <= pkv::kGroupPartBlocks)
+        return 0;
     const size_t parts =
         ((size_t)max_prefix_blocks + pkv::kGroupPartBlocks - 1) / pkv::kGroupPartBlocks;
     const size_t recs = (size_t)num_seqs * num_heads * parts;

@@ -71,17 +71,22 @@ constexpr int kPerUnitMaxHelpers = 64;
 int plan_decode(const DecodeShape& s, DecodePlan* plan);
 
 // Grouped decode (sequences sharing prefix blocks): blocks of a shared prefix per
-// workgroup of the prefix kernel, each leaving one record per (sequence, query head).
-constexpr int kGroupPartBlocks = 64;
+// workgroup; a longer prefix is cut into parts whose records a merge kernel combines.
+constexpr int kGroupPartBlocks = 128;
+// Tiles of 16 columns (16 / group whole members each) that one workgroup of the
+// grouped decode folds every shared block into.
+constexpr int kGroupTilesPerWorkgroup = 2;
 
 // Grouped decode launch sizes and workspace layout (byte offsets; everything lies above
-// the kCounterBytes of merge counters that start every workspace).
+// the kCounterBytes of merge counters that start every workspace). No workspace when
+// every prefix fits one part.
 struct GroupPlan {
-    int pre_parts;   // records per (sequence, query head): ceil(max_prefix / kGroupPartBlocks)
-    int tiles;       // 16-column tiles of the largest group (members x group)
-    int parts8;      // pre_parts rounded up to a multiple of 8
+    int parts;              // most parts of a prefix: max(1, ceil(max_prefix / kGroupPartBlocks))
+    int members_per_tile;   // 16 / group: a tile's 16 columns hold whole members
+    int tiles;              // workgroups per (part, KV head, group): tile sets of the
+                            // largest group, kGroupTilesPerWorkgroup tiles each
     size_t off_prefix, off_m, off_l, off_o;
-    size_t bytes;    // total workspace bytes (0 for an empty batch)
+    size_t bytes;           // total workspace bytes (0 with one part or an empty batch)
 };
 
 // Validate the grouped decode's sizes (matrix-core shapes only) and lay out its

@@ -198,9 +198,10 @@ def test_fp8_decode_rejects_bad_arguments_on_the_host(fused):
 
 
 def _grouped(lib, fp8=False, **kw):
+    # a prefix bound of two 128-block parts: the call needs its workspace
     a = dict(out=1, q=1, nk=None, nv=None, k=1, v=1, ks=0.5, vs=0.5, tables=1, ctx=1, gs=1,
-             gp=1, NG=2, GMAX=4, PMAX=10, scale=1.0, B=8, Hq=32, Hkv=8, D=128, bs=16, MB=64,
-             NB=600, dtype=BF16, ws=1, ws_bytes=1 << 30)
+             gp=1, NG=2, GMAX=4, PMAX=200, scale=1.0, B=8, Hq=32, Hkv=8, D=128, bs=16, MB=256,
+             NB=600, dtype=BF16, ws=None, ws_bytes=0)
     a.update(kw)
     tail = (a["tables"], a["ctx"], a["gs"], a["gp"], a["NG"], a["GMAX"], a["PMAX"],
             a["scale"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"],
@@ -227,9 +228,9 @@ def test_grouped_decode_rejects_bad_arguments_on_the_host(fp8):
     assert _grouped(lib, fp8, NG=0) == E["SHAPE"]
     assert _grouped(lib, fp8, GMAX=0) == E["SHAPE"]
     assert _grouped(lib, fp8, GMAX=9) == E["SHAPE"]
-    assert _grouped(lib, fp8, PMAX=65) == E["SHAPE"]
+    assert _grouped(lib, fp8, PMAX=257) == E["SHAPE"]
     assert _grouped(lib, fp8, PMAX=-1) == E["SHAPE"]
-    assert _grouped(lib, fp8, MB=2049, PMAX=10) == E["SHAPE"]
+    assert _grouped(lib, fp8, MB=(1 << 26) + 1) == E["SHAPE"]
     assert _grouped(lib, fp8, B=-1) == E["SHAPE"]
     # pointers: both appended rows or neither; the group arrays; the workspace
     assert _grouped(lib, fp8, nk=1) == E["NULL"]
@@ -237,30 +238,32 @@ def test_grouped_decode_rejects_bad_arguments_on_the_host(fp8):
     assert _grouped(lib, fp8, gs=None) == E["NULL"]
     assert _grouped(lib, fp8, gp=None) == E["NULL"]
     assert _grouped(lib, fp8, q=None) == E["NULL"]
-    assert _grouped(lib, fp8, ws=None) == E["WORKSPACE"]
-    need = pkv.grouped_workspace_size(8, 32, 10)
-    assert _grouped(lib, fp8, ws_bytes=need - 1) == E["WORKSPACE"]
+    assert _grouped(lib, fp8) == E["WORKSPACE"]
+    need = pkv.grouped_workspace_size(8, 32, 200)
+    assert need > 0
+    assert _grouped(lib, fp8, ws=1, ws_bytes=need - 1) == E["WORKSPACE"]
     if fp8:
         for bad in (0.0, -1.0, float("inf"), float("nan")):
             assert _grouped(lib, fp8, ks=bad) == E["SHAPE"]
             assert _grouped(lib, fp8, vs=bad) == E["SHAPE"]
     # empty batch: nothing to do
-    assert _grouped(lib, fp8, B=0, NG=0, GMAX=0, out=None, q=None, gs=None, gp=None,
-                    ws=None, ws_bytes=0) == E["OK"]
+    assert _grouped(lib, fp8, B=0, NG=0, GMAX=0, out=None, q=None, gs=None, gp=None) == E["OK"]
 
 
 def test_grouped_workspace_arithmetic():
-    # counters' MiB, the per-sequence prefixes, then m, l (256-byte aligned) and o of
-    # one record per (sequence, query head, 64-block part)
-    B, H, P = 256, 32, 2   # 127 prefix blocks -> two parts
+    # none while every prefix fits one 128-block part; else the counters' MiB, the
+    # per-sequence prefixes, then m, l (256-byte aligned) and o of one record per
+    # (sequence, query head, part)
+    B, H = 256, 32
     align = lambda x: (x + 255) // 256 * 256
-    recs = B * H * P
+    assert pkv.grouped_workspace_size(B, H, 127) == 0
+    assert pkv.grouped_workspace_size(B, H, 128) == 0
+    recs = B * H * 2
     expect = (1 << 20) + align(B * 4) + 2 * align(recs * 4) + recs * 128 * 4
-    assert pkv.grouped_workspace_size(B, H, 127) == expect
-    assert pkv.grouped_workspace_size(B, H, 128) == expect
-    assert pkv.grouped_workspace_size(B, H, 129) > expect
-    assert pkv.grouped_workspace_size(B, H, 0) == (1 << 20) + align(B * 4)
-    assert pkv.grouped_workspace_size(0, H, 127) == 0
+    assert pkv.grouped_workspace_size(B, H, 129) == expect
+    assert pkv.grouped_workspace_size(B, H, 256) == expect
+    assert pkv.grouped_workspace_size(B, H, 257) > expect
+    assert pkv.grouped_workspace_size(0, H, 300) == 0
 
 
 def _groups_by_reading(tables, ctx, bs):

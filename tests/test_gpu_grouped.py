@@ -1,13 +1,14 @@
 """GPU parity of the grouped decode: sequences that share prefix blocks, the shared
-blocks attended once per group (pkv_paged_attention_decode_grouped).
+blocks read once per tile of a group's members (pkv_paged_attention_decode_grouped).
 
 Every case compares the whole output with the oracle (bfloat16 bound 2e-2, float16
 5e-3, as in the other parity tests) and, for the fused step, the pools byte for byte
 with the oracle's decode step; a second call must give the same bits. The groups come
 from the host helper (pkv_prefix_groups) on the shared-prefix batch, and are set by
 hand elsewhere: ragged tiles (group x heads not a multiple of 16), prefixes of one, two
-and three 64-block parts, members shorter than their group's prefix, empty contexts,
-groups of one, and the grouped-query factors 1, 4, 8 and 16.
+and three 128-block parts (the merge kernel), members shorter than their group's
+prefix, empty contexts, groups of one, workgroups of one and two full tiles, and the
+grouped-query factors 1, 2, 4, 8 and 16.
 """
 import os
 import subprocess
@@ -79,6 +80,12 @@ CASES = [
     # group 1: 16 members per tile, a group of 20 members
     ("group 1, 20 members", 3104, _lens(3104, 24, 900, 1400), [20, 4], [55, 30], 4, 4,
      torch.bfloat16),
+    # group 1, 40 members: two workgroups of two 16-member tiles, the second half full
+    ("group 1, 40 members", 3110, _lens(3110, 40, 700, 1100), [40], [43], 4, 4,
+     torch.float16),
+    # group 2: 8 members per tile, 17 members (a second workgroup with one member)
+    ("group 2, 17 members", 3111, _lens(3111, 20, 1500, 1900), [17, 3], [70, 20], 16, 8,
+     torch.bfloat16),
 ]
 
 
@@ -144,6 +151,30 @@ def test_grouped_fused_append():
     err = _err(out, want)
     _say(f"  max err {err:.3e}")
     assert err <= TOL[torch.bfloat16], err
+
+
+def test_grouped_long_prefix_fused_append():
+    """Prefixes of three 128-block parts (the merge kernel combines the parts' records)
+    and a group whose prefix is a single block, in one fused step."""
+    lens = _lens(3109, 20, 4900, 5200)
+    s = W.batch_with_lengths(3109, lens, num_heads=32, num_kv_heads=8, head_dim=128,
+                             block_size=16, dtype=torch.bfloat16, device=DEV)
+    s = W.with_shared_prefixes(s, [8, 7, 5], [300, 257, 1])
+    W.with_append(s, seed=3109)
+    _say("grouped decode: three-part prefixes, fused append")
+    want, ek, ev = oracle.decode_step(s.q, s.new_k, s.new_v, s.k_cache, s.v_cache,
+                                      s.block_tables, s.context_lens, s.scale)
+    kc, vc = s.k_cache.clone(), s.v_cache.clone()
+    groups = _groups(s)
+    assert pkv.grouped_workspace_size(20, 32, groups.max_prefix_blocks) > 0
+    out, call = _grouped(s, groups, kc, vc, new=True)
+    assert torch.equal(kc.cpu(), ek) and torch.equal(vc.cpu(), ev), "pools differ"
+    err = _err(out, want)
+    _say(f"  max err {err:.3e}")
+    assert err <= TOL[torch.bfloat16], err
+    again = call().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out, again), "second call differs"
 
 
 def _cow_step_inputs(prefix):
