@@ -703,19 +703,24 @@ def main():
     torch.cuda.synchronize()
 
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    kv_total = 0
+    # A batch whose sequences share blocks reads a shared block from HBM once: its value
+    # counts the distinct blocks read (the logical bytes are reported beside it).
+    shared_sets = all(x.kv_unique < 0.98 * x.kv for x in sets)
+    kv_total = kv_logical = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
         s = sets[i % len(sets)]
         s.run()
-        kv_total += s.kv
+        kv_total += s.kv_unique if shared_sets else s.kv
+        kv_logical += s.kv
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = max(start.elapsed_time(stop), 1e-9)
     value = kv_total / (ms * 1e-3) / 1e9
+    value_logical = kv_logical / (ms * 1e-3) / 1e9
     s0 = sets[0]
     seqs_per_s = s0.num_seqs * args.steps / (ms * 1e-3)
     # spread of single steps: the same steps again, an event between consecutive steps
@@ -793,6 +798,9 @@ def main():
         "dtype": dname,
         "data": "synthetic",
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "value_counts": ("distinct KV blocks read per step (a block shared by several "
+                         "sequences once)" if shared_sets else "algorithmic KV bytes per step"),
+        "value_logical_gbs": round(value_logical, 2) if shared_sets else None,
         "seqs_per_s": round(seqs_per_s, 1),
         "config": {
             "workload": s0.name,
@@ -813,10 +821,10 @@ def main():
                      f"({s0.max_query_len} query tokens per sequence, causal)" if chunk else
                      ("copy_blocks(K, V) + " if s0.copy_pairs is not None and
                       s0.extra.get("prefix_tokens", 0) % s0.block_size == 0 else "") +
-                     (("paged_attention_decode_grouped with the new tokens (the groups' "
-                       "shared prefix blocks attended once per group, then each sequence's "
-                       "own blocks, its new token written first, and the merge; two "
-                       "kernels)" if s0.fused else
+                     (("paged_attention_decode_grouped with the new tokens (each group's "
+                       "shared prefix blocks read once per tile of its members, then each "
+                       "member's own blocks after its new token is written; one kernel, "
+                       "plus a merge kernel for prefixes past 128 blocks)" if s0.fused else
                        "reshape_and_cache(new token) + paged_attention_decode_grouped")
                       if grouped_dec else
                       "paged_attention_decode_append (new token written at each context "
@@ -836,7 +844,7 @@ def main():
         "roofline": {
             "bound": "mfma" if mfma_bound else "hbm",
             "kernel": ("paged_attention_chunk" if chunk else
-                       "paged_attention_decode_grouped (both kernels)" if grouped_dec else
+                       "paged_attention_decode_grouped" if grouped_dec else
                        "paged_attention_decode_append" if s0.fused
                        else "paged_attention_decode") + fp8,
             "achieved": round(tflops if mfma_bound else achieved_hbm, 2),

@@ -5,7 +5,8 @@ prompts placed with prefix caching, parallel samples forked from each prompt, de
 steps whose tokens cross block boundaries, sequences that finish and hand their
 blocks (stale contents and all) to new prompts. Its block tables, context lengths,
 slots and copy-on-write pairs feed pkv_copy_blocks, pkv_reshape_and_cache,
-pkv_paged_attention_decode and the fused decode step.
+pkv_paged_attention_decode, the fused decode step and the grouped decode (groups of
+samples sharing prefix blocks, derived from the manager's tables by pkv_prefix_groups).
 
 The same trace runs through the oracle's block-manager model (oracle/blockmgr.py),
 whose tables and copy pairs drive the oracle's copy, append and fp64 decode. Every
@@ -116,7 +117,23 @@ class Trace:
         lens_d = torch.from_numpy(lens).to(DEV)
         out = torch.full((len(sids), HQ, D), float("nan"), dtype=DT, device=DEV)
         qd = q.to(DEV)
-        if fused:
+        if partition_size == "grouped":
+            # the groups of samples (and prompts) that share prefix blocks, from the
+            # manager's tables; the grouped decode reads each shared block once per tile
+            groups = pkv.prefix_groups(torch.from_numpy(tables), torch.from_numpy(lens), BS,
+                                       device=DEV)
+            assert groups.max_group_size > 1 and groups.max_prefix_blocks > 0
+            if fused:
+                pkv.paged_attention_decode_grouped(out, qd, self.kc, self.vc, tables_d, lens_d,
+                                                   self.scale, groups, new_k=nk.to(DEV),
+                                                   new_v=nv.to(DEV))
+                self.ek, self.ev = oracle.reshape_and_cache(
+                    nk, nv, self.ek, self.ev, torch.from_numpy(slots.copy()))
+            else:
+                self.write(slots.tolist(), nk, nv)
+                pkv.paged_attention_decode_grouped(out, qd, self.kc, self.vc, tables_d, lens_d,
+                                                   self.scale, groups)
+        elif fused:
             pkv.paged_attention_decode_append(out, qd, nk.to(DEV), nv.to(DEV), self.kc,
                                               self.vc, tables_d, lens_d, self.scale,
                                               partition_size=partition_size)
@@ -173,7 +190,8 @@ def test_block_manager_drives_the_device(seed, prompts, samples):
             next_sid += 1
     assert hits > 0, "the trace must exercise the prefix cache"
     total_copies = 0
-    schedule = [(True, 0), (False, 0), (True, 512), (False, 512)]
+    schedule = [(True, 0), (False, 0), (True, 512), (False, 512), (True, "grouped"),
+                (False, "grouped")]
     for step in range(20):
         if step == 9:
             # two samples finish; two new prompts take their blocks (and a cached
