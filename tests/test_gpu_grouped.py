@@ -275,6 +275,46 @@ def test_grouped_shared_workspace():
     assert not torch.any(ws[:1 << 20]), "merge counters left non-zero"
 
 
+def test_grouped_in_graph_replays():
+    """The prepared grouped call (fused step, prefixes of two parts, so the merge kernel
+    and the workspace records run too) captured in a HIP graph and replayed with new
+    queries and rows, eager work and synchronisations between the replays: every replay
+    matches an eager call bit for bit."""
+    lens = _lens(3112, 24, 2300, 2600)
+    s = W.batch_with_lengths(3112, lens, num_heads=32, num_kv_heads=8, head_dim=128,
+                             block_size=16, dtype=torch.bfloat16, device=DEV)
+    s = W.with_shared_prefixes(s, [8, 8, 8], [140, 127, 2])
+    W.with_append(s, seed=3112)
+    _say("grouped decode: graph replays")
+    groups = _groups(s)
+    out = torch.empty_like(s.q)
+    step = pkv.PreparedGroupedDecode(out, s.q, s.k_cache, s.v_cache, s.block_tables,
+                                     s.context_lens, s.scale, groups, new_k=s.new_k,
+                                     new_v=s.new_v)
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    ref = torch.empty_like(s.q)
+    eager = pkv.PreparedGroupedDecode(ref, s.q, s.k_cache, s.v_cache, s.block_tables,
+                                      s.context_lens, s.scale, groups, new_k=s.new_k,
+                                      new_v=s.new_v)
+    for r in range(3):
+        for t in (s.q, s.new_k, s.new_v):
+            t.copy_(torch.randn(t.shape, generator=gen, device=DEV).to(t.dtype))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        eager()
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"replay {r}"
+    want, _, _ = oracle.decode_step(s.q, s.new_k, s.new_v, s.k_cache, s.v_cache,
+                                    s.block_tables, s.context_lens, s.scale)
+    assert _err(ref, want) <= TOL[torch.bfloat16]
+
+
 _VALIDATE_SCRIPT = r"""
 import sys, torch
 sys.path.insert(0, sys.argv[1])
