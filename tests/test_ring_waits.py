@@ -5,7 +5,9 @@ A wave's loop folds one (block, KV head) tile while the next one's loads are in
 flight. The wait before a fold must let the other buffer's loads stay outstanding:
 for 16-bit caches each block is 12 buffer loads (K, V and the query), so the fold's
 waits go down to vmcnt(12), never below; for 8-bit caches a block is 6 loads and the
-waits stop at vmcnt(10) (K is consumed before the last two V loads). A wait that
+waits stop at vmcnt(10) (K is consumed before the last two V loads). The grouped
+decode's tile kernel keeps its queries in registers: 8 loads per block (16-bit) or
+6 (8-bit), and its waits stop there. A wait that
 drains both buffers halves the number of bytes in flight; it appeared once as a
 side effect of an unrelated change (registers kept alive after the loop), with no
 error and no change in results, only in speed. Host-only: compiles with hipcc, no GPU.
@@ -84,7 +86,9 @@ CASES = [(f"decode_mfma_partition_kernelINS_{t}ENS0_{kv}IS2_EELi{g}E", floor)
          for t in ("6bf16_t", "5f16_t") for g in (4, 8, 16)
          for kv, floor in (("8KvNative", 12), ("5KvFp8", 10))] + \
         [(f"decode_mfma_balanced_kernelINS_6bf16_tENS0_8KvNativeIS2_EELi{g}ELi4E", 12)
-         for g in (4, 8, 16)]
+         for g in (4, 8, 16)] + \
+        [(f"group_tile_kernelINS_{t}ENS0_{kv}IS2_EELi2ELi4E", floor)
+         for t in ("6bf16_t", "5f16_t") for kv, floor in (("8KvNative", 8), ("5KvFp8", 6))]
 
 
 @pytest.mark.parametrize("pattern,floor", CASES, ids=[c[0][:60] for c in CASES])
