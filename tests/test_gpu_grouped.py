@@ -8,7 +8,8 @@ from the host helper (pkv_prefix_groups) on the shared-prefix batch, and are set
 hand elsewhere: ragged tiles (group x heads not a multiple of 16), prefixes of one, two
 and three 128-block parts (the merge kernel), members shorter than their group's
 prefix, empty contexts, groups of one, workgroups of one and two full tiles, and the
-grouped-query factors 1, 2, 4, 8 and 16.
+grouped-query factors 1, 2, 4, 8 and 16; twelve seeded random batches of groups mix
+all of these.
 """
 import os
 import subprocess
@@ -313,6 +314,56 @@ def test_grouped_in_graph_replays():
     want, _, _ = oracle.decode_step(s.q, s.new_k, s.new_v, s.k_cache, s.v_cache,
                                     s.block_tables, s.context_lens, s.scale)
     assert _err(ref, want) <= TOL[torch.bfloat16]
+
+
+def _random_case(seed):
+    """A seeded random batch of groups: group sizes 1-12, prefixes from none to past a
+    128-block part, members' own lengths from empty to several hundred tokens."""
+    g = torch.Generator().manual_seed(seed)
+    hkv = [1, 2, 4, 8][int(torch.randint(0, 4, (1,), generator=g))]
+    G = [1, 2, 4, 8, 16][int(torch.randint(0, 5, (1,), generator=g))]
+    dt = torch.bfloat16 if seed % 2 else torch.float16
+    fused = seed % 3 != 0
+    sizes, prefixes, lens = [], [], []
+    while sum(sizes) < 28:
+        k = int(torch.randint(1, 13, (1,), generator=g))
+        p = int(torch.randint(0, 160, (1,), generator=g)) if k > 1 else 0
+        sizes.append(k)
+        prefixes.append(p)
+        for m in range(k):
+            own = int(torch.randint(0 if not fused else 1, 400, (1,), generator=g))
+            # the first member holds the whole prefix; with the append, every member's
+            # newest token lies past the prefix
+            if m == 0 or fused:
+                lens.append(16 * p + max(own, 1))
+            else:
+                lens.append(int(torch.randint(0, 16 * p + 400, (1,), generator=g)))
+    return sizes, prefixes, lens, G * hkv, hkv, dt, fused
+
+
+@pytest.mark.parametrize("seed", list(range(3200, 3212)))
+def test_grouped_random(seed):
+    sizes, prefixes, lens, hq, hkv, dt, fused = _random_case(seed)
+    _say(f"grouped decode: random seed={seed} groups={len(sizes)} heads {hq}/{hkv} {dt} "
+         f"fused={fused} max prefix {max(prefixes)}")
+    s = W.batch_with_lengths(seed, lens, num_heads=hq, num_kv_heads=hkv, head_dim=128,
+                             block_size=16, dtype=dt, device=DEV)
+    s = W.with_shared_prefixes(s, sizes, prefixes)
+    groups = _groups(s)
+    if fused:
+        W.with_append(s, seed=seed)
+        want, ek, ev = oracle.decode_step(s.q, s.new_k, s.new_v, s.k_cache, s.v_cache,
+                                          s.block_tables, s.context_lens, s.scale)
+        kc, vc = s.k_cache.clone(), s.v_cache.clone()
+        out, _ = _grouped(s, groups, kc, vc, new=True)
+        assert torch.equal(kc.cpu(), ek) and torch.equal(vc.cpu(), ev), "pools differ"
+    else:
+        want = oracle.paged_attention(s.q, s.k_cache, s.v_cache, s.block_tables,
+                                      s.context_lens, s.scale)
+        out, _ = _grouped(s, groups)
+    err = _err(out, want)
+    _say(f"  max err {err:.3e}")
+    assert err <= TOL[dt], err
 
 
 _VALIDATE_SCRIPT = r"""
