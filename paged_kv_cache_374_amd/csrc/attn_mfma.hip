@@ -94,6 +94,12 @@ template <> struct Mma<bf16_t> {
         bf16x2_t v = {(__bf16)lo, (__bf16)hi};
         return __builtin_bit_cast(uint32_t, v);
     }
+    // acc + the two packed values (one dot-product instruction)
+    static __device__ __forceinline__ float add_pair(uint32_t packed, float acc) {
+        const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), one, acc,
+                                               false);
+    }
 };
 template <> struct Mma<f16_t> {
     static __device__ __forceinline__ f32x4_t qk(const uint4& a, const uint4& b, f32x4_t c) {
@@ -107,6 +113,10 @@ template <> struct Mma<f16_t> {
     static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
         f16x2_t v = {(_Float16)lo, (_Float16)hi};
         return __builtin_bit_cast(uint32_t, v);
+    }
+    static __device__ __forceinline__ float add_pair(uint32_t packed, float acc) {
+        const f16x2_t one = {(_Float16)1.f, (_Float16)1.f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, packed), one, acc, false);
     }
 };
 
@@ -446,7 +456,7 @@ __device__ __forceinline__ void fold_tile(WaveState& s, const uint4 (&ka)[4],
         mb = fmaxf(mb, x[e]);
     }
     mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    mb = max_xor32(mb);
     // s.m is a reference maximum, moved only when a block's maximum passes it by more
     // than kLazyMax (base-2 units), so weights stay below 2^kLazyMax. Most blocks leave
     // it in place: their rescale factor would be exactly 1, and the wave skips the
@@ -562,8 +572,7 @@ struct Part {
 __device__ __forceinline__ float head_lsum(const WaveState& s) {
     float ls = s.lsum;
     ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    return ls;
+    return sum_xor32(ls);
 }
 
 // A wave's state -> partial record P (LDS).
@@ -2298,7 +2307,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
                 mraw = fmaxf(mraw, sc[v]);
             }
         }
-        mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+        mraw = max_xor32(mraw);
         const float mc = mraw * scale_log2;
         if (__any(mc > m + kFaLazy)) {
             const float mn = fmaxf(m, mc);
@@ -2309,17 +2318,25 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
             m = mn;
         }
         const float mu = (m == kNegInf) ? 0.f : m;
-        float ps = 0.f;
         uint2 pb[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             float p[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(sc[4 * s + e], scale_log2, -mu));
-            ps += (p[0] + p[1]) + (p[2] + p[3]);
             pb[s] = make_uint2(Mma<T>::pack(p[0], p[1]), Mma<T>::pack(p[2], p[3]));
         }
-        lsum += ps;
+        // The row sum adds the weights as rounded for the PV product (a dot product
+        // with ones per packed pair: half the instructions of the float adds), so the
+        // numerator and the denominator see the same weights. Two partial sums keep
+        // the chain short.
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            ps0 = Mma<T>::add_pair(pb[s].x, ps0);
+            ps1 = Mma<T>::add_pair(pb[s].y, ps1);
+        }
+        lsum += ps0 + ps1;
         // PV on 32x32x16 products over 16 tokens each. The k order inside a product is
         // free as long as both operands use it: lane l supplies its own score registers
         // (tokens 16s + 4h + 0..3 and 16s + 8 + 4h + 0..3), and the V operand is read in
@@ -2372,7 +2389,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
             if (i + 2 < ns) step(i + 2, Slot2{}, Slot1{});
         }
     }
-    const float lt = lsum + __shfl_xor(lsum, 32);
+    const float lt = sum_xor32(lsum);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (row_ok) {
         T* orow = out + ((size_t)(r0 + tok_w + rtok) * num_heads + g * group + rhead) * kD;

@@ -74,6 +74,21 @@ __device__ __forceinline__ uint4 load16(const void* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x combined with x of lane l ^ 32, through the gfx950 lane swap (a VALU operation, no
+// LDS round trip as for a general shuffle). The swap exchanges the upper half of its
+// first operand with the lower half of its second; with x in both, one result holds x
+// and the other x of lane l ^ 32 in every lane, in an order that max and sum ignore.
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // binary32 -> OCP FP8 E4M3 code (1 sign bit, 4 exponent bits with bias 7, 3 mantissa
 // bits; largest finite value 448; S.1111.111 is NaN): nearest, ties to an even
 // mantissa; magnitudes of 448 or more (infinity included) give 448; NaN stays NaN.
