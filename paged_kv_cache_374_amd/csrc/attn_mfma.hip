@@ -1139,15 +1139,20 @@ struct LengthKeys {
 __device__ __forceinline__ LengthKeys load_lengths(const int32_t* __restrict__ ctx_lens,
                                                    int nseq, int cap, int lane) {
     static_assert(kPerUnitMaxSeqs <= 256, "four lengths per lane");
+    // all loads first (a wave-uniform test per round, indices clamped into the batch),
+    // then one wait: a test per lane around each load made the compiler wait for each
+    // round before issuing the next
+    const int nr = (nseq + 63) >> 6;
+    int raw[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        if (r < nr) raw[r] = ctx_lens[min(lane + 64 * r, nseq - 1)];
     LengthKeys k;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int u = lane + 64 * r;
         int x = -1;   // no sequence: never counted
-        if (u < nseq) {
-            x = ctx_lens[u];
-            x = x < 0 ? 0 : (x > cap ? cap : x);
-        }
+        if (u < nseq) x = raw[r] < 0 ? 0 : (raw[r] > cap ? cap : raw[r]);
         k.len[r] = x;
         k.key[r] = x < 0 ? -1 : (x + kBS - 1) / kBS;
     }
