@@ -1246,6 +1246,42 @@ __device__ __forceinline__ int select_by_length(const LengthKeys& k, int nseq, i
     return 0;   // not reached for want < nseq
 }
 
+// Position of sequence u in the order select_by_length uses (most blocks first, equal
+// counts by index): the units with more blocks, plus those with as many and a smaller
+// index. u < nseq, wave-uniform.
+__device__ __forceinline__ int rank_of(const LengthKeys& k, int nseq, int u) {
+    const int nr = (nseq + 63) >> 6;
+    const int l = u & 63, ru = u >> 6;
+    const int k0 = __builtin_amdgcn_readlane(k.key[0], l), k1 = __builtin_amdgcn_readlane(k.key[1], l);
+    const int k2 = __builtin_amdgcn_readlane(k.key[2], l), k3 = __builtin_amdgcn_readlane(k.key[3], l);
+    const int ku = ru == 0 ? k0 : ru == 1 ? k1 : ru == 2 ? k2 : k3;
+    const int lane = (int)__lane_id();
+    int c = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        if (r < nr)
+            c += __popcll(__ballot(k.key[r] > ku || (k.key[r] == ku && 64 * r + lane < u)));
+    return c;
+}
+
+// Ranks remembered between calls. A serving loop decodes the same batch step after step,
+// and a unit's position in the order changes only when block counts change it, so each
+// workgroup first tries the sequence that held its position last time: rank_of checks
+// it exactly against the current lengths (a few ballots instead of the search), and only
+// a failed check runs the search and remembers its answer. A wrong or stale guess costs
+// nothing but that search, so the result never depends on the table. Slots are chosen by
+// the address of the lengths array (a loop keeps reusing its buffer; calls with other
+// buffers take other slots); concurrent launches may overwrite each other's entries,
+// which is again only a failed check.
+constexpr int kRankSlots = 32;
+__device__ int rank_memo[kRankSlots][kPerUnitMaxSeqs];
+
+__device__ __forceinline__ int rank_slot(const int32_t* ctx_lens) {
+    // Fibonacci hashing of the address (its top five bits after the multiply)
+    const uint64_t a = reinterpret_cast<uint64_t>(ctx_lens) >> 8;
+    return (int)((a * 0x9E3779B97F4A7C15ull) >> 59);
+}
+
 // Position in the longest-first order of the sequence that workgroup (.., .., b) takes.
 // More workgroups than two per CU: longest first throughout (the grid runs in rounds,
 // and the longest should start earliest); else the second half runs shortest first.
@@ -1309,6 +1345,13 @@ __device__ __forceinline__ bool unit_work(const int32_t* __restrict__ ctx_lens, 
         w.j1 = (w.n + kBS - 1) / kBS;
         return true;
     }
+    // this workgroup's remembered sequence, read alongside the lengths (a vector load,
+    // so that scalar waits do not wait for it)
+    const int want = z < nseq ? pairing_position(nseq, z) : 0;
+    int* memo = &rank_memo[rank_slot(ctx_lens)][0];
+    const int guess = __builtin_amdgcn_raw_buffer_load_b32(
+        __builtin_amdgcn_make_buffer_rsrc((void*)memo, 0, kPerUnitMaxSeqs * 4, kRawBufferWord3),
+        want * 4, 0, 0);
     const LengthKeys k = load_lengths(ctx_lens, nseq, cap, lane);
     auto own = [&](int b) {
         w.b = b;
@@ -1379,12 +1422,18 @@ __device__ __forceinline__ bool unit_work(const int32_t* __restrict__ ctx_lens, 
     if (narrow_range(hi, lo)) {
         own(z);
     } else {
-        int len;
-        const int b = select_by_length(k, nseq, pairing_position(nseq, z),
-                                       (lo + kBS - 1) / kBS, (hi + kBS - 1) / kBS, len);
-        w.b = b;
-        w.n = len;
-        w.j1 = (len + kBS - 1) / kBS;
+        const int gu = uni(guess);
+        if (gu >= 0 && gu < nseq && rank_of(k, nseq, gu) == want) {
+            own(gu);
+        } else {
+            int len;
+            const int b = select_by_length(k, nseq, want, (lo + kBS - 1) / kBS,
+                                           (hi + kBS - 1) / kBS, len);
+            w.b = b;
+            w.n = len;
+            w.j1 = (len + kBS - 1) / kBS;
+            if (lane == 0 && (int)(threadIdx.x >> 6) == 0) memo[want] = b;
+        }
     }
     if (P > 0 && is_long(w.j1) && w.j1 > P) {
         const int b = w.b;

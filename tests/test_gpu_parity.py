@@ -255,6 +255,30 @@ def test_per_unit_path_ragged_lengths(reps):
     assert torch.equal(out_a, out_b), "fused step != two calls"
 
 
+def test_per_unit_remembered_ranks():
+    """The per-unit form remembers, per lengths buffer, which sequence held each position
+    of the longest-first order, and checks the guess exactly before using it. Repeated
+    calls on one buffer (guesses right), lengths rewritten in place so that the order
+    changes (guesses wrong, the search runs again), and the call after that: every output
+    against the oracle, repeated calls bit-identical."""
+    lens = [0, 1, 15, 16, 17, 100, 513, 2048, 2047, 33, 1024, 7, 300, 1500, 64, 65] * 8
+    _say(f"remembered ranks: {len(lens)} sequences x 4 KV heads")
+    s = W.batch_with_lengths(2911, lens, num_heads=16, num_kv_heads=4, head_dim=128,
+                             block_size=16, dtype=torch.bfloat16, device=DEV)
+    assert s.block_tables.shape[1] <= 256
+    first = decode(s)
+    assert _max_err(first, oracle_decode(s)) <= TOL[torch.bfloat16]
+    for _ in range(2):
+        assert torch.equal(decode(s), first), "a repeated call differs"
+    # new lengths in the same buffer, each within its row's blocks: the order changes
+    rng = np.random.default_rng(2911)
+    new = [int(rng.integers(0, n + 1)) for n in lens]
+    s.context_lens.copy_(torch.tensor(new, dtype=torch.int32, device=DEV))
+    second = decode(s)
+    assert _max_err(second, oracle_decode(s)) <= TOL[torch.bfloat16]
+    assert torch.equal(decode(s), second), "a repeated call differs"
+
+
 def test_llama_70b_decode_full():
     """70B-shaped batch (256 sequences, 64/8 heads, log-normal contexts up to 4096):
     every output row against the oracle on the library's own split (one workgroup per
