@@ -1470,7 +1470,7 @@ struct PartLds {
     float part[kWaves][Part<GMAX>::kFloats];
 };
 
-template <typename T, typename KV, int GMAX>
+template <typename T, typename KV, int GMAX, bool PATCH>
 __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     T* __restrict__ out, const T* __restrict__ q, typename KV::Elem* k_cache,
     typename KV::Elem* v_cache, const T* __restrict__ new_k, const T* __restrict__ new_v,
@@ -1520,10 +1520,17 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     }
     // the cache policy's test reads beside the table (its latency hides behind it)
     if (tid == kThreads - 1) S.shared = shares_first_block(tables, b, num_seqs, max_blocks);
-    // fused append: the partition holding the newest token writes its K and V rows
-    // (the barrier below orders the stores before this workgroup's loads)
-    if (new_k != nullptr && (n - 1) / kBS >= j0 && (n - 1) / kBS < j1 &&
-        tid < 2 * KV::kAppendChunks)
+    // Fused append: the partition holding the newest token writes its K and V rows.
+    // The plain form appends here, and the barrier below orders the stores before this
+    // workgroup's loads. The PATCH form (16-bit caches, chosen for grids that start
+    // every unit at once, where this barrier is on the launch's critical path) has no
+    // wait for them: the wave that folds the unit's last block takes the new rows from
+    // new_k / new_v into that block's load registers itself (the bytes the cache will
+    // hold) and stores them to the cache then; no load in this kernel reads them back.
+    static_assert(!PATCH || sizeof(typename KV::Elem) == sizeof(T), "16-bit caches only");
+    const int last = (n - 1) / kBS;                  // the unit's last block
+    const bool appends = new_k != nullptr && last >= j0 && last < j1;
+    if (!PATCH && appends && tid < 2 * KV::kAppendChunks)
         KV::append(k_cache, v_cache, new_k, new_v, tables + (size_t)b * max_blocks, b, g,
                    num_kv_heads, n, num_blocks, tid / KV::kAppendChunks,
                    tid % KV::kAppendChunks, k_inv, v_inv);
@@ -1536,6 +1543,41 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
     // every step issues one block (a zero-record buffer past the end): the loads in
     // flight never depend on the path taken
     const int qbytes = group * kD * (int)sizeof(T), qlane = (lane & 15) * kD * (int)sizeof(T);
+    // PATCH: wave (last - j0) % 4 folds the last block (waves take every fourth block);
+    // every wave loads chunk (lane % 16) of the new K and V rows, from zero-record
+    // buffers unless it is that wave, so that all waves issue the same loads.
+    const bool patches = PATCH && appends && wave == (last - j0) % kWaves;
+    uint4 nk = make_uint4(0, 0, 0, 0), nv = nk;
+    if constexpr (PATCH) {
+        const size_t row = ((size_t)b * num_kv_heads + g) * kD;
+        const int rb = patches ? kD * (int)sizeof(T) : 0;
+        nk = buffer_load16(__builtin_amdgcn_make_buffer_rsrc((void*)(new_k + (patches ? row : 0)),
+                                                             0, rb, kRawBufferWord3),
+                           (lane & 15) * 16);
+        nv = buffer_load16(__builtin_amdgcn_make_buffer_rsrc((void*)(new_v + (patches ? row : 0)),
+                                                             0, rb, kRawBufferWord3),
+                           (lane & 15) * 16);
+    }
+    // Row t of the last block sits in K register t / 4 of the lanes of row group t % 4,
+    // and in V register t % 4 of the lanes of row group t / 4 (the layouts of
+    // KvNative::issue); the new chunks replace whatever the block's loads returned there.
+    auto patch = [&](typename KV::Regs& R) {
+        if constexpr (PATCH) {
+            const int t = (n - 1) & (kBS - 1), grp = lane >> 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (e == (t >> 2) && grp == (t & 3)) R.k[e] = nk;
+                if (e == (t & 3) && grp == (t >> 2)) R.v[e] = nv;
+            }
+            if (lane < 16) {
+                typename KV::AppendSrc a;
+                a.val = nk;
+                KV::append_store(a, k_cache, v_cache, S.tile[last - j0], t, 0, lane, 0.f, 0.f);
+                a.val = nv;
+                KV::append_store(a, k_cache, v_cache, S.tile[last - j0], t, 1, lane, 0.f, 0.f);
+            }
+        }
+    };
     auto stream_blocks = [&](auto policy) {
         constexpr int AUX = decltype(policy)::value;
         auto issue = [&](typename KV::Regs& R, int ji) {
@@ -1550,6 +1592,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_partition_kernel(
         issue(B, j + kWaves);
 #define PKV_STEP(R)                                                                          \
     if (j >= j1) break;                                                                      \
+    if (PATCH && patches && j == last) patch(R);                                             \
     fold_block<T, KV>(st, R, S.ktile[wave], S.valid[j - j0], S.valid[j - j0], scale_log2,    \
                       lane);                                                                 \
     issue(R, j + 2 * kWaves);                                                                \
@@ -2638,7 +2681,16 @@ int launch_partitioned(const DecodeArgs& a, const DecodePlan& plan, int num_cus,
     if (helpers > plan.helpers) helpers = plan.helpers;
     using E = typename KV::Elem;
     const Scales sc = scales_of(a);
-    hipLaunchKernelGGL((decode_mfma_partition_kernel<T, KV, GMAX>),
+    // the patching form of the fused step (16-bit caches, a grid that starts every unit
+    // at once: there the append's wait lies on the launch's critical path; in a grid run
+    // in rounds the extra work in the loop costs more than it saves)
+    auto kernel = decode_mfma_partition_kernel<T, KV, GMAX, false>;
+    if constexpr (sizeof(E) == sizeof(T)) {
+        if (a.new_k != nullptr && !split &&
+            (long long)s.num_seqs * s.num_kv_heads <= kPerUnitMinUnits)
+            kernel = decode_mfma_partition_kernel<T, KV, GMAX, true>;
+    }
+    hipLaunchKernelGGL(kernel,
                        dim3(plan.max_partitions, s.num_kv_heads, s.num_seqs + helpers),
                        dim3(kThreads), 0, stream, (T*)a.out, (const T*)a.q, (E*)a.k_cache,
                        (E*)a.v_cache, (const T*)a.new_k, (const T*)a.new_v, a.block_tables,
