@@ -1305,12 +1305,25 @@ __device__ __forceinline__ int paired_sequence(const int32_t* __restrict__ ctx_l
         return b;
     };
     if (!ranks_lengths(nseq)) return own();
+    // the remembered sequence of this position (see rank_memo), read with the lengths
+    const int want = pairing_position(nseq, b);
+    int* memo = &rank_memo[rank_slot(ctx_lens)][0];
+    const int guess = __builtin_amdgcn_raw_buffer_load_b32(
+        __builtin_amdgcn_make_buffer_rsrc((void*)memo, 0, kPerUnitMaxSeqs * 4, kRawBufferWord3),
+        want * 4, 0, 0);
     const LengthKeys k = load_lengths(ctx_lens, nseq, cap, lane);
     int hi, lo;
     length_range(k, cap, hi, lo);
     if (narrow_range(hi, lo)) return own();
-    return select_by_length(k, nseq, pairing_position(nseq, b), (lo + kBS - 1) / kBS,
-                            (hi + kBS - 1) / kBS, len);
+    const int gu = __builtin_amdgcn_readfirstlane(guess);
+    if (gu >= 0 && gu < nseq && rank_of(k, nseq, gu) == want) {
+        len = length_of(k, gu);
+        return gu;
+    }
+    const int u = select_by_length(k, nseq, want, (lo + kBS - 1) / kBS, (hi + kBS - 1) / kBS,
+                                   len);
+    if (lane == 0 && (int)(threadIdx.x >> 6) == 0) memo[want] = u;
+    return u;
 }
 
 // ------------------------------------------------------------------ long units
