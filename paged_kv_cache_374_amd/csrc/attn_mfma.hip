@@ -1330,10 +1330,10 @@ __device__ __forceinline__ int paired_sequence(const int32_t* __restrict__ ctx_l
 // One workgroup per (sequence, KV head) cannot finish before its longest unit does.
 // With S the blocks of all units over the workgroup slots (two per CU), a unit of more
 // than 2S blocks outlasts any pairing of it with a short one, so it is cut into pieces
-// of P >= S/2 blocks (S rounded up) (helpers start only when a slot frees, so their pieces are half
-// a slot's share; S/3 measured slower, S slower still): its own workgroup folds the
-// first piece, and helper workgroups, launched after the batch's (grid z >=
-// num_seqs), fold the others, each long unit's pieces in turn, in sequence order.
+// of P >= S/2 blocks (S rounded up; half a slot's share measured best, S/3 and S
+// slower): its own workgroup folds the first piece, and helper workgroups (placed
+// first in the grid when some unit is cut, so that they start with the first round)
+// fold the others, each long unit's pieces in turn, in sequence order.
 // Every piece's partial result goes to a workspace record; the last piece to finish
 // (a device-scope counter per unit) merges them all in piece order. P grows when the
 // pieces would outnumber the helpers.
@@ -1395,6 +1395,11 @@ __device__ __forceinline__ bool unit_work(const int32_t* __restrict__ ctx_lens, 
         bl = wave_sum(bl);
         P = max((S + 1) / 2, (bl + helpers - 1) / helpers);
     }
+    // When some unit is cut, the helpers come first in the grid: the dispatcher starts
+    // them with the first round instead of after short units free their slots, so the
+    // pieces of a long unit run alongside the rest (every workgroup derives P from the
+    // same lengths, so all agree on the order).
+    if (P > 0 && helpers > 0) z = z < helpers ? nseq + z : z - helpers;
     // Long units in sequence order: visit(u, blocks, pieces, first record) returns true
     // to stop. Lanes past the batch hold 0 blocks, so they are never long.
     auto walk = [&](auto visit) {
@@ -1435,17 +1440,18 @@ __device__ __forceinline__ bool unit_work(const int32_t* __restrict__ ctx_lens, 
     if (narrow_range(hi, lo)) {
         own(z);
     } else {
+        const int pos = pairing_position(nseq, z);   // z may have moved past the helpers
         const int gu = uni(guess);
-        if (gu >= 0 && gu < nseq && rank_of(k, nseq, gu) == want) {
+        if (pos == want && gu >= 0 && gu < nseq && rank_of(k, nseq, gu) == pos) {
             own(gu);
         } else {
             int len;
-            const int b = select_by_length(k, nseq, want, (lo + kBS - 1) / kBS,
+            const int b = select_by_length(k, nseq, pos, (lo + kBS - 1) / kBS,
                                            (hi + kBS - 1) / kBS, len);
             w.b = b;
             w.n = len;
             w.j1 = (len + kBS - 1) / kBS;
-            if (lane == 0 && (int)(threadIdx.x >> 6) == 0) memo[want] = b;
+            if (lane == 0 && (int)(threadIdx.x >> 6) == 0) memo[pos] = b;
         }
     }
     if (P > 0 && is_long(w.j1) && w.j1 > P) {
