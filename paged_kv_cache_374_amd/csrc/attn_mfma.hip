@@ -2190,9 +2190,10 @@ constexpr int kFaRows = 32;      // query rows per wave (the 32 columns of S^T)
 constexpr int kFaStep = 32;      // context tokens per step: two blocks of 16
 constexpr int kFaRing = 3;       // LDS slots: the step being multiplied and two in flight
 constexpr int kFaTab = 512;      // table entries staged per window (256 steps)
-// A row's reference maximum moves only when a score passes it by more than this (log2
-// units): weights then stay below 2^8, and the final division cancels the reference.
-constexpr float kFaLazy = 8.f;
+// Largest sum of one lane's 16 weights of a step that stands: every weight then lies
+// below it (weights are not negative), and the final division cancels the reference the
+// weights are taken against.
+constexpr float kFaBound = 256.f;
 
 // Batches up to this many sequences run their heaviest work first (see chunk_fa_kernel).
 constexpr int kFaSortMax = kFaTab;
@@ -2407,52 +2408,62 @@ __global__ __launch_bounds__(kThreads) void chunk_fa_kernel(
             sc = Mma32<T>::mma(S.k[sl][r][(2 * s + h) ^ (r & 15)], qv[s], sc);
         // The VALU, not the matrix cores, bounds this loop (a wave64 VALU op takes four
         // cycles): steps that every row of the wave sees whole skip the mask, the scale
-        // enters through one FMA before the exp (scale > 0, so the max of the raw scores
-        // gives the max of the scaled ones), and a row's reference maximum moves (with a
-        // rescale of the accumulator) only when its scores pass it by more than kFaLazy.
+        // enters through one FMA before the exp, and no step takes a row maximum unless
+        // its weights fail the bound below.
         const bool whole = tp0 + kFaStep - 1 <= n - T_b + tok_w && tp0 + kFaStep <= n;
-        float mraw = kNegInf;
-        if (whole) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, sc[v]);
-        } else {
+        if (!whole) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int tp = tp0 + 8 * (v / 4) + 4 * h + (v % 4);
                 sc[v] = (tp <= pos && tp < n) ? sc[v] : kNegInf;
-                mraw = fmaxf(mraw, sc[v]);
             }
         }
-        mraw = max_xor32(mraw);
-        const float mc = mraw * scale_log2;
-        if (__any(mc > m + kFaLazy)) {
-            const float mn = fmaxf(m, mc);
+        // Weights against the row's reference m, and the row sum that adds them as
+        // rounded for the PV product (a dot product with ones per packed pair: half the
+        // instructions of the float adds), so that the numerator and the denominator
+        // see the same weights. Two partial sums keep the chain short.
+        uint2 pb[4];
+        float ps;
+        auto weights = [&](float mu) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                float p[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    p[e] = fast_exp2(__builtin_fmaf(sc[4 * s + e], scale_log2, -mu));
+                pb[s] = make_uint2(Mma<T>::pack(p[0], p[1]), Mma<T>::pack(p[2], p[3]));
+            }
+            float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                ps0 = Mma<T>::add_pair(pb[s].x, ps0);
+                ps1 = Mma<T>::add_pair(pb[s].y, ps1);
+            }
+            ps = ps0 + ps1;
+        };
+        weights(m);
+        // A lane's sum bounds each of its weights, so a sum within kFaBound keeps them
+        // all below it without a maximum. It fails (also as infinity or NaN, on a row's
+        // first step, where m = -inf) when some score passes m by more than
+        // log2(kFaBound / 16): then m moves to the row's maximum, the accumulator and
+        // sum are rescaled, and the weights are taken again. None of them then exceeds
+        // 1 (up to rounding), so the second pass stands. A row that sees no token (m
+        // still -inf: its position lies before the context, which is shorter than the
+        // chunk) takes its weights against 0, so that its masked scores give zeros
+        // instead of NaN.
+        if (__any(!(ps <= kFaBound))) {
+            float mraw = kNegInf;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, sc[v]);
+            const float mn = fmaxf(m, max_xor32(mraw) * scale_log2);
             const float alpha = (m == kNegInf) ? 0.f : fast_exp2(m - mn);
             lsum *= alpha;
 #pragma unroll
             for (int dt = 0; dt < kD / 32; ++dt) acc[dt] *= alpha;
             m = mn;
+            weights(m == kNegInf ? 0.f : m);
         }
-        const float mu = (m == kNegInf) ? 0.f : m;
-        uint2 pb[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            float p[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(sc[4 * s + e], scale_log2, -mu));
-            pb[s] = make_uint2(Mma<T>::pack(p[0], p[1]), Mma<T>::pack(p[2], p[3]));
-        }
-        // The row sum adds the weights as rounded for the PV product (a dot product
-        // with ones per packed pair: half the instructions of the float adds), so the
-        // numerator and the denominator see the same weights. Two partial sums keep
-        // the chain short.
-        float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            ps0 = Mma<T>::add_pair(pb[s].x, ps0);
-            ps1 = Mma<T>::add_pair(pb[s].y, ps1);
-        }
-        lsum += ps0 + ps1;
+        lsum += ps;
         // PV on 32x32x16 products over 16 tokens each. The k order inside a product is
         // free as long as both operands use it: lane l supplies its own score registers
         // (tokens 16s + 4h + 0..3 and 16s + 8 + 4h + 0..3), and the V operand is read in
