@@ -432,10 +432,10 @@ __device__ __forceinline__ uint4 k_operand(const KTile& kt, int kk, int lane) {
     return kt.chunk[c][(4 * kk + grp) ^ c];
 }
 
-// How far (base 2) a block's scores may pass a column's reference maximum before the
-// reference moves: weights stay at most 2^8, far inside the range of binary32 sums and
-// of the bfloat16 / float16 operands of the PV product.
-constexpr float kLazyMax = 8.f;
+// Largest sum of one lane's 4 weights of a block that stands: each weight then lies at
+// most this far above the column's reference (2^8), far inside the range of binary32
+// sums and of the bfloat16 / float16 operands of the PV product.
+constexpr float kWeightBound = 256.f;
 
 // The query-dependent half of a fold: scores of one 16-column tile against the block's
 // K operand `ka` (k_operand order), masked to the first `lim` tokens for the lane's
@@ -449,20 +449,30 @@ __device__ __forceinline__ void fold_tile(WaveState& s, const uint4 (&ka)[4],
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc = Mma<T>::qk(ka[i], qv[i], sc);
     float x[4];
-    float mb = kNegInf;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        x[e] = (4 * grp + e < lim) ? sc[e] * scale_log2 : kNegInf;
-        mb = fmaxf(mb, x[e]);
-    }
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = max_xor32(mb);
-    // s.m is a reference maximum, moved only when a block's maximum passes it by more
-    // than kLazyMax (base-2 units), so weights stay below 2^kLazyMax. Most blocks leave
-    // it in place: their rescale factor would be exactly 1, and the wave skips the
-    // rescale of o (a wave-uniform branch). The result is the same ratio o / l.
-    if (__ballot(mb > s.m + kLazyMax) != 0) {
-        const float mn = mb > s.m + kLazyMax ? mb : s.m;
+    for (int e = 0; e < 4; ++e) x[e] = (4 * grp + e < lim) ? sc[e] * scale_log2 : kNegInf;
+    // Weights against the column's reference s.m (the final ratio o / l cancels it).
+    // A lane's sum of its 4 weights bounds each of them, so a sum within kWeightBound
+    // keeps the reference in place with no column maximum taken (most blocks). It fails
+    // (also as infinity or NaN on a column's first block, s.m = -inf) when some score
+    // passes the reference by more than log2(kWeightBound / 4): then the reference
+    // moves to the column's maximum, o and l are rescaled (a wave-uniform branch), and
+    // the weights are taken again, at most 1 each (up to rounding), so that pass
+    // stands. Either way the reference stays within 8 (base 2) below the maximum of
+    // the scores so far, as the merges of partial results assume.
+    float p[4];
+    float ps;
+    auto weights = [&](float mu) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(x[e] - mu);
+        ps = (p[0] + p[1]) + (p[2] + p[3]);
+    };
+    weights(s.m);
+    if (__ballot(!(ps <= kWeightBound)) != 0) {
+        float mb = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mb = fmaxf(mb, __shfl_xor(mb, 16));
+        mb = max_xor32(mb);
+        const float mn = fmaxf(s.m, mb);
         const float alpha = (s.m == kNegInf) ? 0.f : fast_exp2(s.m - mn);
         s.lsum *= alpha;
         s.m = mn;
@@ -473,14 +483,8 @@ __device__ __forceinline__ void fold_tile(WaveState& s, const uint4 (&ka)[4],
 #pragma unroll
             for (int n = 0; n < 8; ++n) s.o[n][e] *= a;
         }
-    }
-    const float mu = (s.m == kNegInf) ? 0.f : s.m;
-    float p[4];
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        p[e] = fast_exp2(x[e] - mu);
-        ps += p[e];
+        // a column with no token yet in view takes its weights against 0 (zeros, not NaN)
+        weights(mn == kNegInf ? 0.f : mn);
     }
     s.lsum += ps;
     const uint2 pa = make_uint2(Mma<T>::pack(p[0], p[1]), Mma<T>::pack(p[2], p[3]));
